@@ -1,0 +1,295 @@
+"""Pins for the CPU oracle: each checks it against something other than itself.
+
+Closed forms (RoPE angles), identities the pages state (absorption by
+associativity, softmax normalisation, RoPE relative position), a textbook
+attention routine (torch scaled_dot_product_attention in fp64), brute force
+on tiny inputs, special cases with known answers, the constants the pages
+print (tests/golden/mla_constants.json) and a library fp8 cast.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mla_constants.json")
+
+
+def _rand(rng, *shape, std=1.0):
+    return rng.standard_normal(shape) * std
+
+
+def _tiny(rng, H=3, L=9):
+    return dict(
+        q_c=_rand(rng, H, 128), q_r=_rand(rng, H, 64), c_kv=_rand(rng, L, 512), k_r=_rand(rng, L, 64),
+        w_uk=_rand(rng, H, 128, 512, std=512 ** -0.5), w_uv=_rand(rng, H, 128, 512, std=512 ** -0.5))
+
+
+# --------------------------------------------------------------------------- constants
+
+def test_constants_match_pages():
+    g = {k: v["value"] for k, v in json.load(open(GOLDEN)).items() if not k.startswith("_")}
+    assert orc.D_C == g["kv_lora_rank"]
+    assert orc.D_R == g["qk_rope_head_dim"]
+    assert orc.D_H == g["qk_nope_head_dim"]
+    assert orc.D_V == g["v_head_dim"]
+    assert orc.D_H + orc.D_R == g["qk_total_dim"]
+    assert orc.ROW == g["cached_elements_per_token_mla"] == orc.D_C + orc.D_R
+    # standard MHA caches K and V for 128 heads of 192 / 128 ... the page's count is 2*128*192
+    assert 2 * 128 * (orc.D_H + orc.D_R) == g["cached_elements_per_token_mha"]
+    assert round(g["cached_elements_per_token_mha"] / orc.ROW) == g["compression_ratio_approx"]
+    kb = orc.ROW * g["layers"] * 2 / 1000.0  # 2-byte elements, kB
+    assert abs(kb - g["kv_cache_per_token_all_layers_kb_approx"]) < 1.0
+    assert orc.E4M3_MAX == g["e4m3_max"]
+    assert orc.FP8_TILE == g["fp8_activation_tile"]
+    assert math.isclose(orc.default_softmax_scale(), 1.0 / math.sqrt(g["qk_total_dim"]), rel_tol=0, abs_tol=0)
+    theta = orc.rope_frequencies(64, g["rope_base"])
+    assert theta[0] == 1.0 and math.isclose(theta[16], 0.01, rel_tol=1e-15)
+
+
+# --------------------------------------------------------------------------- RoPE
+
+def test_rope_closed_form_angles():
+    # unit vector in pair m, rotated at position p, lands at (cos p*theta_m, sin p*theta_m)
+    for m, p in [(0, 1), (0, 5), (16, 100), (31, 12345), (7, 63)]:
+        x = np.zeros(64)
+        x[2 * m] = 1.0
+        th = 10000.0 ** (-2.0 * m / 64.0)
+        y = orc.rope(x, p)
+        exp = np.zeros(64)
+        exp[2 * m], exp[2 * m + 1] = math.cos(p * th), math.sin(p * th)
+        np.testing.assert_allclose(y, exp, atol=1e-12)
+        # the odd element rotates to (-sin, cos)
+        x = np.zeros(64)
+        x[2 * m + 1] = 1.0
+        y = orc.rope(x, p)
+        exp = np.zeros(64)
+        exp[2 * m], exp[2 * m + 1] = -math.sin(p * th), math.cos(p * th)
+        np.testing.assert_allclose(y, exp, atol=1e-12)
+    # pair 16 at position 100 turns by exactly 1 radian
+    x = np.zeros(64)
+    x[32] = 2.0
+    y = orc.rope(x, 100)
+    assert math.isclose(y[32], 2 * math.cos(1.0), rel_tol=1e-12) and math.isclose(y[33], 2 * math.sin(1.0), rel_tol=1e-12)
+
+
+def test_rope_identity_norm_and_relative_position():
+    rng = np.random.default_rng(1)
+    x, y = rng.standard_normal(64), rng.standard_normal(64)
+    np.testing.assert_array_equal(orc.rope(x, 0), x)  # RoPE_0 = I
+    for p in [1, 17, 4095, 131071]:
+        assert math.isclose(np.linalg.norm(orc.rope(x, p)), np.linalg.norm(x), rel_tol=1e-12)
+    # <RoPE_m x, RoPE_n y> depends only on n - m ("DeepSeek-V3" notes, §RoPE 数据流: R_t^T R_j)
+    for m, n, k in [(3, 10, 5), (0, 100, 1000), (63, 0, 77), (5000, 131071, 13)]:
+        a = orc.rope(x, m) @ orc.rope(y, n)
+        b = orc.rope(x, m + k) @ orc.rope(y, n + k)
+        assert math.isclose(a, b, rel_tol=1e-9, abs_tol=1e-9)
+    # ... and does depend on n - m (so positions are not ignored)
+    assert abs(orc.rope(x, 0) @ orc.rope(y, 1) - orc.rope(x, 0) @ orc.rope(y, 2)) > 1e-3
+
+
+# --------------------------------------------------------------------------- attention
+
+def test_absorbed_equals_expanded():
+    rng = np.random.default_rng(2)
+    for H, L in [(1, 1), (3, 9), (4, 70), (2, 200)]:
+        d = _tiny(rng, H, L)
+        e = orc.decode_sequence(**d)
+        a = orc.decode_sequence_absorbed(**d)
+        for k in ("o", "z", "lse"):
+            scale = max(1.0, np.abs(e[k]).max())
+            assert np.abs(e[k] - a[k]).max() <= 1e-12 * scale, k
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(3)
+    d = _tiny(rng, 4, 50)
+    r = orc.decode_sequence(**d, return_probs=True)
+    np.testing.assert_allclose(r["probs"].sum(axis=1), 1.0, atol=1e-12)
+    assert (r["probs"] >= 0).all()
+    # lse is log-sum-exp of the scaled scores
+    q_t = orc.absorb_query(d["q_c"], d["w_uk"])
+    s = (q_t @ d["c_kv"].T + orc.rope(d["q_r"], 49) @ orc.rope(d["k_r"], np.arange(50)).T) / math.sqrt(192)
+    np.testing.assert_allclose(r["lse"], np.log(np.exp(s).sum(axis=1)), rtol=1e-12)
+
+
+def _sdpa_inputs(d, q_pos, k_pos):
+    H = d["q_c"].shape[0]
+    q = np.concatenate([d["q_c"], orc.rope(d["q_r"], q_pos)], axis=-1)  # [H,192] or [T,H,192]
+    k_r = orc.rope(d["k_r"], k_pos)
+    ks, vs = [], []
+    for i in range(H):
+        ks.append(np.concatenate([d["c_kv"] @ d["w_uk"][i].T, k_r], axis=-1))
+        vs.append(d["c_kv"] @ d["w_uv"][i].T)
+    return q, np.stack(ks), np.stack(vs)
+
+
+def test_expanded_matches_torch_sdpa_decode():
+    rng = np.random.default_rng(4)
+    for H, L in [(3, 9), (5, 64), (2, 129)]:
+        d = _tiny(rng, H, L)
+        r = orc.decode_sequence(**d)
+        q, k, v = _sdpa_inputs(d, L - 1, np.arange(L))
+        out = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[:, None, :], torch.from_numpy(k), torch.from_numpy(v))  # default scale 1/sqrt(192)
+        np.testing.assert_allclose(r["o"], out[:, 0, :].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_expanded_matches_torch_sdpa_causal_prefill():
+    rng = np.random.default_rng(5)
+    T, H = 37, 3
+    d = dict(q_c=_rand(rng, T, H, 128), q_r=_rand(rng, T, H, 64), c_kv=_rand(rng, T, 512),
+             k_r=_rand(rng, T, 64), w_uk=_rand(rng, H, 128, 512, std=512 ** -0.5),
+             w_uv=_rand(rng, H, 128, 512, std=512 ** -0.5))
+    r = orc.prefill_causal(**d)
+    q = np.concatenate([d["q_c"], orc.rope(d["q_r"], np.arange(T)[:, None])], axis=-1)  # [T,H,192]
+    _, k, v = _sdpa_inputs(dict(d, q_c=d["q_c"][0], q_r=d["q_r"][0]), 0, np.arange(T))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), torch.from_numpy(k), torch.from_numpy(v), is_causal=True)
+    np.testing.assert_allclose(r["o"], out.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["k_r_rot"], orc.rope(d["k_r"], np.arange(T)), atol=0)
+
+
+def test_bruteforce_triple_loop():
+    """Scalar loops with math.exp on B=2, H=3, L<=17 (no NumPy linear algebra)."""
+    rng = np.random.default_rng(6)
+    for L in [1, 5, 17]:
+        d = _tiny(rng, 3, L)
+        r = orc.decode_sequence(**d)
+        for i in range(3):
+            def rot(vec, pos):
+                out = [0.0] * 64
+                for m in range(32):
+                    ang = pos * 10000.0 ** (-2.0 * m / 64.0)
+                    x0, x1 = vec[2 * m], vec[2 * m + 1]
+                    out[2 * m] = x0 * math.cos(ang) - x1 * math.sin(ang)
+                    out[2 * m + 1] = x0 * math.sin(ang) + x1 * math.cos(ang)
+                return out
+            qr = rot(d["q_r"][i], L - 1)
+            scores = []
+            for j in range(L):
+                kc = [sum(d["w_uk"][i][a][c] * d["c_kv"][j][c] for c in range(512)) for a in range(128)]
+                kr = rot(d["k_r"][j], j)
+                s = sum(d["q_c"][i][a] * kc[a] for a in range(128)) + sum(qr[a] * kr[a] for a in range(64))
+                scores.append(s / math.sqrt(192.0))
+            mx = max(scores)
+            w = [math.exp(s - mx) for s in scores]
+            tot = sum(w)
+            o = [0.0] * 128
+            for j in range(L):
+                vc = [sum(d["w_uv"][i][a][c] * d["c_kv"][j][c] for c in range(512)) for a in range(128)]
+                for a in range(128):
+                    o[a] += w[j] / tot * vc[a]
+            np.testing.assert_allclose(r["o"][i], o, rtol=1e-9, atol=1e-12)
+
+
+def test_special_cases():
+    rng = np.random.default_rng(7)
+    # one cached token: o = W_UV c_0 regardless of the query
+    d = _tiny(rng, 4, 1)
+    r = orc.decode_sequence(**d)
+    np.testing.assert_allclose(r["o"], np.einsum("hdc,c->hd", d["w_uv"], d["c_kv"][0]), atol=1e-13)
+    np.testing.assert_allclose(r["z"], np.broadcast_to(d["c_kv"][0], (4, 512)), atol=0)
+    # zero query: uniform weights, o = W_UV mean(c)
+    d = _tiny(rng, 3, 23)
+    d["q_c"][:] = 0
+    d["q_r"][:] = 0
+    r = orc.decode_sequence(**d)
+    np.testing.assert_allclose(r["o"], np.einsum("hdc,c->hd", d["w_uv"], d["c_kv"].mean(axis=0)), atol=1e-13)
+    np.testing.assert_allclose(r["lse"], math.log(23.0), atol=1e-13)
+    # identical cached rows (content and position both): output independent of the query
+    d = _tiny(rng, 3, 11)
+    d["c_kv"][:] = d["c_kv"][0]
+    d["k_r"][:] = 0
+    r1 = orc.decode_sequence(**d)
+    d["q_c"] = _rand(rng, 3, 128) * 5
+    r2 = orc.decode_sequence(**d)
+    np.testing.assert_allclose(r1["o"], r2["o"], atol=1e-13)
+
+
+def test_prefill_row_equals_decode_at_length_t_plus_1():
+    rng = np.random.default_rng(8)
+    T, H = 20, 2
+    d = dict(q_c=_rand(rng, T, H, 128), q_r=_rand(rng, T, H, 64), c_kv=_rand(rng, T, 512),
+             k_r=_rand(rng, T, 64), w_uk=_rand(rng, H, 128, 512, std=512 ** -0.5),
+             w_uv=_rand(rng, H, 128, 512, std=512 ** -0.5))
+    rows = [0, 1, 7, 19]
+    p = orc.prefill_causal(**d, rows=rows)
+    for n, t in enumerate(rows):
+        r = orc.decode_sequence(d["q_c"][t], d["q_r"][t], d["c_kv"][: t + 1], d["k_r"][: t + 1], d["w_uk"], d["w_uv"])
+        for k in ("o", "z", "lse", "q_abs"):
+            np.testing.assert_allclose(p[k][n], r[k], rtol=1e-13, atol=1e-13)
+
+
+def test_split_merge_identity():
+    """Attention over a split key set, merged by log-sum-exp weights, equals the
+    unsplit result (the softmax identity the split-KV path relies on)."""
+    rng = np.random.default_rng(9)
+    d = _tiny(rng, 3, 40)
+    full = orc.decode_sequence_absorbed(**d)
+    # split keys [0,13) and [13,40): compute each part's normalised z and lse with the same query
+    q_t = orc.absorb_query(d["q_c"], d["w_uk"])
+    qr = orc.rope(d["q_r"], 39)
+    kr = orc.rope(d["k_r"], np.arange(40))
+    s = (q_t @ d["c_kv"].T + qr @ kr.T) / math.sqrt(192)
+    parts = []
+    for lo, hi in [(0, 13), (13, 40)]:
+        ss = s[:, lo:hi]
+        m = ss.max(axis=1, keepdims=True)
+        e = np.exp(ss - m)
+        parts.append((e @ d["c_kv"][lo:hi] / e.sum(axis=1, keepdims=True), m[:, 0] + np.log(e.sum(axis=1))))
+    lse = np.logaddexp(parts[0][1], parts[1][1])
+    z = sum(np.exp(l - lse)[:, None] * zz for zz, l in parts)
+    np.testing.assert_allclose(z, full["z"], atol=1e-12)
+    np.testing.assert_allclose(lse, full["lse"], atol=1e-12)
+
+
+# --------------------------------------------------------------------------- fp8
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(ours) == nan).all()
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+
+
+def test_quantiser_matches_torch_cast_bit_exact():
+    rng = np.random.default_rng(10)
+    c = rng.standard_normal((300, 512)).astype(np.float32)
+    c[5, :128] = 0.0  # all-zero tile
+    c[6, 128:256] *= 1e-30  # tiny tile (subnormal range after scaling is avoided by the per-tile scale)
+    c[7] = np.float32(3.0)  # constant row
+    codes, scales = orc.quantize_latent_e4m3(c)
+    assert codes.dtype == np.uint8 and scales.dtype == np.float32 and scales.shape == (300, 4)
+    assert scales[5, 0] == 1.0 and (codes[5, :128] == 0).all()
+    # library routine: scale and clamp in fp32, then torch's round-to-nearest-even cast
+    t = torch.from_numpy(c).view(300, 4, 128)
+    amax = t.abs().amax(dim=2)
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    assert torch.equal(sc, torch.from_numpy(scales))
+    x = (t / sc[:, :, None]).clamp(-448.0, 448.0)
+    ref = x.to(torch.float8_e4m3fn).view(torch.uint8).view(300, 512).numpy()
+    np.testing.assert_array_equal(codes, ref)
+    # each tile's largest magnitude maps to +-448
+    big = np.abs(orc.e4m3_decode(codes)).reshape(300, 4, 128).max(axis=2)
+    assert (big[amax.numpy() > 0] == 448.0).all()
+
+
+def test_quantiser_error_bound():
+    rng = np.random.default_rng(11)
+    c = rng.standard_normal((64, 512)).astype(np.float32)
+    codes, scales = orc.quantize_latent_e4m3(c)
+    dq = orc.dequantize_latent_e4m3(codes, scales)
+    s = np.repeat(scales.astype(np.float64), 128, axis=1)
+    normal = np.abs(c) / s >= 2.0 ** -6
+    rel = np.abs(dq - c)[normal] / np.abs(c)[normal]
+    assert rel.max() <= 2.0 ** -4 + 1e-12  # half a unit in the last place of a 3-bit mantissa
+    assert np.abs(dq - c)[~normal].max() <= (2.0 ** -10 * s[~normal]).max() * (1 + 1e-9)
