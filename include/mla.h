@@ -1,0 +1,202 @@
+/*
+ * mla.h — C interface of libmla: absorbed Multi-head Latent Attention (MLA)
+ * over a paged latent KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the "DeepSeek-V3" equation notes, ekkoxiao.github.io):
+ *   - each cached token keeps only (c^KV, k^R): a 512-element joint latent
+ *     and a 64-element RoPE key shared by all heads (§KeyValue);
+ *   - per head i the content key is k^C = W_i^UK c^KV; absorbing W_i^UK into
+ *     the query gives q~_i = (W_i^UK)^T q_i^C, so the content score is
+ *     q~_i . c^KV (§潜在向量的作用);
+ *   - s = (q~_i . c_j + q_i^R . k_j^R) * scale, softmax over the visible
+ *     tokens j, and the values are summed in latent space,
+ *     z_i = sum_j a_{ij} c_j, before the up-projection o_i = W_i^UV z_i
+ *     (§注意力计算 and §潜在向量的作用).
+ *
+ * Dimensions are fixed by the model ("DeepSeek-V3 技术报告精读",
+ * oopvo.github.io, §维度分解详解): d_c = 512, rope 64, nope 128, v 128.
+ * A cached row is 576 elements: c^KV (512) followed by the *rotated* k^R (64).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are device pointers owned by the caller, dense and
+ *     row-major in the shapes given.  The library allocates no memory and
+ *     keeps no state except a per-device property cache.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Arguments are validated on the host before any HIP call; a
+ *     rejected call launches nothing and returns its status synchronously.
+ *   - A kernel launch failure returns MLA_ERR_HIP.  Faults during execution
+ *     surface at the caller's next synchronisation.  No C++ exception
+ *     crosses this interface.
+ *   - RoPE rotates interleaved pairs (x[2m], x[2m+1]) counter-clockwise by
+ *     pos * theta_m with theta_m = rope_base^(-2m/64), m = 0..31 (per-pair
+ *     angle of §YaRN 扩展; frequency formula of "企业官网建设流程全解析",
+ *     discosf.com, §4.3).  rope_base is 10000 for DeepSeek-V3.
+ *   - softmax_scale is 1/sqrt(128 + 64) for the model (§注意力计算); it
+ *     multiplies the raw dot product before the exponential.
+ *   - Entry points are reentrant; concurrent calls on different streams are
+ *     safe as long as their output and workspace buffers do not overlap.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad dtype combination */
+  MLA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement    */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed      */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,      /* IEEE fp32                                             */
+  MLA_BF16 = 1,     /* bfloat16                                              */
+  MLA_FP8_E4M3 = 2  /* OCP E4M3 (max 448), only for the cached latent c^KV  */
+} mla_dtype;
+
+#define MLA_D_C 512
+#define MLA_D_R 64
+#define MLA_D_NOPE 128
+#define MLA_D_V 128
+#define MLA_ROW 576
+#define MLA_PAGE 64
+#define MLA_MAX_HEADS 128
+
+/*
+ * Paged latent cache.  A pool of `num_pages` pages of 64 token slots; a
+ * sequence's block-table row lists the pool page of each of its 64-token
+ * blocks.  Layout by dtype:
+ *   MLA_F32, MLA_BF16: rows      [num_pages][64][576]  (c^KV | rotated k^R)
+ *   MLA_FP8_E4M3:      ckv_fp8   [num_pages][64][512]  e4m3 codes of c^KV
+ *                      ckv_scale [num_pages][64][4]    fp32, one per 128
+ *                                                      channels of a token
+ *                      kr        [num_pages][64][64]   bf16 rotated k^R
+ * The fp8 form follows the 1x128 per-token tile rule ("DeepSeek-V3 Technical
+ * Report", process-cxr.github.io, §Fine-grained quantization): for each token
+ * and 128-channel tile, scale = amax/448 in fp32 (1 for an all-zero tile) and
+ * code = e4m3(round-to-nearest-even(clamp(c/scale, -448, 448))).
+ * Unused pointers for a dtype must be NULL.  page_size must be 64.
+ */
+typedef struct {
+  int32_t dtype;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t reserved;
+  void* rows;
+  void* ckv_fp8;
+  float* ckv_scale;
+  void* kr;
+} mla_cache;
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(int32_t status);
+
+/*
+ * mla_absorb_q — the absorbed query (§潜在向量的作用: q~_i = (W_i^UK)^T q_i^C)
+ * and the rotated position query (§Query: q^R = RoPE_t(...)).
+ *   q_c   [N][H][128]   content query (dtype)
+ *   q_r   [N][H][64]    position query before rotation (dtype)
+ *   pos   [N] int32     position of each query token (>= 0)
+ *   w_uk  [H][128][512] head i's row block of the key up-projection (dtype)
+ *   q_abs [N][H][576]   out: q~ (512) followed by RoPE_pos(q_r) (64) (dtype)
+ *   dtype MLA_F32 (fp32 throughout) or MLA_BF16 (bf16 in/out, fp32 accumulate)
+ * Errors: MLA_ERR_INVALID_ARG for N < 1, H not in [1,128], a NULL pointer or
+ * another dtype.
+ */
+mla_status mla_absorb_q(const void* q_c, const void* q_r, const int32_t* pos, const void* w_uk,
+                        void* q_abs, int32_t N, int32_t H, int32_t dtype, float rope_base,
+                        void* stream);
+
+/*
+ * mla_cache_write — store T tokens' (c^KV, RoPE_pos(k^R)) into the pool
+ * (§KeyValue: only c^KV and the rotated k^R are cached).
+ *   c_kv [T][512], k_r [T][64] (before rotation), in `in_dtype`
+ *   pos  [T] int32   position of each token (the k^R rotation angle)
+ *   slot [T] int32   pool row = page*64 + offset, in [0, num_pages*64)
+ * Combinations: in MLA_F32 -> cache MLA_F32; in MLA_BF16 -> cache MLA_BF16
+ * or MLA_FP8_E4M3 (quantised as described at mla_cache).  Slots must be
+ * distinct; rows not named by `slot` are left untouched.
+ */
+mla_status mla_cache_write(const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* slot,
+                           int32_t T, int32_t in_dtype, const mla_cache* cache, float rope_base,
+                           void* stream);
+
+/*
+ * Workspace bytes mla_decode needs for B sequences, H heads and
+ * `num_splits` (0 = automatic).  Depends only on its arguments and the
+ * current device's compute-unit count.
+ */
+size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits);
+
+/*
+ * mla_decode — one new query token per sequence attends to all of its
+ * cached tokens: scores (§注意力计算 with the absorbed content term of
+ * §潜在向量的作用), softmax over the sequence, latent-space accumulation
+ * z_i = sum_j a_{ij} c_j.  Long sequences are split into chunks whose
+ * partial (z, log-sum-exp) pairs are merged exactly by log-sum-exp weights.
+ *   q_abs        [B][H][576]  from mla_absorb_q (fp32 for an fp32 cache,
+ *                             bf16 for a bf16 or fp8 cache)
+ *   cache        the pool (see mla_cache)
+ *   block_table  [B][max_pages] int32 pool page of each 64-token block
+ *   seq_lens     [B] int32 cached tokens per sequence, 1 <= L <= 64*max_pages
+ *                (the query is the newest of them)
+ *   num_splits   0: the library balances the pages of all sequences over
+ *                the device's compute units (a chunk may span sequences);
+ *                S > 0: sequence b is cut into S chunks of
+ *                ceil(ceil(L_b/64)/S) pages (trailing chunks may be empty).
+ *   workspace    device scratch of at least mla_decode_workspace_size bytes
+ *   z            [B][H][512] fp32 out: normalised latent aggregate
+ *   lse          [B][H] fp32 out (may be NULL): natural-log log-sum-exp of
+ *                the scaled scores
+ * seq_lens is device memory and is not inspected on the host: lengths of 0
+ * or beyond 64*max_pages are undefined behaviour.
+ * Errors: MLA_ERR_INVALID_ARG (NULL, B < 1, H not in [1,128], max_pages < 1,
+ * page_size != 64, softmax_scale not finite and > 0, num_splits < 0 or
+ * > 256, a pointer missing for the cache dtype); MLA_ERR_WORKSPACE.
+ */
+mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                      const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages,
+                      float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
+                      float* z, float* lse, void* stream);
+
+/*
+ * mla_prefill_causal — T new tokens of one sequence, at positions
+ * pos0 .. pos0+T-1, are written into the cache and attend causally: query t
+ * sees cached tokens 0 .. pos0+t inclusive (§注意力计算 sums up to the
+ * current position).  pos0 tokens must already be in the cache.
+ *   q_abs           [T][H][576] from mla_absorb_q with pos = pos0 + t
+ *   c_kv, k_r       [T][512], [T][64] the new tokens (k_r before rotation)
+ *   cache           the pool (bf16 or fp32 rows)
+ *   block_table_row [ceil((pos0+T)/64)] int32 pool pages of the sequence
+ *   z               [T][H][512] fp32 out; lse [T][H] fp32 out or NULL
+ * dtype of q_abs, c_kv, k_r follows the cache (fp32 or bf16).
+ * Errors: MLA_ERR_INVALID_ARG as for mla_decode; MLA_ERR_UNSUPPORTED for an
+ * fp8 cache.
+ */
+mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
+                              const mla_cache* cache, const int32_t* block_table_row, int32_t T,
+                              int32_t H, float softmax_scale, float rope_base, float* z, float* lse,
+                              void* stream);
+
+/*
+ * mla_upproj_v — o_i = W_i^UV z_i (§潜在向量的作用, value up-projection).
+ *   z    [N][H][512] fp32
+ *   w_uv [H][128][512] head i's row block of the value up-projection (w_dtype)
+ *   o    [N][H][128] out (o_dtype)
+ * w_dtype, o_dtype in {MLA_F32, MLA_BF16}; a bf16 weight makes the product run
+ * on bf16 matrix cores (z rounded to bf16, fp32 accumulation).
+ */
+mla_status mla_upproj_v(const float* z, const void* w_uv, void* o, int32_t N, int32_t H, int32_t w_dtype,
+                        int32_t o_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

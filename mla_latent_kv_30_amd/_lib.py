@@ -1,0 +1,269 @@
+"""ctypes binding of libmla (include/mla.h): argument marshalling only.
+
+Every entry point takes torch tensors that already live on the GPU, checks
+their dtype, shape and contiguity, and passes raw device pointers plus the
+current HIP stream to the C library.  Nothing here computes any part of the
+attention; if libmla.so is missing the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mla.h")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+D_C, D_R, D_NOPE, D_V, ROW, PAGE = 512, 64, 128, 128, 576, 64
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+
+class MlaCache(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("num_pages", _i32), ("page_size", _i32), ("reserved", _i32),
+                ("rows", _vp), ("ckv_fp8", _vp), ("ckv_scale", _vp), ("kr", _vp)]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla.so (built in-tree by mla_latent_kv_30_amd.build)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_30_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_status_string.argtypes = [_i32]
+    L.mla_absorb_q.restype = _i32
+    L.mla_absorb_q.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _vp]
+    L.mla_cache_write.restype = _i32
+    L.mla_cache_write.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(MlaCache), _f32, _vp]
+    L.mla_decode_workspace_size.restype = ctypes.c_size_t
+    L.mla_decode_workspace_size.argtypes = [_i32, _i32, _i32]
+    L.mla_decode.restype = _i32
+    L.mla_decode.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp,
+                             ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_prefill_causal.restype = _i32
+    L.mla_prefill_causal.argtypes = [_vp, _vp, _vp, _i32, ctypes.POINTER(MlaCache), _vp, _i32, _i32, _f32, _f32,
+                                     _vp, _vp, _vp]
+    L.mla_upproj_v.restype = _i32
+    L.mla_upproj_v.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+    _LIB = L
+    return L
+
+
+def declared_symbols() -> list:
+    """Names of the functions include/mla.h declares."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(mla_\w+)\s*\(", txt, flags=re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MLA_OK:
+        raise MLAError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dt_code(dtype) -> int:
+    if dtype == torch.float32:
+        return MLA_F32
+    if dtype == torch.bfloat16:
+        return MLA_BF16
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def default_softmax_scale() -> float:
+    return 1.0 / math.sqrt(D_NOPE + D_R)
+
+
+class PagedCache:
+    """A pool of 64-token pages holding each cached token's (c_KV, rotated k_R).
+
+    dtype torch.float32 / torch.bfloat16: rows [num_pages, 64, 576].
+    dtype "fp8": ckv [num_pages, 64, 512] uint8 (E4M3 codes),
+    scale [num_pages, 64, 4] float32, kr [num_pages, 64, 64] bfloat16.
+    `fill` initialises the storage (e.g. float('nan') to poison unused slots).
+    """
+
+    def __init__(self, num_pages: int, dtype, device="cuda", fill: Optional[float] = None):
+        self.num_pages = int(num_pages)
+        self.device = torch.device(device)
+        self.rows = self.ckv = self.scale = self.kr = None
+        if dtype == "fp8":
+            self.code = MLA_FP8_E4M3
+            self.ckv = torch.empty((num_pages, PAGE, D_C), dtype=torch.uint8, device=device)
+            self.scale = torch.empty((num_pages, PAGE, 4), dtype=torch.float32, device=device)
+            self.kr = torch.empty((num_pages, PAGE, D_R), dtype=torch.bfloat16, device=device)
+            if fill is not None:
+                self.ckv.fill_(0x7F if math.isnan(fill) else 0)  # 0x7F is an E4M3 NaN
+                self.scale.fill_(fill)
+                self.kr.fill_(fill)
+        else:
+            self.code = _dt_code(dtype)
+            self.rows = torch.empty((num_pages, PAGE, ROW), dtype=dtype, device=device)
+            if fill is not None:
+                self.rows.fill_(fill)
+
+    @property
+    def is_fp8(self) -> bool:
+        return self.code == MLA_FP8_E4M3
+
+    @property
+    def input_dtype(self):
+        return torch.float32 if self.code == MLA_F32 else torch.bfloat16
+
+    def descriptor(self) -> MlaCache:
+        return MlaCache(self.code, self.num_pages, PAGE, 0, _ptr(self.rows), _ptr(self.ckv), _ptr(self.scale),
+                        _ptr(self.kr))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.rows, self.ckv, self.scale, self.kr) if t is not None)
+
+
+def absorb_q(q_c: torch.Tensor, q_r: torch.Tensor, pos: torch.Tensor, w_uk: torch.Tensor,
+             out: Optional[torch.Tensor] = None, rope_base: float = 10000.0) -> torch.Tensor:
+    """q_abs[N,H,576] = [W_UK^T q_C | RoPE_pos(q_R)] (mla_absorb_q)."""
+    N, H = q_c.shape[0], q_c.shape[1]
+    dt = q_c.dtype
+    _need(q_c, "q_c", dt, (N, H, D_NOPE))
+    _need(q_r, "q_r", dt, (N, H, D_R))
+    _need(pos, "pos", torch.int32, (N,))
+    _need(w_uk, "w_uk", dt, (H, D_NOPE, D_C))
+    if out is None:
+        out = torch.empty((N, H, ROW), dtype=dt, device=q_c.device)
+    _need(out, "out", dt, (N, H, ROW))
+    _check(lib().mla_absorb_q(_ptr(q_c), _ptr(q_r), _ptr(pos), _ptr(w_uk), _ptr(out), N, H, _dt_code(dt),
+                              float(rope_base), _stream(q_c.device)), "mla_absorb_q")
+    return out
+
+
+def cache_write(cache: PagedCache, c_kv: torch.Tensor, k_r: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor,
+                rope_base: float = 10000.0) -> None:
+    """Store T tokens' (c_KV, RoPE_pos(k_R)) at pool rows `slot` (mla_cache_write)."""
+    T = c_kv.shape[0]
+    dt = cache.input_dtype
+    _need(c_kv, "c_kv", dt, (T, D_C))
+    _need(k_r, "k_r", dt, (T, D_R))
+    _need(pos, "pos", torch.int32, (T,))
+    _need(slot, "slot", torch.int32, (T,))
+    desc = cache.descriptor()
+    _check(lib().mla_cache_write(_ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(slot), T, _dt_code(dt), ctypes.byref(desc),
+                                 float(rope_base), _stream(c_kv.device)), "mla_cache_write")
+
+
+def decode_workspace_size(B: int, H: int, num_splits: int = 0) -> int:
+    return int(lib().mla_decode_workspace_size(int(B), int(H), int(num_splits)))
+
+
+def decode(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+           softmax_scale: Optional[float] = None, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+           z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """z[B,H,512], lse[B,H] of one new token per sequence (mla_decode)."""
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    _need(q_abs, "q_abs", cache.input_dtype, (B, H, ROW))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    dev = q_abs.device
+    if z is None:
+        z = torch.empty((B, H, D_C), dtype=torch.float32, device=dev)
+    _need(z, "z", torch.float32, (B, H, D_C))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H))
+    need = decode_workspace_size(B, H, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
+    desc = cache.descriptor()
+    _check(lib().mla_decode(_ptr(q_abs), ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), B, H,
+                            block_table.shape[1], scale, int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
+                            _ptr(lse), _stream(dev)), "mla_decode")
+    return z, lse
+
+
+def prefill_causal(q_abs: torch.Tensor, c_kv: torch.Tensor, k_r: torch.Tensor, cache: PagedCache,
+                   block_table_row: torch.Tensor, pos0: int = 0, softmax_scale: Optional[float] = None,
+                   rope_base: float = 10000.0, z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   want_lse: bool = True):
+    """Append T tokens at positions pos0.. and attend causally (mla_prefill_causal)."""
+    T, H = q_abs.shape[0], q_abs.shape[1]
+    dt = cache.input_dtype
+    _need(q_abs, "q_abs", dt, (T, H, ROW))
+    _need(c_kv, "c_kv", dt, (T, D_C))
+    _need(k_r, "k_r", dt, (T, D_R))
+    _need(block_table_row, "block_table_row", torch.int32)
+    if block_table_row.numel() < (pos0 + T + PAGE - 1) // PAGE:
+        raise ValueError("block_table_row too short for pos0 + T tokens")
+    dev = q_abs.device
+    if z is None:
+        z = torch.empty((T, H, D_C), dtype=torch.float32, device=dev)
+    _need(z, "z", torch.float32, (T, H, D_C))
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
+    desc = cache.descriptor()
+    _check(lib().mla_prefill_causal(_ptr(q_abs), _ptr(c_kv), _ptr(k_r), int(pos0), ctypes.byref(desc),
+                                    _ptr(block_table_row), T, H, scale, float(rope_base), _ptr(z), _ptr(lse),
+                                    _stream(dev)), "mla_prefill_causal")
+    return z, lse
+
+
+def upproj_v(z: torch.Tensor, w_uv: torch.Tensor, out_dtype=torch.float32,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """o[N,H,128] = W_UV z per head (mla_upproj_v)."""
+    N, H = z.shape[0], z.shape[1]
+    _need(z, "z", torch.float32, (N, H, D_C))
+    _need(w_uv, "w_uv", None, (H, D_V, D_C))
+    if out is None:
+        out = torch.empty((N, H, D_V), dtype=out_dtype, device=z.device)
+    _need(out, "out", out_dtype, (N, H, D_V))
+    _check(lib().mla_upproj_v(_ptr(z), _ptr(w_uv), _ptr(out), N, H, _dt_code(w_uv.dtype), _dt_code(out_dtype),
+                              _stream(z.device)), "mla_upproj_v")
+    return out

@@ -1,0 +1,132 @@
+// Absorbed query: q~_i = (W_i^UK)^T q_i^C and the rotated position query
+// RoPE_pos(q_i^R) (the "DeepSeek-V3" notes, ekkoxiao.github.io,
+// §潜在向量的作用 and §Query).  Output row per (token, head): [q~ (512) | q^R' (64)].
+//
+// bf16 path: per head the product is [N x 128] x [128 x 512].  W_i^UK is
+// stored [128 d][512 c] (row block of the up-projection), so the contraction
+// index d is the slow one; a 128 x 128 slice of it is staged in LDS and the
+// gfx950 transposing LDS read hands the matrix cores d-packed operands.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+constexpr int kAbsRowsPerWave = 32;
+constexpr int kAbsRowsPerBlock = 4 * kAbsRowsPerWave;   // 128 query tokens per workgroup
+constexpr int kAbsCols = 128;                           // c-slice of W per workgroup
+constexpr int kAbsLdsStride = kAbsCols * 2 + 32;        // padded row stride (bytes): rows 8 banks apart
+
+// Rotate q_r of rows [n0, n0+rows) of head h into q_abs[..., 512:576].
+template <typename T>
+__device__ __forceinline__ void rope_rows(const AbsorbArgs& a, int h, int n0, int rows) {
+  const T* qr = (const T*)a.q_r;
+  T* out = (T*)a.q_abs;
+  for (int i = threadIdx.x; i < rows * 32; i += blockDim.x) {
+    const int n = n0 + i / 32, m = i % 32;
+    const size_t src = ((size_t)n * a.H + h) * kDr + 2 * m;
+    const float x0 = (float)qr[src], x1 = (float)qr[src + 1];
+    float c, s;
+    rope_cs(a.pos[n], a.rope.theta[m], c, s);
+    const size_t dst = ((size_t)n * a.H + h) * kRow + kDc + 2 * m;
+    out[dst] = (T)(x0 * c - x1 * s);
+    out[dst + 1] = (T)(x0 * s + x1 * c);
+  }
+}
+
+// grid: (H * 4 c-quarters, ceil(N / 128)); 4 waves, each 32 query rows x 128 c.
+__global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[kDn * kAbsLdsStride];  // W[d][c-slice]
+  const int h = blockIdx.x >> 2, cq = blockIdx.x & 3;
+  const int n_blk = blockIdx.y * kAbsRowsPerBlock;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bf16* w = (const bf16*)a.w_uk + (size_t)h * kDn * kDc + cq * kAbsCols;
+  // stage W[0:128][cq*128 : cq*128+128]: 128 rows of 256 bytes, padded stride
+  for (int i = threadIdx.x; i < kDn * (kAbsCols / 8); i += 256) {
+    const int d = i / (kAbsCols / 8), ch = i % (kAbsCols / 8);
+    *(int4v*)(w_lds + d * kAbsLdsStride + ch * 16) = *(const int4v*)(w + (size_t)d * kDc + ch * 8);
+  }
+  const int rows_here = min(kAbsRowsPerBlock, a.N - n_blk);
+  if (cq == 0) rope_rows<bf16>(a, h, n_blk, rows_here);
+  __syncthreads();
+  const int n0 = n_blk + wave * kAbsRowsPerWave;
+  if (n0 >= a.N) return;
+  const int g = lane >> 5;
+  // B operand: q_c^T (k = d, n = query row): lane holds row n0 + lane%32, d = 16kk + 8g + j
+  const int nrow = n0 + (lane & 31);
+  const bool nok = nrow < a.N;
+  const bf16* qc = (const bf16*)a.q_c + ((size_t)(nok ? nrow : n0) * a.H + h) * kDn;
+  bf16x8 qb[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    int4v v = *(const int4v*)(qc + 16 * kk + 8 * g);
+    if (!nok) v = int4v{0, 0, 0, 0};
+    qb[kk] = __builtin_bit_cast(bf16x8, v);
+  }
+  // A operand: W^T (m = c, k = d) by transposing reads: 16-lane group G owns
+  // columns 16*(G%2) .. +15 of the 32-wide tile and rows d0 + 4*(lane%16 / 4)
+  const int dsub = (lane & 15) >> 2;
+  const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  floatx16 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = floatx16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int d0 = 16 * kk + 8 * g + dsub;
+      const uint8_t* p0 = w_lds + d0 * kAbsLdsStride + (32 * mt + cl) * 2;
+      bf16x4 lo = lds_read_tr16(p0);
+      bf16x4 hi = lds_read_tr16(p0 + 4 * kAbsLdsStride);
+      bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[mt] = mfma32(av, qb[kk], acc[mt]);
+    }
+  }
+  // C layout: column = query row n0 + lane%32, rows c = 32mt + 8(r/4) + 4g + r%4
+  if (!nok) return;
+  bf16* out = (bf16*)a.q_abs + ((size_t)nrow * a.H + h) * kRow + cq * kAbsCols;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v = {f2bf(acc[mt][4 * q4]), f2bf(acc[mt][4 * q4 + 1]), f2bf(acc[mt][4 * q4 + 2]),
+                  f2bf(acc[mt][4 * q4 + 3])};
+      *(bf16x4*)(out + 32 * mt + 8 * q4 + 4 * g) = v;
+    }
+}
+
+// fp32: one thread per (row, head, c); W reads coalesce along c.
+__global__ void __launch_bounds__(256) absorb_f32_kernel(AbsorbArgs a) {
+  const int nh = blockIdx.x;  // n * H + h
+  const int n = nh / a.H, h = nh % a.H;
+  __shared__ float qs[kDn];
+  const float* qc = (const float*)a.q_c + (size_t)nh * kDn;
+  if (threadIdx.x < kDn) qs[threadIdx.x] = qc[threadIdx.x];
+  __syncthreads();
+  const float* w = (const float*)a.w_uk + (size_t)h * kDn * kDc;
+  float* out = (float*)a.q_abs + (size_t)nh * kRow;
+  for (int c = threadIdx.x; c < kDc; c += 256) {
+    float acc = 0.f;
+    for (int d = 0; d < kDn; ++d) acc = fmaf(w[(size_t)d * kDc + c], qs[d], acc);
+    out[c] = acc;
+  }
+  if (threadIdx.x < 32) {
+    const int m = threadIdx.x;
+    const float* qr = (const float*)a.q_r + (size_t)nh * kDr;
+    float c, s;
+    rope_cs(a.pos[n], a.rope.theta[m], c, s);
+    const float x0 = qr[2 * m], x1 = qr[2 * m + 1];
+    out[kDc + 2 * m] = x0 * c - x1 * s;
+    out[kDc + 2 * m + 1] = x0 * s + x1 * c;
+  }
+}
+
+hipError_t launch_absorb(const AbsorbArgs& a, int kind, hipStream_t s) {
+  if (kind == kKindF32) {
+    hipLaunchKernelGGL(absorb_f32_kernel, dim3(a.N * a.H), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(absorb_bf16_kernel, dim3(a.H * 4, (a.N + kAbsRowsPerBlock - 1) / kAbsRowsPerBlock),
+                       dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

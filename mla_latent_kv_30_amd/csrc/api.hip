@@ -1,0 +1,219 @@
+// C entry points of libmla: host-side validation, workspace sizing and
+// dispatch to the gfx950 kernels.  See include/mla.h for the contract.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/mla.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace mla;
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+int g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cus[dev] = n;
+  });
+  return g_cus[dev];
+}
+
+RopeTable rope_table(float base) {
+  RopeTable t;
+  for (int m = 0; m < 32; ++m) t.theta[m] = pow((double)base, -2.0 * m / 64.0);
+  return t;
+}
+
+bool dtype_ok(int32_t d) { return d == MLA_F32 || d == MLA_BF16; }
+
+mla_status launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Validate the cache descriptor; returns the kernel kind or -1.
+int cache_kind(const mla_cache* c) {
+  if (c == nullptr || c->page_size != MLA_PAGE || c->num_pages < 1) return -1;
+  switch (c->dtype) {
+    case MLA_F32:
+      return (c->rows && !c->ckv_fp8 && !c->ckv_scale && !c->kr) ? kKindF32 : -1;
+    case MLA_BF16:
+      return (c->rows && !c->ckv_fp8 && !c->ckv_scale && !c->kr) ? kKindBf16 : -1;
+    case MLA_FP8_E4M3:
+      return (!c->rows && c->ckv_fp8 && c->ckv_scale && c->kr) ? kKindFp8 : -1;
+    default:
+      return -1;
+  }
+}
+
+// Split plan for a decode call.
+struct Plan {
+  int splits;  // > 0 uniform, 0 balanced
+  int units;
+  int slots;   // partial slots needed (0: every chunk is a whole sequence)
+};
+
+Plan make_plan(int32_t B, int32_t num_splits) {
+  Plan p;
+  if (num_splits > 0) {
+    p.splits = num_splits;
+    p.units = B * num_splits;
+    p.slots = num_splits > 1 ? B * num_splits : 0;
+  } else if (B > kMaxSchedB) {
+    p.splits = 1;
+    p.units = B;
+    p.slots = 0;
+  } else {
+    p.splits = 0;
+    p.units = device_cus();
+    p.slots = p.units + B;
+  }
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int32_t B, int32_t H, const Plan& p) {
+  if (p.slots == 0) return 0;
+  return align256((size_t)p.slots * H * kDc * sizeof(float)) + align256((size_t)p.slots * H * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: not supported by this build";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown mla_status";
+  }
+}
+
+mla_status mla_absorb_q(const void* q_c, const void* q_r, const int32_t* pos, const void* w_uk, void* q_abs,
+                        int32_t N, int32_t H, int32_t dtype, float rope_base, void* stream) {
+  if (!q_c || !q_r || !pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
+  if (N < 1 || H < 1 || H > MLA_MAX_HEADS || !dtype_ok(dtype)) return MLA_ERR_INVALID_ARG;
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  if ((long long)N * H > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
+  AbsorbArgs a{q_c, q_r, pos, w_uk, q_abs, N, H, rope_table(rope_base)};
+  return launched(launch_absorb(a, dtype == MLA_F32 ? kKindF32 : kKindBf16, (hipStream_t)stream));
+}
+
+mla_status mla_cache_write(const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* slot, int32_t T,
+                           int32_t in_dtype, const mla_cache* cache, float rope_base, void* stream) {
+  if (!c_kv || !k_r || !pos || !slot || T < 1 || !dtype_ok(in_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  const int kind = cache_kind(cache);
+  if (kind < 0) return MLA_ERR_INVALID_ARG;
+  if (in_dtype == MLA_F32 && kind != kKindF32) return MLA_ERR_INVALID_ARG;
+  if (in_dtype == MLA_BF16 && kind == kKindF32) return MLA_ERR_INVALID_ARG;
+  CacheWriteArgs a{c_kv, k_r, pos, slot, nullptr, 0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
+                   cache->ckv_scale, cache->kr, rope_table(rope_base)};
+  return launched(launch_cache_write(a, kind, (hipStream_t)stream));
+}
+
+size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits) {
+  if (B < 1 || H < 1 || H > MLA_MAX_HEADS || num_splits < 0 || num_splits > 256) return 0;
+  return workspace_bytes(B, H, make_plan(B, num_splits));
+}
+
+mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
+                      int32_t B, int32_t H, int32_t max_pages, float softmax_scale, int32_t num_splits, void* workspace,
+                      size_t ws_bytes, float* z, float* lse, void* stream) {
+  if (!q_abs || !block_table || !seq_lens || !z) return MLA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || H > MLA_MAX_HEADS || max_pages < 1) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
+  const int kind = cache_kind(cache);
+  if (kind < 0) return MLA_ERR_INVALID_ARG;
+  if (kind == kKindFp8) return MLA_ERR_UNSUPPORTED;
+  if ((long long)B * num_splits > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
+  const Plan p = make_plan(B, num_splits);
+  const size_t need = workspace_bytes(B, H, p);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q_abs;
+  a.rows = (const uint8_t*)cache->rows;
+  a.ckv8 = (const uint8_t*)cache->ckv_fp8;
+  a.scale8 = cache->ckv_scale;
+  a.kr8 = (const uint8_t*)cache->kr;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.H = H;
+  a.max_pages = max_pages;
+  a.splits = p.splits;
+  a.units = p.units;
+  a.scale_log2 = (float)(softmax_scale * 1.4426950408889634074);
+  a.z = z;
+  a.lse = lse;
+  if (p.slots > 0) {
+    a.zp = (float*)workspace;
+    a.lsep = (float*)((char*)workspace + align256((size_t)p.slots * H * kDc * sizeof(float)));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear a stale error so a launch failure is reported as ours
+  mla_status st = launched(launch_decode(a, kind, s));
+  if (st != MLA_OK || p.slots == 0) return st;
+  return launched(launch_merge(a, s));
+}
+
+mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
+                              const mla_cache* cache, const int32_t* block_table_row, int32_t T, int32_t H,
+                              float softmax_scale, float rope_base, float* z, float* lse, void* stream) {
+  if (!q_abs || !block_table_row || !z || !c_kv || !k_r) return MLA_ERR_INVALID_ARG;
+  if (T < 1 || H < 1 || H > MLA_MAX_HEADS || pos0 < 0) return MLA_ERR_INVALID_ARG;
+  if ((long long)pos0 + T > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  const int kind = cache_kind(cache);
+  if (kind < 0) return MLA_ERR_INVALID_ARG;
+  if (kind == kKindFp8) return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  // 1. append the T new tokens: position pos0 + t, slot from the block-table row
+  CacheWriteArgs w{c_kv, k_r, nullptr, nullptr, block_table_row, pos0, T, cache->rows, nullptr, nullptr, nullptr,
+                   rope_table(rope_base)};
+  mla_status st = launched(launch_cache_write(w, kind, s));
+  if (st != MLA_OK) return st;
+  // 2. causal attention: query row t sees cached tokens 0 .. pos0 + t
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q_abs;
+  a.rows = (const uint8_t*)cache->rows;
+  a.block_table = block_table_row;
+  a.B = T;
+  a.H = H;
+  a.max_pages = (pos0 + T + MLA_PAGE - 1) / MLA_PAGE;
+  a.splits = 1;
+  a.units = T;
+  a.prefill_T = T;
+  a.prefill_pos0 = pos0;
+  a.scale_log2 = (float)(softmax_scale * 1.4426950408889634074);
+  a.z = z;
+  a.lse = lse;
+  return launched(launch_decode(a, kind, s));
+}
+
+mla_status mla_upproj_v(const float* z, const void* w_uv, void* o, int32_t N, int32_t H, int32_t w_dtype,
+                        int32_t o_dtype, void* stream) {
+  if (!z || !w_uv || !o || N < 1 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (!dtype_ok(w_dtype) || !dtype_ok(o_dtype)) return MLA_ERR_INVALID_ARG;
+  if ((long long)N * H > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
+  UpprojArgs a{z, w_uv, o, N, H, o_dtype == MLA_BF16 ? 1 : 0};
+  return launched(launch_upproj(a, w_dtype == MLA_F32 ? kKindF32 : kKindBf16, (hipStream_t)stream));
+}
+
+}  // extern "C"

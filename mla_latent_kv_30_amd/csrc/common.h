@@ -1,0 +1,138 @@
+// Shared device helpers for the gfx950 MLA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDc = 512;      // latent width d_c
+constexpr int kDr = 64;       // RoPE key width
+constexpr int kDn = 128;      // nope (content) head width
+constexpr int kDv = 128;      // value head width
+constexpr int kRow = 576;     // cached elements per token: d_c + rope
+constexpr int kPage = 64;     // tokens per cache page
+constexpr int kMaxHeads = 128;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+__device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }  // round to nearest even
+
+// ---- matrix cores ---------------------------------------------------------
+// Operand layouts (checked on gfx950):
+//   32x32x16: A lane l holds row l%32, k = 8*(l/32)+j; B lane l holds column l%32,
+//             k = 8*(l/32)+j; C lane l holds column l%32, rows 8*(r/4)+4*(l/32)+r%4.
+//   16x16x32: A row l%16, k = 8*(l/16)+j; B column l%16, same k; C column l%16,
+//             rows 4*(l/16)+r.
+//   16x16x16: as 16x16x32 with k = 4*(l/16)+j, j < 4.
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16k16(bf16x4 a, bf16x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*(short4v*)&a, *(short4v*)&b, c, 0, 0, 0);
+}
+
+// ---- LDS ------------------------------------------------------------------
+// Transposing LDS read of four 16-bit elements.  Within each group of 16
+// lanes, lane 4a+b receives element b of the 8-byte chunks addressed by lanes
+// a, a+4, a+8, a+12 (in that order).  So if lane s of the group points at
+// row (s/4) and columns 4*(s%4)..4*(s%4)+3 of a row-major tile, lane n of the
+// group receives column n of rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds_byte_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(lds_byte_ptr));
+}
+__device__ __forceinline__ int4v lds_read_b128(const void* lds_byte_ptr) {
+  return *(const MLA_LDS int4v*)(lds_byte_ptr);
+}
+
+// Value that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const MLA_LDS uint8_t*)p;
+}
+
+// Asynchronous copy HBM -> LDS of 4 bytes per lane: lane i writes LDS bytes
+// [lds_base + 4 i, +4) from buffer offset soff + voff (voff = 4 i); reads past
+// the buffer's record count land as zeros.  Issued as inline assembly so the
+// compiler does not serialise it against every later LDS read; completion is
+// tracked by the caller with wait_vmcnt<>() followed by a workgroup barrier.
+// The instruction has no register results and reads its address operands at
+// issue; it writes M0, which no compiler-generated code in these kernels
+// relies on.  One wait state separates the M0 write from the LDS-DMA that
+// reads it.
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, uint32_t voff,
+                                         uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rs), "s"(soff)
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// ---- cross-lane -----------------------------------------------------------
+// Reductions over the lane pair (l, l^32) and over (l, l^16) inside each
+// half-wave, via the gfx950 lane-swap instructions.
+__device__ __forceinline__ float pair32_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- RoPE -----------------------------------------------------------------
+// Frequencies theta_m = base^(-2m/64), m = 0..31, computed on the host in
+// double and passed by value.
+struct RopeTable {
+  double theta[32];
+};
+
+// cos/sin of pos*theta: the angle is formed and reduced modulo 2*pi in double
+// (positions reach 2^17 radians), then evaluated in fp32.
+__device__ __forceinline__ void rope_cs(int pos, double theta, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = (double)pos * theta;
+  a -= two_pi * rint(a * (1.0 / two_pi));
+  sincosf((float)a, &s, &c);
+}
+
+}  // namespace mla

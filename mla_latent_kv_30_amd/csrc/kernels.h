@@ -1,0 +1,75 @@
+// Internal launch interface between the C entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace mla {
+
+constexpr int kMaxSchedB = 2048;  // sequences a balanced (auto) split can schedule
+constexpr int kKindF32 = 0;
+constexpr int kKindBf16 = 1;
+constexpr int kKindFp8 = 2;
+
+struct DecodeArgs {
+  const void* q;               // [NQ][H][576] fp32 or bf16
+  const uint8_t* rows;         // fp32/bf16 pool [pages][64][576]
+  const uint8_t* ckv8;         // fp8 pool parts
+  const float* scale8;
+  const uint8_t* kr8;
+  const int32_t* block_table;  // [B][max_pages] (prefill: one row)
+  const int32_t* seq_lens;     // [B] (prefill: unused)
+  int32_t B, H, max_pages;
+  int32_t splits;              // > 0: S chunks per sequence; 0: balanced over `units`
+  int32_t units;               // workgroups along x
+  int32_t prefill_T;           // > 0: causal prefill of T rows (unit w -> row T-1-w)
+  int32_t prefill_pos0;
+  float scale_log2;            // softmax_scale * log2(e)
+  float* z;
+  float* lse;
+  float* zp;                   // partials [slots][H][512]
+  float* lsep;                 // partials [slots][H]
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+
+struct AbsorbArgs {
+  const void* q_c;
+  const void* q_r;
+  const int32_t* pos;
+  const void* w_uk;
+  void* q_abs;
+  int32_t N, H;
+  RopeTable rope;
+};
+hipError_t launch_absorb(const AbsorbArgs& a, int kind, hipStream_t s);
+
+struct CacheWriteArgs {
+  const void* c_kv;
+  const void* k_r;
+  const int32_t* pos;   // [T], or NULL: token t is at position pos0 + t
+  const int32_t* slot;  // [T], or NULL: slot from block table `bt` at that position
+  const int32_t* bt;
+  int32_t pos0;
+  int32_t T;
+  void* rows;
+  uint8_t* ckv8;
+  float* scale8;
+  void* kr8;
+  RopeTable rope;
+};
+hipError_t launch_cache_write(const CacheWriteArgs& a, int kind, hipStream_t s);
+
+struct UpprojArgs {
+  const float* z;
+  const void* w_uv;
+  void* o;
+  int32_t N, H;
+  int32_t o_bf16;
+};
+hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,107 @@
+// Value up-projection o_i = W_i^UV z_i (the "DeepSeek-V3" notes,
+// ekkoxiao.github.io, §潜在向量的作用: values are summed in latent space and
+// up-projected afterwards).  W_i^UV is stored [128 d][512 c], so the
+// contraction index c is contiguous in both operands: no transposition needed.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+// bf16 weights: o^T[d, n] = sum_c W[d, c] z^T[c, n] on 32x32x16 matrix cores.
+// Workgroup = (head, 256 query rows); wave = 64 rows (2 column tiles) x all
+// 128 d (4 row tiles).  z is rounded to bf16 on load; accumulation is fp32.
+__global__ void __launch_bounds__(256) upproj_bf16_kernel(UpprojArgs a) {
+  const int h = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = blockIdx.y * 256 + wave * 64;
+  if (n0 >= a.N) return;
+  const int g = lane >> 5;
+  const bf16* w = (const bf16*)a.w_uv + (size_t)h * kDv * kDc;
+  int nrow[2];
+  bool nok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    nrow[nt] = n0 + 32 * nt + (lane & 31);
+    nok[nt] = nrow[nt] < a.N;
+  }
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = floatx16{};
+  for (int kk = 0; kk < kDc / 16; ++kk) {
+    const int c0 = 16 * kk + 8 * g;
+    bf16x8 bz[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float4 u0 = make_float4(0, 0, 0, 0), u1 = u0;
+      if (nok[nt]) {
+        const float4* zp = (const float4*)(a.z + ((size_t)nrow[nt] * a.H + h) * kDc + c0);
+        u0 = zp[0];
+        u1 = zp[1];
+      }
+      bz[nt] = bf16x8{f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
+                      f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int d = 32 * mt + (lane & 31);
+      bf16x8 aw = __builtin_bit_cast(bf16x8, *(const int4v*)(w + (size_t)d * kDc + c0));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(aw, bz[nt], acc[mt][nt]);
+    }
+  }
+  // C layout: column = query row, rows d = 32mt + 8(r/4) + 4g + r%4
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if (!nok[nt]) continue;
+    const size_t base = ((size_t)nrow[nt] * a.H + h) * kDv;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * mt + 8 * q4 + 4 * g;
+        const floatx16& v = acc[mt][nt];
+        if (a.o_bf16) {
+          bf16x4 ov = {f2bf(v[4 * q4]), f2bf(v[4 * q4 + 1]), f2bf(v[4 * q4 + 2]), f2bf(v[4 * q4 + 3])};
+          *(bf16x4*)((bf16*)a.o + base + d) = ov;
+        } else {
+          *(float4*)((float*)a.o + base + d) = make_float4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
+        }
+      }
+  }
+}
+
+// fp32 weights: one workgroup per (row, head), z in LDS, one thread per d
+// with 2 threads sharing a row of W (halves of c), exact fp32 FMA chains.
+__global__ void __launch_bounds__(256) upproj_f32_kernel(UpprojArgs a) {
+  const int nh = blockIdx.x;
+  const int h = nh % a.H;
+  __shared__ float zs[kDc];
+  __shared__ float part[256];
+  const float* zr = a.z + (size_t)nh * kDc;
+  for (int i = threadIdx.x; i < kDc; i += 256) zs[i] = zr[i];
+  __syncthreads();
+  const int d = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const float* w = (const float*)a.w_uv + ((size_t)h * kDv + d) * kDc + half * 256;
+  float acc = 0.f;
+  for (int c = 0; c < 256; ++c) acc = fmaf(w[c], zs[half * 256 + c], acc);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  if (half == 0) {
+    const float v = part[threadIdx.x] + part[threadIdx.x + 1];
+    if (a.o_bf16) ((bf16*)a.o)[(size_t)nh * kDv + d] = f2bf(v);
+    else ((float*)a.o)[(size_t)nh * kDv + d] = v;
+  }
+}
+
+hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s) {
+  if (w_kind == kKindF32) {
+    hipLaunchKernelGGL(upproj_f32_kernel, dim3(a.N * a.H), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(upproj_bf16_kernel, dim3(a.H, (a.N + 255) / 256), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,107 @@
+"""C-ABI contract checks that run without a GPU: the library loads, exports
+every function include/mla.h declares, and rejects bad arguments on the host
+before any HIP call (status codes, no launch)."""
+
+import ctypes
+
+import pytest
+
+from mla_latent_kv_30_amd import _lib
+
+L = _lib.lib()
+P = ctypes.c_void_p(0x1000)  # a non-null pointer that is never dereferenced
+NULL = None
+
+
+def _cache(dtype=_lib.MLA_BF16, rows=P, ckv=NULL, scale=NULL, kr=NULL, num_pages=4, page=64):
+    return _lib.MlaCache(dtype, num_pages, page, 0, rows, ckv, scale, kr)
+
+
+def test_every_declared_symbol_is_exported():
+    names = _lib.declared_symbols()
+    assert set(names) >= {"mla_absorb_q", "mla_decode", "mla_prefill_causal", "mla_upproj_v", "mla_cache_write",
+                          "mla_decode_workspace_size", "mla_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in range(5):
+        assert _lib.status_string(code).startswith(["MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED",
+                                                     "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"][code])
+    assert "unknown" in _lib.status_string(99)
+
+
+def test_absorb_rejects_bad_arguments():
+    f = L.mla_absorb_q
+    assert f(NULL, P, P, P, P, 1, 16, 1, 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert f(P, P, P, P, P, 0, 16, 1, 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert f(P, P, P, P, P, 1, 0, 1, 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert f(P, P, P, P, P, 1, 129, 1, 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert f(P, P, P, P, P, 1, 16, 2, 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG  # fp8 is a cache-only format
+    assert f(P, P, P, P, P, 1, 16, 1, float("nan"), NULL) == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_cache_write_rejects_bad_descriptors():
+    f = L.mla_cache_write
+    ok = _cache()
+    assert f(P, P, P, P, 0, 1, ctypes.byref(ok), 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    bad_page = _cache(page=32)
+    assert f(P, P, P, P, 5, 1, ctypes.byref(bad_page), 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    mixed = _cache(ckv=P)  # bf16 cache must not carry fp8 pointers
+    assert f(P, P, P, P, 5, 1, ctypes.byref(mixed), 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    f32in_bf16cache = _cache()
+    assert f(P, P, P, P, 5, 0, ctypes.byref(f32in_bf16cache), 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    fp8_missing = _cache(dtype=_lib.MLA_FP8_E4M3, rows=NULL, ckv=P, scale=NULL, kr=P)
+    assert f(P, P, P, P, 5, 1, ctypes.byref(fp8_missing), 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert f(P, P, P, P, 5, 1, None, 10000.0, NULL) == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_decode_rejects_bad_arguments_and_small_workspace():
+    f = L.mla_decode
+    c = _cache()
+    args = lambda **k: dict(dict(q=P, cache=ctypes.byref(c), bt=P, lens=P, B=2, H=16, mp=4, scale=0.07, S=0,
+                                 ws=NULL, wsb=0, z=P, lse=NULL), **k)
+
+    def call(**k):
+        a = args(**k)
+        return f(a["q"], a["cache"], a["bt"], a["lens"], a["B"], a["H"], a["mp"], a["scale"], a["S"], a["ws"],
+                 a["wsb"], a["z"], a["lse"], NULL)
+
+    assert call(q=NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert call(z=NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert call(B=0) == _lib.MLA_ERR_INVALID_ARG
+    assert call(H=200) == _lib.MLA_ERR_INVALID_ARG
+    assert call(mp=0) == _lib.MLA_ERR_INVALID_ARG
+    assert call(scale=-1.0) == _lib.MLA_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == _lib.MLA_ERR_INVALID_ARG
+    assert call(S=-1) == _lib.MLA_ERR_INVALID_ARG
+    assert call(S=257) == _lib.MLA_ERR_INVALID_ARG
+    assert call(cache=None) == _lib.MLA_ERR_INVALID_ARG
+    # automatic splitting needs a workspace of mla_decode_workspace_size bytes
+    need = _lib.decode_workspace_size(2, 16, 0)
+    assert need > 0
+    assert call(S=0, ws=NULL, wsb=0) == _lib.MLA_ERR_WORKSPACE
+    assert call(S=0, ws=P, wsb=need - 1) == _lib.MLA_ERR_WORKSPACE
+    assert call(S=4, ws=P, wsb=_lib.decode_workspace_size(2, 16, 4) - 1) == _lib.MLA_ERR_WORKSPACE
+
+
+def test_workspace_size_contract():
+    assert _lib.decode_workspace_size(16, 16, 1) == 0  # one chunk per sequence needs no partials
+    assert _lib.decode_workspace_size(8, 128, 32) >= 8 * 32 * 128 * (512 + 1) * 4
+    assert _lib.decode_workspace_size(0, 16, 0) == 0
+    assert _lib.decode_workspace_size(4, 16, -1) == 0
+
+
+def test_prefill_and_upproj_reject_bad_arguments():
+    c = _cache()
+    assert L.mla_prefill_causal(P, P, P, -1, ctypes.byref(c), P, 8, 16, 0.07, 10000.0, P, NULL, NULL) \
+        == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_prefill_causal(P, P, P, 0, ctypes.byref(c), P, 0, 16, 0.07, 10000.0, P, NULL, NULL) \
+        == _lib.MLA_ERR_INVALID_ARG
+    fp8 = _cache(dtype=_lib.MLA_FP8_E4M3, rows=NULL, ckv=P, scale=P, kr=P)
+    assert L.mla_prefill_causal(P, P, P, 0, ctypes.byref(fp8), P, 8, 16, 0.07, 10000.0, P, NULL, NULL) \
+        == _lib.MLA_ERR_UNSUPPORTED
+    assert L.mla_upproj_v(NULL, P, P, 1, 16, 1, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_upproj_v(P, P, P, 1, 16, 2, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_upproj_v(P, P, P, 1, 0, 1, 0, NULL) == _lib.MLA_ERR_INVALID_ARG

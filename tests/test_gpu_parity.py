@@ -1,0 +1,246 @@
+"""GPU parity of the HIP path (through the C-ABI) against the fp64 CPU oracle.
+
+Tolerances (stated for the three precisions of the path):
+  fp32:       max |gpu - oracle| <= 1e-5 (absolute)
+  bf16:       max |gpu - oracle| / max |oracle| <= 2e-2 over the whole tensor
+  fp8 cache:  the same ratio <= 6e-2, against the oracle on the unquantised cache
+The oracle always sees exactly the values the GPU received (bf16 inputs are
+rounded before both sides get them).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_30_amd as mla
+from mla_latent_kv_30_amd import device_inputs as DI
+from mla_latent_kv_30_amd import workload as W
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _rel(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(gpu).all(), "non-finite GPU output"
+    return float(np.abs(gpu - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle_decode(dd, seqs=None, heads=None):
+    h = dd.host
+    off = h["offsets"]
+    seqs = range(dd.wl.B) if seqs is None else seqs
+    out = {"o": [], "z": [], "lse": [], "q_abs": []}
+    for b in seqs:
+        qc, qr, wk, wv = h["q_c"][b], h["q_r"][b], h["w_uk"], h["w_uv"]
+        if heads is not None:
+            qc, qr, wk, wv = qc[heads], qr[heads], wk[heads], wv[heads]
+        r = orc.decode_sequence(qc, qr, h["c_kv"][off[b]:off[b + 1]], h["k_r"][off[b]:off[b + 1]], wk, wv)
+        for k in out:
+            out[k].append(r[k])
+    return {k: np.stack(v) for k, v in out.items()}
+
+
+def _run_decode(dd, num_splits=0, out_dtype=torch.float32):
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    z, lse = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=num_splits)
+    o = mla.upproj_v(z, dd.w_uv, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return {"q_abs": q_abs.float().cpu().numpy(), "z": z.cpu().numpy(), "lse": lse.cpu().numpy(),
+            "o": o.float().cpu().numpy()}
+
+
+# --------------------------------------------------------------------------- fp32
+
+def test_tiny_f32_full_path():
+    wl = W.make_workload("tiny_f32")
+    _note(f"case tiny_f32 B={wl.B} H={wl.H} lens={list(wl.lens)}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    ref = _oracle_decode(dd)
+    for S in (0, 1, 2, 3):
+        got = _run_decode(dd, num_splits=S)
+        for k in ("q_abs", "z", "lse", "o"):
+            err = np.abs(got[k] - ref[k]).max()
+            assert err <= 1e-5, (S, k, err)
+
+
+def test_f32_ragged_lengths_and_splits():
+    wl = W.make_workload("tiny_f32", B=4, lens=[1, 63, 130, 300])
+    _note(f"case f32 ragged lens={list(wl.lens)}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=3)
+    ref = _oracle_decode(dd)
+    for S in (0, 1, 5):
+        got = _run_decode(dd, num_splits=S)
+        for k in ("z", "lse", "o"):
+            err = np.abs(got[k] - ref[k]).max()
+            assert err <= 1e-5, (S, k, err)
+
+
+# --------------------------------------------------------------------------- bf16 decode
+
+@pytest.mark.parametrize("H,lens", [
+    (16, [1, 17, 64, 65, 130, 1000]),
+    (32, [40, 300, 129]),
+    (64, [64, 257]),
+    (128, [33, 700]),
+    (24, [90, 5]),
+    (100, [200]),
+])
+def test_bf16_decode_matches_oracle(H, lens):
+    wl = W.make_workload("decode_h16", B=len(lens), H=H, lens=lens)
+    _note(f"case bf16 decode H={H} lens={lens}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=3)
+    ref = _oracle_decode(dd)
+    for S in (0, 1, 3):
+        got = _run_decode(dd, num_splits=S)
+        assert _rel(got["o"], ref["o"]) <= 2e-2, ("o", S)
+        assert _rel(got["z"], ref["z"]) <= 2e-2, ("z", S)
+        assert np.abs(got["lse"] - ref["lse"]).max() <= 2e-2, ("lse", S)
+        assert _rel(got["q_abs"], ref["q_abs"]) <= 1e-2
+
+
+def test_bf16_split_count_invariance_and_determinism():
+    wl = W.make_workload("decode_h16", B=3, H=16, lens=[3000, 1234, 77])
+    _note(f"case bf16 split invariance lens={list(wl.lens)}")
+    dd = DI.decode_inputs(wl, DEV)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    outs = {}
+    for S in (0, 1, 2, 7, 32):
+        z, lse = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=S)
+        outs[S] = (z.clone(), lse.clone())
+    torch.cuda.synchronize()
+    base = outs[1][0].cpu().numpy()
+    for S, (z, lse) in outs.items():
+        assert _rel(z.cpu().numpy(), base) <= 1e-2, S
+    # same call twice: bit-identical (no atomics, fixed reduction order)
+    z2, _ = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(z2, outs[0][0])
+
+
+def test_bf16_page_permutation_invariance():
+    """Physical page placement must not matter (same values, different pool order)."""
+    wl = W.make_workload("decode_h16", B=2, H=16, lens=[500, 129])
+    _note("case bf16 page permutation")
+    dd = DI.decode_inputs(wl, DEV, spare_pages=5)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    z1, _ = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens)
+    # move every page to a new pool slot and rewrite the table
+    n = dd.cache.num_pages
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(3)).to(DEV)
+    moved = mla.PagedCache(n, torch.bfloat16, DEV, fill=float("nan"))
+    moved.rows[perm] = dd.cache.rows
+    bt2 = perm[dd.block_table.long()].to(torch.int32)
+    z2, _ = mla.decode(q_abs, moved, bt2, dd.seq_lens)
+    torch.cuda.synchronize()
+    assert torch.equal(z1, z2)
+
+
+# --------------------------------------------------------------------------- pieces
+
+def test_cache_write_rows_match_oracle_rope():
+    wl = W.make_workload("decode_h16", B=2, H=16, lens=[70, 131])
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=1)
+    torch.cuda.synchronize()
+    rows = dd.cache.rows.float().cpu().numpy().reshape(-1, 576)
+    slots = dd.layout.slots
+    c, k = dd.host["c_kv"], dd.host["k_r"]
+    np.testing.assert_array_equal(rows[slots, :512], c)
+    kr_ref = orc.rope(k, dd.layout.positions)
+    assert np.abs(rows[slots, 512:] - kr_ref).max() <= 2 ** -8 * np.abs(kr_ref).max()
+    # untouched slots keep their poison
+    unused = np.setdiff1d(np.arange(rows.shape[0]), slots)
+    assert np.isnan(rows[unused]).all()
+
+
+def test_fp8_cache_write_bit_exact():
+    wl = W.make_workload("long_fp8", B=2, H=16, lens=[100, 64])
+    _note("case fp8 cache write")
+    dd = DI.decode_inputs(wl, DEV, spare_pages=1)
+    torch.cuda.synchronize()
+    slots = dd.layout.slots
+    codes = dd.cache.ckv.cpu().numpy().reshape(-1, 512)[slots]
+    scales = dd.cache.scale.cpu().numpy().reshape(-1, 4)[slots]
+    rc, rs = orc.quantize_latent_e4m3(dd.host["c_kv"])
+    np.testing.assert_array_equal(scales, rs)
+    np.testing.assert_array_equal(codes, rc)
+    kr = dd.cache.kr.float().cpu().numpy().reshape(-1, 64)[slots]
+    kr_ref = orc.rope(dd.host["k_r"], dd.layout.positions)
+    assert np.abs(kr - kr_ref).max() <= 2 ** -8 * np.abs(kr_ref).max()
+
+
+def test_upproj_bf16_and_f32():
+    g = torch.Generator().manual_seed(5)
+    for H, N in [(16, 3), (128, 300), (7, 1)]:
+        z = torch.randn(N, H, 512, generator=g)
+        w = (torch.randn(H, 128, 512, generator=g) / math.sqrt(512)).to(torch.bfloat16)
+        ref = np.einsum("hdc,nhc->nhd", w.double().numpy(), z.double().numpy())
+        o = mla.upproj_v(z.to(DEV), w.to(DEV), out_dtype=torch.float32)
+        ob = mla.upproj_v(z.to(DEV), w.to(DEV), out_dtype=torch.bfloat16)
+        of = mla.upproj_v(z.to(DEV), w.float().to(DEV), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert _rel(o.cpu().numpy(), ref) <= 1e-2
+        assert _rel(ob.float().cpu().numpy(), ref) <= 2e-2
+        assert np.abs(of.cpu().numpy() - ref).max() <= 1e-5
+
+
+# --------------------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("H,T", [(16, 200), (128, 130)])
+def test_bf16_prefill_matches_oracle(H, T):
+    wl = W.make_workload("prefill_h128", H=H, lens=[T])
+    _note(f"case bf16 prefill H={H} T={T}")
+    dt = torch.bfloat16
+    w_uk, w_uv = W.weights(wl)
+    q_c, q_r = W.queries(wl)
+    c, k = W.sequence_latents(wl, 0)
+    npg = (T + 63) // 64
+    cache = mla.PagedCache(npg + 2, dt, DEV, fill=float("nan"))
+    bt = torch.tensor(np.random.default_rng(1).permutation(npg + 2)[:npg], dtype=torch.int32, device=DEV)
+    pos = torch.arange(T, dtype=torch.int32, device=DEV)
+    td = lambda x: torch.from_numpy(x).to(DEV, dt)
+    q_abs = mla.absorb_q(td(q_c), td(q_r), pos, td(w_uk))
+    z, lse = mla.prefill_causal(q_abs, td(c), td(k), cache, bt)
+    o = mla.upproj_v(z, td(w_uv))
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 65, T // 2, T - 1]
+    ref = orc.prefill_causal(q_c, q_r, c, k, w_uk, w_uv, rows=rows)
+    assert _rel(o.cpu().numpy()[rows], ref["o"]) <= 2e-2
+    assert _rel(z.cpu().numpy()[rows], ref["z"]) <= 2e-2
+    assert np.abs(lse.cpu().numpy()[rows] - ref["lse"]).max() <= 2e-2
+    # the cache now holds exactly what a cache write produces
+    pool = cache.rows.float().cpu().numpy().reshape(-1, 576)
+    j = np.arange(T)
+    slot = bt.cpu().numpy()[j // 64] * 64 + j % 64
+    np.testing.assert_array_equal(pool[slot, :512], c)
+    assert np.abs(pool[slot, 512:] - ref["k_r_rot"]).max() <= 2 ** -8 * np.abs(ref["k_r_rot"]).max()
+
+
+def test_prefill_row_equals_decode_at_length_t_plus_1():
+    wl = W.make_workload("prefill_h128", H=16, lens=[150])
+    dt = torch.bfloat16
+    w_uk, _ = W.weights(wl)
+    q_c, q_r = W.queries(wl)
+    c, k = W.sequence_latents(wl, 0)
+    T = 150
+    cache = mla.PagedCache(3, dt, DEV)
+    bt = torch.tensor([2, 0, 1], dtype=torch.int32, device=DEV)
+    td = lambda x: torch.from_numpy(x).to(DEV, dt)
+    q_abs = mla.absorb_q(td(q_c), td(q_r), torch.arange(T, dtype=torch.int32, device=DEV), td(w_uk))
+    zp, _ = mla.prefill_causal(q_abs, td(c), td(k), cache, bt)
+    rows = [0, 63, 64, 149]
+    lens = torch.tensor([t + 1 for t in rows], dtype=torch.int32, device=DEV)
+    zd, _ = mla.decode(q_abs[rows].contiguous(), cache, bt.repeat(len(rows), 1), lens, num_splits=1)
+    torch.cuda.synchronize()
+    assert _rel(zd.cpu().numpy(), zp[rows].cpu().numpy()) <= 1e-3
