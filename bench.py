@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of absorbed-MLA decode on one MI355X, against its roofline.
+
+One step = the whole decode path for one batch: absorbed query
+(mla_absorb_q), the split pass over the paged latent cache
+(mla_decode_partial), the split merge (mla_decode_merge) and the W_UV
+up-projection (mla_upproj_v).  Inputs are synthetic with the workload's
+shapes and distributions and are resident in HBM before timing starts.  To
+keep the 256 MB last-level cache from serving repeated reads, the step
+rotates over enough replicas of its inputs (cache, weights, queries) to
+exceed 600 MB.
+
+Prints one JSON line: value = cached tokens per second over the whole step,
+plus the decode kernel's achieved HBM bandwidth and matrix-core rate against
+MI355X's published peaks, and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode cached-tokens/s + TB/s & TFLOP/s as % of MI355X roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix cores
+PEAK_F32_TFLOPS = 157.3        # fp32 matrix
+FLOP_PER_TOKEN_HEAD = 2 * 576 + 2 * 512   # score + latent accumulation
+REPLICA_TARGET_BYTES = 600 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode_h16",
+                    choices=["decode_h16", "decode_h128", "long_bf16", "long_fp8", "tiny_f32"])
+    ap.add_argument("--splits", type=int, default=-1, help="num_splits (-1: the workload's own, 0: automatic)")
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0: enough for 600 MB)")
+    ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of as a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, host, budget_s):
+    """The oracle as it stands, on whole sequences until the time budget is used."""
+    import numpy as np
+    from oracle import mla_oracle as orc
+
+    cores = len(os.sched_getaffinity(0))
+    off = host["offsets"]
+    heads = list(range(wl.H)) if wl.H <= 16 else list(range(8))
+    tokens = 0
+    seqs = 0
+    t0 = time.perf_counter()
+    for b in range(wl.B):
+        orc.decode_sequence(host["q_c"][b][heads], host["q_r"][b][heads], host["c_kv"][off[b]:off[b + 1]],
+                            host["k_r"][off[b]:off[b + 1]], host["w_uk"][heads], host["w_uv"][heads])
+        tokens += int(wl.lens[b])
+        seqs += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    # cached tokens per second with all of the workload's heads
+    rate = tokens * len(heads) / wl.H / dt
+    return {"value": rate, "unit": "cached-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{seqs} of {wl.B} sequences ({tokens} cached tokens) x {len(heads)} of {wl.H} heads, "
+                      f"fp64 NumPy, {dt:.1f} s; rate scaled to all {wl.H} heads"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit(f"bench.py measures the decode path on one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) "
+                 f"is not supported: sharding across GPUs is not part of this library.")
+
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_30_amd as mla
+    from mla_latent_kv_30_amd import device_inputs as DI
+    from mla_latent_kv_30_amd import workload as W
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = W.make_workload(args.config, seed=args.seed)
+    splits = wl.splits if args.splits < 0 else args.splits
+    t_setup = time.perf_counter()
+    dd = DI.decode_inputs(wl, dev, keep_host=not args.no_cpu_baseline)
+    torch.cuda.synchronize()
+    B, H, total = wl.B, wl.H, wl.total_tokens
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    # ---- replicas of everything a step reads
+    per_rep = dd.cache.nbytes() + sum(t.numel() * t.element_size() for t in (dd.q_c, dd.q_r, dd.w_uk, dd.w_uv))
+    R = args.replicas or max(1, min(16, math.ceil(REPLICA_TARGET_BYTES / per_rep)))
+    reps = [(dd.cache, dd.q_c, dd.q_r, dd.w_uk, dd.w_uv)]
+    for _ in range(R - 1):
+        c = mla.PagedCache.__new__(mla.PagedCache)
+        c.__dict__.update(dd.cache.__dict__)
+        for name in ("rows", "ckv", "scale", "kr"):
+            t = getattr(dd.cache, name)
+            setattr(c, name, None if t is None else t.clone())
+        reps.append((c, dd.q_c.clone(), dd.q_r.clone(), dd.w_uk.clone(), dd.w_uv.clone()))
+    q_abs = torch.empty((B, H, 576), dtype=dt, device=dev)
+    z = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, 128), dtype=torch.float32, device=dev)
+    ws_bytes = mla.decode_workspace_size(B, H, splits)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step(r):
+        cache, q_c, q_r, w_uk, w_uv = reps[r]
+        mla.absorb_q(q_c, q_r, dd.pos, w_uk, out=q_abs)
+        mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
+        mla.decode_merge(dd.seq_lens, H, ws, z, lse, num_splits=splits)
+        mla.upproj_v(z, w_uv, out=o)
+
+    for k in range(max(1, args.warmup)):
+        step(k % R)
+    torch.cuda.synchronize()
+
+    graphs = None
+    if not args.no_graph:
+        try:
+            graphs = []
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for r in range(R):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=side):
+                        step(r)
+                    graphs.append(g)
+            torch.cuda.current_stream().wait_stream(side)
+            for k in range(max(1, args.warmup)):
+                graphs[k % R].replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture not available: fall back to eager launches
+            print(f"note: graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graphs = None
+
+    # ---- timed region: exactly `steps` steps between two synchronisations
+    K = args.steps
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for k in range(K):
+        if graphs is not None:
+            graphs[k % R].replay()
+        else:
+            step(k % R)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / K
+
+    # ---- the decode kernel alone (split pass), timed with events on its own
+    # stream; a GPU sleep first lets the host enqueue every launch ahead of the
+    # device, so no host latency lands between an event and its kernel
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    try:
+        torch.cuda._sleep(int(2.4e9 * (0.002 + 60e-6 * K)))
+    except Exception:  # no device sleep available: host latency may inflate the kernel time
+        pass
+    for k in range(K):
+        cache, *_ = reps[k % R]
+        starts[k].record()
+        mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
+        ends[k].record()
+    torch.cuda.synchronize()
+    kern_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kern_avg_ms = sum(kern_ms) / K
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---- roofline of the decode kernel (algorithmic bytes / FLOPs per launch)
+    tok_bytes = {"f32": 2304, "bf16": 1152, "fp8": 656}[wl.dtype]
+    q_bytes = B * H * 576 * (4 if wl.dtype == "f32" else 2)
+    out_bytes = B * H * (512 + 1) * 4
+    alg_bytes = total * tok_bytes + q_bytes + out_bytes
+    alg_flops = total * H * FLOP_PER_TOKEN_HEAD
+    gbs = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    tflops = alg_flops / (kern_avg_ms * 1e-3) / 1e12
+    mfma_peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, dd.host, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": total / (ms_per_step * 1e-3),
+        "unit": "cached-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "heads": H, "cached_tokens": total,
+            "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
+            "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
+            "step": "absorb_q + decode_partial + decode_merge + upproj_v",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": None, "kernel": "decode_bf16_kernel" if wl.dtype != "f32" else "decode_f32_kernel",
+            "kernel_avg_us": kern_avg_ms * 1e3, "kernel_p10_us": kern_ms[K // 10] * 1e3,
+            "kernel_p90_us": kern_ms[(9 * K) // 10] * 1e3, "alg_bytes_per_launch": alg_bytes,
+            "alg_flops_per_launch": alg_flops, "tflops": tflops, "mfma_peak_tflops": mfma_peak,
+            "mfma_frac": tflops / mfma_peak,
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+        "setup_s": setup_s,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

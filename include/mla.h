@@ -166,6 +166,34 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
                       float* z, float* lse, void* stream);
 
 /*
+ * The two halves of mla_decode, for callers that schedule the merge
+ * themselves (overlapping it with other work, or combining chunk partials
+ * produced by several calls).  mla_decode(...) is exactly
+ * mla_decode_partial(...) followed by mla_decode_merge(...) on the same
+ * stream with the same arguments.
+ *
+ * mla_decode_partial: the split pass.  Sequences that fall into a single
+ * chunk get their final z / lse; every other chunk leaves its normalised
+ * partial (z_c, lse_c) in the workspace.  Same arguments and errors as
+ * mla_decode.
+ */
+mla_status mla_decode_partial(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
+                              int32_t num_splits, void* workspace, size_t ws_bytes, float* z, float* lse,
+                              void* stream);
+
+/*
+ * mla_decode_merge: lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c
+ * over the chunks of each sequence that mla_decode_partial split (sequences
+ * it finished in one chunk are left untouched).  B, H, num_splits,
+ * seq_lens and the workspace must be those of the preceding partial pass.
+ * Errors: MLA_ERR_INVALID_ARG (NULL seq_lens or z, B < 1, H not in [1,128],
+ * num_splits < 0 or > 256); MLA_ERR_WORKSPACE.
+ */
+mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits, void* workspace,
+                            size_t ws_bytes, float* z, float* lse, void* stream);
+
+/*
  * mla_prefill_causal — T new tokens of one sequence, at positions
  * pos0 .. pos0+T-1, are written into the cache and attend causally: query t
  * sees cached tokens 0 .. pos0+t inclusive (§注意力计算 sums up to the

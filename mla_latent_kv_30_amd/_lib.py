@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.mla_decode.restype = _i32
     L.mla_decode.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp,
                              ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_decode_partial.restype = _i32
+    L.mla_decode_partial.argtypes = list(L.mla_decode.argtypes)
+    L.mla_decode_merge.restype = _i32
+    L.mla_decode_merge.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp]
     L.mla_prefill_causal.restype = _i32
     L.mla_prefill_causal.argtypes = [_vp, _vp, _vp, _i32, ctypes.POINTER(MlaCache), _vp, _i32, _i32, _f32, _f32,
                                      _vp, _vp, _vp]
@@ -198,10 +202,8 @@ def decode_workspace_size(B: int, H: int, num_splits: int = 0) -> int:
     return int(lib().mla_decode_workspace_size(int(B), int(H), int(num_splits)))
 
 
-def decode(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
-           softmax_scale: Optional[float] = None, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
-           z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True):
-    """z[B,H,512], lse[B,H] of one new token per sequence (mla_decode)."""
+def _decode_call(fn_name, q_abs, cache, block_table, seq_lens, softmax_scale, num_splits, workspace, z, lse,
+                 want_lse):
     B, H = q_abs.shape[0], q_abs.shape[1]
     _need(q_abs, "q_abs", cache.input_dtype, (B, H, ROW))
     _need(block_table, "block_table", torch.int32)
@@ -222,10 +224,39 @@ def decode(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, se
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
     desc = cache.descriptor()
-    _check(lib().mla_decode(_ptr(q_abs), ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), B, H,
-                            block_table.shape[1], scale, int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
-                            _ptr(lse), _stream(dev)), "mla_decode")
+    fn = getattr(lib(), fn_name)
+    _check(fn(_ptr(q_abs), ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), B, H, block_table.shape[1], scale,
+              int(num_splits), _ptr(workspace), ws_bytes, _ptr(z), _ptr(lse), _stream(dev)), fn_name)
+    return z, lse, workspace
+
+
+def decode(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+           softmax_scale: Optional[float] = None, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+           z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """z[B,H,512], lse[B,H] of one new token per sequence (mla_decode)."""
+    z, lse, _ = _decode_call("mla_decode", q_abs, cache, block_table, seq_lens, softmax_scale, num_splits,
+                             workspace, z, lse, want_lse)
     return z, lse
+
+
+def decode_partial(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                   workspace: Optional[torch.Tensor], z: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                   softmax_scale: Optional[float] = None, num_splits: int = 0):
+    """The split pass of mla_decode (mla_decode_partial); returns the workspace."""
+    _, _, ws = _decode_call("mla_decode_partial", q_abs, cache, block_table, seq_lens, softmax_scale, num_splits,
+                            workspace, z, lse, lse is not None)
+    return ws
+
+
+def decode_merge(seq_lens: torch.Tensor, H: int, workspace: Optional[torch.Tensor], z: torch.Tensor,
+                 lse: Optional[torch.Tensor] = None, num_splits: int = 0) -> None:
+    """The merge pass of mla_decode (mla_decode_merge)."""
+    B = seq_lens.shape[0]
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(z, "z", torch.float32, (B, H, D_C))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_merge(_ptr(seq_lens), B, int(H), int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
+                                  _ptr(lse), _stream(z.device)), "mla_decode_merge")
 
 
 def prefill_causal(q_abs: torch.Tensor, c_kv: torch.Tensor, k_r: torch.Tensor, cache: PagedCache,

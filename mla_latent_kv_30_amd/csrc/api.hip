@@ -128,21 +128,24 @@ size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits) {
   return workspace_bytes(B, H, make_plan(B, num_splits));
 }
 
-mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
-                      int32_t B, int32_t H, int32_t max_pages, float softmax_scale, int32_t num_splits, void* workspace,
-                      size_t ws_bytes, float* z, float* lse, void* stream) {
+namespace {
+
+// Validate a decode call and fill its launch arguments.
+mla_status prepare_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                          const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
+                          int32_t num_splits, void* workspace, size_t ws_bytes, float* z, float* lse, DecodeArgs& a,
+                          int& kind, Plan& p) {
   if (!q_abs || !block_table || !seq_lens || !z) return MLA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || H > MLA_MAX_HEADS || max_pages < 1) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
-  const int kind = cache_kind(cache);
+  kind = cache_kind(cache);
   if (kind < 0) return MLA_ERR_INVALID_ARG;
   if (kind == kKindFp8) return MLA_ERR_UNSUPPORTED;
   if ((long long)B * num_splits > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
-  const Plan p = make_plan(B, num_splits);
+  p = make_plan(B, num_splits);
   const size_t need = workspace_bytes(B, H, p);
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return MLA_ERR_WORKSPACE;
-  DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q_abs;
   a.rows = (const uint8_t*)cache->rows;
@@ -163,11 +166,55 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
     a.zp = (float*)workspace;
     a.lsep = (float*)((char*)workspace + align256((size_t)p.slots * H * kDc * sizeof(float)));
   }
-  hipStream_t s = (hipStream_t)stream;
+  return MLA_OK;
+}
+
+}  // namespace
+
+mla_status mla_decode_partial(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
+                              int32_t num_splits, void* workspace, size_t ws_bytes, float* z, float* lse,
+                              void* stream) {
+  DecodeArgs a;
+  int kind;
+  Plan p;
+  mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
+                                 workspace, ws_bytes, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
   (void)hipGetLastError();  // clear a stale error so a launch failure is reported as ours
-  mla_status st = launched(launch_decode(a, kind, s));
-  if (st != MLA_OK || p.slots == 0) return st;
-  return launched(launch_merge(a, s));
+  return launched(launch_decode(a, kind, (hipStream_t)stream));
+}
+
+mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits, void* workspace,
+                            size_t ws_bytes, float* z, float* lse, void* stream) {
+  if (!seq_lens || !z || B < 1 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
+  const Plan p = make_plan(B, num_splits);
+  const size_t need = workspace_bytes(B, H, p);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (p.slots == 0) return MLA_OK;  // every sequence was finished in one chunk
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.H = H;
+  a.splits = p.splits;
+  a.units = p.units;
+  a.z = z;
+  a.lse = lse;
+  a.zp = (float*)workspace;
+  a.lsep = (float*)((char*)workspace + align256((size_t)p.slots * H * kDc * sizeof(float)));
+  (void)hipGetLastError();
+  return launched(launch_merge(a, (hipStream_t)stream));
+}
+
+mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
+                      int32_t B, int32_t H, int32_t max_pages, float softmax_scale, int32_t num_splits, void* workspace,
+                      size_t ws_bytes, float* z, float* lse, void* stream) {
+  mla_status st = mla_decode_partial(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
+                                     workspace, ws_bytes, z, lse, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_merge(seq_lens, B, H, num_splits, workspace, ws_bytes, z, lse, stream);
 }
 
 mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,

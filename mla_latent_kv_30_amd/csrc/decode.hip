@@ -39,19 +39,23 @@ constexpr int kPageBytes = kPage * kRowBytes;       // 73728
 // Chunk schedule shared by the decode and merge kernels.
 // ---------------------------------------------------------------------------
 
-// Exclusive prefix sums of pages per sequence into pfx[0..B]; returns total.
-// Called by all 256 threads; B <= kMaxSchedB.
-__device__ int block_page_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx) {
-  __shared__ int wsum[4];
+// Exclusive prefix sums of pages per sequence into pfx[0..B] and the
+// lengths into lens[0..B); returns the total page count.  Called by all
+// threads of the workgroup; B <= kMaxSchedB.
+__device__ int block_page_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx, int* lens) {
+  __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (B + 255) / 256;  // <= 8
+  const int nthreads = blockDim.x;
+  const int per = (B + nthreads - 1) / nthreads;  // <= 4
   const int base = tid * per;
-  int loc[8];
+  int loc[4];
   int sum = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    int v = 0;
-    if (k < per && base + k < B) v = (seq_lens[base + k] + kPage - 1) / kPage;
+  for (int k = 0; k < 4; ++k) {
+    const int i = min(base + k, B - 1);
+    const int L = seq_lens[i];  // loaded unconditionally so the loads overlap
+    const int v = (k < per && base + k < B) ? (L + kPage - 1) / kPage : 0;
+    if (k < per && base + k < B) lens[base + k] = L;
     loc[k] = v;
     sum += v;
   }
@@ -66,11 +70,11 @@ __device__ int block_page_prefix(const int32_t* __restrict__ seq_lens, int B, in
   int excl = x - sum;
   for (int w = 0; w < wave; ++w) excl += wsum[w];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 4; ++k) {
     if (k < per && base + k < B) pfx[base + k] = excl;
     excl += loc[k];
   }
-  if (tid == 255) pfx[B] = excl;
+  if (tid == nthreads - 1) pfx[B] = excl;
   __syncthreads();
   return pfx[B];
 }
@@ -213,6 +217,14 @@ __device__ __forceinline__ void load_query(WaveState& st, const bf16* __restrict
   }
 }
 
+// Use the query registers, so the compiler's own wait for their loads is
+// placed here and not at the first score product, where later page copies
+// (which its counter does not see) would be waited for as well.
+__device__ __forceinline__ void consume_query(WaveState& st) {
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(st.q[kk]));
+}
+
 // Online softmax over NV scores per lane.  x: scaled (log2 units) scores,
 // -inf where masked; p: probabilities relative to the running maximum.  The
 // maximum is only moved when it grows by more than kLazyRescale, so the
@@ -347,6 +359,7 @@ decode_bf16_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   static_assert(TPW % TT == 0, "tile must divide the wave's slice");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kBufBytes];
   __shared__ int pfx[kMaxSchedB + 1];
+  __shared__ int lens[kMaxSchedB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const bool computes = wave < HG * TG;
@@ -354,7 +367,7 @@ decode_bf16_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   const int h0 = hg * 16;
 
   int total = 0;
-  if (a.splits == 0 && a.prefill_T == 0) total = block_page_prefix(a.seq_lens, a.B, pfx);
+  if (a.splits == 0 && a.prefill_T == 0) total = block_page_prefix(a.seq_lens, a.B, pfx, lens);
 
   SegmentIter it = segments_begin(a, pfx, total);
   Segment seg;
@@ -364,23 +377,28 @@ decode_bf16_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     seg.pe = uniform(seg.pe);
     seg.slot = uniform(seg.slot);
     seg.whole = uniform(seg.whole);
-    const int L = uniform(a.prefill_T > 0 ? a.prefill_pos0 + seg.b + 1 : a.seq_lens[seg.b]);
+    const int L = uniform(a.prefill_T > 0 ? a.prefill_pos0 + seg.b + 1
+                                          : (a.splits == 0 ? lens[seg.b] : a.seq_lens[seg.b]));
     const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)seg.b * a.max_pages;
     const bf16* qrow = (const bf16*)a.q + (size_t)seg.b * a.H * kRow;
-
-    WaveState st;
-    load_query(st, qrow, a.H, h0 + (lane & 15), lane >> 4);
-#pragma unroll
-    for (int t = 0; t < 32; ++t) st.zacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    st.m = -INFINITY;
-    st.l = 0.f;
 
     const int npg = seg.pe - seg.pb;
     // block-table reads use a uniform index, so they are scalar loads that do
     // not wait behind the page copies in flight
     auto page_ptr = [&](int pi) { return a.rows + (size_t)bt[uniform(pi)] * kPageBytes; };
     auto page_valid = [&](int pi) { return min(kPage, L - pi * kPage); };
+
+    // The query loads and the first page copy travel together; consuming the
+    // query right after waits for both (the compiler's counter only knows the
+    // query loads), before the second page's copy is issued.
+    WaveState st;
+    load_query(st, qrow, a.H, h0 + (lane & 15), lane >> 4);
     issue_page_copy(page_ptr(seg.pb), smem, page_valid(seg.pb), wave, lane);
+    consume_query(st);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) st.zacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
     for (int i = 0; i < npg; ++i) {
       const int pi = seg.pb + i;
       const uint8_t* buf = smem + (i & 1) * kBufBytes;
@@ -463,10 +481,11 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
   __shared__ float ps[256];
   __shared__ float red[8];
   __shared__ int pfx[kMaxSchedB + 1];
+  __shared__ int lens[kMaxSchedB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
   int total = 0;
-  if (a.splits == 0 && a.prefill_T == 0) total = block_page_prefix(a.seq_lens, a.B, pfx);
+  if (a.splits == 0 && a.prefill_T == 0) total = block_page_prefix(a.seq_lens, a.B, pfx, lens);
   SegmentIter it = segments_begin(a, pfx, total);
   Segment seg;
   while (segments_next(a, pfx, it, seg)) {
@@ -534,9 +553,12 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Split merge: lse = log sum_c e^{lse_c};  z = sum_c e^{lse_c - lse} z_c
 // ---------------------------------------------------------------------------
-// One workgroup per (sequence, 4 heads); one wave per head, 8 channels per lane.
+// One workgroup per (sequence, 4 heads); one wave per head.  The chunks'
+// log-sum-exps are read one per lane and reduced across the wave; then each
+// lane folds its 8 channels of every chunk, several chunk loads in flight.
 __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
   __shared__ int pfx[kMaxSchedB + 1];
+  __shared__ int lens[kMaxSchedB];
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int head = blockIdx.y * 4 + wave;
@@ -552,7 +574,7 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
     last = used - 1;
     slot0 = b * S;
   } else {
-    total = block_page_prefix(a.seq_lens, a.B, pfx);
+    total = block_page_prefix(a.seq_lens, a.B, pfx, lens);
     G = a.units;
     first = unit_of_page(pfx[b], G, total);
     last = unit_of_page(pfx[b + 1] - 1, G, total);
@@ -560,22 +582,53 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
     slot0 = b;  // slot of unit w for sequence b is w + b
   }
   if (head >= a.H) return;
+  const int n = last - first + 1;
   auto owns_pages = [&](int c) { return G == 0 || c * total / G < (c + 1) * total / G; };
+  // pass 1: maximum log-sum-exp over the chunks
   float mmax = -INFINITY;
-  for (int c = first; c <= last; ++c)
-    if (owns_pages(c)) mmax = fmaxf(mmax, a.lsep[(size_t)(slot0 + c) * a.H + head]);
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int c = first + c0 + lane;
+    if (c0 + lane < n && owns_pages(c)) mmax = fmaxf(mmax, a.lsep[(size_t)(slot0 + c) * a.H + head]);
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, d));
+  // pass 2: weights (one chunk per lane) and the weighted sum of the chunks' z
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float wsum = 0.f;
-  for (int c = first; c <= last; ++c) {
-    if (!owns_pages(c)) continue;
-    const size_t sl = (size_t)(slot0 + c) * a.H + head;
-    const float w = __expf(a.lsep[sl] - mmax);
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int c = first + c0 + lane;
+    float w = 0.f;
+    if (c0 + lane < n && owns_pages(c)) w = __expf(a.lsep[(size_t)(slot0 + c) * a.H + head] - mmax);
     wsum += w;
-    const float4* zp = (const float4*)(a.zp + sl * kDc) + lane * 2;
-    const float4 v0 = zp[0], v1 = zp[1];
-    acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
-    acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+    const int m = min(64, n - c0);
+    // Chunks go in batches of 8 whose loads are all in flight together.
+    // Every slot loaded lies inside the workspace; slots of units without
+    // pages hold no partial and are dropped by the select, not by a multiply.
+    for (int i0 = 0; i0 < m; i0 += 8) {
+      float wv[8];
+      float4 v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = min(i0 + u, m - 1);
+        wv[u] = i0 + u < m ? __shfl(w, i) : 0.f;
+        const size_t sl = (size_t)(slot0 + first + c0 + i) * a.H + head;
+        const float4* zp = (const float4*)(a.zp + sl * kDc) + lane * 2;
+        v0[u] = zp[0];
+        v1[u] = zp[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wi = wv[u];
+        const bool use = wi != 0.f;
+        acc[0] += use ? wi * v0[u].x : 0.f; acc[1] += use ? wi * v0[u].y : 0.f;
+        acc[2] += use ? wi * v0[u].z : 0.f; acc[3] += use ? wi * v0[u].w : 0.f;
+        acc[4] += use ? wi * v1[u].x : 0.f; acc[5] += use ? wi * v1[u].y : 0.f;
+        acc[6] += use ? wi * v1[u].z : 0.f; acc[7] += use ? wi * v1[u].w : 0.f;
+      }
+    }
   }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) wsum += __shfl_xor(wsum, d);
   const float inv = 1.0f / wsum;
   float4* zo = (float4*)(a.z + ((size_t)b * a.H + head) * kDc) + lane * 2;
   zo[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);

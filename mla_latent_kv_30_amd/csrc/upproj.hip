@@ -72,6 +72,71 @@ __global__ void __launch_bounds__(256) upproj_bf16_kernel(UpprojArgs a) {
   }
 }
 
+// Few query rows (decode, N <= 64): workgroup = (head, 32-row tile of d);
+// the 4 waves split the contraction over c (128 each) so every wave keeps
+// only 8 operand loads in flight, and the partial sums meet in LDS.
+__global__ void __launch_bounds__(256) upproj_bf16_small_kernel(UpprojArgs a) {
+  __shared__ floatx16 red[3][2][64];
+  const int h = blockIdx.x >> 2, dt = blockIdx.x & 3;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const bf16* w = (const bf16*)a.w_uv + ((size_t)h * kDv + 32 * dt + (lane & 31)) * kDc;
+  int nrow[2];
+  bool nok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    nrow[nt] = 32 * nt + (lane & 31);
+    nok[nt] = nrow[nt] < a.N;
+  }
+  floatx16 acc[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int c0 = 128 * wave + 16 * kk + 8 * g;
+    const bf16x8 aw = __builtin_bit_cast(bf16x8, *(const int4v*)(w + c0));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (32 * nt >= a.N) break;
+      float4 u0 = make_float4(0, 0, 0, 0), u1 = u0;
+      if (nok[nt]) {
+        const float4* zp = (const float4*)(a.z + ((size_t)nrow[nt] * a.H + h) * kDc + c0);
+        u0 = zp[0];
+        u1 = zp[1];
+      }
+      const bf16x8 bz = {f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
+                         f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
+      acc[nt] = mfma32(aw, bz, acc[nt]);
+    }
+  }
+  if (wave > 0) {
+    red[wave - 1][0][lane] = acc[0];
+    red[wave - 1][1][lane] = acc[1];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int o = 0; o < 3; ++o) {
+    acc[0] += red[o][0][lane];
+    acc[1] += red[o][1][lane];
+  }
+  // C layout: column = query row, rows d = 32 dt + 8(r/4) + 4g + r%4
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if (!nok[nt]) continue;
+    const size_t base = ((size_t)nrow[nt] * a.H + h) * kDv + 32 * dt;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 8 * q4 + 4 * g;
+      const floatx16& v = acc[nt];
+      if (a.o_bf16) {
+        bf16x4 ov = {f2bf(v[4 * q4]), f2bf(v[4 * q4 + 1]), f2bf(v[4 * q4 + 2]), f2bf(v[4 * q4 + 3])};
+        *(bf16x4*)((bf16*)a.o + base + d) = ov;
+      } else {
+        *(float4*)((float*)a.o + base + d) = make_float4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
+      }
+    }
+  }
+}
+
 // fp32 weights: one workgroup per (row, head), z in LDS, one thread per d
 // with 2 threads sharing a row of W (halves of c), exact fp32 FMA chains.
 __global__ void __launch_bounds__(256) upproj_f32_kernel(UpprojArgs a) {
@@ -98,6 +163,8 @@ __global__ void __launch_bounds__(256) upproj_f32_kernel(UpprojArgs a) {
 hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s) {
   if (w_kind == kKindF32) {
     hipLaunchKernelGGL(upproj_f32_kernel, dim3(a.N * a.H), dim3(256), 0, s, a);
+  } else if (a.N <= 64) {
+    hipLaunchKernelGGL(upproj_bf16_small_kernel, dim3(a.H * 4), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(upproj_bf16_kernel, dim3(a.H, (a.N + 255) / 256), dim3(256), 0, s, a);
   }
