@@ -146,11 +146,17 @@ size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits);
  *   block_table  [B][max_pages] int32 pool page of each 64-token block
  *   seq_lens     [B] int32 cached tokens per sequence, 1 <= L <= 64*max_pages
  *                (the query is the newest of them)
- *   num_splits   0: the library balances the pages of all sequences over
- *                the device's compute units (a chunk may span sequences);
- *                S > 0: sequence b is cut into S chunks of
+ *   num_splits   0: the library cuts the 32-token blocks of all sequences
+ *                into one nearly equal range per compute unit (a range may
+ *                span sequences); S > 0: sequence b is cut into S chunks of
  *                ceil(ceil(L_b/64)/S) pages (trailing chunks may be empty).
- *   workspace    device scratch of at least mla_decode_workspace_size bytes
+ *   workspace    device scratch of at least mla_decode_workspace_size bytes.
+ *                It starts with one arrival counter per sequence, through
+ *                which the last chunk to finish merges a split sequence in
+ *                the same kernel: the workspace must be zero-filled once
+ *                before its first use with mla_decode, and every completed
+ *                call leaves the counters at zero again.  Calls that share a
+ *                workspace must not run concurrently.
  *   z            [B][H][512] fp32 out: normalised latent aggregate
  *   lse          [B][H] fp32 out (may be NULL): natural-log log-sum-exp of
  *                the scaled scores
@@ -168,14 +174,15 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
 /*
  * The two halves of mla_decode, for callers that schedule the merge
  * themselves (overlapping it with other work, or combining chunk partials
- * produced by several calls).  mla_decode(...) is exactly
+ * produced by several calls).  mla_decode(...) computes exactly what
  * mla_decode_partial(...) followed by mla_decode_merge(...) on the same
- * stream with the same arguments.
+ * stream with the same arguments computes.
  *
  * mla_decode_partial: the split pass.  Sequences that fall into a single
  * chunk get their final z / lse; every other chunk leaves its normalised
  * partial (z_c, lse_c) in the workspace.  Same arguments and errors as
- * mla_decode.
+ * mla_decode; the arrival counters are neither read nor written, so the
+ * workspace needs no zero fill for this pair of calls.
  */
 mla_status mla_decode_partial(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
                               const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
@@ -200,12 +207,12 @@ mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32
  * current position).  pos0 tokens must already be in the cache.
  *   q_abs           [T][H][576] from mla_absorb_q with pos = pos0 + t
  *   c_kv, k_r       [T][512], [T][64] the new tokens (k_r before rotation)
- *   cache           the pool (bf16 or fp32 rows)
+ *   cache           the pool (fp32 or bf16 rows, or the fp8 form, into which
+ *                   the new tokens are quantised as mla_cache_write does)
  *   block_table_row [ceil((pos0+T)/64)] int32 pool pages of the sequence
  *   z               [T][H][512] fp32 out; lse [T][H] fp32 out or NULL
- * dtype of q_abs, c_kv, k_r follows the cache (fp32 or bf16).
- * Errors: MLA_ERR_INVALID_ARG as for mla_decode; MLA_ERR_UNSUPPORTED for an
- * fp8 cache.
+ * dtype of q_abs, c_kv, k_r: fp32 for an fp32 cache, bf16 otherwise.
+ * Errors: MLA_ERR_INVALID_ARG as for mla_decode.
  */
 mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
                               const mla_cache* cache, const int32_t* block_table_row, int32_t T,

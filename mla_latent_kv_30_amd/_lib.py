@@ -202,6 +202,12 @@ def decode_workspace_size(B: int, H: int, num_splits: int = 0) -> int:
     return int(lib().mla_decode_workspace_size(int(B), int(H), int(num_splits)))
 
 
+def decode_workspace(B: int, H: int, num_splits: int = 0, device="cuda") -> Optional[torch.Tensor]:
+    """A zero-filled workspace for mla_decode (its arrival counters must start at zero)."""
+    need = decode_workspace_size(B, H, num_splits)
+    return torch.zeros(need, dtype=torch.uint8, device=device) if need > 0 else None
+
+
 def _decode_call(fn_name, q_abs, cache, block_table, seq_lens, softmax_scale, num_splits, workspace, z, lse,
                  want_lse):
     B, H = q_abs.shape[0], q_abs.shape[1]
@@ -218,9 +224,8 @@ def _decode_call(fn_name, q_abs, cache, block_table, seq_lens, softmax_scale, nu
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, H))
-    need = decode_workspace_size(B, H, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = decode_workspace(B, H, num_splits, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
     desc = cache.descriptor()
@@ -233,7 +238,11 @@ def _decode_call(fn_name, q_abs, cache, block_table, seq_lens, softmax_scale, nu
 def decode(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
            softmax_scale: Optional[float] = None, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
            z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True):
-    """z[B,H,512], lse[B,H] of one new token per sequence (mla_decode)."""
+    """z[B,H,512], lse[B,H] of one new token per sequence (mla_decode).
+
+    A workspace passed in must have been zero-filled once (decode_workspace);
+    every completed call leaves it ready for the next one.
+    """
     z, lse, _ = _decode_call("mla_decode", q_abs, cache, block_table, seq_lens, softmax_scale, num_splits,
                              workspace, z, lse, want_lse)
     return z, lse

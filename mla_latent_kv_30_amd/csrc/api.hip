@@ -80,9 +80,28 @@ Plan make_plan(int32_t B, int32_t num_splits) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t workspace_bytes(int32_t B, int32_t H, const Plan& p) {
-  if (p.slots == 0) return 0;
-  return align256((size_t)p.slots * H * kDc * sizeof(float)) + align256((size_t)p.slots * H * sizeof(float));
+// Workspace layout: [B arrival counters][partial z: slots x H x 512][partial lse: slots x H]
+struct WsLayout {
+  size_t counters, zp, lsep, total;
+};
+
+WsLayout ws_layout(int32_t B, int32_t H, const Plan& p) {
+  WsLayout w{0, 0, 0, 0};
+  if (p.slots == 0) return w;
+  w.counters = 0;
+  w.zp = align256((size_t)B * sizeof(int32_t));
+  w.lsep = w.zp + align256((size_t)p.slots * H * kDc * sizeof(float));
+  w.total = w.lsep + align256((size_t)p.slots * H * sizeof(float));
+  return w;
+}
+
+size_t workspace_bytes(int32_t B, int32_t H, const Plan& p) { return ws_layout(B, H, p).total; }
+
+void set_workspace(DecodeArgs& a, void* workspace, int32_t B, int32_t H, const Plan& p) {
+  if (p.slots == 0) return;
+  const WsLayout w = ws_layout(B, H, p);
+  a.zp = (float*)((char*)workspace + w.zp);
+  a.lsep = (float*)((char*)workspace + w.lsep);
 }
 
 }  // namespace
@@ -141,7 +160,6 @@ mla_status prepare_decode(const void* q_abs, const mla_cache* cache, const int32
   if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
   kind = cache_kind(cache);
   if (kind < 0) return MLA_ERR_INVALID_ARG;
-  if (kind == kKindFp8) return MLA_ERR_UNSUPPORTED;
   if ((long long)B * num_splits > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
   p = make_plan(B, num_splits);
   const size_t need = workspace_bytes(B, H, p);
@@ -162,10 +180,7 @@ mla_status prepare_decode(const void* q_abs, const mla_cache* cache, const int32
   a.scale_log2 = (float)(softmax_scale * 1.4426950408889634074);
   a.z = z;
   a.lse = lse;
-  if (p.slots > 0) {
-    a.zp = (float*)workspace;
-    a.lsep = (float*)((char*)workspace + align256((size_t)p.slots * H * kDc * sizeof(float)));
-  }
+  set_workspace(a, workspace, B, H, p);
   return MLA_OK;
 }
 
@@ -202,8 +217,7 @@ mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32
   a.units = p.units;
   a.z = z;
   a.lse = lse;
-  a.zp = (float*)workspace;
-  a.lsep = (float*)((char*)workspace + align256((size_t)p.slots * H * kDc * sizeof(float)));
+  set_workspace(a, workspace, B, H, p);
   (void)hipGetLastError();
   return launched(launch_merge(a, (hipStream_t)stream));
 }
@@ -211,10 +225,23 @@ mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32
 mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
                       int32_t B, int32_t H, int32_t max_pages, float softmax_scale, int32_t num_splits, void* workspace,
                       size_t ws_bytes, float* z, float* lse, void* stream) {
-  mla_status st = mla_decode_partial(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
-                                     workspace, ws_bytes, z, lse, stream);
+  DecodeArgs a;
+  int kind;
+  Plan p;
+  mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
+                                 workspace, ws_bytes, z, lse, a, kind, p);
   if (st != MLA_OK) return st;
-  return mla_decode_merge(seq_lens, B, H, num_splits, workspace, ws_bytes, z, lse, stream);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (kind == kKindF32) {  // the fp32 path leaves its partials to the merge kernel
+    st = launched(launch_decode(a, kind, s));
+    if (st != MLA_OK || p.slots == 0) return st;
+    return launched(launch_merge(a, s));
+  }
+  // matrix-core paths merge in place: the last unit to finish a piece of a
+  // sequence combines its pieces (arrival counters at the workspace start)
+  if (p.slots > 0) a.counters = (int32_t*)((char*)workspace + ws_layout(B, H, p).counters);
+  return launched(launch_decode(a, kind, s));
 }
 
 mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
@@ -227,12 +254,11 @@ mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k
   if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
   const int kind = cache_kind(cache);
   if (kind < 0) return MLA_ERR_INVALID_ARG;
-  if (kind == kKindFp8) return MLA_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   // 1. append the T new tokens: position pos0 + t, slot from the block-table row
-  CacheWriteArgs w{c_kv, k_r, nullptr, nullptr, block_table_row, pos0, T, cache->rows, nullptr, nullptr, nullptr,
-                   rope_table(rope_base)};
+  CacheWriteArgs w{c_kv,         k_r, nullptr, nullptr, block_table_row, pos0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
+                   cache->ckv_scale, cache->kr, rope_table(rope_base)};
   mla_status st = launched(launch_cache_write(w, kind, s));
   if (st != MLA_OK) return st;
   // 2. causal attention: query row t sees cached tokens 0 .. pos0 + t
@@ -240,6 +266,9 @@ mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k
   memset(&a, 0, sizeof(a));
   a.q = q_abs;
   a.rows = (const uint8_t*)cache->rows;
+  a.ckv8 = (const uint8_t*)cache->ckv_fp8;
+  a.scale8 = cache->ckv_scale;
+  a.kr8 = (const uint8_t*)cache->kr;
   a.block_table = block_table_row;
   a.B = T;
   a.H = H;

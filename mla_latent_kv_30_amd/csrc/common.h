@@ -57,6 +57,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds_byte_ptr) {
 __device__ __forceinline__ int4v lds_read_b128(const void* lds_byte_ptr) {
   return *(const MLA_LDS int4v*)(lds_byte_ptr);
 }
+// The same reads at a 32-bit LDS byte address (keeps address arithmetic in
+// single registers instead of 64-bit generic pointers).
+__device__ __forceinline__ bf16x4 lds_read_tr16_at(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(uintptr_t)addr);
+}
+__device__ __forceinline__ int4v lds_read_b128_at(uint32_t addr) {
+  return *(const MLA_LDS int4v*)(uintptr_t)addr;
+}
 
 // Value that is the same in every lane, moved to scalar registers.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

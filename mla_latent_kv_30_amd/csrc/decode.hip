@@ -4,29 +4,34 @@
 //   s_j = (q~_i . c_j + q^R_i . k^R_j) * scale     (§注意力计算 + §潜在向量的作用)
 //   a_j = softmax_j(s),  z_i = sum_j a_j c_j        (§潜在向量的作用)
 // All heads of a sequence read the same cached rows, so for a 64-token page
-// the scores of the wave's heads are one dense product S^T = R Q^T
+// the scores of a wave's heads are one dense product S^T = R Q^T
 // (R: 64 x 576 rows, Q: heads x 576), and the latent accumulation is a second
 // one, Z^T += C^T P^T (C: the 512-wide c^KV part of the rows).  Both run on
 // bf16 matrix cores with fp32 accumulation.
 //
-// Work decomposition (one 256-thread workgroup per chunk of pages):
-//   * The page's 64 rows (72 KB bf16) are copied HBM -> LDS with
-//     asynchronous 16-byte LDS-DMA loads into one of two buffers while the
-//     other buffer is being consumed, so every row is read from HBM once and
-//     shared by all heads.
-//   * Wave w owns HPW heads (hg = w % HG) and a token slice of each page
-//     (tg = w / HG).  Its absorbed query stays in VGPRs for the whole chunk,
-//     its accumulator Z^T (HPW x 512 fp32) in accumulation registers, and
-//     every value a lane holds belongs to one head, so the online softmax
-//     rescale never leaves the lane.
+// Work decomposition (one 512-thread workgroup per unit of work):
+//   * Pages stream HBM -> LDS with asynchronous LDS-DMA loads into one
+//     buffer while the previous page is consumed; every row is read from HBM
+//     once and shared by all heads.  The stream runs on across the sequence
+//     boundaries inside a unit, so a unit never waits for a cold first page.
+//   * Wave w owns 16 heads (hg = w % HG) and a token slice of each page
+//     (tg = w / HG).  Its absorbed query stays in VGPRs, its accumulator Z^T
+//     (16 heads x 512 fp32) in accumulation registers, and every value a lane
+//     holds belongs to one head, so the online softmax never leaves the lane.
 //   * Score operand: 16-byte LDS reads of rows.  Value operand: gfx950's
 //     transposing LDS read (ds_read_b64_tr_b16) turns row-major c^KV into
 //     token-packed matrix-core operands without a transposed copy.
-//   * Row pairs are padded in LDS so the operand reads of consecutive rows,
-//     and of the rows the transposing reads fetch together, hit distinct banks.
+//   * fp8 cache: the e4m3 codes, their per-(token, 128-channel) scales and
+//     the bf16 k^R of a page land in a staging buffer and are expanded once
+//     into the same bf16 row layout (code * scale rounded to bf16), so the
+//     matrix-core part is shared with the bf16 cache ("DeepSeek-V3 Technical
+//     Report", process-cxr.github.io, §Fine-grained quantization: scaling per
+//     1 x 128 tile of a token, applied when the tile is consumed).
 //   * Long sequences are cut into chunks; each chunk leaves a normalised
-//     partial (z_c, lse_c) that the merge kernel combines exactly:
-//     lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c.
+//     partial (z_c, lse_c) that is combined exactly:
+//     lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c.  Either a
+//     separate merge kernel does it, or the last unit to finish a chunk of a
+//     sequence (found with a per-sequence arrival counter) merges it in place.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,15 +39,25 @@ namespace mla {
 
 constexpr int kRowBytes = kRow * 2;                 // 1152
 constexpr int kPageBytes = kPage * kRowBytes;       // 73728
+constexpr int kBlock = 32;                          // scheduling granule (tokens)
 
 // ---------------------------------------------------------------------------
-// Chunk schedule shared by the decode and merge kernels.
+// Work schedule shared by the decode and merge kernels.
 // ---------------------------------------------------------------------------
+//
+// Three modes:
+//   prefill  unit w = query row T-1-w of one sequence (longest rows first);
+//   uniform  S chunks per sequence, chunk = ceil(ceil(L/64)/S) pages,
+//            unit w = (b = w/S, chunk w%S), partial slot w;
+//   balanced the 32-token blocks of all sequences, concatenated, are cut into
+//            G nearly equal ranges (G = min(units, blocks)); a unit walks the
+//            sequences its range touches.  Unit w's piece of sequence b goes
+//            to partial slot w + b (unique: the pieces of unit w have
+//            increasing b, and unit w+1 starts at or after unit w's last b).
 
-// Exclusive prefix sums of pages per sequence into pfx[0..B] and the
-// lengths into lens[0..B); returns the total page count.  Called by all
-// threads of the workgroup; B <= kMaxSchedB.
-__device__ int block_page_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx, int* lens) {
+// Exclusive prefix sums of the 32-token block counts into pfx[0..B];
+// returns the total.  Called by all threads; B <= kMaxSchedB.
+__device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthreads = blockDim.x;
@@ -54,8 +69,7 @@ __device__ int block_page_prefix(const int32_t* __restrict__ seq_lens, int B, in
   for (int k = 0; k < 4; ++k) {
     const int i = min(base + k, B - 1);
     const int L = seq_lens[i];  // loaded unconditionally so the loads overlap
-    const int v = (k < per && base + k < B) ? (L + kPage - 1) / kPage : 0;
-    if (k < per && base + k < B) lens[base + k] = L;
+    const int v = (k < per && base + k < B) ? (L + kBlock - 1) / kBlock : 0;
     loc[k] = v;
     sum += v;
   }
@@ -76,124 +90,230 @@ __device__ int block_page_prefix(const int32_t* __restrict__ seq_lens, int B, in
   }
   if (tid == nthreads - 1) pfx[B] = excl;
   __syncthreads();
-  return pfx[B];
+  return uniform(pfx[B]);
 }
 
-// Unit that owns global page g in the balanced split of `total` pages over G units.
-__device__ __forceinline__ int unit_of_page(long long g, long long G, long long total) {
-  return (int)(((g + 1) * G - 1) / total);
+// Unit of the balanced split that owns block g (G units over P blocks).
+__device__ __forceinline__ int unit_of_block(long long g, long long G, long long P) {
+  return (int)(((g + 1) * G - 1) / P);
 }
 
+// One piece of work: tokens [t0, t1) of sequence b, whose length is L.
 struct Segment {
-  int b, pb, pe, slot, whole;
+  int b, t0, t1, L;
+  int slot;   // partial slot of this piece
+  int slot0;  // partial slot of the sequence's first piece
+  int parts;  // pieces the sequence was cut into (1: this one is whole)
 };
 
-// Walks the segments (sequence, page range) of this workgroup's unit in order.
-// Every thread of the workgroup sees the same sequence of segments.
-struct SegmentIter {
-  int mode;             // 0 prefill, 1 uniform splits, 2 balanced
-  int b, b_end;         // balanced: next sequence to look at
-  long long g0, g1;     // balanced: global page range of this unit
+struct Schedule {
+  int mode;          // 0 prefill, 1 uniform, 2 balanced
+  int w;             // this unit
+  long long G, P;    // balanced: units in use, total blocks
+  long long g0, g1;  // balanced: this unit's block range
+  int b;             // balanced: next sequence to look at
   int done;
 };
 
-__device__ __forceinline__ SegmentIter segments_begin(const DecodeArgs& a, const int* pfx, int total) {
-  SegmentIter it{};
-  const int w = blockIdx.x;
+__device__ __forceinline__ Schedule schedule_begin(const DecodeArgs& a, const int* pfx, int P) {
+  Schedule s{};
+  s.w = blockIdx.x;
   if (a.prefill_T > 0) {
-    it.mode = 0;
+    s.mode = 0;
   } else if (a.splits > 0) {
-    it.mode = 1;
+    s.mode = 1;
   } else {
-    it.mode = 2;
-    const long long G = a.units;
-    it.g0 = (long long)w * total / G;
-    it.g1 = (long long)(w + 1) * total / G;
-    int lo = 0, hi = a.B;  // last b with pfx[b] <= g0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pfx[mid] <= it.g0) lo = mid; else hi = mid;
+    s.mode = 2;
+    s.P = P;
+    s.G = min((long long)a.units, (long long)P);
+    s.done = s.w >= s.G;
+    if (!s.done) {
+      s.g0 = (long long)s.w * s.P / s.G;
+      s.g1 = (long long)(s.w + 1) * s.P / s.G;
+      int lo = 0, hi = a.B;  // last b with pfx[b] <= g0
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pfx[mid] <= s.g0) lo = mid; else hi = mid;
+      }
+      s.b = uniform(lo);
     }
-    it.b = lo;
-    it.done = it.g0 >= it.g1;
   }
-  return it;
+  return s;
 }
 
-__device__ __forceinline__ bool segments_next(const DecodeArgs& a, const int* pfx, SegmentIter& it, Segment& seg) {
-  if (it.done) return false;
-  const int w = blockIdx.x;
-  if (it.mode == 0) {  // one query row per unit, longest rows first
-    it.done = 1;
-    const int t = a.prefill_T - 1 - w;
+// Next piece of this unit's work; every thread of the workgroup gets the
+// same answer.
+__device__ __forceinline__ bool schedule_next(const DecodeArgs& a, const int* pfx, Schedule& s, Segment& seg) {
+  if (s.done) return false;
+  if (s.mode == 0) {
+    s.done = 1;
+    const int t = a.prefill_T - 1 - s.w;
     const int L = a.prefill_pos0 + t + 1;
-    seg = Segment{t, 0, (L + kPage - 1) / kPage, 0, 1};
+    seg = Segment{t, 0, L, L, 0, 0, 1};
     return true;
   }
-  if (it.mode == 1) {
-    it.done = 1;
+  if (s.mode == 1) {
+    s.done = 1;
     const int S = a.splits;
-    const int b = w / S, s = w % S;
-    const int np = (a.seq_lens[b] + kPage - 1) / kPage;
+    const int b = s.w / S, k = s.w % S;
+    const int L = a.seq_lens[b];
+    const int np = (L + kPage - 1) / kPage;
     const int chunk = (np + S - 1) / S;
-    const int pb = s * chunk, pe = min(pb + chunk, np);
-    seg = Segment{b, pb, pe, w, (pb == 0 && pe == np) ? 1 : 0};
-    return pb < pe;
+    const int pb = k * chunk, pe = min(pb + chunk, np);
+    if (pb >= pe) return false;
+    seg = Segment{b, pb * kPage, min(pe * kPage, L), L, s.w, b * S, (np + chunk - 1) / chunk};
+    return true;
   }
-  while (it.b < a.B && pfx[it.b] < it.g1) {
-    const int b = it.b++;
-    const int np = pfx[b + 1] - pfx[b];
-    const int pb = (int)(max(it.g0, (long long)pfx[b]) - pfx[b]);
-    const int pe = (int)(min(it.g1, (long long)pfx[b + 1]) - pfx[b]);
-    if (pb < pe) {
-      seg = Segment{b, pb, pe, w + b, (pb == 0 && pe == np) ? 1 : 0};
+  while (s.b < a.B) {
+    const int b = s.b;
+    const int p0 = uniform(pfx[b]), p1 = uniform(pfx[b + 1]);
+    if (p0 >= s.g1) break;
+    s.b = b + 1;
+    const int k0 = (int)(max(s.g0, (long long)p0) - p0);
+    const int k1 = (int)(min(s.g1, (long long)p1) - p0);
+    if (k0 < k1) {
+      const int L = a.seq_lens[b];
+      const int first = unit_of_block(p0, s.G, s.P);
+      const int last = unit_of_block(p1 - 1, s.G, s.P);
+      seg = Segment{b, k0 * kBlock, min(k1 * kBlock, L), L, s.w + b, first + b, last - first + 1};
       return true;
     }
   }
-  it.done = 1;
+  s.done = 1;
   return false;
 }
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core decode
+// LDS page layout
 // ---------------------------------------------------------------------------
 //
-// LDS page layout.  A page is 64 rows of 1152 bytes.  Rows are kept in
-// pairs: rows 2k and 2k+1 are 2304 contiguous bytes in HBM and land in LDS at
-// k * kGroupStride, copied by nine 256-byte LDS-DMA instructions (4 bytes per
-// lane, fully coalesced).  The 16 extra bytes per pair put 16 consecutive rows
-// on 16 distinct 16-byte bank slots (row 2k+1 sits 128 bytes after row 2k
-// mod 256), and rows i, i+4, i+8, i+12 on one contiguous 128-byte span, which
-// is what the value-operand transposing reads below fetch together.
-constexpr int kGroupBytes = 2 * kRowBytes;             // 2304
-constexpr int kGroupStride = kGroupBytes + 16;         // 2320
-constexpr int kBufBytes = (kPage / 2) * kGroupStride;  // 74240
+// A page is 64 rows of 1152 bytes, stored unpadded: row r at r * 1152.  The
+// 16-byte chunks of a row are permuted inside each aligned group of eight:
+// chunk c of row r sits at chunk position c ^ swz(r).  gfx950 serves a
+// 16-byte LDS read per half-wave (even lanes, then odd lanes) over 128 banks
+// of 4 bytes, and the transposing 8-byte read per quarter-wave; without the
+// permutation the rows of an operand tile (1152 = 9 * 128) would pile onto a
+// quarter of the banks.  With it, the score operand reads, the transposing
+// value reads and the dequantising writes below are all conflict-free.
+// Rows 2k and 2k+1 share swz, so a row pair (2304 contiguous bytes in HBM)
+// is still moved by nine 256-byte LDS-DMA instructions: lane i fetches the
+// 4 bytes that belong at pair offset (256 k + 4 i), i.e. HBM pair offset
+// 256 k + ((4 i) ^ (swz << 4)).
+constexpr int kBufBytes = kPageBytes;                  // one bf16 page
 constexpr int kDmaBytes = 256;                         // 64 lanes x 4 bytes
-constexpr int kDmaPerGroup = kGroupBytes / kDmaBytes;  // 9
+constexpr int kPairBytes = 2 * kRowBytes;              // 2304
+constexpr int kDmaPerPair = kPairBytes / kDmaBytes;    // 9
 constexpr int kWaves = 8;                              // every decode workgroup has 8 waves
-constexpr int kDmaPerWave = (kPage / 2) / kWaves * kDmaPerGroup;  // 36 (< 64 outstanding)
+constexpr int kRowsPerWave = kPage / kWaves;           // 8
+constexpr int kDmaPerWave = kRowsPerWave / 2 * kDmaPerPair;  // 36 (< 64 outstanding)
 constexpr int kRsrcWord3 = 0x00020000;                 // raw untyped buffer access
 
-__device__ __forceinline__ int lds_row(int t) { return (t >> 1) * kGroupStride + (t & 1) * kRowBytes; }
+__device__ __forceinline__ int swz(int r) { return 2 * ((r >> 2) & 3) + ((r >> 4) & 1); }
+// LDS byte offset of byte x (x < 1152) of row r.
+__device__ __forceinline__ int lds_off(int r, int x) { return r * kRowBytes + (x ^ (swz(r) << 4)); }
 
-// Copy one cache page into an LDS buffer: wave w moves row pairs 4w .. 4w+3.
-// The buffer resource covers exactly the `valid` rows of the page: the copy
-// cannot leave them, and rows past the end of the sequence arrive as zeros,
-// so stale or non-finite pool contents never reach the matrix cores.
-__device__ __forceinline__ void issue_page_copy(const uint8_t* page, uint8_t* buf, int valid, int wave, int lane) {
-  // Re-derive the wave's offsets at every copy instead of keeping dozens of
-  // loop-invariant scalars alive across the page loop.
-  asm volatile("" : "+s"(wave));
+// Copy rows [lo, hi) of a bf16 page into an LDS buffer; wave w moves rows
+// 8w .. 8w+7.  The buffer resource covers exactly the first `hi` rows, so
+// rows at or past hi (past the sequence end, or owned by the next unit)
+// arrive as zeros and stale or non-finite pool contents never reach the
+// matrix cores.  Rows below lo (only ever 0 or 32) belong to the previous
+// unit: waves whose rows all lie there issue nothing, and the compute skips
+// those rows.
+__device__ __forceinline__ void issue_page_bf16(const uint8_t* page, uint8_t* buf, int lo, int hi, int wave,
+                                                int lane) {
+  asm volatile("" : "+s"(wave));  // re-derived per copy, not kept live across the loop
+  if (wave * kRowsPerWave + kRowsPerWave <= lo) return;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(page), (short)0,
-                                                                      uniform(valid * kRowBytes), kRsrcWord3);
-  const uint32_t vo = lane * 4;
+                                                                      uniform(hi * kRowBytes), kRsrcWord3);
   const uint32_t lb = lds_addr(buf);
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int grp = wave * (kDmaPerWave / kDmaPerGroup) + i / kDmaPerGroup, part = i % kDmaPerGroup;
-    lds_dma4(rs, lb + grp * kGroupStride + part * kDmaBytes, vo, grp * kGroupBytes + part * kDmaBytes);
+  for (int j = 0; j < kRowsPerWave / 2; ++j) {
+    const int pair = wave * (kRowsPerWave / 2) + j;
+    const uint32_t vo = (uint32_t)((lane * 4) ^ (swz(2 * pair) << 4));
+#pragma unroll
+    for (int k = 0; k < kDmaPerPair; ++k) {
+      const int off = pair * kPairBytes + k * kDmaBytes;
+      lds_dma4(rs, lb + off, vo, off);
+    }
   }
 }
+
+// fp8 staging buffer of one page: codes [64][512], scales [64][4] fp32,
+// rotated k^R [64][64] bf16.
+constexpr int kStCkv = 0;
+constexpr int kStScale = kPage * kDc;                  // 32768
+constexpr int kStKr = kStScale + kPage * 4 * 4;        // 33792
+constexpr int kStageBytes = kStKr + kPage * kDr * 2;   // 41984
+constexpr int kFp8DmaPerWave = 16 + 1 + 4;             // codes, scales (half wave), k^R
+
+__device__ __forceinline__ void issue_page_fp8(const uint8_t* ckv8, const float* scale8, const uint8_t* kr8,
+                                               int page, uint8_t* stage, int lo, int hi, int wave, int lane) {
+  asm volatile("" : "+s"(wave));
+  if (wave * kRowsPerWave + kRowsPerWave <= lo) return;
+  const size_t pg = (size_t)page;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(ckv8 + pg * (kPage * kDc)), (short)0, uniform(hi * kDc), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(scale8 + pg * (kPage * 4)), (short)0, uniform(hi * 16), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(kr8 + pg * (kPage * kDr * 2)), (short)0, uniform(hi * kDr * 2), kRsrcWord3);
+  const uint32_t lb = lds_addr(stage);
+  const uint32_t vo = lane * 4;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {  // codes: rows 8w .. 8w+7 are 4096 contiguous bytes
+    const int off = wave * (kRowsPerWave * kDc) + k * kDmaBytes;
+    lds_dma4(rc, lb + kStCkv + off, vo, off);
+  }
+  if (lane < 32) {  // scales: 8 rows x 16 bytes
+    const int off = wave * (kRowsPerWave * 16);
+    lds_dma4(rsc, lb + kStScale + off, vo, off);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // k^R: 8 rows x 128 bytes
+    const int off = wave * (kRowsPerWave * kDr * 2) + k * kDmaBytes;
+    lds_dma4(rk, lb + kStKr + off, vo, off);
+  }
+}
+
+// Expand a staged fp8 page into the bf16 row layout.  Thread t: row t/8,
+// channels 64(t%8) .. +63 (one 128-channel tile's half, one scale), plus one
+// 16-byte chunk of the row's k^R.  Rows past the valid range are zeros in
+// the staging buffer (codes and scales), so they expand to zeros.
+__device__ __forceinline__ void dequant_page(const uint8_t* stage, uint8_t* buf) {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));  // offsets recomputed per page, not held across the loop
+  const int r = t >> 3, sub = t & 7;
+  const float sc = *(const float*)(stage + kStScale + (r * 4 + (sub >> 1)) * 4);
+  const uint8_t* src = stage + kStCkv + r * kDc + sub * 64;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int4v raw = lds_read_b128(src + 16 * j);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int word = raw[2 * h + e];
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+        v[4 * e + 0] = f2bf(lo[0] * sc);
+        v[4 * e + 1] = f2bf(lo[1] * sc);
+        v[4 * e + 2] = f2bf(hi[0] * sc);
+        v[4 * e + 3] = f2bf(hi[1] * sc);
+      }
+      const int chunk = sub * 8 + 2 * j + h;  // 8 channels = one 16-byte chunk
+      *(MLA_LDS bf16x8*)(buf + lds_off(r, chunk * 16)) = v;
+    }
+    asm volatile("" ::: "memory");  // one 16-code read in flight at a time
+  }
+  const int kc = t & 7;
+  const int4v kr = lds_read_b128(stage + kStKr + r * (kDr * 2) + kc * 16);
+  *(MLA_LDS int4v*)(buf + lds_off(r, kDc * 2 + kc * 16)) = kr;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core compute on one page buffer
+// ---------------------------------------------------------------------------
 
 // Per-wave state: 16 heads.  Lane l serves head h0 + l%16; its lane group
 // g = l/16 picks which channels / tokens of each matrix-core operand it holds.
@@ -225,6 +345,13 @@ __device__ __forceinline__ void consume_query(WaveState& st) {
   for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(st.q[kk]));
 }
 
+__device__ __forceinline__ void reset_state(WaveState& st) {
+#pragma unroll
+  for (int t = 0; t < 32; ++t) st.zacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
 // Online softmax over NV scores per lane.  x: scaled (log2 units) scores,
 // -inf where masked; p: probabilities relative to the running maximum.  The
 // maximum is only moved when it grows by more than kLazyRescale, so the
@@ -253,34 +380,42 @@ __device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[NV], fl
   st.l += sum;
 }
 
-// Score of one 16-token subtile (rows t0 .. t0+15): S^T (16 tokens x 16 heads),
-// K = 576 in 18 steps of 32 channels.  Row index m of the product maps to
-// token t0 + 4(m%4) + m/4, so score register r of lane group g is token
-// t0 + 4r + g.
-__device__ __forceinline__ floatx4 score16(const WaveState& st, const uint8_t* buf, int t0, int lane) {
+// Score of one 16-token subtile (rows t0 .. t0+15, t0 a multiple of 16):
+// S^T (16 tokens x 16 heads), K = 576 in 18 steps of 32 channels.  Row index
+// m of the product maps to token t0 + 4(m%4) + m/4, so score register r of
+// lane group g is token t0 + 4r + g.
+__device__ __forceinline__ floatx4 score16(const WaveState& st, uint32_t buf, int t0, int lane) {
   const int g = lane >> 4, m = lane & 15;
-  const uint8_t* ap = buf + lds_row(t0 + 4 * (m & 3) + (m >> 2)) + g * 16;
+  const int r = t0 + 4 * (m & 3) + (m >> 2);
+  // byte 64kk + 16g of the row: the permutation only touches bits 4..6, so
+  // even and odd kk each have one base and a constant stride of 128 bytes
+  const uint32_t ap0 = buf + lds_off(r, 16 * g);
+  const uint32_t ap1 = buf + lds_off(r, 64 + 16 * g);
+  auto rd = [&](int kk) { return lds_read_b128_at((kk & 1 ? ap1 : ap0) + 128 * (kk >> 1)); };
   floatx4 S = {};
   constexpr int D = 3;  // operand reads in flight
   int4v a[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) a[i] = lds_read_b128(ap + 64 * i);
+  for (int i = 0; i < D; ++i) a[i] = rd(i);
 #pragma unroll
   for (int kk = 0; kk < 18; ++kk) {
     const int4v cur = a[kk % D];
-    if (kk + D < 18) a[kk % D] = lds_read_b128(ap + 64 * (kk + D));
+    if (kk + D < 18) a[kk % D] = rd(kk + D);
     S = mfma16(__builtin_bit_cast(bf16x8, cur), st.q[kk], S);
   }
   return S;
 }
 
-// One tile of TT (16 or 32) tokens starting at row t0 of the page buffer.
-// Value product Z^T += C^T P^T: A = C^T (16 channels x TT tokens) through
-// transposing LDS reads, B = P^T.  For TT = 32 the K = 32 slots of lane group
-// g are tokens t0 + 4j + g (j < 4, subtile 0) and t0 + 16 + 4(j-4) + g.
+// One tile of TT (16 or 32) tokens starting at row t0 of the page buffer;
+// rows at or past `hi` are masked.  Value product Z^T += C^T P^T: A = C^T
+// (16 channels x TT tokens) through transposing LDS reads, B = P^T.  For
+// TT = 32 the K = 32 slots of lane group g are tokens t0 + 4j + g (j < 4,
+// first subtile) and t0 + 16 + 4(j-4) + g.
 template <int TT>
-__device__ __forceinline__ void tile(WaveState& st, const uint8_t* buf, int t0, int valid, int lane,
-                                     float scale_log2) {
+__device__ __forceinline__ void tile(WaveState& st, uint32_t buf, int t0, int hi, int lane, float scale_log2) {
+  // Recompute the lane's operand offsets in every tile rather than let the
+  // compiler keep one set per tile position and buffer live across the loop.
+  asm volatile("" : "+v"(lane));
   constexpr int NS = TT / 16;
   const int g = lane >> 4;
   float x[4 * NS], p[4 * NS];
@@ -290,21 +425,28 @@ __device__ __forceinline__ void tile(WaveState& st, const uint8_t* buf, int t0, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float v = S[r] * scale_log2;
-      x[4 * u + r] = t0 + 16 * u + 4 * r + g < valid ? v : -INFINITY;
+      x[4 * u + r] = t0 + 16 * u + 4 * r + g < hi ? v : -INFINITY;
     }
   }
   softmax_update<4 * NS>(st, x, p);
-  // source lane s' of each 16-lane group points at row t0 + 16u + 4(s'/4) + g,
-  // channels 16mt + 4(s'%4) .. +3
-  const uint8_t* vp = buf + lds_row(t0 + g + 4 * ((lane & 15) >> 2)) + 8 * (lane & 3);
+  // Source lane s' of each 16-lane group points at row t0 + 4(s'/4) + g,
+  // channels 16mt + 4(s'%4) .. +3, i.e. row byte 32mt + 8(s'%4); as above,
+  // the permutation leaves a base per mt%4 and a stride of 128 bytes.
+  const int vr = t0 + g + 4 * ((lane & 15) >> 2);
+  const int vx = 8 * (lane & 3);
+  uint32_t vb[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) vb[q4] = buf + lds_off(vr, 32 * q4 + vx);
   constexpr int D = 3;
   if constexpr (TT == 32) {
+    // rows + 16 differ only in bit 0 of swz, i.e. by 16 * 1152 +- 16 bytes
+    const uint32_t dh = lds_off(vr + 16, vx) - lds_off(vr, vx);
     bf16x8 pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[j] = f2bf(p[j]);
     auto vread = [&](int mt) {
-      bf16x4 lo = lds_read_tr16(vp + mt * 32);
-      bf16x4 hi = lds_read_tr16(vp + 8 * kGroupStride + mt * 32);  // rows + 16
+      bf16x4 lo = lds_read_tr16_at(vb[mt & 3] + 128 * (mt >> 2));
+      bf16x4 hi = lds_read_tr16_at(vb[mt & 3] + dh + 128 * (mt >> 2));
       return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     bf16x8 va[D];
@@ -318,7 +460,7 @@ __device__ __forceinline__ void tile(WaveState& st, const uint8_t* buf, int t0, 
     }
   } else {
     const bf16x4 pb = {f2bf(p[0]), f2bf(p[1]), f2bf(p[2]), f2bf(p[3])};
-    auto vread = [&](int mt) { return lds_read_tr16(vp + mt * 32); };
+    auto vread = [&](int mt) { return lds_read_tr16_at(vb[mt & 3] + 128 * (mt >> 2)); };
     bf16x4 va[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) va[i] = vread(i);
@@ -348,126 +490,256 @@ __device__ __forceinline__ void store_state(const WaveState& st, float l_tot, fl
   if (ldst != nullptr && g == 0) ldst[head] = (st.m + __log2f(l_tot)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// Merge of one sequence's partials (shared by the merge kernel and the
+// in-kernel merge of the last-arriving unit)
+// ---------------------------------------------------------------------------
+// One wave per head: the chunks' log-sum-exps are read one per lane and
+// reduced across the wave; then each lane folds its 8 channels of every
+// chunk, 8 chunk loads in flight.
+__device__ __forceinline__ void merge_head(const DecodeArgs& a, int b, int head, int slot0, int n, int lane) {
+  // pass 1: maximum log-sum-exp over the chunks
+  float mmax = -INFINITY;
+  for (int c0 = 0; c0 < n; c0 += 64)
+    if (c0 + lane < n) mmax = fmaxf(mmax, a.lsep[(size_t)(slot0 + c0 + lane) * a.H + head]);
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, d));
+  // pass 2: weights (one chunk per lane) and the weighted sum of the chunks' z
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float wsum = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    float w = 0.f;
+    if (c0 + lane < n) w = __expf(a.lsep[(size_t)(slot0 + c0 + lane) * a.H + head] - mmax);
+    wsum += w;
+    const int m = min(64, n - c0);
+    for (int i0 = 0; i0 < m; i0 += 8) {
+      float wv[8];
+      float4 v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = min(i0 + u, m - 1);  // every slot loaded holds a partial of this sequence
+        wv[u] = i0 + u < m ? __shfl(w, i) : 0.f;
+        const size_t sl = (size_t)(slot0 + c0 + i) * a.H + head;
+        const float4* zp = (const float4*)(a.zp + sl * kDc) + lane * 2;
+        v0[u] = zp[0];
+        v1[u] = zp[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wi = wv[u];
+        acc[0] += wi * v0[u].x; acc[1] += wi * v0[u].y; acc[2] += wi * v0[u].z; acc[3] += wi * v0[u].w;
+        acc[4] += wi * v1[u].x; acc[5] += wi * v1[u].y; acc[6] += wi * v1[u].z; acc[7] += wi * v1[u].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) wsum += __shfl_xor(wsum, d);
+  const float inv = 1.0f / wsum;
+  float4* zo = (float4*)(a.z + ((size_t)b * a.H + head) * kDc) + lane * 2;
+  zo[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  zo[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.H + head] = mmax + __logf(wsum);
+}
+
+// After this workgroup stored its partial of `seg`: count the arrival and
+// report whether this was the sequence's last piece (the counter is left at
+// zero for the next call).  Called by all threads.
+__device__ __forceinline__ bool arrive(const DecodeArgs& a, const Segment& seg, int expected, int* flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's partial stores
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // system scope: performed past every XCD's L2, so all units count on one copy
+    const int old = __hip_atomic_fetch_add(a.counters + seg.b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int last = old == expected - 1;
+    if (last) __hip_atomic_exchange(a.counters + seg.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    *flag = last;
+  }
+  __syncthreads();
+  const bool last = uniform(*flag) != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other pieces' stores
+  return last;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp8-cache matrix-core decode
+// ---------------------------------------------------------------------------
+//
 // 8 waves: all of them copy pages; the first HG*TG compute.  HG head groups
-// of 16 heads, TG token slices of each page.
-template <int HG, int TG>
+// of 16 heads, TG token slices of each page.  FP8 selects the fp8 pool: two
+// staging buffers (the next page's copy lands in one while the other is
+// expanded) and one bf16 page buffer.
+template <int HG, int TG, bool FP8>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-decode_bf16_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
+decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   static_assert(HG * TG <= kWaves, "too many compute waves");
   constexpr int TPW = kPage / TG;           // tokens of each page a wave scores
   constexpr int TT = TPW >= 32 ? 32 : 16;   // tokens per tile
   static_assert(TPW % TT == 0, "tile must divide the wave's slice");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kBufBytes];
+  constexpr int kSmem = FP8 ? 2 * kStageBytes + kBufBytes : 2 * kBufBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   __shared__ int pfx[kMaxSchedB + 1];
-  __shared__ int lens[kMaxSchedB];
+  __shared__ int flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const bool computes = wave < HG * TG;
   const int hg = wave % HG, tg = wave / HG;
   const int h0 = hg * 16;
+  const bool fused = a.counters != nullptr;
 
-  int total = 0;
-  if (a.splits == 0 && a.prefill_T == 0) total = block_page_prefix(a.seq_lens, a.B, pfx, lens);
-
-  SegmentIter it = segments_begin(a, pfx, total);
+  int P = 0;
+  if (a.splits == 0 && a.prefill_T == 0) P = block_prefix(a.seq_lens, a.B, pfx);
+  Schedule sch = schedule_begin(a, pfx, P);
   Segment seg;
-  while (segments_next(a, pfx, it, seg)) {
-    seg.b = uniform(seg.b);
-    seg.pb = uniform(seg.pb);
-    seg.pe = uniform(seg.pe);
-    seg.slot = uniform(seg.slot);
-    seg.whole = uniform(seg.whole);
-    const int L = uniform(a.prefill_T > 0 ? a.prefill_pos0 + seg.b + 1
-                                          : (a.splits == 0 ? lens[seg.b] : a.seq_lens[seg.b]));
-    const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)seg.b * a.max_pages;
-    const bf16* qrow = (const bf16*)a.q + (size_t)seg.b * a.H * kRow;
+  if (!schedule_next(a, pfx, sch, seg)) return;
 
-    const int npg = seg.pe - seg.pb;
-    // block-table reads use a uniform index, so they are scalar loads that do
-    // not wait behind the page copies in flight
-    auto page_ptr = [&](int pi) { return a.rows + (size_t)bt[uniform(pi)] * kPageBytes; };
-    auto page_valid = [&](int pi) { return min(kPage, L - pi * kPage); };
+  // page buffers: bf16 -> smem + (i&1) * kBufBytes; fp8 -> stage (i&1), one bf16 buffer
+  uint8_t* const bfbuf = FP8 ? smem + 2 * kStageBytes : smem;
+  auto bt_row = [&](const Segment& s) {
+    return a.prefill_T > 0 ? block_table : block_table + (size_t)s.b * a.max_pages;
+  };
+  auto qrow = [&](const Segment& s) { return (const bf16*)a.q + (size_t)s.b * a.H * kRow; };
+  auto page_lo = [&](const Segment& s, int p) { return max(s.t0 - p * kPage, 0); };
+  auto page_hi = [&](const Segment& s, int p) { return min(s.t1 - p * kPage, kPage); };
+  // block-table reads use a uniform index, so they are scalar loads that do
+  // not wait behind the page copies in flight
+  auto issue = [&](const Segment& s, int p, int i) {
+    const int page = bt_row(s)[uniform(p)];
+    if constexpr (FP8) {
+      issue_page_fp8(a.ckv8, a.scale8, a.kr8, page, smem + (i & 1) * kStageBytes, page_lo(s, p), page_hi(s, p),
+                     wave, lane);
+    } else {
+      issue_page_bf16(a.rows + (size_t)page * kPageBytes, smem + (i & 1) * kBufBytes, page_lo(s, p), page_hi(s, p),
+                      wave, lane);
+    }
+  };
 
-    // The query loads and the first page copy travel together; consuming the
-    // query right after waits for both (the compiler's counter only knows the
-    // query loads), before the second page's copy is issued.
-    WaveState st;
-    load_query(st, qrow, a.H, h0 + (lane & 15), lane >> 4);
-    issue_page_copy(page_ptr(seg.pb), smem, page_valid(seg.pb), wave, lane);
-    consume_query(st);
-#pragma unroll
-    for (int t = 0; t < 32; ++t) st.zacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    st.m = -INFINITY;
-    st.l = 0.f;
-    for (int i = 0; i < npg; ++i) {
-      const int pi = seg.pb + i;
-      const uint8_t* buf = smem + (i & 1) * kBufBytes;
-      if (i + 1 < npg) {
-        issue_page_copy(page_ptr(pi + 1), smem + ((i + 1) & 1) * kBufBytes, page_valid(pi + 1), wave, lane);
-        wait_vmcnt<kDmaPerWave>();
-      } else {
-        wait_vmcnt<0>();
-      }
+  // Pieces of sequences whose merge falls to this unit: at most the first
+  // and the last piece of a unit can be partial, so two at most.
+  int pend_n = 0, pb0 = 0, ps0 = 0, pc0 = 0, pb1 = 0, ps1 = 0, pc1 = 0;
+
+  // The query loads and the first page copy travel together; consuming the
+  // query right after waits for both (the compiler's counter only knows the
+  // query loads), before the second page's copy is issued.
+  WaveState st;
+  int p = seg.t0 / kPage;
+  load_query(st, qrow(seg), a.H, h0 + (lane & 15), lane >> 4);
+  issue(seg, p, 0);
+  consume_query(st);
+  reset_state(st);
+  for (int i = 0;; ++i) {
+    const bool seg_last = p == (seg.t1 - 1) / kPage;
+    Segment nseg = seg;
+    int np = p + 1;
+    bool more = true;
+    if (seg_last) {
+      more = schedule_next(a, pfx, sch, nseg);
+      np = nseg.t0 / kPage;
+    }
+    if (more) {
+      issue(nseg, np, i + 1);
+      if constexpr (FP8) wait_vmcnt<kFp8DmaPerWave>(); else wait_vmcnt<kDmaPerWave>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    uint8_t* buf;
+    if constexpr (FP8) {
+      dequant_page(smem + (i & 1) * kStageBytes, bfbuf);
       __syncthreads();
-      const int valid = page_valid(pi);
-      if (computes) {
-#pragma unroll
-        for (int t = 0; t < TPW / TT; ++t) {
-          const int t0 = tg * TPW + t * TT;
-          if (t0 < valid) tile<TT>(st, buf, t0, valid, lane, a.scale_log2);
-        }
-      }
-      __syncthreads();
+      buf = bfbuf;
+    } else {
+      buf = smem + (i & 1) * kBufBytes;
     }
+    const uint32_t bufa = lds_addr(buf);
+    const int lo = page_lo(seg, p), hi = page_hi(seg, p);
+    if (computes) {
+#pragma unroll
+      for (int t = 0; t < TPW / TT; ++t) {
+        const int t0 = tg * TPW + t * TT;
+        if (t0 + TT > lo && t0 < hi) tile<TT>(st, bufa, t0, hi, lane, a.scale_log2);
+      }
+    }
+    __syncthreads();  // the buffer is free: refilled next round, or merge scratch below
 
-    // combine the token slices of the TG waves that share a head group:
-    // a tree over LDS, half of the remaining slices handing over per round
-    float l_tot = pair32_sum(pair16_sum(st.l));
-    if constexpr (TG > 1) {
-      // slot (tg - half, hg) carries slice tg over to slice tg - half
-      floatx4* zx = (floatx4*)smem;  // [(TG/2) * HG][32 tiles][64 lanes]
-      float* ml = (float*)(smem + 2 * kBufBytes) - 2 * (TG / 2) * HG * 64;
-      static_assert((TG / 2) * HG * 32 * 64 * 16 + 2 * (TG / 2) * HG * 64 * 4 <= 2 * kBufBytes, "merge space");
+    if (seg_last) {
+      // combine the token slices of the TG waves that share a head group: a
+      // tree over LDS in the free page buffer, at most two slots per pass
+      float l_tot = pair32_sum(pair16_sum(st.l));
+      if constexpr (TG > 1) {
+        uint8_t* scratch = buf;
+        floatx4* zx = (floatx4*)scratch;                   // [2][32 tiles][64 lanes]
+        float* ml = (float*)(scratch + 2 * 32 * 64 * 16);  // [2][2][64]
+        static_assert(2 * 32 * 64 * 16 + 2 * 2 * 64 * 4 <= kBufBytes, "merge scratch");
+        // Runtime loops on purpose: unrolled, the conditional accumulator
+        // update would be duplicated per pass and cost register copies.
+#pragma unroll 1
+        for (int half = TG / 2; half >= 1; half /= 2) {
+#pragma unroll 1
+          for (int s0 = 0; s0 < half * HG; s0 += 2) {
+            const int slw = (tg - half) * HG + hg - s0;  // slot this wave hands over
+            if (computes && tg >= half && tg < 2 * half && slw >= 0 && slw < 2) {
+              floatx4* dst = zx + (size_t)slw * 32 * 64;
 #pragma unroll
-      for (int half = TG / 2; half >= 1; half /= 2) {
-        if (computes && tg >= half && tg < 2 * half) {
-          const int slot = (tg - half) * HG + hg;
-          floatx4* dst = zx + (size_t)slot * 32 * 64;
+              for (int t = 0; t < 32; ++t) dst[t * 64 + lane] = st.zacc[t];
+              ml[(slw * 2) * 64 + lane] = st.m;
+              ml[(slw * 2 + 1) * 64 + lane] = l_tot;
+            }
+            __syncthreads();
+            const int slr = tg * HG + hg - s0;  // slot this wave takes over
+            if (computes && tg < half && slr >= 0 && slr < 2) {
+              const float mo = ml[(slr * 2) * 64 + lane];
+              const float lo2 = ml[(slr * 2 + 1) * 64 + lane];
+              const float mstar = fmaxf(st.m, mo);
+              const float a0 = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mstar);
+              const float ao = mo == -INFINITY ? 0.f : fast_exp2(mo - mstar);
+              l_tot = l_tot * a0 + lo2 * ao;
+              const floatx4* src = zx + (size_t)slr * 32 * 64;
 #pragma unroll
-          for (int t = 0; t < 32; ++t) dst[t * 64 + lane] = st.zacc[t];
-          ml[(slot * 2) * 64 + lane] = st.m;
-          ml[(slot * 2 + 1) * 64 + lane] = l_tot;
+              for (int t = 0; t < 32; ++t) {
+                st.zacc[t] = st.zacc[t] * a0 + src[t * 64 + lane] * ao;
+                if (t % 8 == 7) asm volatile("" ::: "memory");  // 8 tiles' loads in flight, not 32
+              }
+              st.m = mstar;
+            }
+            __syncthreads();
+          }
         }
-        __syncthreads();
-        if (computes && tg < half) {
-          const int slot = tg * HG + hg;
-          const float mo = ml[(slot * 2) * 64 + lane];
-          const float lo = ml[(slot * 2 + 1) * 64 + lane];
-          const float mstar = fmaxf(st.m, mo);
-          const float a0 = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mstar);
-          const float ao = mo == -INFINITY ? 0.f : fast_exp2(mo - mstar);
-          l_tot = l_tot * a0 + lo * ao;
-          const floatx4* src = zx + (size_t)slot * 32 * 64;
-#pragma unroll
-          for (int t = 0; t < 32; ++t) st.zacc[t] = st.zacc[t] * a0 + src[t * 64 + lane] * ao;
-          st.m = mstar;
+      }
+      const bool whole = seg.parts == 1;
+      if (computes && tg == 0) {
+        float* zdst;
+        float* ldst;
+        if (whole) {
+          zdst = a.z + (size_t)seg.b * a.H * kDc;
+          ldst = a.lse ? a.lse + (size_t)seg.b * a.H : nullptr;
+        } else {
+          zdst = a.zp + (size_t)seg.slot * a.H * kDc;
+          ldst = a.lsep + (size_t)seg.slot * a.H;
         }
-        __syncthreads();
+        store_state(st, l_tot, zdst, ldst, h0, a.H, lane);
       }
-    }
-    if (computes && tg == 0) {
-      float* zdst;
-      float* ldst;
-      if (seg.whole) {
-        zdst = a.z + (size_t)seg.b * a.H * kDc;
-        ldst = a.lse ? a.lse + (size_t)seg.b * a.H : nullptr;
-      } else {
-        zdst = a.zp + (size_t)seg.slot * a.H * kDc;
-        ldst = a.lsep + (size_t)seg.slot * a.H;
+      if (!whole && fused && arrive(a, seg, seg.parts, &flag)) {
+        if (pend_n == 0) {
+          pb0 = seg.b, ps0 = seg.slot0, pc0 = seg.parts;
+        } else {
+          pb1 = seg.b, ps1 = seg.slot0, pc1 = seg.parts;
+        }
+        ++pend_n;
       }
-      store_state(st, l_tot, zdst, ldst, h0, a.H, lane);
+      if (more) {
+        load_query(st, qrow(nseg), a.H, h0 + (lane & 15), lane >> 4);
+        consume_query(st);
+        reset_state(st);
+      }
+      seg = nseg;
     }
-    __syncthreads();  // LDS is reused by the next segment
+    if (!more) break;
+    p = np;
+  }
+
+  for (int k = 0; k < pend_n; ++k) {
+    const int b = uniform(k ? pb1 : pb0), s0 = uniform(k ? ps1 : ps0), n = uniform(k ? pc1 : pc0);
+    for (int h = wave; h < a.H; h += kWaves) merge_head(a, b, h, s0, n, lane);
   }
 }
 
@@ -475,21 +747,20 @@ decode_bf16_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 // fp32 decode (VALU; small and exact-arithmetic cases)
 // ---------------------------------------------------------------------------
 // One workgroup per (unit, head).  Tokens are scored 256 at a time (one per
-// thread), then every thread folds them into its two channels of z.
+// thread), then every thread folds them into its two channels of z.  Partials
+// are always merged by the merge kernel.
 __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
   __shared__ float qs[kRow];
   __shared__ float ps[256];
   __shared__ float red[8];
   __shared__ int pfx[kMaxSchedB + 1];
-  __shared__ int lens[kMaxSchedB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
-  int total = 0;
-  if (a.splits == 0 && a.prefill_T == 0) total = block_page_prefix(a.seq_lens, a.B, pfx, lens);
-  SegmentIter it = segments_begin(a, pfx, total);
+  int P = 0;
+  if (a.splits == 0 && a.prefill_T == 0) P = block_prefix(a.seq_lens, a.B, pfx);
+  Schedule sch = schedule_begin(a, pfx, P);
   Segment seg;
-  while (segments_next(a, pfx, it, seg)) {
-    const int L = a.prefill_T > 0 ? a.prefill_pos0 + seg.b + 1 : a.seq_lens[seg.b];
+  while (schedule_next(a, pfx, sch, seg)) {
     const int32_t* bt = a.prefill_T > 0 ? a.block_table : a.block_table + (size_t)seg.b * a.max_pages;
     const float* q = (const float*)a.q + ((size_t)seg.b * a.H + head) * kRow;
     const float* pool = (const float*)a.rows;
@@ -497,7 +768,7 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
     for (int i = tid; i < kRow; i += 256) qs[i] = q[i];
     __syncthreads();
     float m = -INFINITY, l = 0.f, z0 = 0.f, z1 = 0.f;
-    const int j0 = seg.pb * kPage, j1 = min(seg.pe * kPage, L);
+    const int j0 = seg.t0, j1 = seg.t1;
     for (int jb = j0; jb < j1; jb += 256) {
       const int j = jb + tid;
       float s = -INFINITY;
@@ -537,7 +808,7 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
     }
     float* zdst;
     float* ldst;
-    if (seg.whole) {
+    if (seg.parts == 1) {
       zdst = a.z + ((size_t)seg.b * a.H + head) * kDc;
       ldst = a.lse ? a.lse + (size_t)seg.b * a.H + head : nullptr;
     } else {
@@ -551,112 +822,62 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: lse = log sum_c e^{lse_c};  z = sum_c e^{lse_c - lse} z_c
+// Split merge kernel: one workgroup per (sequence, 8 heads), one wave per head
 // ---------------------------------------------------------------------------
-// One workgroup per (sequence, 4 heads); one wave per head.  The chunks'
-// log-sum-exps are read one per lane and reduced across the wave; then each
-// lane folds its 8 channels of every chunk, several chunk loads in flight.
-__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(512) merge_kernel(DecodeArgs a) {
   __shared__ int pfx[kMaxSchedB + 1];
-  __shared__ int lens[kMaxSchedB];
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int head = blockIdx.y * 4 + wave;
-  int first = 0, last = 0, slot0 = 0;
-  long long G = 0, total = 0;  // balanced split: units with no pages wrote no partial
-  const int np = (a.seq_lens[b] + kPage - 1) / kPage;
+  const int head = blockIdx.y * 8 + wave;
+  int slot0, n;
   if (a.splits > 0) {
     const int S = a.splits;
+    const int np = (a.seq_lens[b] + kPage - 1) / kPage;
     const int chunk = (np + S - 1) / S;
-    const int used = (np + chunk - 1) / chunk;
-    if (used <= 1) return;
-    first = 0;
-    last = used - 1;
+    n = (np + chunk - 1) / chunk;
     slot0 = b * S;
   } else {
-    total = block_page_prefix(a.seq_lens, a.B, pfx, lens);
-    G = a.units;
-    first = unit_of_page(pfx[b], G, total);
-    last = unit_of_page(pfx[b + 1] - 1, G, total);
-    if (first == last) return;
-    slot0 = b;  // slot of unit w for sequence b is w + b
+    const int P = block_prefix(a.seq_lens, a.B, pfx);
+    const long long G = min((long long)a.units, (long long)P);
+    const int first = unit_of_block(pfx[b], G, P);
+    const int last = unit_of_block(pfx[b + 1] - 1, G, P);
+    n = last - first + 1;
+    slot0 = first + b;
   }
-  if (head >= a.H) return;
-  const int n = last - first + 1;
-  auto owns_pages = [&](int c) { return G == 0 || c * total / G < (c + 1) * total / G; };
-  // pass 1: maximum log-sum-exp over the chunks
-  float mmax = -INFINITY;
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    const int c = first + c0 + lane;
-    if (c0 + lane < n && owns_pages(c)) mmax = fmaxf(mmax, a.lsep[(size_t)(slot0 + c) * a.H + head]);
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, d));
-  // pass 2: weights (one chunk per lane) and the weighted sum of the chunks' z
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float wsum = 0.f;
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    const int c = first + c0 + lane;
-    float w = 0.f;
-    if (c0 + lane < n && owns_pages(c)) w = __expf(a.lsep[(size_t)(slot0 + c) * a.H + head] - mmax);
-    wsum += w;
-    const int m = min(64, n - c0);
-    // Chunks go in batches of 8 whose loads are all in flight together.
-    // Every slot loaded lies inside the workspace; slots of units without
-    // pages hold no partial and are dropped by the select, not by a multiply.
-    for (int i0 = 0; i0 < m; i0 += 8) {
-      float wv[8];
-      float4 v0[8], v1[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = min(i0 + u, m - 1);
-        wv[u] = i0 + u < m ? __shfl(w, i) : 0.f;
-        const size_t sl = (size_t)(slot0 + first + c0 + i) * a.H + head;
-        const float4* zp = (const float4*)(a.zp + sl * kDc) + lane * 2;
-        v0[u] = zp[0];
-        v1[u] = zp[1];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wi = wv[u];
-        const bool use = wi != 0.f;
-        acc[0] += use ? wi * v0[u].x : 0.f; acc[1] += use ? wi * v0[u].y : 0.f;
-        acc[2] += use ? wi * v0[u].z : 0.f; acc[3] += use ? wi * v0[u].w : 0.f;
-        acc[4] += use ? wi * v1[u].x : 0.f; acc[5] += use ? wi * v1[u].y : 0.f;
-        acc[6] += use ? wi * v1[u].z : 0.f; acc[7] += use ? wi * v1[u].w : 0.f;
-      }
-    }
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) wsum += __shfl_xor(wsum, d);
-  const float inv = 1.0f / wsum;
-  float4* zo = (float4*)(a.z + ((size_t)b * a.H + head) * kDc) + lane * 2;
-  zo[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  zo[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.H + head] = mmax + __logf(wsum);
+  if (n <= 1 || head >= a.H) return;
+  merge_head(a, b, head, slot0, n, lane);
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s) {
-  const dim3 blk(256);
-  if (kind == kKindF32) {
-    hipLaunchKernelGGL(decode_f32_kernel, dim3(a.units, a.H), blk, 0, s, a);
-  } else if (a.H <= 16) {
-    hipLaunchKernelGGL((decode_bf16_kernel<1, 4>), dim3(a.units), dim3(kWaves * 64), 0, s, a, a.block_table);
+template <bool FP8>
+static void launch_mfma(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.units), blk(kWaves * 64);
+  if (a.H <= 16) {
+    hipLaunchKernelGGL((decode_mfma_kernel<1, 4, FP8>), grid, blk, 0, s, a, a.block_table);
   } else if (a.H <= 32) {
-    hipLaunchKernelGGL((decode_bf16_kernel<2, 4>), dim3(a.units), dim3(kWaves * 64), 0, s, a, a.block_table);
+    hipLaunchKernelGGL((decode_mfma_kernel<2, 4, FP8>), grid, blk, 0, s, a, a.block_table);
   } else if (a.H <= 64) {
-    hipLaunchKernelGGL((decode_bf16_kernel<4, 2>), dim3(a.units), dim3(kWaves * 64), 0, s, a, a.block_table);
+    hipLaunchKernelGGL((decode_mfma_kernel<4, 2, FP8>), grid, blk, 0, s, a, a.block_table);
   } else {
-    hipLaunchKernelGGL((decode_bf16_kernel<8, 1>), dim3(a.units), dim3(kWaves * 64), 0, s, a, a.block_table);
+    hipLaunchKernelGGL((decode_mfma_kernel<8, 1, FP8>), grid, blk, 0, s, a, a.block_table);
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s) {
+  if (kind == kKindF32) {
+    hipLaunchKernelGGL(decode_f32_kernel, dim3(a.units, a.H), dim3(256), 0, s, a);
+  } else if (kind == kKindFp8) {
+    launch_mfma<true>(a, s);
+  } else {
+    launch_mfma<false>(a, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B, (a.H + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B, (a.H + 7) / 8), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

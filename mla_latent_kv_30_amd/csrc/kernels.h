@@ -23,6 +23,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;     // [B] (prefill: unused)
   int32_t B, H, max_pages;
   int32_t splits;              // > 0: S chunks per sequence; 0: balanced over `units`
+                               // (32-token blocks of all sequences in equal ranges)
   int32_t units;               // workgroups along x
   int32_t prefill_T;           // > 0: causal prefill of T rows (unit w -> row T-1-w)
   int32_t prefill_pos0;
@@ -31,6 +32,8 @@ struct DecodeArgs {
   float* lse;
   float* zp;                   // partials [slots][H][512]
   float* lsep;                 // partials [slots][H]
+  int32_t* counters;           // [B] arrival counts (zero between calls), or
+                               // NULL: partials are left for the merge kernel
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s);

@@ -99,9 +99,12 @@ def test_prefill_and_upproj_reject_bad_arguments():
         == _lib.MLA_ERR_INVALID_ARG
     assert L.mla_prefill_causal(P, P, P, 0, ctypes.byref(c), P, 0, 16, 0.07, 10000.0, P, NULL, NULL) \
         == _lib.MLA_ERR_INVALID_ARG
-    fp8 = _cache(dtype=_lib.MLA_FP8_E4M3, rows=NULL, ckv=P, scale=P, kr=P)
+    fp8 = _cache(dtype=_lib.MLA_FP8_E4M3, rows=NULL, ckv=P, scale=NULL, kr=P)  # scales missing
     assert L.mla_prefill_causal(P, P, P, 0, ctypes.byref(fp8), P, 8, 16, 0.07, 10000.0, P, NULL, NULL) \
-        == _lib.MLA_ERR_UNSUPPORTED
+        == _lib.MLA_ERR_INVALID_ARG
+    fp8 = _cache(dtype=_lib.MLA_FP8_E4M3, rows=NULL, ckv=P, scale=P, kr=P)
+    assert L.mla_prefill_causal(P, P, P, 0, ctypes.byref(fp8), P, 8, 0, 0.07, 10000.0, P, NULL, NULL) \
+        == _lib.MLA_ERR_INVALID_ARG
     assert L.mla_upproj_v(NULL, P, P, 1, 16, 1, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
     assert L.mla_upproj_v(P, P, P, 1, 16, 2, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
     assert L.mla_upproj_v(P, P, P, 1, 0, 1, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
