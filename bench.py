@@ -2,9 +2,9 @@
 """Throughput of absorbed-MLA decode on one MI355X, against its roofline.
 
 One step = the whole decode path for one batch: absorbed query
-(mla_absorb_q), the split pass over the paged latent cache
-(mla_decode_partial), the split merge (mla_decode_merge) and the W_UV
-up-projection (mla_upproj_v).  Inputs are synthetic with the workload's
+(mla_absorb_q), attention over the paged latent cache and the split merge
+(mla_decode: decode kernel + merge kernel), and the W_UV up-projection
+(mla_upproj_v).  Inputs are synthetic with the workload's
 shapes and distributions and are resident in HBM before timing starts.  To
 keep the 256 MB last-level cache from serving repeated reads, the step
 rotates over enough replicas of its inputs (cache, weights, queries) to
@@ -121,16 +121,14 @@ def main():
     z = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     o = torch.empty((B, H, 128), dtype=torch.float32, device=dev)
-    ws_bytes = mla.decode_workspace_size(B, H, splits)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = mla.decode_workspace(B, H, splits, dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
     def step(r):
         cache, q_c, q_r, w_uk, w_uv = reps[r]
         mla.absorb_q(q_c, q_r, dd.pos, w_uk, out=q_abs)
-        mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
-        mla.decode_merge(dd.seq_lens, H, ws, z, lse, num_splits=splits)
+        mla.decode(q_abs, cache, dd.block_table, dd.seq_lens, num_splits=splits, workspace=ws, z=z, lse=lse)
         mla.upproj_v(z, w_uv, out=o)
 
     for k in range(max(1, args.warmup)):
@@ -173,9 +171,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / K
 
-    # ---- the decode kernel alone (split pass), timed with events on its own
-    # stream; a GPU sleep first lets the host enqueue every launch ahead of the
-    # device, so no host latency lands between an event and its kernel
+    # ---- the decode kernel alone (mla_decode_partial), timed with events on
+    # the stream it runs on; a GPU sleep first lets the host enqueue every
+    # launch ahead of the device, so no host latency lands between an event
+    # and its kernel
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
@@ -229,11 +228,11 @@ def main():
             "workload": wl.name, "batch": B, "heads": H, "cached_tokens": total,
             "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
             "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
-            "step": "absorb_q + decode_partial + decode_merge + upproj_v",
+            "step": "absorb_q + decode (decode kernel + split merge) + upproj_v",
         },
         "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-            "traffic": None, "kernel": "decode_bf16_kernel" if wl.dtype != "f32" else "decode_f32_kernel",
+            "traffic": None, "kernel": "decode_mfma_kernel" if wl.dtype != "f32" else "decode_f32_kernel",
             "kernel_avg_us": kern_avg_ms * 1e3, "kernel_p10_us": kern_ms[K // 10] * 1e3,
             "kernel_p90_us": kern_ms[(9 * K) // 10] * 1e3, "alg_bytes_per_launch": alg_bytes,
             "alg_flops_per_launch": alg_flops, "tflops": tflops, "mfma_peak_tflops": mfma_peak,

@@ -150,13 +150,9 @@ size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits);
  *                into one nearly equal range per compute unit (a range may
  *                span sequences); S > 0: sequence b is cut into S chunks of
  *                ceil(ceil(L_b/64)/S) pages (trailing chunks may be empty).
- *   workspace    device scratch of at least mla_decode_workspace_size bytes.
- *                It starts with one arrival counter per sequence, through
- *                which the last chunk to finish merges a split sequence in
- *                the same kernel: the workspace must be zero-filled once
- *                before its first use with mla_decode, and every completed
- *                call leaves the counters at zero again.  Calls that share a
- *                workspace must not run concurrently.
+ *   workspace    device scratch of at least mla_decode_workspace_size bytes
+ *                (no initialisation needed); calls that share a workspace
+ *                must not run concurrently.
  *   z            [B][H][512] fp32 out: normalised latent aggregate
  *   lse          [B][H] fp32 out (may be NULL): natural-log log-sum-exp of
  *                the scaled scores
@@ -174,15 +170,14 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
 /*
  * The two halves of mla_decode, for callers that schedule the merge
  * themselves (overlapping it with other work, or combining chunk partials
- * produced by several calls).  mla_decode(...) computes exactly what
+ * produced by several calls).  mla_decode(...) is exactly
  * mla_decode_partial(...) followed by mla_decode_merge(...) on the same
- * stream with the same arguments computes.
+ * stream with the same arguments.
  *
  * mla_decode_partial: the split pass.  Sequences that fall into a single
  * chunk get their final z / lse; every other chunk leaves its normalised
  * partial (z_c, lse_c) in the workspace.  Same arguments and errors as
- * mla_decode; the arrival counters are neither read nor written, so the
- * workspace needs no zero fill for this pair of calls.
+ * mla_decode.
  */
 mla_status mla_decode_partial(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
                               const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,

@@ -203,9 +203,9 @@ def decode_workspace_size(B: int, H: int, num_splits: int = 0) -> int:
 
 
 def decode_workspace(B: int, H: int, num_splits: int = 0, device="cuda") -> Optional[torch.Tensor]:
-    """A zero-filled workspace for mla_decode (its arrival counters must start at zero)."""
+    """A workspace for mla_decode / mla_decode_partial (None when none is needed)."""
     need = decode_workspace_size(B, H, num_splits)
-    return torch.zeros(need, dtype=torch.uint8, device=device) if need > 0 else None
+    return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
 
 
 def _decode_call(fn_name, q_abs, cache, block_table, seq_lens, softmax_scale, num_splits, workspace, z, lse,
@@ -238,11 +238,7 @@ def _decode_call(fn_name, q_abs, cache, block_table, seq_lens, softmax_scale, nu
 def decode(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
            softmax_scale: Optional[float] = None, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
            z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True):
-    """z[B,H,512], lse[B,H] of one new token per sequence (mla_decode).
-
-    A workspace passed in must have been zero-filled once (decode_workspace);
-    every completed call leaves it ready for the next one.
-    """
+    """z[B,H,512], lse[B,H] of one new token per sequence (mla_decode)."""
     z, lse, _ = _decode_call("mla_decode", q_abs, cache, block_table, seq_lens, softmax_scale, num_splits,
                              workspace, z, lse, want_lse)
     return z, lse

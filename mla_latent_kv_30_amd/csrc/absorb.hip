@@ -93,6 +93,76 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a) {
     }
 }
 
+// Few query rows (decode, N <= 32): workgroup = (head, 64-channel slice of
+// q~), so a launch has H * 8 workgroups and each reads only its 16 KB of W.
+// All W loads of a thread are issued before any of them is stored to LDS
+// (one memory round trip).  Wave w computes channels 16w .. 16w+15 of the
+// slice for every row on 16x16x32 matrix cores: A = W^T (16 c x 32 d) by
+// transposing LDS reads, B = q_c^T straight from memory.
+constexpr int kAbsSmallCols = 64;
+constexpr int kAbsSmallStride = kAbsSmallCols * 2 + 16;  // 144 B: transposing reads hit distinct banks
+constexpr int kAbsSmallMaxN = 32;
+
+__global__ void __launch_bounds__(256) absorb_small_kernel(AbsorbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[kDn * kAbsSmallStride];  // W[d][64-channel slice]
+  const int h = blockIdx.x, cs = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = lane >> 4, s = lane & 15;
+  const bf16* w = (const bf16*)a.w_uk + (size_t)h * kDn * kDc + cs * kAbsSmallCols;
+  int4v wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // 128 rows x 8 chunks of 16 bytes
+    const int idx = tid + 256 * i, d = idx >> 3, ch = idx & 7;
+    wv[i] = *(const int4v*)(w + (size_t)d * kDc + ch * 8);
+  }
+  // B operand q_c^T: lane holds query row 16nt + s, d = 32kk + 8G + j
+  bf16x8 qb[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = 16 * nt + s;
+    const bool ok = n < a.N;
+    const bf16* qc = (const bf16*)a.q_c + ((size_t)(ok ? n : 0) * a.H + h) * kDn;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      int4v v = *(const int4v*)(qc + 32 * kk + 8 * G);
+      if (!ok) v = int4v{0, 0, 0, 0};
+      qb[nt][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i, d = idx >> 3, ch = idx & 7;
+    *(int4v*)(w_lds + d * kAbsSmallStride + ch * 16) = wv[i];
+  }
+  if (cs == 0) rope_rows<bf16>(a, h, 0, a.N);
+  __syncthreads();
+  // A operand by transposing reads: source lane s of group G points at row
+  // d = 32kk + 8G + s/4 (+4), columns c0 + 4(s%4) .. +3; lane s receives
+  // column c0 + s of four consecutive rows.
+  const int c0 = 16 * wave;
+  const uint8_t* ap = w_lds + (8 * G + (s >> 2)) * kAbsSmallStride + 2 * (c0 + 4 * (s & 3));
+  bf16x8 av[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x4 lo = lds_read_tr16(ap + 32 * kk * kAbsSmallStride);
+    bf16x4 hi = lds_read_tr16(ap + (32 * kk + 4) * kAbsSmallStride);
+    av[kk] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if (16 * nt >= a.N) break;
+    floatx4 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mfma16(av[kk], qb[nt][kk], acc);
+    // C layout: column = query row 16nt + s, rows c = c0 + 4G + r
+    const int n = 16 * nt + s;
+    if (n < a.N) {
+      bf16* out = (bf16*)a.q_abs + ((size_t)n * a.H + h) * kRow + cs * kAbsSmallCols + c0 + 4 * G;
+      *(bf16x4*)out = bf16x4{f2bf(acc[0]), f2bf(acc[1]), f2bf(acc[2]), f2bf(acc[3])};
+    }
+  }
+}
+
 // fp32: one thread per (row, head, c); W reads coalesce along c.
 __global__ void __launch_bounds__(256) absorb_f32_kernel(AbsorbArgs a) {
   const int nh = blockIdx.x;  // n * H + h
@@ -122,6 +192,8 @@ __global__ void __launch_bounds__(256) absorb_f32_kernel(AbsorbArgs a) {
 hipError_t launch_absorb(const AbsorbArgs& a, int kind, hipStream_t s) {
   if (kind == kKindF32) {
     hipLaunchKernelGGL(absorb_f32_kernel, dim3(a.N * a.H), dim3(256), 0, s, a);
+  } else if (a.N <= kAbsSmallMaxN) {
+    hipLaunchKernelGGL(absorb_small_kernel, dim3(a.H, kDc / kAbsSmallCols), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(absorb_bf16_kernel, dim3(a.H * 4, (a.N + kAbsRowsPerBlock - 1) / kAbsRowsPerBlock),
                        dim3(256), 0, s, a);

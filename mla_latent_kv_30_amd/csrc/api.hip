@@ -80,16 +80,17 @@ Plan make_plan(int32_t B, int32_t num_splits) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout: [B arrival counters][partial z: slots x H x 512][partial lse: slots x H]
+// Workspace layout: [per-sequence piece record: B x (first slot, count) int32]
+//                   [partial z: slots x H x 512 fp32][partial lse: slots x H fp32]
 struct WsLayout {
-  size_t counters, zp, lsep, total;
+  size_t meta, zp, lsep, total;
 };
 
 WsLayout ws_layout(int32_t B, int32_t H, const Plan& p) {
   WsLayout w{0, 0, 0, 0};
   if (p.slots == 0) return w;
-  w.counters = 0;
-  w.zp = align256((size_t)B * sizeof(int32_t));
+  w.meta = 0;
+  w.zp = align256((size_t)B * 2 * sizeof(int32_t));
   w.lsep = w.zp + align256((size_t)p.slots * H * kDc * sizeof(float));
   w.total = w.lsep + align256((size_t)p.slots * H * sizeof(float));
   return w;
@@ -100,6 +101,7 @@ size_t workspace_bytes(int32_t B, int32_t H, const Plan& p) { return ws_layout(B
 void set_workspace(DecodeArgs& a, void* workspace, int32_t B, int32_t H, const Plan& p) {
   if (p.slots == 0) return;
   const WsLayout w = ws_layout(B, H, p);
+  a.meta = (int32_t*)((char*)workspace + w.meta);
   a.zp = (float*)((char*)workspace + w.zp);
   a.lsep = (float*)((char*)workspace + w.lsep);
 }
@@ -233,15 +235,9 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
   if (st != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  if (kind == kKindF32) {  // the fp32 path leaves its partials to the merge kernel
-    st = launched(launch_decode(a, kind, s));
-    if (st != MLA_OK || p.slots == 0) return st;
-    return launched(launch_merge(a, s));
-  }
-  // matrix-core paths merge in place: the last unit to finish a piece of a
-  // sequence combines its pieces (arrival counters at the workspace start)
-  if (p.slots > 0) a.counters = (int32_t*)((char*)workspace + ws_layout(B, H, p).counters);
-  return launched(launch_decode(a, kind, s));
+  st = launched(launch_decode(a, kind, s));
+  if (st != MLA_OK || p.slots == 0) return st;
+  return launched(launch_merge(a, s));
 }
 
 mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,

@@ -14,10 +14,10 @@
 //     buffer while the previous page is consumed; every row is read from HBM
 //     once and shared by all heads.  The stream runs on across the sequence
 //     boundaries inside a unit, so a unit never waits for a cold first page.
-//   * Wave w owns 16 heads (hg = w % HG) and a token slice of each page
-//     (tg = w / HG).  Its absorbed query stays in VGPRs, its accumulator Z^T
-//     (16 heads x 512 fp32) in accumulation registers, and every value a lane
-//     holds belongs to one head, so the online softmax never leaves the lane.
+//   * Wave w owns 16 heads (hg = w % HG) and a slice of the 512 latent
+//     channels (cg = w / HG).  Its absorbed query and its accumulator Z^T
+//     stay in registers, and every value a lane holds belongs to one head, so
+//     the online softmax never leaves the lane.
 //   * Score operand: 16-byte LDS reads of rows.  Value operand: gfx950's
 //     transposing LDS read (ds_read_b64_tr_b16) turns row-major c^KV into
 //     token-packed matrix-core operands without a transposed copy.
@@ -28,10 +28,8 @@
 //     Report", process-cxr.github.io, §Fine-grained quantization: scaling per
 //     1 x 128 tile of a token, applied when the tile is consumed).
 //   * Long sequences are cut into chunks; each chunk leaves a normalised
-//     partial (z_c, lse_c) that is combined exactly:
-//     lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c.  Either a
-//     separate merge kernel does it, or the last unit to finish a chunk of a
-//     sequence (found with a per-sequence arrival counter) merges it in place.
+//     partial (z_c, lse_c) that the merge kernel combines exactly:
+//     lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c.
 #include "common.h"
 #include "kernels.h"
 
@@ -51,13 +49,19 @@ constexpr int kBlock = 32;                          // scheduling granule (token
 //            unit w = (b = w/S, chunk w%S), partial slot w;
 //   balanced the 32-token blocks of all sequences, concatenated, are cut into
 //            G nearly equal ranges (G = min(units, blocks)); a unit walks the
-//            sequences its range touches.  Unit w's piece of sequence b goes
-//            to partial slot w + b (unique: the pieces of unit w have
-//            increasing b, and unit w+1 starts at or after unit w's last b).
+//            sequences its range touches.  Each sequence is preceded by
+//            kStartCost blocks that hold no tokens: they stand for the cost of
+//            starting a sequence (query load, first copies, final store), so a
+//            unit that switches sequences gets correspondingly fewer tokens.
+//            Unit w's piece of sequence b goes to partial slot w + b (unique:
+//            the pieces of unit w have increasing b, and unit w+1 starts at or
+//            after unit w's last b).
+constexpr int kStartCost = 2;
 
-// Exclusive prefix sums of the 32-token block counts into pfx[0..B];
-// returns the total.  Called by all threads; B <= kMaxSchedB.
-__device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx) {
+// Exclusive prefix sums of kStartCost + the 32-token block count of every
+// sequence into pfx[0..B], and the lengths into lens[0..B); returns the
+// total.  Called by all threads; B <= kMaxSchedB.
+__device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx, int* lens) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthreads = blockDim.x;
@@ -69,7 +73,8 @@ __device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pf
   for (int k = 0; k < 4; ++k) {
     const int i = min(base + k, B - 1);
     const int L = seq_lens[i];  // loaded unconditionally so the loads overlap
-    const int v = (k < per && base + k < B) ? (L + kBlock - 1) / kBlock : 0;
+    const int v = (k < per && base + k < B) ? kStartCost + (L + kBlock - 1) / kBlock : 0;
+    if (k < per && base + k < B) lens[base + k] = L;
     loc[k] = v;
     sum += v;
   }
@@ -113,11 +118,15 @@ struct Schedule {
   long long g0, g1;  // balanced: this unit's block range
   int b;             // balanced: next sequence to look at
   int done;
+  const int* pfx;    // balanced: block prefix and lengths in LDS
+  const int* lens;
 };
 
-__device__ __forceinline__ Schedule schedule_begin(const DecodeArgs& a, const int* pfx, int P) {
+__device__ __forceinline__ Schedule schedule_begin(const DecodeArgs& a, const int* pfx, const int* lens, int P) {
   Schedule s{};
   s.w = blockIdx.x;
+  s.pfx = pfx;
+  s.lens = lens;
   if (a.prefill_T > 0) {
     s.mode = 0;
   } else if (a.splits > 0) {
@@ -143,7 +152,7 @@ __device__ __forceinline__ Schedule schedule_begin(const DecodeArgs& a, const in
 
 // Next piece of this unit's work; every thread of the workgroup gets the
 // same answer.
-__device__ __forceinline__ bool schedule_next(const DecodeArgs& a, const int* pfx, Schedule& s, Segment& seg) {
+__device__ __forceinline__ bool schedule_next(const DecodeArgs& a, Schedule& s, Segment& seg) {
   if (s.done) return false;
   if (s.mode == 0) {
     s.done = 1;
@@ -166,15 +175,15 @@ __device__ __forceinline__ bool schedule_next(const DecodeArgs& a, const int* pf
   }
   while (s.b < a.B) {
     const int b = s.b;
-    const int p0 = uniform(pfx[b]), p1 = uniform(pfx[b + 1]);
-    if (p0 >= s.g1) break;
+    const int r0 = uniform(s.pfx[b]) + kStartCost, r1 = uniform(s.pfx[b + 1]);  // token blocks of b
+    if (r0 >= s.g1) break;
     s.b = b + 1;
-    const int k0 = (int)(max(s.g0, (long long)p0) - p0);
-    const int k1 = (int)(min(s.g1, (long long)p1) - p0);
+    const int k0 = (int)(max(s.g0, (long long)r0) - r0);
+    const int k1 = (int)(min(s.g1, (long long)r1) - r0);
     if (k0 < k1) {
-      const int L = a.seq_lens[b];
-      const int first = unit_of_block(p0, s.G, s.P);
-      const int last = unit_of_block(p1 - 1, s.G, s.P);
+      const int L = uniform(s.lens[b]);
+      const int first = unit_of_block(r0, s.G, s.P);
+      const int last = unit_of_block(r1 - 1, s.G, s.P);
       seg = Segment{b, k0 * kBlock, min(k1 * kBlock, L), L, s.w + b, first + b, last - first + 1};
       return true;
     }
@@ -187,49 +196,48 @@ __device__ __forceinline__ bool schedule_next(const DecodeArgs& a, const int* pf
 // LDS page layout
 // ---------------------------------------------------------------------------
 //
-// A page is 64 rows of 1152 bytes, stored unpadded: row r at r * 1152.  The
-// 16-byte chunks of a row are permuted inside each aligned group of eight:
-// chunk c of row r sits at chunk position c ^ swz(r).  gfx950 serves a
-// 16-byte LDS read per half-wave (even lanes, then odd lanes) over 128 banks
-// of 4 bytes, and the transposing 8-byte read per quarter-wave; without the
-// permutation the rows of an operand tile (1152 = 9 * 128) would pile onto a
-// quarter of the banks.  With it, the score operand reads, the transposing
-// value reads and the dequantising writes below are all conflict-free.
-// Rows 2k and 2k+1 share swz, so a row pair (2304 contiguous bytes in HBM)
-// is still moved by nine 256-byte LDS-DMA instructions: lane i fetches the
-// 4 bytes that belong at pair offset (256 k + 4 i), i.e. HBM pair offset
-// 256 k + ((4 i) ^ (swz << 4)).
-constexpr int kBufBytes = kPageBytes;                  // one bf16 page
+// Pages are streamed in blocks of 32 rows (half a page).  A block buffer in
+// LDS holds 32 rows of 1152 bytes, unpadded: row r at r * 1152.  The 16-byte
+// chunks of a row are permuted inside each aligned group of eight: chunk c
+// of row r sits at chunk position c ^ swz(r).  gfx950 serves a 16-byte LDS
+// read per half-wave (even lanes, then odd lanes) over 128 banks of 4 bytes,
+// and the transposing 8-byte read per quarter-wave; without the permutation
+// the rows of an operand tile (1152 = 9 * 128) would pile onto a quarter of
+// the banks.  With it, the score operand reads, the transposing value reads
+// and the dequantising writes below are all conflict-free.  Rows 2k and 2k+1
+// share swz, so a row pair (2304 contiguous bytes in HBM) is still moved by
+// nine 256-byte LDS-DMA instructions: lane i fetches the 4 bytes that belong
+// at pair offset (256 k + 4 i), i.e. HBM pair offset 256 k + ((4 i) ^ (swz << 4)).
+constexpr int kBlockRows = kBlock;                     // 32
+constexpr int kBlockBytes = kBlockRows * kRowBytes;    // 36864
+constexpr int kNBuf = 4;                               // block buffers: 3 in flight + 1 in use
 constexpr int kDmaBytes = 256;                         // 64 lanes x 4 bytes
 constexpr int kPairBytes = 2 * kRowBytes;              // 2304
 constexpr int kDmaPerPair = kPairBytes / kDmaBytes;    // 9
 constexpr int kWaves = 8;                              // every decode workgroup has 8 waves
-constexpr int kRowsPerWave = kPage / kWaves;           // 8
-constexpr int kDmaPerWave = kRowsPerWave / 2 * kDmaPerPair;  // 36 (< 64 outstanding)
+constexpr int kRowsPerWave = kBlockRows / kWaves;      // 4
+constexpr int kDmaPerWave = kRowsPerWave / 2 * kDmaPerPair;  // 18 per block
 constexpr int kRsrcWord3 = 0x00020000;                 // raw untyped buffer access
 
 __device__ __forceinline__ int swz(int r) { return 2 * ((r >> 2) & 3) + ((r >> 4) & 1); }
 // LDS byte offset of byte x (x < 1152) of row r.
 __device__ __forceinline__ int lds_off(int r, int x) { return r * kRowBytes + (x ^ (swz(r) << 4)); }
 
-// Copy rows [lo, hi) of a bf16 page into an LDS buffer; wave w moves rows
-// 8w .. 8w+7.  The buffer resource covers exactly the first `hi` rows, so
-// rows at or past hi (past the sequence end, or owned by the next unit)
-// arrive as zeros and stale or non-finite pool contents never reach the
-// matrix cores.  Rows below lo (only ever 0 or 32) belong to the previous
-// unit: waves whose rows all lie there issue nothing, and the compute skips
-// those rows.
-__device__ __forceinline__ void issue_page_bf16(const uint8_t* page, uint8_t* buf, int lo, int hi, int wave,
-                                                int lane) {
+// Copy the first `hi` rows of a 32-row block (rows 32*half .. of a bf16
+// page) into an LDS block buffer; wave w moves rows 4w .. 4w+3.  The buffer
+// resource covers exactly those rows, so rows at or past hi (past the
+// sequence end, or owned by the next unit) arrive as zeros and stale or
+// non-finite pool contents never reach the matrix cores.
+__device__ __forceinline__ void issue_block_bf16(const uint8_t* page, int half, uint8_t* buf, int hi, int wave,
+                                                 int lane) {
   asm volatile("" : "+s"(wave));  // re-derived per copy, not kept live across the loop
-  if (wave * kRowsPerWave + kRowsPerWave <= lo) return;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(page), (short)0,
-                                                                      uniform(hi * kRowBytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(page + half * kBlockBytes), (short)0, uniform(hi * kRowBytes), kRsrcWord3);
   const uint32_t lb = lds_addr(buf);
+  const uint32_t vo = (uint32_t)((lane * 4) ^ (swz(wave * kRowsPerWave) << 4));  // both pairs share swz
 #pragma unroll
   for (int j = 0; j < kRowsPerWave / 2; ++j) {
     const int pair = wave * (kRowsPerWave / 2) + j;
-    const uint32_t vo = (uint32_t)((lane * 4) ^ (swz(2 * pair) << 4));
 #pragma unroll
     for (int k = 0; k < kDmaPerPair; ++k) {
       const int off = pair * kPairBytes + k * kDmaBytes;
@@ -238,55 +246,55 @@ __device__ __forceinline__ void issue_page_bf16(const uint8_t* page, uint8_t* bu
   }
 }
 
-// fp8 staging buffer of one page: codes [64][512], scales [64][4] fp32,
-// rotated k^R [64][64] bf16.
+// fp8 staging buffer of one block: codes [32][512], scales [32][4] fp32,
+// rotated k^R [32][64] bf16.
 constexpr int kStCkv = 0;
-constexpr int kStScale = kPage * kDc;                  // 32768
-constexpr int kStKr = kStScale + kPage * 4 * 4;        // 33792
-constexpr int kStageBytes = kStKr + kPage * kDr * 2;   // 41984
-constexpr int kFp8DmaPerWave = 16 + 1 + 4;             // codes, scales (half wave), k^R
+constexpr int kStScale = kBlockRows * kDc;                  // 16384
+constexpr int kStKr = kStScale + kBlockRows * 4 * 4;        // 16896
+constexpr int kStageBytes = kStKr + kBlockRows * kDr * 2;   // 20992
+constexpr int kFp8DmaPerWave = 8 + 1 + 2;                   // codes, scales (16 lanes), k^R
 
-__device__ __forceinline__ void issue_page_fp8(const uint8_t* ckv8, const float* scale8, const uint8_t* kr8,
-                                               int page, uint8_t* stage, int lo, int hi, int wave, int lane) {
+__device__ __forceinline__ void issue_block_fp8(const uint8_t* ckv8, const float* scale8, const uint8_t* kr8,
+                                                int page, int half, uint8_t* stage, int hi, int wave, int lane) {
   asm volatile("" : "+s"(wave));
-  if (wave * kRowsPerWave + kRowsPerWave <= lo) return;
-  const size_t pg = (size_t)page;
+  const size_t row0 = (size_t)page * kPage + half * kBlockRows;
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(ckv8 + pg * (kPage * kDc)), (short)0, uniform(hi * kDc), kRsrcWord3);
+      (void*)uniform_ptr(ckv8 + row0 * kDc), (short)0, uniform(hi * kDc), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(scale8 + pg * (kPage * 4)), (short)0, uniform(hi * 16), kRsrcWord3);
+      (void*)uniform_ptr(scale8 + row0 * 4), (short)0, uniform(hi * 16), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(kr8 + pg * (kPage * kDr * 2)), (short)0, uniform(hi * kDr * 2), kRsrcWord3);
+      (void*)uniform_ptr(kr8 + row0 * (kDr * 2)), (short)0, uniform(hi * kDr * 2), kRsrcWord3);
   const uint32_t lb = lds_addr(stage);
   const uint32_t vo = lane * 4;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {  // codes: rows 8w .. 8w+7 are 4096 contiguous bytes
+  for (int k = 0; k < 8; ++k) {  // codes: rows 4w .. 4w+3 are 2048 contiguous bytes
     const int off = wave * (kRowsPerWave * kDc) + k * kDmaBytes;
     lds_dma4(rc, lb + kStCkv + off, vo, off);
   }
-  if (lane < 32) {  // scales: 8 rows x 16 bytes
+  if (lane < 16) {  // scales: 4 rows x 16 bytes
     const int off = wave * (kRowsPerWave * 16);
     lds_dma4(rsc, lb + kStScale + off, vo, off);
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {  // k^R: 8 rows x 128 bytes
+  for (int k = 0; k < 2; ++k) {  // k^R: 4 rows x 128 bytes
     const int off = wave * (kRowsPerWave * kDr * 2) + k * kDmaBytes;
     lds_dma4(rk, lb + kStKr + off, vo, off);
   }
 }
 
-// Expand a staged fp8 page into the bf16 row layout.  Thread t: row t/8,
-// channels 64(t%8) .. +63 (one 128-channel tile's half, one scale), plus one
-// 16-byte chunk of the row's k^R.  Rows past the valid range are zeros in
-// the staging buffer (codes and scales), so they expand to zeros.
-__device__ __forceinline__ void dequant_page(const uint8_t* stage, uint8_t* buf) {
+// Expand a staged fp8 block into the bf16 row layout.  Thread t: row t/16,
+// channels 32(t%16) .. +31 (a quarter of a 128-channel tile, one scale);
+// threads t < 256 also copy one 16-byte chunk of a row's k^R.  Rows past
+// the valid range are zeros in the staging buffer (codes and scales), so
+// they expand to zeros.
+__device__ __forceinline__ void dequant_block(const uint8_t* stage, uint8_t* buf) {
   int t = threadIdx.x;
-  asm volatile("" : "+v"(t));  // offsets recomputed per page, not held across the loop
-  const int r = t >> 3, sub = t & 7;
-  const float sc = *(const float*)(stage + kStScale + (r * 4 + (sub >> 1)) * 4);
-  const uint8_t* src = stage + kStCkv + r * kDc + sub * 64;
+  asm volatile("" : "+v"(t));  // offsets recomputed per block, not held across the loop
+  const int r = t >> 4, sub = t & 15;
+  const float sc = *(const float*)(stage + kStScale + (r * 4 + (sub >> 2)) * 4);
+  const uint8_t* src = stage + kStCkv + r * kDc + sub * 32;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int4v raw = lds_read_b128(src + 16 * j);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -301,53 +309,58 @@ __device__ __forceinline__ void dequant_page(const uint8_t* stage, uint8_t* buf)
         v[4 * e + 2] = f2bf(hi[0] * sc);
         v[4 * e + 3] = f2bf(hi[1] * sc);
       }
-      const int chunk = sub * 8 + 2 * j + h;  // 8 channels = one 16-byte chunk
+      const int chunk = sub * 4 + 2 * j + h;  // 8 channels = one 16-byte chunk
       *(MLA_LDS bf16x8*)(buf + lds_off(r, chunk * 16)) = v;
     }
-    asm volatile("" ::: "memory");  // one 16-code read in flight at a time
   }
-  const int kc = t & 7;
-  const int4v kr = lds_read_b128(stage + kStKr + r * (kDr * 2) + kc * 16);
-  *(MLA_LDS int4v*)(buf + lds_off(r, kDc * 2 + kc * 16)) = kr;
+  if (t < kBlockRows * 8) {
+    const int kr_row = t >> 3, kc = t & 7;
+    const int4v kr = lds_read_b128(stage + kStKr + kr_row * (kDr * 2) + kc * 16);
+    *(MLA_LDS int4v*)(buf + lds_off(kr_row, kDc * 2 + kc * 16)) = kr;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core compute on one page buffer
+// Matrix-core compute on one block buffer
 // ---------------------------------------------------------------------------
 
-// Per-wave state: 16 heads.  Lane l serves head h0 + l%16; its lane group
-// g = l/16 picks which channels / tokens of each matrix-core operand it holds.
+// Per-wave state: 16 heads and NT tiles of 16 latent channels.  Lane l serves
+// head h0 + l%16; its lane group g = l/16 picks which channels / tokens of
+// each matrix-core operand it holds.
+template <int NT>
 struct WaveState {
   bf16x8 q[18];      // absorbed query, B operand of S^T = R Q^T: channels 32kk + 8g + j
-  floatx4 zacc[32];  // Z^T channel tile mt: channels 16mt + 4g + r, column = head
+  floatx4 zacc[NT];  // Z^T tile j: channels c0 + 16j + 4g + r, column = head
   float m, l;        // running max (log2 units) and this lane's partial sum
 };
 
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is refreshed
 
-__device__ __forceinline__ void load_query(WaveState& st, const bf16* __restrict__ q, int H, int head, int g) {
+__device__ __forceinline__ void load_query(bf16x8 (&q)[18], const bf16* __restrict__ src_rows, int H, int head,
+                                           int g) {
   const int hc = head < H ? head : H - 1;
   const int keep = head < H ? -1 : 0;
-  const int4v* src = (const int4v*)(q + (size_t)hc * kRow);
+  const int4v* src = (const int4v*)(src_rows + (size_t)hc * kRow);
 #pragma unroll
   for (int kk = 0; kk < 18; ++kk) {
     int4v v = src[4 * kk + g];
     v &= keep;
-    st.q[kk] = __builtin_bit_cast(bf16x8, v);
+    q[kk] = __builtin_bit_cast(bf16x8, v);
   }
 }
 
 // Use the query registers, so the compiler's own wait for their loads is
 // placed here and not at the first score product, where later page copies
 // (which its counter does not see) would be waited for as well.
-__device__ __forceinline__ void consume_query(WaveState& st) {
+__device__ __forceinline__ void consume_query(bf16x8 (&q)[18]) {
 #pragma unroll
-  for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(st.q[kk]));
+  for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(q[kk]));
 }
 
-__device__ __forceinline__ void reset_state(WaveState& st) {
+template <int NT>
+__device__ __forceinline__ void reset_state(WaveState<NT>& st) {
 #pragma unroll
-  for (int t = 0; t < 32; ++t) st.zacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) st.zacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
 }
@@ -356,8 +369,8 @@ __device__ __forceinline__ void reset_state(WaveState& st) {
 // -inf where masked; p: probabilities relative to the running maximum.  The
 // maximum is only moved when it grows by more than kLazyRescale, so the
 // accumulator is rescaled rarely; p stays <= 2^kLazyRescale.
-template <int NV>
-__device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[NV], float (&p)[NV]) {
+template <int NT, int NV>
+__device__ __forceinline__ void softmax_update(WaveState<NT>& st, float (&x)[NV], float (&p)[NV]) {
   float mx = x[0];
 #pragma unroll
   for (int r = 1; r < NV; ++r) mx = fmaxf(mx, x[r]);
@@ -369,7 +382,7 @@ __device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[NV], fl
     if (need) st.m = mnew;
     st.l *= alpha;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) st.zacc[t] *= alpha;
+    for (int t = 0; t < NT; ++t) st.zacc[t] *= alpha;
   }
   float sum = 0.f;
 #pragma unroll
@@ -380,366 +393,263 @@ __device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[NV], fl
   st.l += sum;
 }
 
-// Score of one 16-token subtile (rows t0 .. t0+15, t0 a multiple of 16):
-// S^T (16 tokens x 16 heads), K = 576 in 18 steps of 32 channels.  Row index
-// m of the product maps to token t0 + 4(m%4) + m/4, so score register r of
-// lane group g is token t0 + 4r + g.
-__device__ __forceinline__ floatx4 score16(const WaveState& st, uint32_t buf, int t0, int lane) {
+// Scores of the 32 rows of a block buffer as two 16-token subtiles, S^T
+// (16 tokens x 16 heads) each, K = 576 in 18 steps of 32 channels; the two
+// accumulation chains are interleaved so that back-to-back matrix-core ops
+// never wait on each other.  Row index m of a subtile's product maps to
+// token 16u + 4(m%4) + m/4, so score register r of lane group g in subtile u
+// is token 16u + 4r + g.
+__device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int lane, floatx4& S0, floatx4& S1) {
   const int g = lane >> 4, m = lane & 15;
-  const int r = t0 + 4 * (m & 3) + (m >> 2);
+  const int r = 4 * (m & 3) + (m >> 2);
   // byte 64kk + 16g of the row: the permutation only touches bits 4..6, so
-  // even and odd kk each have one base and a constant stride of 128 bytes
-  const uint32_t ap0 = buf + lds_off(r, 16 * g);
-  const uint32_t ap1 = buf + lds_off(r, 64 + 16 * g);
-  auto rd = [&](int kk) { return lds_read_b128_at((kk & 1 ? ap1 : ap0) + 128 * (kk >> 1)); };
-  floatx4 S = {};
-  constexpr int D = 3;  // operand reads in flight
-  int4v a[D];
+  // even and odd kk each have one base per subtile and a constant stride of
+  // 128 bytes
+  uint32_t ap[2][2];  // [subtile][kk parity]
+  ap[0][0] = buf + lds_off(r, 16 * g);
+  ap[0][1] = buf + lds_off(r, 64 + 16 * g);
+  ap[1][0] = buf + lds_off(r + 16, 16 * g);
+  ap[1][1] = buf + lds_off(r + 16, 64 + 16 * g);
+  // opaque bases: every read is then one base register plus an immediate offset
+  asm volatile("" : "+v"(ap[0][0]), "+v"(ap[0][1]), "+v"(ap[1][0]), "+v"(ap[1][1]));
+  auto rd = [&](int u, int kk) { return lds_read_b128_at(ap[u][kk & 1] + 128 * (kk >> 1)); };
+  S0 = floatx4{};
+  S1 = floatx4{};
+  constexpr int D = 2;  // operand reads in flight per chain
+  int4v a0[D], a1[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) a[i] = rd(i);
+  for (int i = 0; i < D; ++i) {
+    a0[i] = rd(0, i);
+    a1[i] = rd(1, i);
+  }
 #pragma unroll
   for (int kk = 0; kk < 18; ++kk) {
-    const int4v cur = a[kk % D];
-    if (kk + D < 18) a[kk % D] = rd(kk + D);
-    S = mfma16(__builtin_bit_cast(bf16x8, cur), st.q[kk], S);
+    const int4v c0 = a0[kk % D], c1 = a1[kk % D];
+    if (kk + D < 18) {
+      a0[kk % D] = rd(0, kk + D);
+      a1[kk % D] = rd(1, kk + D);
+    }
+    S0 = mfma16(__builtin_bit_cast(bf16x8, c0), q[kk], S0);
+    S1 = mfma16(__builtin_bit_cast(bf16x8, c1), q[kk], S1);
   }
-  return S;
 }
 
-// One tile of TT (16 or 32) tokens starting at row t0 of the page buffer;
-// rows at or past `hi` are masked.  Value product Z^T += C^T P^T: A = C^T
-// (16 channels x TT tokens) through transposing LDS reads, B = P^T.  For
-// TT = 32 the K = 32 slots of lane group g are tokens t0 + 4j + g (j < 4,
-// first subtile) and t0 + 16 + 4(j-4) + g.
-template <int TT>
-__device__ __forceinline__ void tile(WaveState& st, uint32_t buf, int t0, int hi, int lane, float scale_log2) {
-  // Recompute the lane's operand offsets in every tile rather than let the
-  // compiler keep one set per tile position and buffer live across the loop.
+// One block buffer (32 rows); rows at or past `hi` are masked.  Scores for
+// the wave's 16 heads over the 32 tokens, then the value product
+// Z^T += C^T P^T for the wave's NT channel tiles, starting at tile mt0 (a
+// multiple of 4): A = C^T (16 channels x 32 tokens) through transposing LDS
+// reads, B = P^T.  The K = 32 slots of lane group g are tokens 4j + g
+// (j < 4) and 16 + 4(j-4) + g.
+template <int NT>
+__device__ __forceinline__ void block_compute(WaveState<NT>& st, uint32_t buf, int hi, int lane, int mt0,
+                                              float scale_log2) {
+  // Recompute the lane's operand offsets in every call rather than let the
+  // compiler keep one set per buffer live across the block loop.
   asm volatile("" : "+v"(lane));
-  constexpr int NS = TT / 16;
   const int g = lane >> 4;
-  float x[4 * NS], p[4 * NS];
+  float x[8], p[8];
+  floatx4 S[2];
+  score32(st.q, buf, lane, S[0], S[1]);
 #pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    const floatx4 S = score16(st, buf, t0 + 16 * u, lane);
+  for (int u = 0; u < 2; ++u) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float v = S[r] * scale_log2;
-      x[4 * u + r] = t0 + 16 * u + 4 * r + g < hi ? v : -INFINITY;
+      const float v = S[u][r] * scale_log2;
+      x[4 * u + r] = 16 * u + 4 * r + g < hi ? v : -INFINITY;
     }
   }
-  softmax_update<4 * NS>(st, x, p);
-  // Source lane s' of each 16-lane group points at row t0 + 4(s'/4) + g,
-  // channels 16mt + 4(s'%4) .. +3, i.e. row byte 32mt + 8(s'%4); as above,
-  // the permutation leaves a base per mt%4 and a stride of 128 bytes.
-  const int vr = t0 + g + 4 * ((lane & 15) >> 2);
+  softmax_update<NT, 8>(st, x, p);
+  // Source lane s' of each 16-lane group points at row 4(s'/4) + g,
+  // channels 16mt + 4(s'%4) .. +3, i.e. row byte 32mt + 8(s'%4); the
+  // permutation leaves a base per mt%4 (and per row half) and a stride of
+  // 128 bytes.
+  const int vr = g + 4 * ((lane & 15) >> 2);
   const int vx = 8 * (lane & 3);
-  uint32_t vb[4];
+  uint32_t vb[2][4];  // [rows +0 / +16][mt % 4]
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) vb[q4] = buf + lds_off(vr, 32 * q4 + vx);
-  constexpr int D = 3;
-  if constexpr (TT == 32) {
-    // rows + 16 differ only in bit 0 of swz, i.e. by 16 * 1152 +- 16 bytes
-    const uint32_t dh = lds_off(vr + 16, vx) - lds_off(vr, vx);
-    bf16x8 pb;
+  for (int q4 = 0; q4 < 4; ++q4) {
+    vb[0][q4] = buf + lds_off(vr, 32 * q4 + vx) + 32 * mt0;
+    vb[1][q4] = buf + lds_off(vr + 16, 32 * q4 + vx) + 32 * mt0;
+  }
+  asm volatile("" : "+v"(vb[0][0]), "+v"(vb[0][1]), "+v"(vb[0][2]), "+v"(vb[0][3]));
+  asm volatile("" : "+v"(vb[1][0]), "+v"(vb[1][1]), "+v"(vb[1][2]), "+v"(vb[1][3]));
+  bf16x8 pb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pb[j] = f2bf(p[j]);
-    auto vread = [&](int mt) {
-      bf16x4 lo = lds_read_tr16_at(vb[mt & 3] + 128 * (mt >> 2));
-      bf16x4 hi = lds_read_tr16_at(vb[mt & 3] + dh + 128 * (mt >> 2));
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    bf16x8 va[D];
+  for (int j = 0; j < 8; ++j) pb[j] = f2bf(p[j]);
+  auto vread = [&](int j) {
+    bf16x4 lo = lds_read_tr16_at(vb[0][j & 3] + 128 * (j >> 2));
+    bf16x4 hi = lds_read_tr16_at(vb[1][j & 3] + 128 * (j >> 2));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  constexpr int D = NT < 3 ? NT : 3;
+  bf16x8 va[D];
 #pragma unroll
-    for (int i = 0; i < D; ++i) va[i] = vread(i);
+  for (int i = 0; i < D; ++i) va[i] = vread(i);
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const bf16x8 cur = va[mt % D];
-      if (mt + D < 32) va[mt % D] = vread(mt + D);
-      st.zacc[mt] = mfma16(cur, pb, st.zacc[mt]);
-    }
-  } else {
-    const bf16x4 pb = {f2bf(p[0]), f2bf(p[1]), f2bf(p[2]), f2bf(p[3])};
-    auto vread = [&](int mt) { return lds_read_tr16_at(vb[mt & 3] + 128 * (mt >> 2)); };
-    bf16x4 va[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) va[i] = vread(i);
-#pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const bf16x4 cur = va[mt % D];
-      if (mt + D < 32) va[mt % D] = vread(mt + D);
-      st.zacc[mt] = mfma16k16(cur, pb, st.zacc[mt]);
-    }
+  for (int j = 0; j < NT; ++j) {
+    const bf16x8 cur = va[j % D];
+    if (j + D < NT) va[j % D] = vread(j + D);
+    st.zacc[j] = mfma16(cur, pb, st.zacc[j]);
   }
 }
 
-// Normalise and write one wave's 16 heads: z rows [head][512], lse[head].
-__device__ __forceinline__ void store_state(const WaveState& st, float l_tot, float* zdst, float* ldst, int h0, int H,
-                                            int lane) {
+// Normalise and write one wave's part: z rows [head][512] at channels
+// c0 .. c0 + 16 NT, and lse[head] if with_lse.
+template <int NT>
+__device__ __forceinline__ void store_state(const WaveState<NT>& st, float l_tot, float* zdst, float* ldst, int h0,
+                                            int H, int lane, int c0, bool with_lse) {
   constexpr float kLn2 = 0.69314718055994530942f;
   const int head = h0 + (lane & 15);
   const int g = lane >> 4;
   if (head >= H) return;
   const float inv = 1.0f / l_tot;
-  float* row = zdst + (size_t)head * kDc;
+  float* row = zdst + (size_t)head * kDc + c0;
 #pragma unroll
-  for (int mt = 0; mt < 32; ++mt) {
-    *(float4*)(row + 16 * mt + 4 * g) = make_float4(st.zacc[mt][0] * inv, st.zacc[mt][1] * inv,
-                                                    st.zacc[mt][2] * inv, st.zacc[mt][3] * inv);
+  for (int j = 0; j < NT; ++j) {
+    *(float4*)(row + 16 * j + 4 * g) = make_float4(st.zacc[j][0] * inv, st.zacc[j][1] * inv,
+                                                   st.zacc[j][2] * inv, st.zacc[j][3] * inv);
   }
-  if (ldst != nullptr && g == 0) ldst[head] = (st.m + __log2f(l_tot)) * kLn2;
-}
-
-// ---------------------------------------------------------------------------
-// Merge of one sequence's partials (shared by the merge kernel and the
-// in-kernel merge of the last-arriving unit)
-// ---------------------------------------------------------------------------
-// One wave per head: the chunks' log-sum-exps are read one per lane and
-// reduced across the wave; then each lane folds its 8 channels of every
-// chunk, 8 chunk loads in flight.
-__device__ __forceinline__ void merge_head(const DecodeArgs& a, int b, int head, int slot0, int n, int lane) {
-  // pass 1: maximum log-sum-exp over the chunks
-  float mmax = -INFINITY;
-  for (int c0 = 0; c0 < n; c0 += 64)
-    if (c0 + lane < n) mmax = fmaxf(mmax, a.lsep[(size_t)(slot0 + c0 + lane) * a.H + head]);
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, d));
-  // pass 2: weights (one chunk per lane) and the weighted sum of the chunks' z
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float wsum = 0.f;
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    float w = 0.f;
-    if (c0 + lane < n) w = __expf(a.lsep[(size_t)(slot0 + c0 + lane) * a.H + head] - mmax);
-    wsum += w;
-    const int m = min(64, n - c0);
-    for (int i0 = 0; i0 < m; i0 += 8) {
-      float wv[8];
-      float4 v0[8], v1[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = min(i0 + u, m - 1);  // every slot loaded holds a partial of this sequence
-        wv[u] = i0 + u < m ? __shfl(w, i) : 0.f;
-        const size_t sl = (size_t)(slot0 + c0 + i) * a.H + head;
-        const float4* zp = (const float4*)(a.zp + sl * kDc) + lane * 2;
-        v0[u] = zp[0];
-        v1[u] = zp[1];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wi = wv[u];
-        acc[0] += wi * v0[u].x; acc[1] += wi * v0[u].y; acc[2] += wi * v0[u].z; acc[3] += wi * v0[u].w;
-        acc[4] += wi * v1[u].x; acc[5] += wi * v1[u].y; acc[6] += wi * v1[u].z; acc[7] += wi * v1[u].w;
-      }
-    }
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) wsum += __shfl_xor(wsum, d);
-  const float inv = 1.0f / wsum;
-  float4* zo = (float4*)(a.z + ((size_t)b * a.H + head) * kDc) + lane * 2;
-  zo[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  zo[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.H + head] = mmax + __logf(wsum);
-}
-
-// After this workgroup stored its partial of `seg`: count the arrival and
-// report whether this was the sequence's last piece (the counter is left at
-// zero for the next call).  Called by all threads.
-__device__ __forceinline__ bool arrive(const DecodeArgs& a, const Segment& seg, int expected, int* flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's partial stores
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // system scope: performed past every XCD's L2, so all units count on one copy
-    const int old = __hip_atomic_fetch_add(a.counters + seg.b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    const int last = old == expected - 1;
-    if (last) __hip_atomic_exchange(a.counters + seg.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    *flag = last;
-  }
-  __syncthreads();
-  const bool last = uniform(*flag) != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other pieces' stores
-  return last;
+  if (with_lse && ldst != nullptr && g == 0) ldst[head] = (st.m + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
 // bf16 / fp8-cache matrix-core decode
 // ---------------------------------------------------------------------------
+
+// Position in a unit's stream of 32-token blocks: block k of a piece.
+struct Cursor {
+  Schedule sch;
+  Segment seg;
+  int k;
+  int valid;
+};
+
+__device__ __forceinline__ void cursor_next(const DecodeArgs& a, Cursor& c) {
+  if (c.k < (c.seg.t1 - 1) / kBlock) {
+    ++c.k;
+    return;
+  }
+  c.valid = schedule_next(a, c.sch, c.seg);
+  c.k = c.valid ? c.seg.t0 / kBlock : 0;
+}
+
+// 8 waves: all of them copy blocks; the first HG*CG compute.  HG head groups
+// of 16 heads times CG groups of 512/CG latent channels: every computing wave
+// scores all tokens of a block for its heads (the CG waves of a head group
+// compute the same scores) and accumulates only its channels, so the waves
+// never combine partial softmax states.
 //
-// 8 waves: all of them copy pages; the first HG*TG compute.  HG head groups
-// of 16 heads, TG token slices of each page.  FP8 selects the fp8 pool: two
-// staging buffers (the next page's copy lands in one while the other is
-// expanded) and one bf16 page buffer.
-template <int HG, int TG, bool FP8>
+// Pipeline (bf16): block i sits in buffer i % 4.  Each step waits for its
+// own copy of block i, meets the other waves at one barrier (after which
+// block i is complete and buffer (i+3) % 4 = (i-1) % 4 is no longer read),
+// computes block i and then issues the copy of block i+3, so up to three
+// blocks are in flight while one is consumed.  fp8: the copies land in four
+// staging buffers and every block is expanded into one bf16 buffer between
+// two barriers.
+template <int HG, int CG, bool FP8>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
-  static_assert(HG * TG <= kWaves, "too many compute waves");
-  constexpr int TPW = kPage / TG;           // tokens of each page a wave scores
-  constexpr int TT = TPW >= 32 ? 32 : 16;   // tokens per tile
-  static_assert(TPW % TT == 0, "tile must divide the wave's slice");
-  constexpr int kSmem = FP8 ? 2 * kStageBytes + kBufBytes : 2 * kBufBytes;
+  static_assert(HG * CG <= kWaves, "too many compute waves");
+  constexpr int NT = 32 / CG;  // channel tiles per wave
+  static_assert(NT % 4 == 0, "channel groups start on a multiple of 4 tiles");
+  constexpr int kSmem = FP8 ? kNBuf * kStageBytes + kBlockBytes : kNBuf * kBlockBytes;
+  constexpr int kDmaBlock = FP8 ? kFp8DmaPerWave : kDmaPerWave;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   __shared__ int pfx[kMaxSchedB + 1];
-  __shared__ int flag;
+  __shared__ int lens[kMaxSchedB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const bool computes = wave < HG * TG;
-  const int hg = wave % HG, tg = wave / HG;
+  const bool computes = wave < HG * CG;
+  const int hg = wave % HG, cg = wave / HG;
   const int h0 = hg * 16;
-  const bool fused = a.counters != nullptr;
+  const int mt0 = cg * NT;
 
   int P = 0;
-  if (a.splits == 0 && a.prefill_T == 0) P = block_prefix(a.seq_lens, a.B, pfx);
-  Schedule sch = schedule_begin(a, pfx, P);
-  Segment seg;
-  if (!schedule_next(a, pfx, sch, seg)) return;
+  if (a.splits == 0 && a.prefill_T == 0) P = block_prefix(a.seq_lens, a.B, pfx, lens);
+  Cursor cp;
+  cp.sch = schedule_begin(a, pfx, lens, P);
+  cp.valid = schedule_next(a, cp.sch, cp.seg);
+  if (!cp.valid) return;
+  cp.k = cp.seg.t0 / kBlock;
 
-  // page buffers: bf16 -> smem + (i&1) * kBufBytes; fp8 -> stage (i&1), one bf16 buffer
-  uint8_t* const bfbuf = FP8 ? smem + 2 * kStageBytes : smem;
-  auto bt_row = [&](const Segment& s) {
-    return a.prefill_T > 0 ? block_table : block_table + (size_t)s.b * a.max_pages;
-  };
   auto qrow = [&](const Segment& s) { return (const bf16*)a.q + (size_t)s.b * a.H * kRow; };
-  auto page_lo = [&](const Segment& s, int p) { return max(s.t0 - p * kPage, 0); };
-  auto page_hi = [&](const Segment& s, int p) { return min(s.t1 - p * kPage, kPage); };
+  auto block_hi = [&](const Cursor& c) { return min(c.seg.t1 - c.k * kBlock, kBlock); };
   // block-table reads use a uniform index, so they are scalar loads that do
-  // not wait behind the page copies in flight
-  auto issue = [&](const Segment& s, int p, int i) {
-    const int page = bt_row(s)[uniform(p)];
+  // not wait behind the copies in flight
+  auto issue = [&](const Cursor& c, int slot) {
+    const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)c.seg.b * a.max_pages;
+    const int page = bt[uniform(c.k >> 1)];
     if constexpr (FP8) {
-      issue_page_fp8(a.ckv8, a.scale8, a.kr8, page, smem + (i & 1) * kStageBytes, page_lo(s, p), page_hi(s, p),
-                     wave, lane);
+      issue_block_fp8(a.ckv8, a.scale8, a.kr8, page, c.k & 1, smem + slot * kStageBytes, block_hi(c), wave, lane);
     } else {
-      issue_page_bf16(a.rows + (size_t)page * kPageBytes, smem + (i & 1) * kBufBytes, page_lo(s, p), page_hi(s, p),
-                      wave, lane);
+      issue_block_bf16(a.rows + (size_t)page * kPageBytes, c.k & 1, smem + slot * kBlockBytes, block_hi(c), wave,
+                       lane);
     }
   };
+  // The first piece of every sequence records where its partials start and
+  // how many pieces there are (1: finished here), for the merge kernel.
+  auto note_pieces = [&](const Segment& s) {
+    if (a.meta != nullptr && s.slot == s.slot0 && tid == 0) *(int2*)(a.meta + 2 * s.b) = make_int2(s.slot0, s.parts);
+  };
 
-  // Pieces of sequences whose merge falls to this unit: at most the first
-  // and the last piece of a unit can be partial, so two at most.
-  int pend_n = 0, pb0 = 0, ps0 = 0, pc0 = 0, pb1 = 0, ps1 = 0, pc1 = 0;
-
-  // The query loads and the first page copy travel together; consuming the
+  // The query loads and the first copies travel together; consuming the
   // query right after waits for both (the compiler's counter only knows the
-  // query loads), before the second page's copy is issued.
-  WaveState st;
-  int p = seg.t0 / kPage;
-  load_query(st, qrow(seg), a.H, h0 + (lane & 15), lane >> 4);
-  issue(seg, p, 0);
-  consume_query(st);
+  // query loads).
+  WaveState<NT> st;
+  load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4);
+  Cursor ld = cp;
+  int issued = 0;
+#pragma unroll
+  for (int j = 0; j < kNBuf - 1; ++j) {
+    if (ld.valid) {
+      issue(ld, j);
+      ++issued;
+      cursor_next(a, ld);
+    }
+  }
+  consume_query(st.q);
   reset_state(st);
+  note_pieces(cp.seg);
   for (int i = 0;; ++i) {
-    const bool seg_last = p == (seg.t1 - 1) / kPage;
-    Segment nseg = seg;
-    int np = p + 1;
-    bool more = true;
-    if (seg_last) {
-      more = schedule_next(a, pfx, sch, nseg);
-      np = nseg.t0 / kPage;
-    }
-    if (more) {
-      issue(nseg, np, i + 1);
-      if constexpr (FP8) wait_vmcnt<kFp8DmaPerWave>(); else wait_vmcnt<kDmaPerWave>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // wait for this wave's part of block i: the copies issued after it may stay in flight
+    const int after = issued - i - 1;
+    if (after >= 2) wait_vmcnt<2 * kDmaBlock>();
+    else if (after == 1) wait_vmcnt<kDmaBlock>();
+    else wait_vmcnt<0>();
     __syncthreads();
     uint8_t* buf;
     if constexpr (FP8) {
-      dequant_page(smem + (i & 1) * kStageBytes, bfbuf);
+      dequant_block(smem + (i % kNBuf) * kStageBytes, smem + kNBuf * kStageBytes);
       __syncthreads();
-      buf = bfbuf;
+      buf = smem + kNBuf * kStageBytes;
     } else {
-      buf = smem + (i & 1) * kBufBytes;
+      buf = smem + (i % kNBuf) * kBlockBytes;
     }
-    const uint32_t bufa = lds_addr(buf);
-    const int lo = page_lo(seg, p), hi = page_hi(seg, p);
-    if (computes) {
-#pragma unroll
-      for (int t = 0; t < TPW / TT; ++t) {
-        const int t0 = tg * TPW + t * TT;
-        if (t0 + TT > lo && t0 < hi) tile<TT>(st, bufa, t0, hi, lane, a.scale_log2);
-      }
+    if (computes) block_compute<NT>(st, lds_addr(buf), block_hi(cp), lane, mt0, a.scale_log2);
+    if (ld.valid) {  // into the buffer of block i-1, which every wave finished before the barrier
+      issue(ld, (i + kNBuf - 1) % kNBuf);
+      ++issued;
+      cursor_next(a, ld);
     }
-    __syncthreads();  // the buffer is free: refilled next round, or merge scratch below
 
-    if (seg_last) {
-      // combine the token slices of the TG waves that share a head group: a
-      // tree over LDS in the free page buffer, at most two slots per pass
-      float l_tot = pair32_sum(pair16_sum(st.l));
-      if constexpr (TG > 1) {
-        uint8_t* scratch = buf;
-        floatx4* zx = (floatx4*)scratch;                   // [2][32 tiles][64 lanes]
-        float* ml = (float*)(scratch + 2 * 32 * 64 * 16);  // [2][2][64]
-        static_assert(2 * 32 * 64 * 16 + 2 * 2 * 64 * 4 <= kBufBytes, "merge scratch");
-        // Runtime loops on purpose: unrolled, the conditional accumulator
-        // update would be duplicated per pass and cost register copies.
-#pragma unroll 1
-        for (int half = TG / 2; half >= 1; half /= 2) {
-#pragma unroll 1
-          for (int s0 = 0; s0 < half * HG; s0 += 2) {
-            const int slw = (tg - half) * HG + hg - s0;  // slot this wave hands over
-            if (computes && tg >= half && tg < 2 * half && slw >= 0 && slw < 2) {
-              floatx4* dst = zx + (size_t)slw * 32 * 64;
-#pragma unroll
-              for (int t = 0; t < 32; ++t) dst[t * 64 + lane] = st.zacc[t];
-              ml[(slw * 2) * 64 + lane] = st.m;
-              ml[(slw * 2 + 1) * 64 + lane] = l_tot;
-            }
-            __syncthreads();
-            const int slr = tg * HG + hg - s0;  // slot this wave takes over
-            if (computes && tg < half && slr >= 0 && slr < 2) {
-              const float mo = ml[(slr * 2) * 64 + lane];
-              const float lo2 = ml[(slr * 2 + 1) * 64 + lane];
-              const float mstar = fmaxf(st.m, mo);
-              const float a0 = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mstar);
-              const float ao = mo == -INFINITY ? 0.f : fast_exp2(mo - mstar);
-              l_tot = l_tot * a0 + lo2 * ao;
-              const floatx4* src = zx + (size_t)slr * 32 * 64;
-#pragma unroll
-              for (int t = 0; t < 32; ++t) {
-                st.zacc[t] = st.zacc[t] * a0 + src[t * 64 + lane] * ao;
-                if (t % 8 == 7) asm volatile("" ::: "memory");  // 8 tiles' loads in flight, not 32
-              }
-              st.m = mstar;
-            }
-            __syncthreads();
-          }
-        }
+    if (cp.k == (cp.seg.t1 - 1) / kBlock) {  // last block of this piece
+      const float l_tot = pair32_sum(pair16_sum(st.l));
+      if (computes) {
+        const Segment& sg = cp.seg;
+        const bool whole = sg.parts == 1;
+        float* zdst = whole ? a.z + (size_t)sg.b * a.H * kDc : a.zp + (size_t)sg.slot * a.H * kDc;
+        float* ldst = whole ? (a.lse ? a.lse + (size_t)sg.b * a.H : nullptr) : a.lsep + (size_t)sg.slot * a.H;
+        store_state(st, l_tot, zdst, ldst, h0, a.H, lane, mt0 * 16, cg == 0);
       }
-      const bool whole = seg.parts == 1;
-      if (computes && tg == 0) {
-        float* zdst;
-        float* ldst;
-        if (whole) {
-          zdst = a.z + (size_t)seg.b * a.H * kDc;
-          ldst = a.lse ? a.lse + (size_t)seg.b * a.H : nullptr;
-        } else {
-          zdst = a.zp + (size_t)seg.slot * a.H * kDc;
-          ldst = a.lsep + (size_t)seg.slot * a.H;
-        }
-        store_state(st, l_tot, zdst, ldst, h0, a.H, lane);
-      }
-      if (!whole && fused && arrive(a, seg, seg.parts, &flag)) {
-        if (pend_n == 0) {
-          pb0 = seg.b, ps0 = seg.slot0, pc0 = seg.parts;
-        } else {
-          pb1 = seg.b, ps1 = seg.slot0, pc1 = seg.parts;
-        }
-        ++pend_n;
-      }
-      if (more) {
-        load_query(st, qrow(nseg), a.H, h0 + (lane & 15), lane >> 4);
-        consume_query(st);
-        reset_state(st);
-      }
-      seg = nseg;
+      cursor_next(a, cp);
+      if (!cp.valid) break;
+      load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4);
+      consume_query(st.q);
+      reset_state(st);
+      note_pieces(cp.seg);
+    } else {
+      cursor_next(a, cp);
     }
-    if (!more) break;
-    p = np;
-  }
-
-  for (int k = 0; k < pend_n; ++k) {
-    const int b = uniform(k ? pb1 : pb0), s0 = uniform(k ? ps1 : ps0), n = uniform(k ? pc1 : pc0);
-    for (int h = wave; h < a.H; h += kWaves) merge_head(a, b, h, s0, n, lane);
   }
 }
 
@@ -747,20 +657,22 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 // fp32 decode (VALU; small and exact-arithmetic cases)
 // ---------------------------------------------------------------------------
 // One workgroup per (unit, head).  Tokens are scored 256 at a time (one per
-// thread), then every thread folds them into its two channels of z.  Partials
-// are always merged by the merge kernel.
+// thread), then every thread folds them into its two channels of z.
 __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
   __shared__ float qs[kRow];
   __shared__ float ps[256];
   __shared__ float red[8];
   __shared__ int pfx[kMaxSchedB + 1];
+  __shared__ int lens[kMaxSchedB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
   int P = 0;
-  if (a.splits == 0 && a.prefill_T == 0) P = block_prefix(a.seq_lens, a.B, pfx);
-  Schedule sch = schedule_begin(a, pfx, P);
+  if (a.splits == 0 && a.prefill_T == 0) P = block_prefix(a.seq_lens, a.B, pfx, lens);
+  Schedule sch = schedule_begin(a, pfx, lens, P);
   Segment seg;
-  while (schedule_next(a, pfx, sch, seg)) {
+  while (schedule_next(a, sch, seg)) {
+    if (a.meta != nullptr && head == 0 && seg.slot == seg.slot0 && tid == 0)
+      *(int2*)(a.meta + 2 * seg.b) = make_int2(seg.slot0, seg.parts);
     const int32_t* bt = a.prefill_T > 0 ? a.block_table : a.block_table + (size_t)seg.b * a.max_pages;
     const float* q = (const float*)a.q + ((size_t)seg.b * a.H + head) * kRow;
     const float* pool = (const float*)a.rows;
@@ -822,30 +734,50 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split merge kernel: one workgroup per (sequence, 8 heads), one wave per head
+// Split merge: lse = log sum_c e^{lse_c};  z = sum_c e^{lse_c - lse} z_c
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(512) merge_kernel(DecodeArgs a) {
-  __shared__ int pfx[kMaxSchedB + 1];
-  const int b = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int head = blockIdx.y * 8 + wave;
-  int slot0, n;
-  if (a.splits > 0) {
-    const int S = a.splits;
-    const int np = (a.seq_lens[b] + kPage - 1) / kPage;
-    const int chunk = (np + S - 1) / S;
-    n = (np + chunk - 1) / chunk;
-    slot0 = b * S;
-  } else {
-    const int P = block_prefix(a.seq_lens, a.B, pfx);
-    const long long G = min((long long)a.units, (long long)P);
-    const int first = unit_of_block(pfx[b], G, P);
-    const int last = unit_of_block(pfx[b + 1] - 1, G, P);
-    n = last - first + 1;
-    slot0 = first + b;
+// One workgroup per (head, sequence), 128 threads of 4 channels each.  The
+// sequence's first slot and piece count come from the decode pass's record;
+// every piece's log-sum-exp and z slice are loaded together (one round trip
+// per batch of kMergeBatch pieces) and folded with a running maximum.
+constexpr int kMergeBatch = 32;
+
+__global__ void __launch_bounds__(128) merge_kernel(DecodeArgs a) {
+  const int head = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int2 mt = *(const int2*)(a.meta + 2 * b);
+  const int slot0 = mt.x, n = mt.y;
+  if (n <= 1) return;  // finished in one piece by the decode pass
+  float m = -INFINITY, wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < n; c0 += kMergeBatch) {
+    float lv[kMergeBatch];
+    float4 zv[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int c = min(c0 + u, n - 1);  // every slot loaded holds a piece of this sequence
+      const size_t sl = (size_t)(slot0 + c) * a.H + head;
+      lv[u] = c0 + u < n ? a.lsep[sl] : -INFINITY;
+      zv[u] = *(const float4*)(a.zp + sl * kDc + 4 * tid);
+    }
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, lv[u]);
+    const float alpha = __expf(m - mb);  // m = -inf on the first batch: alpha = 0
+    wsum *= alpha;
+    acc.x *= alpha; acc.y *= alpha; acc.z *= alpha; acc.w *= alpha;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = __expf(lv[u] - mb);  // 0 for the padding entries
+      wsum += w;
+      acc.x += w * zv[u].x; acc.y += w * zv[u].y; acc.z += w * zv[u].z; acc.w += w * zv[u].w;
+    }
+    m = mb;
   }
-  if (n <= 1 || head >= a.H) return;
-  merge_head(a, b, head, slot0, n, lane);
+  const float inv = 1.0f / wsum;
+  *(float4*)(a.z + ((size_t)b * a.H + head) * kDc + 4 * tid) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (a.lse != nullptr && tid == 0) a.lse[(size_t)b * a.H + head] = m + __logf(wsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -877,7 +809,7 @@ hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s) {
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B, (a.H + 7) / 8), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.H, a.B), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

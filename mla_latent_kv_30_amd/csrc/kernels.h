@@ -32,8 +32,8 @@ struct DecodeArgs {
   float* lse;
   float* zp;                   // partials [slots][H][512]
   float* lsep;                 // partials [slots][H]
-  int32_t* counters;           // [B] arrival counts (zero between calls), or
-                               // NULL: partials are left for the merge kernel
+  int32_t* meta;               // [B][2] first partial slot and piece count of each
+                               // split sequence (written by decode, read by merge)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s);

@@ -72,39 +72,48 @@ __global__ void __launch_bounds__(256) upproj_bf16_kernel(UpprojArgs a) {
   }
 }
 
-// Few query rows (decode, N <= 64): workgroup = (head, 32-row tile of d);
-// the 4 waves split the contraction over c (128 each) so every wave keeps
-// only 8 operand loads in flight, and the partial sums meet in LDS.
+// Few query rows (decode, N <= 32): workgroup = (head, 16-row tile of d), so
+// a launch has H * 8 workgroups.  The 4 waves split the contraction over c
+// (128 each); every operand load of a lane is issued before the first
+// product (one memory round trip), and the partial sums meet in LDS.
+// 16x16x32 matrix cores: A = W (16 d x 32 c), B = z^T (32 c x 16 rows).
+constexpr int kUpSmallMaxN = 32;
+
 __global__ void __launch_bounds__(256) upproj_bf16_small_kernel(UpprojArgs a) {
-  __shared__ floatx16 red[3][2][64];
-  const int h = blockIdx.x >> 2, dt = blockIdx.x & 3;
+  __shared__ floatx4 red[3][2][64];
+  const int h = blockIdx.x, dt = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 5;
-  const bf16* w = (const bf16*)a.w_uv + ((size_t)h * kDv + 32 * dt + (lane & 31)) * kDc;
-  int nrow[2];
-  bool nok[2];
+  const int G = lane >> 4, s = lane & 15;
+  const bf16* w = (const bf16*)a.w_uv + ((size_t)h * kDv + 16 * dt + s) * kDc + 128 * wave + 8 * G;
+  bf16x8 aw[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) aw[kk] = __builtin_bit_cast(bf16x8, *(const int4v*)(w + 32 * kk));
+  float4 zr[2][4][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    nrow[nt] = 32 * nt + (lane & 31);
-    nok[nt] = nrow[nt] < a.N;
-  }
-  floatx16 acc[2] = {floatx16{}, floatx16{}};
+    const int n = 16 * nt + s;
+    const bool ok = n < a.N;
+    const float* zp = a.z + ((size_t)(ok ? n : 0) * a.H + h) * kDc + 128 * wave + 8 * G;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int c0 = 128 * wave + 16 * kk + 8 * g;
-    const bf16x8 aw = __builtin_bit_cast(bf16x8, *(const int4v*)(w + c0));
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if (32 * nt >= a.N) break;
+    for (int kk = 0; kk < 4; ++kk) {
       float4 u0 = make_float4(0, 0, 0, 0), u1 = u0;
-      if (nok[nt]) {
-        const float4* zp = (const float4*)(a.z + ((size_t)nrow[nt] * a.H + h) * kDc + c0);
-        u0 = zp[0];
-        u1 = zp[1];
+      if (ok && 16 * nt < a.N) {
+        u0 = *(const float4*)(zp + 32 * kk);
+        u1 = *(const float4*)(zp + 32 * kk + 4);
       }
+      zr[nt][kk][0] = u0;
+      zr[nt][kk][1] = u1;
+    }
+  }
+  floatx4 acc[2] = {floatx4{}, floatx4{}};
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float4 u0 = zr[nt][kk][0], u1 = zr[nt][kk][1];
       const bf16x8 bz = {f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
                          f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
-      acc[nt] = mfma32(aw, bz, acc[nt]);
+      acc[nt] = mfma16(aw[kk], bz, acc[nt]);
     }
   }
   if (wave > 0) {
@@ -118,21 +127,17 @@ __global__ void __launch_bounds__(256) upproj_bf16_small_kernel(UpprojArgs a) {
     acc[0] += red[o][0][lane];
     acc[1] += red[o][1][lane];
   }
-  // C layout: column = query row, rows d = 32 dt + 8(r/4) + 4g + r%4
+  // C layout: column = query row 16nt + s, rows d = 16 dt + 4G + r
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    if (!nok[nt]) continue;
-    const size_t base = ((size_t)nrow[nt] * a.H + h) * kDv + 32 * dt;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 8 * q4 + 4 * g;
-      const floatx16& v = acc[nt];
-      if (a.o_bf16) {
-        bf16x4 ov = {f2bf(v[4 * q4]), f2bf(v[4 * q4 + 1]), f2bf(v[4 * q4 + 2]), f2bf(v[4 * q4 + 3])};
-        *(bf16x4*)((bf16*)a.o + base + d) = ov;
-      } else {
-        *(float4*)((float*)a.o + base + d) = make_float4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
-      }
+    const int n = 16 * nt + s;
+    if (n >= a.N) continue;
+    const size_t base = ((size_t)n * a.H + h) * kDv + 16 * dt + 4 * G;
+    const floatx4& v = acc[nt];
+    if (a.o_bf16) {
+      *(bf16x4*)((bf16*)a.o + base) = bf16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+    } else {
+      *(float4*)((float*)a.o + base) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -163,8 +168,8 @@ __global__ void __launch_bounds__(256) upproj_f32_kernel(UpprojArgs a) {
 hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s) {
   if (w_kind == kKindF32) {
     hipLaunchKernelGGL(upproj_f32_kernel, dim3(a.N * a.H), dim3(256), 0, s, a);
-  } else if (a.N <= 64) {
-    hipLaunchKernelGGL(upproj_bf16_small_kernel, dim3(a.H * 4), dim3(256), 0, s, a);
+  } else if (a.N <= kUpSmallMaxN) {
+    hipLaunchKernelGGL(upproj_bf16_small_kernel, dim3(a.H, kDv / 16), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(upproj_bf16_kernel, dim3(a.H, (a.N + 255) / 256), dim3(256), 0, s, a);
   }

@@ -147,13 +147,12 @@ def test_bf16_page_permutation_invariance():
     assert torch.equal(z1, z2)
 
 
-def test_bf16_in_kernel_merge_equals_merge_kernel_and_resets_counters():
-    """mla_decode merges split sequences inside the decode kernel; the result
-    must equal the two-kernel path bit for bit, and the workspace's arrival
-    counters must be back at zero so that the next call can reuse it."""
+def test_bf16_decode_equals_partial_plus_merge_and_reuses_workspace():
+    """mla_decode is mla_decode_partial followed by mla_decode_merge (bit for
+    bit), and a workspace can be reused by the next call."""
     lens = [4096, 1, 2500, 33, 700, 64, 65, 1900]
     wl = W.make_workload("decode_h16", B=len(lens), H=16, lens=lens)
-    _note(f"case in-kernel merge lens={lens}")
+    _note(f"case decode == partial + merge lens={lens}")
     dd = DI.decode_inputs(wl, DEV)
     q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
     B, H = wl.B, wl.H
@@ -169,7 +168,6 @@ def test_bf16_in_kernel_merge_equals_merge_kernel_and_resets_counters():
         torch.cuda.synchronize()
         assert torch.equal(z1, z2) and torch.equal(l1, l2), S
         assert torch.equal(z1, zt) and torch.equal(l1, lt), S
-        assert int(ws[: 4 * B].view(torch.int32).abs().sum()) == 0, S
 
 
 def test_bf16_many_short_sequences_share_units():
