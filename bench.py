@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_h16",
-                    choices=["decode_h16", "decode_h128", "long_bf16", "long_fp8", "tiny_f32"])
+                    choices=["decode_h16", "decode_h128", "long_bf16", "long_fp8", "tiny_f32", "prefill_h128"])
     ap.add_argument("--splits", type=int, default=-1, help="num_splits (-1: the workload's own, 0: automatic)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0: enough for 600 MB)")
     ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of as a HIP graph")
@@ -79,6 +79,82 @@ def cpu_baseline(wl, host, budget_s):
                       f"fp64 NumPy, {dt:.1f} s; rate scaled to all {wl.H} heads"}
 
 
+def run_prefill(args, wl, dev):
+    """Causal prefill of one sequence: absorb_q + prefill_causal (cache append and
+    causal attention) + upproj_v over all T rows; value = algorithmic TFLOP/s."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_30_amd as mla
+    from mla_latent_kv_30_amd import workload as W
+
+    T, H = int(wl.lens[0]), wl.H
+    w_uk, w_uv = W.weights(wl)
+    q_c, q_r = W.queries(wl)
+    c, k = W.sequence_latents(wl, 0)
+    td = lambda x: torch.from_numpy(x).to(dev, torch.bfloat16)
+    w_uk, w_uv, q_c, q_r, c, k = (td(x) for x in (w_uk, w_uv, q_c, q_r, c, k))
+    npg = (T + 63) // 64
+    cache = mla.PagedCache(npg, torch.bfloat16, dev)
+    perm = np.random.default_rng(args.seed).permutation(npg).astype(np.int32)
+    bt = torch.from_numpy(perm).to(dev)
+    pos = torch.arange(T, dtype=torch.int32, device=dev)
+    q_abs = torch.empty((T, H, 576), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((T, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    o = torch.empty((T, H, 128), dtype=torch.float32, device=dev)
+
+    def step():
+        mla.absorb_q(q_c, q_r, pos, w_uk, out=q_abs)
+        mla.prefill_causal(q_abs, c, k, cache, bt, z=z, lse=lse)
+        mla.upproj_v(z, w_uv, out=o)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(K):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / K
+    # the attention (cache append + causal decode kernel) alone
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        starts[i].record()
+        mla.prefill_causal(q_abs, c, k, cache, bt, z=z, lse=lse)
+        ends[i].record()
+    torch.cuda.synchronize()
+    kern_ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    kern_avg_ms = sum(kern_ms) / K
+    pairs = T * (T + 1) // 2
+    attn_flops = pairs * H * FLOP_PER_TOKEN_HEAD
+    proj_flops = 2 * T * H * 2 * 128 * 512
+    tflops_kernel = attn_flops / (kern_avg_ms * 1e-3) / 1e12
+    out = {
+        "metric": "MLA causal prefill TFLOP/s (absorbed attention + absorb + up-projection)",
+        "value": (attn_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "heads": H, "causal_pairs": pairs,
+                   "step": "absorb_q + prefill_causal (cache append + causal attention) + upproj_v"},
+        "roofline": {
+            "bound": "mfma", "achieved": tflops_kernel, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops_kernel / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "decode_mfma_kernel (prefill)",
+            "kernel_avg_us": kern_avg_ms * 1e3, "kernel_p10_us": kern_ms[K // 10] * 1e3,
+            "kernel_p90_us": kern_ms[(9 * K) // 10] * 1e3, "alg_flops_per_launch": attn_flops,
+        },
+        "cpu_baseline": None,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -99,6 +175,9 @@ def main():
     torch.cuda.set_device(dev)
 
     wl = W.make_workload(args.config, seed=args.seed)
+    if wl.kind == "prefill":
+        run_prefill(args, wl, dev)
+        return
     splits = wl.splits if args.splits < 0 else args.splits
     t_setup = time.perf_counter()
     dd = DI.decode_inputs(wl, dev, keep_host=not args.no_cpu_baseline)

@@ -148,7 +148,8 @@ size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits);
  *                (the query is the newest of them)
  *   num_splits   0: the library cuts the 32-token blocks of all sequences
  *                into one nearly equal range per compute unit (a range may
- *                span sequences); S > 0: sequence b is cut into S chunks of
+ *                span sequences; for B > 512 every sequence is one chunk);
+ *                S > 0: sequence b is cut into S chunks of
  *                ceil(ceil(L_b/64)/S) pages (trailing chunks may be empty).
  *   workspace    device scratch of at least mla_decode_workspace_size bytes
  *                (no initialisation needed); calls that share a workspace

@@ -66,6 +66,14 @@ __device__ __forceinline__ int4v lds_read_b128_at(uint32_t addr) {
   return *(const MLA_LDS int4v*)(uintptr_t)addr;
 }
 
+// This lane's index in its wave, computed afresh at every call: the asm is
+// volatile, so a loop recomputes it instead of keeping it live (or spilled).
+__device__ __forceinline__ int lane_id_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Value that is the same in every lane, moved to scalar registers.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 template <typename T>
@@ -93,6 +101,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, uint32_t voff,
                                          uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rs), "s"(soff)
+               : "memory");
+}
+
+// As lds_dma4 with 16 bytes per lane: lane i writes LDS bytes
+// [lds_base + 16 i, +16) from buffer offset soff + voff.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, uint32_t voff,
+                                          uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_base), "v"(voff), "s"(rs), "s"(soff)
                : "memory");

@@ -30,295 +30,9 @@
 //   * Long sequences are cut into chunks; each chunk leaves a normalised
 //     partial (z_c, lse_c) that the merge kernel combines exactly:
 //     lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c.
-#include "common.h"
-#include "kernels.h"
+#include "decode_common.h"
 
 namespace mla {
-
-constexpr int kRowBytes = kRow * 2;                 // 1152
-constexpr int kPageBytes = kPage * kRowBytes;       // 73728
-constexpr int kBlock = 32;                          // scheduling granule (tokens)
-
-// ---------------------------------------------------------------------------
-// Work schedule shared by the decode and merge kernels.
-// ---------------------------------------------------------------------------
-//
-// Three modes:
-//   prefill  unit w = query row T-1-w of one sequence (longest rows first);
-//   uniform  S chunks per sequence, chunk = ceil(ceil(L/64)/S) pages,
-//            unit w = (b = w/S, chunk w%S), partial slot w;
-//   balanced the 32-token blocks of all sequences, concatenated, are cut into
-//            G nearly equal ranges (G = min(units, blocks)); a unit walks the
-//            sequences its range touches.  Each sequence is preceded by
-//            kStartCost blocks that hold no tokens: they stand for the cost of
-//            starting a sequence (query load, first copies, final store), so a
-//            unit that switches sequences gets correspondingly fewer tokens.
-//            Unit w's piece of sequence b goes to partial slot w + b (unique:
-//            the pieces of unit w have increasing b, and unit w+1 starts at or
-//            after unit w's last b).
-constexpr int kStartCost = 2;
-
-// Exclusive prefix sums of kStartCost + the 32-token block count of every
-// sequence into pfx[0..B], and the lengths into lens[0..B); returns the
-// total.  Called by all threads; B <= kMaxSchedB.
-__device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx, int* lens) {
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthreads = blockDim.x;
-  const int per = (B + nthreads - 1) / nthreads;  // <= 4
-  const int base = tid * per;
-  int loc[4];
-  int sum = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = min(base + k, B - 1);
-    const int L = seq_lens[i];  // loaded unconditionally so the loads overlap
-    const int v = (k < per && base + k < B) ? kStartCost + (L + kBlock - 1) / kBlock : 0;
-    if (k < per && base + k < B) lens[base + k] = L;
-    loc[k] = v;
-    sum += v;
-  }
-  int x = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int excl = x - sum;
-  for (int w = 0; w < wave; ++w) excl += wsum[w];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (k < per && base + k < B) pfx[base + k] = excl;
-    excl += loc[k];
-  }
-  if (tid == nthreads - 1) pfx[B] = excl;
-  __syncthreads();
-  return uniform(pfx[B]);
-}
-
-// Unit of the balanced split that owns block g (G units over P blocks).
-__device__ __forceinline__ int unit_of_block(long long g, long long G, long long P) {
-  return (int)(((g + 1) * G - 1) / P);
-}
-
-// One piece of work: tokens [t0, t1) of sequence b, whose length is L.
-struct Segment {
-  int b, t0, t1, L;
-  int slot;   // partial slot of this piece
-  int slot0;  // partial slot of the sequence's first piece
-  int parts;  // pieces the sequence was cut into (1: this one is whole)
-};
-
-struct Schedule {
-  int mode;          // 0 prefill, 1 uniform, 2 balanced
-  int w;             // this unit
-  long long G, P;    // balanced: units in use, total blocks
-  long long g0, g1;  // balanced: this unit's block range
-  int b;             // balanced: next sequence to look at
-  int done;
-  const int* pfx;    // balanced: block prefix and lengths in LDS
-  const int* lens;
-};
-
-__device__ __forceinline__ Schedule schedule_begin(const DecodeArgs& a, const int* pfx, const int* lens, int P) {
-  Schedule s{};
-  s.w = blockIdx.x;
-  s.pfx = pfx;
-  s.lens = lens;
-  if (a.prefill_T > 0) {
-    s.mode = 0;
-  } else if (a.splits > 0) {
-    s.mode = 1;
-  } else {
-    s.mode = 2;
-    s.P = P;
-    s.G = min((long long)a.units, (long long)P);
-    s.done = s.w >= s.G;
-    if (!s.done) {
-      s.g0 = (long long)s.w * s.P / s.G;
-      s.g1 = (long long)(s.w + 1) * s.P / s.G;
-      int lo = 0, hi = a.B;  // last b with pfx[b] <= g0
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pfx[mid] <= s.g0) lo = mid; else hi = mid;
-      }
-      s.b = uniform(lo);
-    }
-  }
-  return s;
-}
-
-// Next piece of this unit's work; every thread of the workgroup gets the
-// same answer.
-__device__ __forceinline__ bool schedule_next(const DecodeArgs& a, Schedule& s, Segment& seg) {
-  if (s.done) return false;
-  if (s.mode == 0) {
-    s.done = 1;
-    const int t = a.prefill_T - 1 - s.w;
-    const int L = a.prefill_pos0 + t + 1;
-    seg = Segment{t, 0, L, L, 0, 0, 1};
-    return true;
-  }
-  if (s.mode == 1) {
-    s.done = 1;
-    const int S = a.splits;
-    const int b = s.w / S, k = s.w % S;
-    const int L = a.seq_lens[b];
-    const int np = (L + kPage - 1) / kPage;
-    const int chunk = (np + S - 1) / S;
-    const int pb = k * chunk, pe = min(pb + chunk, np);
-    if (pb >= pe) return false;
-    seg = Segment{b, pb * kPage, min(pe * kPage, L), L, s.w, b * S, (np + chunk - 1) / chunk};
-    return true;
-  }
-  while (s.b < a.B) {
-    const int b = s.b;
-    const int r0 = uniform(s.pfx[b]) + kStartCost, r1 = uniform(s.pfx[b + 1]);  // token blocks of b
-    if (r0 >= s.g1) break;
-    s.b = b + 1;
-    const int k0 = (int)(max(s.g0, (long long)r0) - r0);
-    const int k1 = (int)(min(s.g1, (long long)r1) - r0);
-    if (k0 < k1) {
-      const int L = uniform(s.lens[b]);
-      const int first = unit_of_block(r0, s.G, s.P);
-      const int last = unit_of_block(r1 - 1, s.G, s.P);
-      seg = Segment{b, k0 * kBlock, min(k1 * kBlock, L), L, s.w + b, first + b, last - first + 1};
-      return true;
-    }
-  }
-  s.done = 1;
-  return false;
-}
-
-// ---------------------------------------------------------------------------
-// LDS page layout
-// ---------------------------------------------------------------------------
-//
-// Pages are streamed in blocks of 32 rows (half a page).  A block buffer in
-// LDS holds 32 rows of 1152 bytes, unpadded: row r at r * 1152.  The 16-byte
-// chunks of a row are permuted inside each aligned group of eight: chunk c
-// of row r sits at chunk position c ^ swz(r).  gfx950 serves a 16-byte LDS
-// read per half-wave (even lanes, then odd lanes) over 128 banks of 4 bytes,
-// and the transposing 8-byte read per quarter-wave; without the permutation
-// the rows of an operand tile (1152 = 9 * 128) would pile onto a quarter of
-// the banks.  With it, the score operand reads, the transposing value reads
-// and the dequantising writes below are all conflict-free.  Rows 2k and 2k+1
-// share swz, so a row pair (2304 contiguous bytes in HBM) is still moved by
-// nine 256-byte LDS-DMA instructions: lane i fetches the 4 bytes that belong
-// at pair offset (256 k + 4 i), i.e. HBM pair offset 256 k + ((4 i) ^ (swz << 4)).
-constexpr int kBlockRows = kBlock;                     // 32
-constexpr int kBlockBytes = kBlockRows * kRowBytes;    // 36864
-constexpr int kNBuf = 4;                               // block buffers: 3 in flight + 1 in use
-constexpr int kDmaBytes = 256;                         // 64 lanes x 4 bytes
-constexpr int kPairBytes = 2 * kRowBytes;              // 2304
-constexpr int kDmaPerPair = kPairBytes / kDmaBytes;    // 9
-constexpr int kWaves = 8;                              // every decode workgroup has 8 waves
-constexpr int kRowsPerWave = kBlockRows / kWaves;      // 4
-constexpr int kDmaPerWave = kRowsPerWave / 2 * kDmaPerPair;  // 18 per block
-constexpr int kRsrcWord3 = 0x00020000;                 // raw untyped buffer access
-
-__device__ __forceinline__ int swz(int r) { return 2 * ((r >> 2) & 3) + ((r >> 4) & 1); }
-// LDS byte offset of byte x (x < 1152) of row r.
-__device__ __forceinline__ int lds_off(int r, int x) { return r * kRowBytes + (x ^ (swz(r) << 4)); }
-
-// Copy the first `hi` rows of a 32-row block (rows 32*half .. of a bf16
-// page) into an LDS block buffer; wave w moves rows 4w .. 4w+3.  The buffer
-// resource covers exactly those rows, so rows at or past hi (past the
-// sequence end, or owned by the next unit) arrive as zeros and stale or
-// non-finite pool contents never reach the matrix cores.
-__device__ __forceinline__ void issue_block_bf16(const uint8_t* page, int half, uint8_t* buf, int hi, int wave,
-                                                 int lane) {
-  asm volatile("" : "+s"(wave));  // re-derived per copy, not kept live across the loop
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(page + half * kBlockBytes), (short)0, uniform(hi * kRowBytes), kRsrcWord3);
-  const uint32_t lb = lds_addr(buf);
-  const uint32_t vo = (uint32_t)((lane * 4) ^ (swz(wave * kRowsPerWave) << 4));  // both pairs share swz
-#pragma unroll
-  for (int j = 0; j < kRowsPerWave / 2; ++j) {
-    const int pair = wave * (kRowsPerWave / 2) + j;
-#pragma unroll
-    for (int k = 0; k < kDmaPerPair; ++k) {
-      const int off = pair * kPairBytes + k * kDmaBytes;
-      lds_dma4(rs, lb + off, vo, off);
-    }
-  }
-}
-
-// fp8 staging buffer of one block: codes [32][512], scales [32][4] fp32,
-// rotated k^R [32][64] bf16.
-constexpr int kStCkv = 0;
-constexpr int kStScale = kBlockRows * kDc;                  // 16384
-constexpr int kStKr = kStScale + kBlockRows * 4 * 4;        // 16896
-constexpr int kStageBytes = kStKr + kBlockRows * kDr * 2;   // 20992
-constexpr int kFp8DmaPerWave = 8 + 1 + 2;                   // codes, scales (16 lanes), k^R
-
-__device__ __forceinline__ void issue_block_fp8(const uint8_t* ckv8, const float* scale8, const uint8_t* kr8,
-                                                int page, int half, uint8_t* stage, int hi, int wave, int lane) {
-  asm volatile("" : "+s"(wave));
-  const size_t row0 = (size_t)page * kPage + half * kBlockRows;
-  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(ckv8 + row0 * kDc), (short)0, uniform(hi * kDc), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(scale8 + row0 * 4), (short)0, uniform(hi * 16), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(kr8 + row0 * (kDr * 2)), (short)0, uniform(hi * kDr * 2), kRsrcWord3);
-  const uint32_t lb = lds_addr(stage);
-  const uint32_t vo = lane * 4;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {  // codes: rows 4w .. 4w+3 are 2048 contiguous bytes
-    const int off = wave * (kRowsPerWave * kDc) + k * kDmaBytes;
-    lds_dma4(rc, lb + kStCkv + off, vo, off);
-  }
-  if (lane < 16) {  // scales: 4 rows x 16 bytes
-    const int off = wave * (kRowsPerWave * 16);
-    lds_dma4(rsc, lb + kStScale + off, vo, off);
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {  // k^R: 4 rows x 128 bytes
-    const int off = wave * (kRowsPerWave * kDr * 2) + k * kDmaBytes;
-    lds_dma4(rk, lb + kStKr + off, vo, off);
-  }
-}
-
-// Expand a staged fp8 block into the bf16 row layout.  Thread t: row t/16,
-// channels 32(t%16) .. +31 (a quarter of a 128-channel tile, one scale);
-// threads t < 256 also copy one 16-byte chunk of a row's k^R.  Rows past
-// the valid range are zeros in the staging buffer (codes and scales), so
-// they expand to zeros.
-__device__ __forceinline__ void dequant_block(const uint8_t* stage, uint8_t* buf) {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));  // offsets recomputed per block, not held across the loop
-  const int r = t >> 4, sub = t & 15;
-  const float sc = *(const float*)(stage + kStScale + (r * 4 + (sub >> 2)) * 4);
-  const uint8_t* src = stage + kStCkv + r * kDc + sub * 32;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int4v raw = lds_read_b128(src + 16 * j);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 v;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int word = raw[2 * h + e];
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-        v[4 * e + 0] = f2bf(lo[0] * sc);
-        v[4 * e + 1] = f2bf(lo[1] * sc);
-        v[4 * e + 2] = f2bf(hi[0] * sc);
-        v[4 * e + 3] = f2bf(hi[1] * sc);
-      }
-      const int chunk = sub * 4 + 2 * j + h;  // 8 channels = one 16-byte chunk
-      *(MLA_LDS bf16x8*)(buf + lds_off(r, chunk * 16)) = v;
-    }
-  }
-  if (t < kBlockRows * 8) {
-    const int kr_row = t >> 3, kc = t & 7;
-    const int4v kr = lds_read_b128(stage + kStKr + kr_row * (kDr * 2) + kc * 16);
-    *(MLA_LDS int4v*)(buf + lds_off(kr_row, kDc * 2 + kc * 16)) = kr;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Matrix-core compute on one block buffer
@@ -333,29 +47,6 @@ struct WaveState {
   floatx4 zacc[NT];  // Z^T tile j: channels c0 + 16j + 4g + r, column = head
   float m, l;        // running max (log2 units) and this lane's partial sum
 };
-
-constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is refreshed
-
-__device__ __forceinline__ void load_query(bf16x8 (&q)[18], const bf16* __restrict__ src_rows, int H, int head,
-                                           int g) {
-  const int hc = head < H ? head : H - 1;
-  const int keep = head < H ? -1 : 0;
-  const int4v* src = (const int4v*)(src_rows + (size_t)hc * kRow);
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    int4v v = src[4 * kk + g];
-    v &= keep;
-    q[kk] = __builtin_bit_cast(bf16x8, v);
-  }
-}
-
-// Use the query registers, so the compiler's own wait for their loads is
-// placed here and not at the first score product, where later page copies
-// (which its counter does not see) would be waited for as well.
-__device__ __forceinline__ void consume_query(bf16x8 (&q)[18]) {
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(q[kk]));
-}
 
 template <int NT>
 __device__ __forceinline__ void reset_state(WaveState<NT>& st) {
@@ -399,6 +90,7 @@ __device__ __forceinline__ void softmax_update(WaveState<NT>& st, float (&x)[NV]
 // never wait on each other.  Row index m of a subtile's product maps to
 // token 16u + 4(m%4) + m/4, so score register r of lane group g in subtile u
 // is token 16u + 4r + g.
+template <int D>  // operand reads in flight per chain
 __device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int lane, floatx4& S0, floatx4& S1) {
   const int g = lane >> 4, m = lane & 15;
   const int r = 4 * (m & 3) + (m >> 2);
@@ -415,7 +107,6 @@ __device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int
   auto rd = [&](int u, int kk) { return lds_read_b128_at(ap[u][kk & 1] + 128 * (kk >> 1)); };
   S0 = floatx4{};
   S1 = floatx4{};
-  constexpr int D = 2;  // operand reads in flight per chain
   int4v a0[D], a1[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -445,11 +136,12 @@ __device__ __forceinline__ void block_compute(WaveState<NT>& st, uint32_t buf, i
                                               float scale_log2) {
   // Recompute the lane's operand offsets in every call rather than let the
   // compiler keep one set per buffer live across the block loop.
-  asm volatile("" : "+v"(lane));
+  lane = lane_id_fresh();
   const int g = lane >> 4;
   float x[8], p[8];
   floatx4 S[2];
-  score32(st.q, buf, lane, S[0], S[1]);
+  // deeper operand prefetch where the accumulator leaves registers for it
+  score32<NT <= 16 ? 4 : 2>(st.q, buf, lane, S[0], S[1]);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -516,23 +208,6 @@ __device__ __forceinline__ void store_state(const WaveState<NT>& st, float l_tot
 // bf16 / fp8-cache matrix-core decode
 // ---------------------------------------------------------------------------
 
-// Position in a unit's stream of 32-token blocks: block k of a piece.
-struct Cursor {
-  Schedule sch;
-  Segment seg;
-  int k;
-  int valid;
-};
-
-__device__ __forceinline__ void cursor_next(const DecodeArgs& a, Cursor& c) {
-  if (c.k < (c.seg.t1 - 1) / kBlock) {
-    ++c.k;
-    return;
-  }
-  c.valid = schedule_next(a, c.sch, c.seg);
-  c.k = c.valid ? c.seg.t0 / kBlock : 0;
-}
-
 // 8 waves: all of them copy blocks; the first HG*CG compute.  HG head groups
 // of 16 heads times CG groups of 512/CG latent channels: every computing wave
 // scores all tokens of a block for its heads (the CG waves of a head group
@@ -553,7 +228,8 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   constexpr int NT = 32 / CG;  // channel tiles per wave
   static_assert(NT % 4 == 0, "channel groups start on a multiple of 4 tiles");
   constexpr int kSmem = FP8 ? kNBuf * kStageBytes + kBlockBytes : kNBuf * kBlockBytes;
-  constexpr int kDmaBlock = FP8 ? kFp8DmaPerWave : kDmaPerWave;
+  constexpr int kCopyLo = FP8 ? kFp8Copies : kCopiesLo;  // copies per block of waves 0..3
+  constexpr int kCopyHi = FP8 ? kFp8Copies : kCopiesHi;  // and of waves 4..7
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   __shared__ int pfx[kMaxSchedB + 1];
   __shared__ int lens[kMaxSchedB];
@@ -592,11 +268,20 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     if (a.meta != nullptr && s.slot == s.slot0 && tid == 0) *(int2*)(a.meta + 2 * s.b) = make_int2(s.slot0, s.parts);
   };
 
-  // The query loads and the first copies travel together; consuming the
-  // query right after waits for both (the compiler's counter only knows the
-  // query loads).
+  // First query: for up to two head groups it is copied into LDS like the
+  // blocks (into the one buffer the first three blocks leave free), so that
+  // waiting for it does not also wait for the blocks issued after it; with
+  // more head groups it is loaded into registers directly.  Either way the
+  // first three blocks are in flight meanwhile.
   WaveState<NT> st;
-  load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4);
+  constexpr bool kQueryViaLds = HG <= 2;
+  uint8_t* const qlds = FP8 ? smem + kNBuf * kStageBytes : smem + (kNBuf - 1) * kBlockBytes;
+  static_assert(HG > 2 || 2 * 16 * kRowBytes <= kBlockBytes, "query staging space");
+  if constexpr (kQueryViaLds) {
+    issue_query_copy<HG>((const uint8_t*)qrow(cp.seg), a.H, qlds, wave, lane);
+  } else {
+    load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4);
+  }
   Cursor ld = cp;
   int issued = 0;
 #pragma unroll
@@ -607,19 +292,25 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
       cursor_next(a, ld);
     }
   }
-  consume_query(st.q);
+  if constexpr (kQueryViaLds) {
+    wait_blocks<kCopyLo, kCopyHi>(issued, wave);  // the query copies, issued before the blocks, are done
+    __syncthreads();
+    // lane: head h0 + l%16, channels 32kk + 8g .. +7 of its row
+    const uint32_t qa = lds_addr(qlds) + (16 * hg + (lane & 15)) * kRowBytes + 16 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) st.q[kk] = __builtin_bit_cast(bf16x8, lds_read_b128_at(qa + 64 * kk));
+  } else {
+    consume_query(st.q);
+  }
   reset_state(st);
   note_pieces(cp.seg);
   for (int i = 0;; ++i) {
     // wait for this wave's part of block i: the copies issued after it may stay in flight
-    const int after = issued - i - 1;
-    if (after >= 2) wait_vmcnt<2 * kDmaBlock>();
-    else if (after == 1) wait_vmcnt<kDmaBlock>();
-    else wait_vmcnt<0>();
+    wait_blocks<kCopyLo, kCopyHi>(issued - i - 1, wave);
     __syncthreads();
     uint8_t* buf;
     if constexpr (FP8) {
-      dequant_block(smem + (i % kNBuf) * kStageBytes, smem + kNBuf * kStageBytes);
+      dequant_block<kWaves * 64>(smem + (i % kNBuf) * kStageBytes, smem + kNBuf * kStageBytes, wave);
       __syncthreads();
       buf = smem + kNBuf * kStageBytes;
     } else {

@@ -8,7 +8,7 @@
 
 namespace mla {
 
-constexpr int kMaxSchedB = 1024;  // sequences a balanced (auto) split can schedule
+constexpr int kMaxSchedB = 512;  // sequences a balanced (auto) split can schedule
 constexpr int kKindF32 = 0;
 constexpr int kKindBf16 = 1;
 constexpr int kKindFp8 = 2;
