@@ -122,16 +122,15 @@ def run_prefill(args, wl, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / K
-    # the attention (cache append + causal decode kernel) alone
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    for i in range(K):
-        starts[i].record()
-        mla.prefill_causal(q_abs, c, k, cache, bt, z=z, lse=lse)
-        ends[i].record()
+    # the attention (cache append + causal decode kernel) alone: K launches between two events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    kern_ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
-    kern_avg_ms = sum(kern_ms) / K
+    e0.record()
+    for _ in range(K):
+        mla.prefill_causal(q_abs, c, k, cache, bt, z=z, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    kern_avg_ms = e0.elapsed_time(e1) / K
     pairs = T * (T + 1) // 2
     attn_flops = pairs * H * FLOP_PER_TOKEN_HEAD
     proj_flops = 2 * T * H * 2 * 128 * 512
@@ -146,8 +145,7 @@ def run_prefill(args, wl, dev):
         "roofline": {
             "bound": "mfma", "achieved": tflops_kernel, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops_kernel / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "decode_mfma_kernel (prefill)",
-            "kernel_avg_us": kern_avg_ms * 1e3, "kernel_p10_us": kern_ms[K // 10] * 1e3,
-            "kernel_p90_us": kern_ms[(9 * K) // 10] * 1e3, "alg_flops_per_launch": attn_flops,
+            "kernel_avg_us": kern_avg_ms * 1e3, "alg_flops_per_launch": attn_flops,
         },
         "cpu_baseline": None,
         "wall_s_timed": wall,
@@ -250,25 +248,27 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / K
 
-    # ---- the decode kernel alone (mla_decode_partial), timed with events on
-    # the stream it runs on; a GPU sleep first lets the host enqueue every
-    # launch ahead of the device, so no host latency lands between an event
-    # and its kernel
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    try:
-        torch.cuda._sleep(int(2.4e9 * (0.002 + 60e-6 * K)))
-    except Exception:  # no device sleep available: host latency may inflate the kernel time
-        pass
-    for k in range(K):
-        cache, *_ = reps[k % R]
-        starts[k].record()
-        mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
-        ends[k].record()
-    torch.cuda.synchronize()
-    kern_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    kern_avg_ms = sum(kern_ms) / K
+    # ---- the decode kernel alone (mla_decode_partial): K back-to-back launches
+    # between two events on the stream it runs on, three times; a GPU sleep
+    # first lets the host enqueue every launch ahead of the device, so no host
+    # latency lands inside the timed batch
+    kern_ms = []
+    for _rep in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * K)))
+        except Exception:  # no device sleep available: host latency may inflate the kernel time
+            pass
+        e0.record()
+        for k in range(K):
+            cache, *_ = reps[k % R]
+            mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms.append(e0.elapsed_time(e1) / K)
+    kern_ms.sort()
+    kern_avg_ms = kern_ms[1]  # median of the three batches
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -289,6 +289,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, dd.host, args.cpu_seconds)
+
+    # HBM bytes per launch from the stored counter runs, if they were taken on
+    # the current kernel sources
+    from mla_latent_kv_30_amd import traffic as TR
+    kname = "decode_mfma_kernel" if wl.dtype != "f32" else "decode_f32_kernel"
+    tr = TR.load(kname, wl.name, os.path.join(ROOT, "profiles"))
 
     out = {
         "metric": METRIC,
@@ -311,9 +317,11 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-            "traffic": None, "kernel": "decode_mfma_kernel" if wl.dtype != "f32" else "decode_f32_kernel",
-            "kernel_avg_us": kern_avg_ms * 1e3, "kernel_p10_us": kern_ms[K // 10] * 1e3,
-            "kernel_p90_us": kern_ms[(9 * K) // 10] * 1e3, "alg_bytes_per_launch": alg_bytes,
+            "traffic": None if tr is None else tr["traffic_bytes"], "kernel": kname,
+            "traffic_fetch_bytes": None if tr is None else tr["fetch_bytes"],
+            "traffic_write_bytes": None if tr is None else tr["write_bytes"],
+            "kernel_avg_us": kern_avg_ms * 1e3, "kernel_batches_us": [x * 1e3 for x in kern_ms],
+            "alg_bytes_per_launch": alg_bytes,
             "alg_flops_per_launch": alg_flops, "tflops": tflops, "mfma_peak_tflops": mfma_peak,
             "mfma_frac": tflops / mfma_peak,
         },

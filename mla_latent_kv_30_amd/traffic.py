@@ -1,0 +1,118 @@
+"""HBM traffic of a kernel from rocprofv3 counter runs, for the roofline report.
+
+Two counter passes of the same command (one with FETCH_SIZE, one with
+WRITE_SIZE; each needs its own pass on the hardware) give kilobytes per
+dispatch as the memory controller saw them.  Both are scaled by what the same
+counter reads for a plain device copy of known size run in the same command
+(bench.py --calibrate-copy copies 256 MiB), so the figure is in true bytes.
+
+    python -m mla_latent_kv_30_amd.traffic summarize --fetch DIR --write DIR \\
+        --kernel decode_mfma_kernel --workload decode_h16 --out profiles/X.json
+
+The summary records a digest of the kernel sources; bench.py reports the
+traffic only while the sources still have that digest.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 256 << 20        # bench.py --calibrate-copy
+COPY_KERNEL = "copyBuffer"    # the runtime's device-to-device copy kernel
+
+
+def source_digest() -> str:
+    """Digest of every kernel source the library is built from."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        if path.endswith((".hip", ".h")):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_csv(run_dir: str) -> str:
+    found = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not found:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    return found[0]
+
+
+def per_dispatch(run_dir: str, counter: str, kernel_substr: str) -> list:
+    """Values of `counter` for every dispatch whose kernel name contains kernel_substr."""
+    vals = {}
+    with open(_counter_csv(run_dir)) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+                vals[int(row["Dispatch_Id"])] = vals.get(int(row["Dispatch_Id"]), 0.0) + float(row["Counter_Value"])
+    return [vals[k] for k in sorted(vals)]
+
+
+def summarize(fetch_dir: str, write_dir: str, kernel: str, workload: str) -> dict:
+    fk = per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
+    wk = per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    fc = per_dispatch(fetch_dir, "FETCH_SIZE", COPY_KERNEL)
+    wc = per_dispatch(write_dir, "WRITE_SIZE", COPY_KERNEL)
+    if not fk or not wk:
+        raise RuntimeError(f"no dispatches of {kernel} in the counter runs")
+    if not fc or not wc:
+        raise RuntimeError("no calibration copy in the counter runs (bench.py --calibrate-copy)")
+    # the largest copy dispatch is the calibration copy
+    f_scale = COPY_BYTES / (max(fc) * 1024.0)
+    w_scale = COPY_BYTES / (max(wc) * 1024.0)
+    fetch_kib = statistics.median(fk)
+    write_kib = statistics.median(wk)
+    fetch_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    return {
+        "workload": workload, "kernel": kernel, "source_digest": source_digest(),
+        "dispatches": {"fetch": len(fk), "write": len(wk)},
+        "fetch_kib_median": fetch_kib, "write_kib_median": write_kib,
+        "copy_fetch_kib": max(fc), "copy_write_kib": max(wc),
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "fetch_bytes": fetch_b, "write_bytes": write_b, "traffic_bytes": fetch_b + write_b,
+    }
+
+
+def load(kernel: str, workload: str, profiles_dir: str):
+    """The stored traffic summary for (kernel, workload) if it matches the current sources, else None."""
+    path = os.path.join(profiles_dir, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    return d if d.get("source_digest") == source_digest() else None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("summarize")
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--kernel", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--command", default="", help="the profiled command, recorded in the summary")
+    s.add_argument("--out", required=True)
+    d = sub.add_parser("digest")
+    args = ap.parse_args()
+    if args.cmd == "digest":
+        print(source_digest())
+        return
+    out = summarize(args.fetch, args.write, args.kernel, args.workload)
+    out["command"] = args.command
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
