@@ -2,9 +2,10 @@
 """Throughput of absorbed-MLA decode on one MI355X, against its roofline.
 
 One step = the whole decode path for one batch: absorbed query
-(mla_absorb_q), attention over the paged latent cache and the split merge
-(mla_decode: decode kernel + merge kernel), and the W_UV up-projection
-(mla_upproj_v).  Inputs are synthetic with the workload's
+(mla_absorb_q), attention over the paged latent cache (mla_decode_partial),
+and the split merge with the W_UV up-projection (mla_decode_merge_upproj:
+one launch for up to 32 sequences, else the merge and up-projection
+kernels).  Inputs are synthetic with the workload's
 shapes and distributions and are resident in HBM before timing starts.  To
 keep the 256 MB last-level cache from serving repeated reads, the step
 rotates over enough replicas of its inputs (cache, weights, queries) to
@@ -205,8 +206,8 @@ def main():
     def step(r):
         cache, q_c, q_r, w_uk, w_uv = reps[r]
         mla.absorb_q(q_c, q_r, dd.pos, w_uk, out=q_abs)
-        mla.decode(q_abs, cache, dd.block_table, dd.seq_lens, num_splits=splits, workspace=ws, z=z, lse=lse)
-        mla.upproj_v(z, w_uv, out=o)
+        mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
+        mla.decode_merge_upproj(dd.seq_lens, H, ws, z, w_uv, lse=lse, num_splits=splits, out=o)
 
     for k in range(max(1, args.warmup)):
         step(k % R)
@@ -313,7 +314,7 @@ def main():
             "workload": wl.name, "batch": B, "heads": H, "cached_tokens": total,
             "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
             "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
-            "step": "absorb_q + decode (decode kernel + split merge) + upproj_v",
+            "step": "absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)",
         },
         "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,

@@ -197,6 +197,20 @@ mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32
                             size_t ws_bytes, float* z, float* lse, void* stream);
 
 /*
+ * mla_decode_merge_upproj: mla_decode_merge followed by mla_upproj_v on its z
+ * (o_i = W_i^UV z_i, §潜在向量的作用), with N = B.  Arguments as for those
+ * two calls; z and lse are written as mla_decode_merge writes them.  With a
+ * bf16 weight and B <= 32 both run in one launch, whose product keeps z in
+ * fp32 (bf16 weight values, fp32 accumulation); otherwise it is the two
+ * calls.  Errors: those of mla_decode_merge, plus MLA_ERR_INVALID_ARG for a
+ * NULL w_uv or o, or a dtype outside {MLA_F32, MLA_BF16}.
+ */
+mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits,
+                                   void* workspace, size_t ws_bytes, float* z, float* lse, const void* w_uv,
+                                   int32_t w_dtype, void* o, int32_t o_dtype, void* stream);
+
+/*
+ * mla_prefill_causal/*
  * mla_prefill_causal — T new tokens of one sequence, at positions
  * pos0 .. pos0+T-1, are written into the cache and attend causally: query t
  * sees cached tokens 0 .. pos0+t inclusive (§注意力计算 sums up to the

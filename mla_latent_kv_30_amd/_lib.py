@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_partial.argtypes = list(L.mla_decode.argtypes)
     L.mla_decode_merge.restype = _i32
     L.mla_decode_merge.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_decode_merge_upproj.restype = _i32
+    L.mla_decode_merge_upproj.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp,
+                                          _i32, _vp]
     L.mla_prefill_causal.restype = _i32
     L.mla_prefill_causal.argtypes = [_vp, _vp, _vp, _i32, ctypes.POINTER(MlaCache), _vp, _i32, _i32, _f32, _f32,
                                      _vp, _vp, _vp]
@@ -262,6 +265,24 @@ def decode_merge(seq_lens: torch.Tensor, H: int, workspace: Optional[torch.Tenso
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_merge(_ptr(seq_lens), B, int(H), int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
                                   _ptr(lse), _stream(z.device)), "mla_decode_merge")
+
+
+def decode_merge_upproj(seq_lens: torch.Tensor, H: int, workspace: Optional[torch.Tensor], z: torch.Tensor,
+                        w_uv: torch.Tensor, lse: Optional[torch.Tensor] = None, num_splits: int = 0,
+                        out_dtype=torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The merge pass followed by the value up-projection (mla_decode_merge_upproj); returns o[B,H,128]."""
+    B = seq_lens.shape[0]
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(z, "z", torch.float32, (B, H, D_C))
+    _need(w_uv, "w_uv", None, (H, D_V, D_C))
+    if out is None:
+        out = torch.empty((B, H, D_V), dtype=out_dtype, device=z.device)
+    _need(out, "out", out_dtype, (B, H, D_V))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_merge_upproj(_ptr(seq_lens), B, int(H), int(num_splits), _ptr(workspace), ws_bytes,
+                                         _ptr(z), _ptr(lse), _ptr(w_uv), _dt_code(w_uv.dtype), _ptr(out),
+                                         _dt_code(out_dtype), _stream(z.device)), "mla_decode_merge_upproj")
+    return out
 
 
 def prefill_causal(q_abs: torch.Tensor, c_kv: torch.Tensor, k_r: torch.Tensor, cache: PagedCache,

@@ -224,6 +224,36 @@ mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32
   return launched(launch_merge(a, (hipStream_t)stream));
 }
 
+mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits, void* workspace,
+                                   size_t ws_bytes, float* z, float* lse, const void* w_uv, int32_t w_dtype, void* o,
+                                   int32_t o_dtype, void* stream) {
+  if (!seq_lens || !z || !w_uv || !o || B < 1 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
+  if (!dtype_ok(w_dtype) || !dtype_ok(o_dtype)) return MLA_ERR_INVALID_ARG;
+  if ((long long)B * H > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
+  const Plan p = make_plan(B, num_splits);
+  const size_t need = workspace_bytes(B, H, p);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (w_dtype == MLA_BF16 && B <= kFusedMaxB) {
+    MergeUpArgs m;
+    memset(&m, 0, sizeof(m));
+    m.d.B = B;
+    m.d.H = H;
+    m.d.z = z;
+    m.d.lse = lse;
+    set_workspace(m.d, workspace, B, H, p);
+    m.w_uv = w_uv;
+    m.o = o;
+    m.o_bf16 = o_dtype == MLA_BF16 ? 1 : 0;
+    return launched(launch_merge_upproj(m, s));
+  }
+  mla_status st = mla_decode_merge(seq_lens, B, H, num_splits, workspace, ws_bytes, z, lse, stream);
+  if (st != MLA_OK) return st;
+  return mla_upproj_v(z, w_uv, o, B, H, w_dtype, o_dtype, stream);
+}
+
 mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
                       int32_t B, int32_t H, int32_t max_pages, float softmax_scale, int32_t num_splits, void* workspace,
                       size_t ws_bytes, float* z, float* lse, void* stream) {

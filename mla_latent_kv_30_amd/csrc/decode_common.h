@@ -29,15 +29,27 @@ constexpr int kBlock = 32;                          // scheduling granule (token
 //            Unit w's piece of sequence b goes to partial slot w + b (unique:
 //            the pieces of unit w have increasing b, and unit w+1 starts at or
 //            after unit w's last b).
-constexpr int kStartCost = 2;
+constexpr int kStartCost = 4;
 
 // Exclusive prefix sums of kStartCost + the 32-token block count of every
 // sequence into pfx[0..B], and the lengths into lens[0..B); returns the
-// total.  Called by all threads; B <= kMaxSchedB.
-static __device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx, int* lens) {
+// total.  Called by all threads; B <= kMaxSchedB.  If bt is given, its
+// nbt <= 4 * blockDim.x entries (the whole block table) are copied into
+// bt_lds as well: the loads go out together with the length loads, so the
+// page lookups of the copy issue need no further round trip to memory.
+static __device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx, int* lens,
+                                   const int32_t* __restrict__ bt = nullptr, int nbt = 0, int* bt_lds = nullptr) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthreads = blockDim.x;
+  int btv[4];
+  if (bt != nullptr) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + k * nthreads;
+      btv[k] = i < nbt ? bt[i] : 0;
+    }
+  }
   const int per = (B + nthreads - 1) / nthreads;  // <= 4
   const int base = tid * per;
   int loc[4];
@@ -58,6 +70,13 @@ static __device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, 
     if (lane >= d) x += y;
   }
   if (lane == 63) wsum[wave] = x;
+  if (bt != nullptr) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + k * nthreads;
+      if (i < nbt) bt_lds[i] = btv[k];
+    }
+  }
   __syncthreads();
   int excl = x - sum;
   for (int w = 0; w < wave; ++w) excl += wsum[w];

@@ -9,6 +9,7 @@
 namespace mla {
 
 constexpr int kMaxSchedB = 512;  // sequences a balanced (auto) split can schedule
+constexpr int kBtLds = 2048;     // block-table entries a decode workgroup keeps in LDS
 constexpr int kKindF32 = 0;
 constexpr int kKindBf16 = 1;
 constexpr int kKindFp8 = 2;
@@ -38,6 +39,16 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+
+// merge + value up-projection in one launch (bf16 W^UV, B <= kFusedMaxB)
+constexpr int kFusedMaxB = 32;
+struct MergeUpArgs {
+  DecodeArgs d;      // B, H, z, lse and the workspace parts (meta == NULL: no partials)
+  const void* w_uv;  // [H][128][512] bf16
+  void* o;           // [B][H][128]
+  int32_t o_bf16;
+};
+hipError_t launch_merge_upproj(const MergeUpArgs& m, hipStream_t s);
 
 struct AbsorbArgs {
   const void* q_c;

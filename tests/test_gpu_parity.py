@@ -271,6 +271,71 @@ def test_upproj_bf16_and_f32():
         assert np.abs(of.cpu().numpy() - ref).max() <= 1e-5
 
 
+@pytest.mark.parametrize("H,lens,S", [
+    (16, [1, 17, 64, 65, 130, 1000, 2500], 0),   # balanced split: pieces merged, some sequences whole
+    (16, [300, 1000], 3),                        # uniform split
+    (128, [33, 700, 5], 0),
+    (16, [50, 900], 1),                          # no partials at all: z straight from the decode pass
+])
+def test_merge_upproj_matches_oracle_and_separate_calls(H, lens, S):
+    wl = W.make_workload("decode_h16", B=len(lens), H=H, lens=lens)
+    _note(f"case merge+upproj H={H} lens={lens} S={S}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    ref = _oracle_decode(dd)
+    B = wl.B
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    ws = mla.decode_workspace(B, H, S, DEV)
+    # separate calls
+    z1 = torch.empty((B, H, 512), device=DEV)
+    l1 = torch.empty((B, H), device=DEV)
+    mla.decode_partial(q_abs, dd.cache, dd.block_table, dd.seq_lens, ws, z1, l1, num_splits=S)
+    mla.decode_merge(dd.seq_lens, H, ws, z1, l1, num_splits=S)
+    o1 = mla.upproj_v(z1, dd.w_uv)
+    # fused, into buffers holding garbage
+    z2 = torch.full((B, H, 512), float("nan"), device=DEV)
+    l2 = torch.full((B, H), float("nan"), device=DEV)
+    mla.decode_partial(q_abs, dd.cache, dd.block_table, dd.seq_lens, ws, z2, l2, num_splits=S)
+    o2 = mla.decode_merge_upproj(dd.seq_lens, H, ws, z2, dd.w_uv, lse=l2, num_splits=S)
+    o2b = mla.decode_merge_upproj(dd.seq_lens, H, ws, z2, dd.w_uv, lse=l2, num_splits=S, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # same merge, pieces folded in batches of 16 instead of 32: equal up to rounding order
+    assert _rel(z2.cpu().numpy(), z1.cpu().numpy()) <= 1e-6
+    assert (l2 - l1).abs().max().item() <= 1e-5
+    o2n, o1n = o2.cpu().numpy(), o1.cpu().numpy()
+    assert _rel(o2n, ref["o"]) <= 2e-2
+    assert _rel(o2b.float().cpu().numpy(), ref["o"]) <= 2e-2
+    # the fused product keeps z in fp32; the matrix-core one rounds it to bf16
+    assert _rel(o2n, o1n) <= 1e-2
+    zz = z2.double().cpu().numpy()
+    o_exact = np.einsum("hdc,bhc->bhd", dd.host["w_uv"], zz)
+    assert np.abs(o2n - o_exact).max() <= 1e-4 * max(1.0, np.abs(o_exact).max())
+
+
+def test_merge_upproj_many_sequences_and_f32_weights_take_the_two_launch_path():
+    wl = W.make_workload("decode_h16", B=40, H=16, lens=[int(x) for x in np.random.default_rng(3).integers(1, 400, 40)])
+    _note(f"case merge+upproj B={wl.B}")
+    dd = DI.decode_inputs(wl, DEV)
+    ref = _oracle_decode(dd, seqs=[0, 13, 39])
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    ws = mla.decode_workspace(wl.B, wl.H, 0, DEV)
+    z = torch.empty((wl.B, wl.H, 512), device=DEV)
+    mla.decode_partial(q_abs, dd.cache, dd.block_table, dd.seq_lens, ws, z, None)
+    o = mla.decode_merge_upproj(dd.seq_lens, wl.H, ws, z, dd.w_uv)
+    torch.cuda.synchronize()
+    assert _rel(o.cpu().numpy()[[0, 13, 39]], ref["o"]) <= 2e-2
+    # fp32 weights on a small batch: merge then the fp32 up-projection
+    wl2 = W.make_workload("tiny_f32", B=2, lens=[64, 200])
+    dd2 = DI.decode_inputs(wl2, DEV)
+    ref2 = _oracle_decode(dd2)
+    q2 = mla.absorb_q(dd2.q_c, dd2.q_r, dd2.pos, dd2.w_uk)
+    ws2 = mla.decode_workspace(2, wl2.H, 0, DEV)
+    z2 = torch.empty((2, wl2.H, 512), device=DEV)
+    mla.decode_partial(q2, dd2.cache, dd2.block_table, dd2.seq_lens, ws2, z2, None)
+    o2 = mla.decode_merge_upproj(dd2.seq_lens, wl2.H, ws2, z2, dd2.w_uv)
+    torch.cuda.synchronize()
+    assert np.abs(o2.cpu().numpy() - ref2["o"]).max() <= 1e-5
+
+
 # --------------------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("H,T", [(16, 200), (128, 130)])
