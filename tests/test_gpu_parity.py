@@ -336,6 +336,50 @@ def test_merge_upproj_many_sequences_and_f32_weights_take_the_two_launch_path():
     assert np.abs(o2.cpu().numpy() - ref2["o"]).max() <= 1e-5
 
 
+@pytest.mark.parametrize("H,lens", [(16, [3000, 1, 700, 64, 1500]), (128, [900, 33, 2048])])
+def test_step_graph_replays_match_eager(H, lens):
+    """The decode step captured as a HIP graph, as bench.py times it: every
+    replay, with eager work and synchronisations between replays, equals the
+    eager result bit for bit.  (The step records no memset: the workspace
+    needs no clearing.)"""
+    wl = W.make_workload("decode_h16", B=len(lens), H=H, lens=lens)
+    _note(f"case graph replay H={H} lens={lens}")
+    dd = DI.decode_inputs(wl, DEV)
+    B = wl.B
+    q_abs = torch.empty((B, H, 576), dtype=torch.bfloat16, device=DEV)
+    z = torch.empty((B, H, 512), device=DEV)
+    lse = torch.empty((B, H), device=DEV)
+    o = torch.empty((B, H, 128), device=DEV)
+    ws = mla.decode_workspace(B, H, 0, DEV)
+
+    def step():
+        mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk, out=q_abs)
+        mla.decode_partial(q_abs, dd.cache, dd.block_table, dd.seq_lens, ws, z, lse)
+        mla.decode_merge_upproj(dd.seq_lens, H, ws, z, dd.w_uv, lse=lse, out=o)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (q_abs, z, lse, o)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (q_abs, z, lse, o):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((q_abs, z, lse, o), ref):
+            assert torch.equal(got, want), rep
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("H,T", [(16, 200), (128, 130)])
