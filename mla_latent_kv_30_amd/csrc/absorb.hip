@@ -34,34 +34,63 @@ __device__ __forceinline__ void rope_rows(const AbsorbArgs& a, int h, int n0, in
 }
 
 // grid: (H * 4 c-quarters, ceil(N / 128)); 4 waves, each 32 query rows x 128 c.
+// Every global load of a workgroup (its W slice, the q_c operand of each
+// wave, and the q_r rows it rotates) is issued before any result is used,
+// so a workgroup costs one memory round trip before its products; the
+// rotation of the 128 rows is shared by the four c-quarter workgroups.
 __global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kDn * kAbsLdsStride];  // W[d][c-slice]
   const int h = blockIdx.x >> 2, cq = blockIdx.x & 3;
   const int n_blk = blockIdx.y * kAbsRowsPerBlock;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bf16* w = (const bf16*)a.w_uk + (size_t)h * kDn * kDc + cq * kAbsCols;
-  // stage W[0:128][cq*128 : cq*128+128]: 128 rows of 256 bytes, padded stride
-  for (int i = threadIdx.x; i < kDn * (kAbsCols / 8); i += 256) {
-    const int d = i / (kAbsCols / 8), ch = i % (kAbsCols / 8);
-    *(int4v*)(w_lds + d * kAbsLdsStride + ch * 16) = *(const int4v*)(w + (size_t)d * kDc + ch * 8);
-  }
-  const int rows_here = min(kAbsRowsPerBlock, a.N - n_blk);
-  if (cq == 0) rope_rows<bf16>(a, h, n_blk, rows_here);
-  __syncthreads();
-  const int n0 = n_blk + wave * kAbsRowsPerWave;
-  if (n0 >= a.N) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5;
+  const bf16* __restrict__ w = (const bf16*)a.w_uk + (size_t)h * kDn * kDc + cq * kAbsCols;
+  // W[0:128][cq*128 : cq*128+128]: 128 rows of 16 chunks of 16 bytes
+  int4v wv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = tid + 256 * i, d = idx >> 4, ch = idx & 15;
+    wv[i] = *(const int4v*)(w + (size_t)d * kDc + ch * 8);
+  }
   // B operand: q_c^T (k = d, n = query row): lane holds row n0 + lane%32, d = 16kk + 8g + j
+  const int n0 = n_blk + wave * kAbsRowsPerWave;
   const int nrow = n0 + (lane & 31);
   const bool nok = nrow < a.N;
-  const bf16* qc = (const bf16*)a.q_c + ((size_t)(nok ? nrow : n0) * a.H + h) * kDn;
+  const bf16* __restrict__ qc = (const bf16*)a.q_c + ((size_t)(nok ? nrow : 0) * a.H + h) * kDn;
+  int4v qv[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) qv[kk] = *(const int4v*)(qc + 16 * kk + 8 * g);
+  // rotation: this workgroup's 32 rows n_blk + 32cq .. +31, one pair (2m, 2m+1) per item
+  uint32_t rx[4];
+  int rpos[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int item = tid + 256 * j, n = n_blk + 32 * cq + (item >> 5), m = item & 31;
+    const int nc = n < a.N ? n : 0;
+    rx[j] = *(const uint32_t*)((const bf16*)a.q_r + ((size_t)nc * a.H + h) * kDr + 2 * m);
+    rpos[j] = a.pos[nc];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = tid + 256 * i, d = idx >> 4, ch = idx & 15;
+    *(int4v*)(w_lds + d * kAbsLdsStride + ch * 16) = wv[i];
+  }
   bf16x8 qb[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    int4v v = *(const int4v*)(qc + 16 * kk + 8 * g);
-    if (!nok) v = int4v{0, 0, 0, 0};
-    qb[kk] = __builtin_bit_cast(bf16x8, v);
+  for (int kk = 0; kk < 8; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, nok ? qv[kk] : int4v{0, 0, 0, 0});
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int item = tid + 256 * j, n = n_blk + 32 * cq + (item >> 5), m = item & 31;
+    if (n < a.N) {
+      float c, sn;
+      rope_cs(rpos[j], a.rope.theta[m], c, sn);
+      const float x0 = __uint_as_float(rx[j] << 16), x1 = __uint_as_float(rx[j] & 0xffff0000u);
+      bf16* out = (bf16*)a.q_abs + ((size_t)n * a.H + h) * kRow + kDc + 2 * m;
+      *(bf16x2*)out = bf16x2{f2bf(x0 * c - x1 * sn), f2bf(x0 * sn + x1 * c)};
+    }
   }
+  __syncthreads();
+  if (n0 >= a.N) return;
   // A operand: W^T (m = c, k = d) by transposing reads: 16-lane group G owns
   // columns 16*(G%2) .. +15 of the 32-wide tile and rows d0 + 4*(lane%16 / 4)
   const int dsub = (lane & 15) >> 2;

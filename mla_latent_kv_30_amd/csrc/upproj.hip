@@ -10,46 +10,80 @@ namespace mla {
 // bf16 weights: o^T[d, n] = sum_c W[d, c] z^T[c, n] on 32x32x16 matrix cores.
 // Workgroup = (head, 256 query rows); wave = 64 rows (2 column tiles) x all
 // 128 d (4 row tiles).  z is rounded to bf16 on load; accumulation is fp32.
+// The contraction runs in chunks of two 16-wide steps whose 16 operand loads
+// are issued one chunk ahead, so memory latency overlaps the products.
+struct UpChunk {
+  int4v w[2][4];     // [step][row tile]: W[32mt + l%32][c0 .. c0+7]
+  float4 z[2][2][2]; // [step][column tile][half]: z[row][c0 .. c0+7]
+};
+
+// A query row past N reads the workgroup's first row instead: it only feeds
+// its own output column, which is not stored.
+__device__ __forceinline__ void up_load(UpChunk& ch, const bf16* __restrict__ w, const float* const (&zr)[2], int k0,
+                                        int lane) {
+  const int g = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int c0 = 16 * (k0 + s) + 8 * g;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) ch.w[s][mt] = *(const int4v*)(w + (size_t)(32 * mt + (lane & 31)) * kDc + c0);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float4* zp = (const float4*)(zr[nt] + c0);
+      ch.z[s][nt][0] = zp[0];
+      ch.z[s][nt][1] = zp[1];
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) upproj_bf16_kernel(UpprojArgs a) {
   const int h = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = blockIdx.y * 256 + wave * 64;
   if (n0 >= a.N) return;
   const int g = lane >> 5;
-  const bf16* w = (const bf16*)a.w_uv + (size_t)h * kDv * kDc;
+  const bf16* __restrict__ w = (const bf16*)a.w_uv + (size_t)h * kDv * kDc;
   int nrow[2];
   bool nok[2];
+  const float* zr[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     nrow[nt] = n0 + 32 * nt + (lane & 31);
     nok[nt] = nrow[nt] < a.N;
+    zr[nt] = a.z + ((size_t)(nok[nt] ? nrow[nt] : n0) * a.H + h) * kDc;
   }
   floatx16 acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = floatx16{};
-  for (int kk = 0; kk < kDc / 16; ++kk) {
-    const int c0 = 16 * kk + 8 * g;
-    bf16x8 bz[2];
+  auto compute = [&](const UpChunk& ch) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float4 u0 = make_float4(0, 0, 0, 0), u1 = u0;
-      if (nok[nt]) {
-        const float4* zp = (const float4*)(a.z + ((size_t)nrow[nt] * a.H + h) * kDc + c0);
-        u0 = zp[0];
-        u1 = zp[1];
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 bz[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float4 u0 = ch.z[s][nt][0], u1 = ch.z[s][nt][1];
+        bz[nt] = bf16x8{f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
+                        f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
       }
-      bz[nt] = bf16x8{f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
-                      f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
-    }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int d = 32 * mt + (lane & 31);
-      bf16x8 aw = __builtin_bit_cast(bf16x8, *(const int4v*)(w + (size_t)d * kDc + c0));
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 aw = __builtin_bit_cast(bf16x8, ch.w[s][mt]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(aw, bz[nt], acc[mt][nt]);
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(aw, bz[nt], acc[mt][nt]);
+      }
     }
+  };
+  // two chunk buffers used in turn (no copy between them, so a chunk's loads
+  // are only waited for when that chunk is consumed)
+  UpChunk ca, cb;
+  up_load(ca, w, zr, 0, lane);
+  for (int k0 = 0; k0 < kDc / 16; k0 += 4) {
+    up_load(cb, w, zr, k0 + 2, lane);
+    compute(ca);
+    if (k0 + 4 < kDc / 16) up_load(ca, w, zr, k0 + 4, lane);
+    compute(cb);
   }
   // C layout: column = query row, rows d = 32mt + 8(r/4) + 4g + r%4
 #pragma unroll
