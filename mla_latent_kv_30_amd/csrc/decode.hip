@@ -90,8 +90,11 @@ __device__ __forceinline__ void softmax_update(WaveState<NT>& st, float (&x)[NV]
 // never wait on each other.  Row index m of a subtile's product maps to
 // token 16u + 4(m%4) + m/4, so score register r of lane group g in subtile u
 // is token 16u + 4r + g.
-template <int D>  // operand reads in flight per chain
-__device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int lane, floatx4& S0, floatx4& S1) {
+// dma(t) is called after K-steps 2, 5, 8, 11, 14 and 17 (t = 0..5): it issues
+// the wave's t-th copy of a later block, if there is one.
+template <int D, class Dma>  // operand reads in flight per chain
+__device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int lane, floatx4& S0, floatx4& S1,
+                                        Dma&& dma) {
   const int g = lane >> 4, m = lane & 15;
   const int r = 4 * (m & 3) + (m >> 2);
   // byte 64kk + 16g of the row: the permutation only touches bits 4..6, so
@@ -122,6 +125,7 @@ __device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int
     }
     S0 = mfma16(__builtin_bit_cast(bf16x8, c0), q[kk], S0);
     S1 = mfma16(__builtin_bit_cast(bf16x8, c1), q[kk], S1);
+    if (kk % 3 == 2) dma(kk / 3);
   }
 }
 
@@ -131,9 +135,9 @@ __device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int
 // multiple of 4): A = C^T (16 channels x 32 tokens) through transposing LDS
 // reads, B = P^T.  The K = 32 slots of lane group g are tokens 4j + g
 // (j < 4) and 16 + 4(j-4) + g.
-template <int NT>
+template <int NT, class Dma>
 __device__ __forceinline__ void block_compute(WaveState<NT>& st, uint32_t buf, int hi, int lane, int mt0,
-                                              float scale_log2) {
+                                              float scale_log2, Dma&& dma) {
   // Recompute the lane's operand offsets in every call rather than let the
   // compiler keep one set per buffer live across the block loop.
   lane = lane_id_fresh();
@@ -141,7 +145,7 @@ __device__ __forceinline__ void block_compute(WaveState<NT>& st, uint32_t buf, i
   float x[8], p[8];
   floatx4 S[2];
   // deeper operand prefetch where the accumulator leaves registers for it
-  score32<NT <= 16 ? 4 : 2>(st.q, buf, lane, S[0], S[1]);
+  score32<NT <= 16 ? 4 : 1>(st.q, buf, lane, S[0], S[1], dma);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -257,14 +261,13 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   auto block_hi = [&](const Cursor& c) { return min(c.seg.t1 - c.k * kBlock, kBlock); };
   // block-table reads use a uniform index, so they are scalar loads that do
   // not wait behind the copies in flight
+  auto page_of = [&](const Cursor& c) {
+    if (bt_local) return uniform(bt_lds[c.seg.b * a.max_pages + (c.k >> 1)]);
+    const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)c.seg.b * a.max_pages;
+    return bt[uniform(c.k >> 1)];
+  };
   auto issue = [&](const Cursor& c, int slot) {
-    int page;
-    if (bt_local) {
-      page = uniform(bt_lds[c.seg.b * a.max_pages + (c.k >> 1)]);
-    } else {
-      const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)c.seg.b * a.max_pages;
-      page = bt[uniform(c.k >> 1)];
-    }
+    const int page = page_of(c);
     if constexpr (FP8) {
       issue_block_fp8(a.ckv8, a.scale8, a.kr8, page, c.k & 1, smem + slot * kStageBytes, block_hi(c), wave, lane);
     } else {
@@ -326,9 +329,29 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     } else {
       buf = smem + (i % kNBuf) * kBlockBytes;
     }
-    if (computes) block_compute<NT>(st, lds_addr(buf), block_hi(cp), lane, mt0, a.scale_log2);
-    if (ld.valid) {  // into the buffer of block i-1, which every wave finished before the barrier
-      issue(ld, (i + kNBuf - 1) % kNBuf);
+    // The copy of block i+3 goes into the buffer of block i-1, which every
+    // wave finished before the barrier.  bf16: a computing wave issues its
+    // copies one by one between its score products.
+    BlockCopies nb;
+    nb.n = 0;
+    if constexpr (!FP8) {
+      if (ld.valid)
+        nb = plan_block_bf16(a.rows + (size_t)page_of(ld) * kPageBytes, ld.k & 1,
+                             smem + ((i + kNBuf - 1) % kNBuf) * kBlockBytes, block_hi(ld), wave);
+    }
+    auto dma = [&](int t) {
+      if constexpr (!FP8) {
+        if (t < nb.n) issue_copy(nb, t);
+      }
+    };
+    if (computes) {
+      block_compute<NT>(st, lds_addr(buf), block_hi(cp), lane, mt0, a.scale_log2, dma);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kCopiesLo; ++t) dma(t);
+    }
+    if (ld.valid) {
+      if constexpr (FP8) issue(ld, (i + kNBuf - 1) % kNBuf);
       ++issued;
       cursor_next(a, ld);
     }

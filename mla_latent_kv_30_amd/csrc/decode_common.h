@@ -246,6 +246,37 @@ __device__ __forceinline__ void issue_block_bf16(const uint8_t* page, int half, 
   }
 }
 
+// The same copies prepared for issue one at a time, so that a computing wave
+// can spread them over its score products (copies issued back to back by all
+// waves at once queue at the address unit).  n = 0: nothing to copy.
+struct BlockCopies {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t lb;  // LDS address of this wave's 8-row group
+  int g;        // the group
+  int j0, n;    // this wave's first copy of the group and how many
+};
+
+__device__ __forceinline__ BlockCopies plan_block_bf16(const uint8_t* page, int half, uint8_t* buf, int hi, int wave) {
+  BlockCopies c;
+  c.g = wave & 3;
+  c.rs = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(page + half * kBlockBytes), (short)0,
+                                           uniform(hi * kRowBytes), kRsrcWord3);
+  c.lb = lds_addr(buf) + c.g * kGroupBytes;
+  c.j0 = wave < 4 ? 0 : kCopiesLo;
+  c.n = wave < 4 ? kCopiesLo : kCopiesHi;
+  return c;
+}
+
+// Copy t (< c.n) of this wave.
+__device__ __forceinline__ void issue_copy(const BlockCopies& c, int t) {
+  const int lane = lane_id_fresh();
+  const int j = c.j0 + t;
+  const int q = 64 * j + lane;
+  const int r = q / 72, cc = q - 72 * r;
+  const uint32_t vo = (uint32_t)(r * kRowBytes + 16 * (cc ^ swz(kGroupRows * c.g + r)));
+  lds_dma16(c.rs, c.lb + kCopyBytes * j, vo, c.g * kGroupBytes);
+}
+
 // Wait until at most the copies of this wave's `n` (0..3) most recently
 // issued blocks are in flight (waves 0..3 issue C_LO copies per block,
 // waves 4..7 C_HI).
