@@ -16,23 +16,6 @@ constexpr int kAbsRowsPerBlock = 4 * kAbsRowsPerWave;   // 128 query tokens per 
 constexpr int kAbsCols = 128;                           // c-slice of W per workgroup
 constexpr int kAbsLdsStride = kAbsCols * 2 + 32;        // padded row stride (bytes): rows 8 banks apart
 
-// Rotate q_r of rows [n0, n0+rows) of head h into q_abs[..., 512:576].
-template <typename T>
-__device__ __forceinline__ void rope_rows(const AbsorbArgs& a, int h, int n0, int rows) {
-  const T* qr = (const T*)a.q_r;
-  T* out = (T*)a.q_abs;
-  for (int i = threadIdx.x; i < rows * 32; i += blockDim.x) {
-    const int n = n0 + i / 32, m = i % 32;
-    const size_t src = ((size_t)n * a.H + h) * kDr + 2 * m;
-    const float x0 = (float)qr[src], x1 = (float)qr[src + 1];
-    float c, s;
-    rope_cs(a.pos[n], a.rope.theta[m], c, s);
-    const size_t dst = ((size_t)n * a.H + h) * kRow + kDc + 2 * m;
-    out[dst] = (T)(x0 * c - x1 * s);
-    out[dst + 1] = (T)(x0 * s + x1 * c);
-  }
-}
-
 // grid: (H * 4 c-quarters, ceil(N / 128)); 4 waves, each 32 query rows x 128 c.
 // Every global load of a workgroup (its W slice, the q_c operand of each
 // wave, and the q_r rows it rotates) is issued before any result is used,
@@ -63,12 +46,14 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a) {
   // rotation: this workgroup's 32 rows n_blk + 32cq .. +31, one pair (2m, 2m+1) per item
   uint32_t rx[4];
   int rpos[4];
+  double rth[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int item = tid + 256 * j, n = n_blk + 32 * cq + (item >> 5), m = item & 31;
     const int nc = n < a.N ? n : 0;
     rx[j] = *(const uint32_t*)((const bf16*)a.q_r + ((size_t)nc * a.H + h) * kDr + 2 * m);
     rpos[j] = a.pos[nc];
+    rth[j] = a.rope.theta[m];
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -78,18 +63,19 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a) {
   bf16x8 qb[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, nok ? qv[kk] : int4v{0, 0, 0, 0});
+  __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 4; ++j) {  // after the barrier: the operands arrived with the W slice
     const int item = tid + 256 * j, n = n_blk + 32 * cq + (item >> 5), m = item & 31;
     if (n < a.N) {
+      asm volatile("" : "+v"(rpos[j]));  // converted here, not where it was loaded
       float c, sn;
-      rope_cs(rpos[j], a.rope.theta[m], c, sn);
+      rope_cs(rpos[j], rth[j], c, sn);
       const float x0 = __uint_as_float(rx[j] << 16), x1 = __uint_as_float(rx[j] & 0xffff0000u);
       bf16* out = (bf16*)a.q_abs + ((size_t)n * a.H + h) * kRow + kDc + 2 * m;
       *(bf16x2*)out = bf16x2{f2bf(x0 * c - x1 * sn), f2bf(x0 * sn + x1 * c)};
     }
   }
-  __syncthreads();
   if (n0 >= a.N) return;
   // A operand: W^T (m = c, k = d) by transposing reads: 16-lane group G owns
   // columns 16*(G%2) .. +15 of the 32-wide tile and rows d0 + 4*(lane%16 / 4)
@@ -158,13 +144,33 @@ __global__ void __launch_bounds__(256) absorb_small_kernel(AbsorbArgs a) {
       qb[nt][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // rotation: the N x 32 pairs of this head are shared by the 8 workgroups
+  // of the head (4N pairs each, one per thread); loads issued with the rest
+  const int ritem = cs * 4 * a.N + tid;
+  const bool rot = tid < 4 * a.N;
+  const int rn = rot ? ritem >> 5 : 0, rm = ritem & 31;
+  uint32_t rx = 0;
+  int rpos = 0;
+  double rth = 0.0;
+  if (rot) {
+    rx = *(const uint32_t*)((const bf16*)a.q_r + ((size_t)rn * a.H + h) * kDr + 2 * rm);
+    rpos = a.pos[rn];
+    rth = a.rope.theta[rm];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + 256 * i, d = idx >> 3, ch = idx & 7;
     *(int4v*)(w_lds + d * kAbsSmallStride + ch * 16) = wv[i];
   }
-  if (cs == 0) rope_rows<bf16>(a, h, 0, a.N);
   __syncthreads();
+  if (rot) {  // after the barrier: its operands arrived with the W slice
+    asm volatile("" : "+v"(rpos));  // converted here, not where it was loaded
+    float c, sn;
+    rope_cs(rpos, rth, c, sn);
+    const float x0 = __uint_as_float(rx << 16), x1 = __uint_as_float(rx & 0xffff0000u);
+    bf16* out = (bf16*)a.q_abs + ((size_t)rn * a.H + h) * kRow + kDc + 2 * rm;
+    *(bf16x2*)out = bf16x2{f2bf(x0 * c - x1 * sn), f2bf(x0 * sn + x1 * c)};
+  }
   // A operand by transposing reads: source lane s of group G points at row
   // d = 32kk + 8G + s/4 (+4), columns c0 + 4(s%4) .. +3; lane s receives
   // column c0 + s of four consecutive rows.
