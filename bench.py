@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence (multi-token decode, mla_decode_multi); decode workloads only")
     return ap.parse_args()
 
 
@@ -187,27 +189,39 @@ def main():
     # ---- replicas of everything a step reads
     per_rep = dd.cache.nbytes() + sum(t.numel() * t.element_size() for t in (dd.q_c, dd.q_r, dd.w_uk, dd.w_uv))
     R = args.replicas or max(1, min(16, math.ceil(REPLICA_TARGET_BYTES / per_rep)))
-    reps = [(dd.cache, dd.q_c, dd.q_r, dd.w_uk, dd.w_uv)]
+    QL = max(1, args.q_len)
+    if QL * H > 128:
+        sys.exit(f"--q-len {QL} with {H} heads: multi-token decode takes q_len * H <= 128")
+    if QL > 1:  # q_len new tokens per sequence at positions L - q_len + t
+        q_c0, q_r0, pos_q, _, _ = DI.multi_query_inputs(dd, QL)
+    else:
+        q_c0, q_r0, pos_q = dd.q_c, dd.q_r, dd.pos
+    reps = [(dd.cache, q_c0, q_r0, dd.w_uk, dd.w_uv)]
     for _ in range(R - 1):
         c = mla.PagedCache.__new__(mla.PagedCache)
         c.__dict__.update(dd.cache.__dict__)
         for name in ("rows", "ckv", "scale", "kr"):
             t = getattr(dd.cache, name)
             setattr(c, name, None if t is None else t.clone())
-        reps.append((c, dd.q_c.clone(), dd.q_r.clone(), dd.w_uk.clone(), dd.w_uv.clone()))
-    q_abs = torch.empty((B, H, 576), dtype=dt, device=dev)
-    z = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    o = torch.empty((B, H, 128), dtype=torch.float32, device=dev)
-    ws = mla.decode_workspace(B, H, splits, dev)
+        reps.append((c, q_c0.clone(), q_r0.clone(), dd.w_uk.clone(), dd.w_uv.clone()))
+    q_abs = torch.empty((B * QL, H, 576), dtype=dt, device=dev)
+    z = torch.empty((B * QL, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B * QL, H), dtype=torch.float32, device=dev)
+    o = torch.empty((B * QL, H, 128), dtype=torch.float32, device=dev)
+    ws = mla.decode_workspace(B, QL * H, splits, dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
     def step(r):
         cache, q_c, q_r, w_uk, w_uv = reps[r]
-        mla.absorb_q(q_c, q_r, dd.pos, w_uk, out=q_abs)
-        mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
-        mla.decode_merge_upproj(dd.seq_lens, H, ws, z, w_uv, lse=lse, num_splits=splits, out=o)
+        mla.absorb_q(q_c, q_r, pos_q, w_uk, out=q_abs)
+        if QL > 1:
+            mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
+                             workspace=ws, z=z.view(B, QL, H, 512), lse=lse.view(B, QL, H))
+            mla.upproj_v(z, w_uv, out=o)
+        else:
+            mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
+            mla.decode_merge_upproj(dd.seq_lens, H, ws, z, w_uv, lse=lse, num_splits=splits, out=o)
 
     for k in range(max(1, args.warmup)):
         step(k % R)
@@ -264,7 +278,11 @@ def main():
         e0.record()
         for k in range(K):
             cache, *_ = reps[k % R]
-            mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
+            if QL > 1:  # the multi-token entry point is decode + merge
+                mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
+                                 workspace=ws, z=z.view(B, QL, H, 512), lse=lse.view(B, QL, H))
+            else:
+                mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
         e1.record()
         torch.cuda.synchronize()
         kern_ms.append(e0.elapsed_time(e1) / K)
@@ -279,23 +297,27 @@ def main():
 
     # ---- roofline of the decode kernel (algorithmic bytes / FLOPs per launch)
     tok_bytes = {"f32": 2304, "bf16": 1152, "fp8": 656}[wl.dtype]
-    q_bytes = B * H * 576 * (4 if wl.dtype == "f32" else 2)
-    out_bytes = B * H * (512 + 1) * 4
+    q_bytes = B * QL * H * 576 * (4 if wl.dtype == "f32" else 2)
+    out_bytes = B * QL * H * (512 + 1) * 4
     alg_bytes = total * tok_bytes + q_bytes + out_bytes
-    alg_flops = total * H * FLOP_PER_TOKEN_HEAD
+    # query token t of a sequence of L cached tokens sees L - q_len + t + 1 of them
+    seen = int(sum(QL * int(L) - QL * (QL - 1) // 2 for L in wl.lens))
+    alg_flops = seen * H * FLOP_PER_TOKEN_HEAD
     gbs = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
     tflops = alg_flops / (kern_avg_ms * 1e-3) / 1e12
     mfma_peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and QL == 1:
         cpu = cpu_baseline(wl, dd.host, args.cpu_seconds)
 
     # HBM bytes per launch from the stored counter runs, if they were taken on
     # the current kernel sources
     from mla_latent_kv_30_amd import traffic as TR
     kname = "decode_mfma_kernel" if wl.dtype != "f32" else "decode_f32_kernel"
-    tr = TR.load(kname, wl.name, os.path.join(ROOT, "profiles"))
+    tr = TR.load(kname, wl.name, os.path.join(ROOT, "profiles")) if QL == 1 else None
+    if QL > 1:
+        kname += " + merge_kernel"
 
     out = {
         "metric": METRIC,
@@ -314,7 +336,9 @@ def main():
             "workload": wl.name, "batch": B, "heads": H, "cached_tokens": total,
             "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
             "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
-            "step": "absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)",
+            "step": ("absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)" if QL == 1
+                     else "absorb_q + decode_multi (decode + split merge) + upproj_v"),
+            "q_len": QL, "query_tokens_per_s": B * QL / (ms_per_step * 1e-3),
         },
         "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,

@@ -197,6 +197,27 @@ mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32
                             size_t ws_bytes, float* z, float* lse, void* stream);
 
 /*
+ * mla_decode_multi — q_len new tokens per sequence attend at once (the
+ * multi-token decode of speculative verification, "DeepSeek-V3" notes
+ * §Multi-Token Prediction): query token t of sequence b is at position
+ * L_b - q_len + t and attends to cached tokens 0 .. L_b - q_len + t, i.e.
+ * causally among the new tokens, which are already in the cache.
+ *   q_abs      [B][q_len][H][576] (mla_absorb_q with N = B*q_len rows at those
+ *              positions)
+ *   seq_lens   [B] cached tokens including the q_len new ones; L_b >= q_len
+ *   z          [B][q_len][H][512] fp32 out; lse [B][q_len][H] or NULL
+ *   workspace  mla_decode_workspace_size(B, q_len*H, num_splits) bytes
+ * Otherwise as mla_decode, with q_len*H heads: q_len*H <= 128.  The value
+ * up-projection is mla_upproj_v with N = B*q_len.  (mla_decode_merge_upproj
+ * is for one query token per sequence.)  Errors: as mla_decode, and
+ * MLA_ERR_INVALID_ARG for q_len < 1 or q_len*H > 128.
+ */
+mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
+                            float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes, float* z,
+                            float* lse, void* stream);
+
+/*
  * mla_decode_merge_upproj: mla_decode_merge followed by mla_upproj_v on its z
  * (o_i = W_i^UV z_i, §潜在向量的作用), with N = B.  Arguments as for those
  * two calls; z and lse are written as mla_decode_merge writes them.  With a

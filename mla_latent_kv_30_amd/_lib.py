@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_partial.argtypes = list(L.mla_decode.argtypes)
     L.mla_decode_merge.restype = _i32
     L.mla_decode_merge.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_decode_multi.restype = _i32
+    L.mla_decode_multi.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
+                                   ctypes.c_size_t, _vp, _vp, _vp]
     L.mla_decode_merge_upproj.restype = _i32
     L.mla_decode_merge_upproj.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp,
                                           _i32, _vp]
@@ -265,6 +268,35 @@ def decode_merge(seq_lens: torch.Tensor, H: int, workspace: Optional[torch.Tenso
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_merge(_ptr(seq_lens), B, int(H), int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
                                   _ptr(lse), _stream(z.device)), "mla_decode_merge")
+
+
+def decode_multi(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                 softmax_scale: Optional[float] = None, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """z[B,q_len,H,512], lse[B,q_len,H] of q_len new tokens per sequence (mla_decode_multi)."""
+    B, q_len, H = q_abs.shape[0], q_abs.shape[1], q_abs.shape[2]
+    _need(q_abs, "q_abs", cache.input_dtype, (B, q_len, H, ROW))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    dev = q_abs.device
+    if z is None:
+        z = torch.empty((B, q_len, H, D_C), dtype=torch.float32, device=dev)
+    _need(z, "z", torch.float32, (B, q_len, H, D_C))
+    if lse is None and want_lse:
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, q_len, H))
+    if workspace is None:
+        workspace = decode_workspace(B, q_len * H, num_splits, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
+    desc = cache.descriptor()
+    _check(lib().mla_decode_multi(_ptr(q_abs), ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), B, q_len, H,
+                                  block_table.shape[1], scale, int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
+                                  _ptr(lse), _stream(dev)), "mla_decode_multi")
+    return z, lse
 
 
 def decode_merge_upproj(seq_lens: torch.Tensor, H: int, workspace: Optional[torch.Tensor], z: torch.Tensor,

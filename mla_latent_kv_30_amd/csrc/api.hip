@@ -180,6 +180,8 @@ mla_status prepare_decode(const void* q_abs, const mla_cache* cache, const int32
   a.splits = p.splits;
   a.units = p.units;
   a.scale_log2 = (float)(softmax_scale * 1.4426950408889634074);
+  a.q_len = 1;
+  a.hs = H;
   a.z = z;
   a.lse = lse;
   set_workspace(a, workspace, B, H, p);
@@ -270,6 +272,26 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
   return launched(launch_merge(a, s));
 }
 
+mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
+                            float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes, float* z,
+                            float* lse, void* stream) {
+  if (q_len < 1 || H < 1 || (long long)q_len * H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  DecodeArgs a;
+  int kind;
+  Plan p;
+  mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, q_len * H, max_pages, softmax_scale,
+                                 num_splits, workspace, ws_bytes, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
+  a.q_len = q_len;
+  a.hs = H;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  st = launched(launch_decode(a, kind, s));
+  if (st != MLA_OK || p.slots == 0) return st;
+  return launched(launch_merge(a, s));
+}
+
 mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
                               const mla_cache* cache, const int32_t* block_table_row, int32_t T, int32_t H,
                               float softmax_scale, float rope_base, float* z, float* lse, void* stream) {
@@ -303,6 +325,8 @@ mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k
   a.units = T;
   a.prefill_T = T;
   a.prefill_pos0 = pos0;
+  a.q_len = 1;
+  a.hs = H;
   a.scale_log2 = (float)(softmax_scale * 1.4426950408889634074);
   a.z = z;
   a.lse = lse;

@@ -75,10 +75,13 @@ __device__ __forceinline__ void softmax_update(WaveState<NT>& st, float (&x)[NV]
 #pragma unroll
     for (int t = 0; t < NT; ++t) st.zacc[t] *= alpha;
   }
+  // a head that has seen only masked scores so far keeps m = -inf: its
+  // probabilities are 0 (exp2(-inf - 0)), not exp2(-inf + inf)
+  const float mref = st.m == -INFINITY ? 0.f : st.m;
   float sum = 0.f;
 #pragma unroll
   for (int r = 0; r < NV; ++r) {
-    p[r] = fast_exp2(x[r] - st.m);
+    p[r] = fast_exp2(x[r] - mref);
     sum += p[r];
   }
   st.l += sum;
@@ -129,7 +132,8 @@ __device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int
   }
 }
 
-// One block buffer (32 rows); rows at or past `hi` are masked.  Scores for
+// One block buffer (32 rows); rows at or past `hi` (per lane: it may differ
+// between the query tokens of multi-token decode) are masked.  Scores for
 // the wave's 16 heads over the 32 tokens, then the value product
 // Z^T += C^T P^T for the wave's NT channel tiles, starting at tile mt0 (a
 // multiple of 4): A = C^T (16 channels x 32 tokens) through transposing LDS
@@ -198,7 +202,9 @@ __device__ __forceinline__ void store_state(const WaveState<NT>& st, float l_tot
   const int head = h0 + (lane & 15);
   const int g = lane >> 4;
   if (head >= H) return;
-  const float inv = 1.0f / l_tot;
+  // l_tot = 0: a piece all of whose keys lie after this query token (multi-
+  // token decode); it leaves z = 0 and lse = -inf, which the merge weighs 0
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   float* row = zdst + (size_t)head * kDc + c0;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -345,7 +351,14 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
       }
     };
     if (computes) {
-      block_compute<NT>(st, lds_addr(buf), block_hi(cp), lane, mt0, a.scale_log2, dma);
+      // multi-token decode: query token t of the sequence sees keys up to
+      // L - q_len + t, so the last q_len - 1 - t keys are masked for it
+      int hi = block_hi(cp);
+      if (a.q_len > 1) {
+        const int head = min(h0 + (lane_id_fresh() & 15), a.H - 1);
+        hi = min(hi, cp.seg.L - (a.q_len - 1 - head / a.hs) - kBlock * cp.k);
+      }
+      block_compute<NT>(st, lds_addr(buf), hi, lane, mt0, a.scale_log2, dma);
     } else {
 #pragma unroll
       for (int t = 0; t < kCopiesLo; ++t) dma(t);
@@ -404,7 +417,8 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
     for (int i = tid; i < kRow; i += 256) qs[i] = q[i];
     __syncthreads();
     float m = -INFINITY, l = 0.f, z0 = 0.f, z1 = 0.f;
-    const int j0 = seg.t0, j1 = seg.t1;
+    // multi-token decode: query token head / hs sees keys up to L - q_len + token
+    const int j0 = seg.t0, j1 = a.q_len > 1 ? min(seg.t1, seg.L - (a.q_len - 1 - head / a.hs)) : seg.t1;
     for (int jb = j0; jb < j1; jb += 256) {
       const int j = jb + tid;
       float s = -INFINITY;
@@ -451,9 +465,10 @@ __global__ void __launch_bounds__(256) decode_f32_kernel(DecodeArgs a) {
       zdst = a.zp + ((size_t)seg.slot * a.H + head) * kDc;
       ldst = a.lsep + (size_t)seg.slot * a.H + head;
     }
-    zdst[tid] = z0 / l;
-    zdst[tid + 256] = z1 / l;
-    if (ldst != nullptr && tid == 0) *ldst = (m + log2f(l)) * 0.69314718055994530942f;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;  // l = 0: every key of the piece is masked
+    zdst[tid] = z0 * inv;
+    zdst[tid + 256] = z1 * inv;
+    if (ldst != nullptr && tid == 0) *ldst = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
   }
 }
 

@@ -29,6 +29,8 @@ struct DecodeArgs {
   int32_t prefill_T;           // > 0: causal prefill of T rows (unit w -> row T-1-w)
   int32_t prefill_pos0;
   float scale_log2;            // softmax_scale * log2(e)
+  int32_t q_len;               // query tokens per sequence (multi-token decode), 1 otherwise
+  int32_t hs;                  // heads of one query token (H / q_len): head h' is token h' / hs
   float* z;
   float* lse;
   float* zp;                   // partials [slots][H][512]

@@ -63,3 +63,16 @@ def decode_inputs(wl: W.Workload, device="cuda", spare_pages: int = 0, poison: b
         pos=_t(wl.lens - 1, torch.int32, device), w_uk=_t(w_uk, dt, device), w_uv=_t(w_uv, dt, device),
         block_table=_t(np.where(layout.block_table < 0, 0, layout.block_table), torch.int32, device),
         seq_lens=_t(wl.lens, torch.int32, device), host=host)
+
+
+def multi_query_inputs(dd: DeviceDecode, q_len: int):
+    """Multi-token queries of a decode workload on the device of `dd`:
+    q_c [B*q_len,H,128], q_r [B*q_len,H,64] (token-major within a sequence)
+    and their positions L_b - q_len + t, plus the host copies."""
+    wl = dd.wl
+    dt = dd.q_c.dtype
+    dev = dd.q_c.device
+    q_c, q_r = W.multi_queries(wl, q_len)
+    pos = (np.asarray(wl.lens)[:, None] - q_len + np.arange(q_len)[None, :]).reshape(-1)
+    return (_t(q_c.reshape(-1, wl.H, q_c.shape[-1]), dt, dev), _t(q_r.reshape(-1, wl.H, q_r.shape[-1]), dt, dev),
+            _t(pos, torch.int32, dev), q_c, q_r)

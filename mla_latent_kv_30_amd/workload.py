@@ -149,6 +149,15 @@ def queries(wl: Workload):
     return q_c, q_r
 
 
+def multi_queries(wl: Workload, q_len: int):
+    """q_C [B,q_len,H,128] and raw q_R [B,q_len,H,64] ~ N(0,1) for multi-token
+    decode: the q_len newest tokens of every sequence are queries, token t of
+    sequence b at position L_b - q_len + t."""
+    q_c = _cast(_normal(stream(wl.seed, wl.name, "q_C_multi", q_len), (wl.B, q_len, wl.H, D_H)), wl.dtype)
+    q_r = _cast(_normal(stream(wl.seed, wl.name, "q_R_multi", q_len), (wl.B, q_len, wl.H, D_R)), wl.dtype)
+    return q_c, q_r
+
+
 def sequence_latents(wl: Workload, b: int):
     """c_KV [L_b,512] and raw (un-rotated) k_R [L_b,64] of sequence b, ~ N(0,1).
 

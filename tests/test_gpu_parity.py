@@ -380,6 +380,70 @@ def test_step_graph_replays_match_eager(H, lens):
         torch.cuda.synchronize()
 
 
+# --------------------------------------------------------------------------- multi-token decode
+
+def _oracle_multi(dd, q_c, q_r, q_len, seqs=None):
+    """Query token t of sequence b is the newest token of the prefix of length
+    L_b - q_len + t + 1: the oracle's one-token decode on that prefix."""
+    h = dd.host
+    off = h["offsets"]
+    seqs = range(dd.wl.B) if seqs is None else seqs
+    out = {"o": [], "z": [], "lse": []}
+    for b in seqs:
+        L = int(dd.wl.lens[b])
+        per = {"o": [], "z": [], "lse": []}
+        for t in range(q_len):
+            n = L - q_len + t + 1
+            r = orc.decode_sequence(q_c[b, t], q_r[b, t], h["c_kv"][off[b]:off[b] + n], h["k_r"][off[b]:off[b] + n],
+                                    h["w_uk"], h["w_uv"])
+            for k in per:
+                per[k].append(r[k])
+        for k in out:
+            out[k].append(np.stack(per[k]))
+    return {k: np.stack(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("name,H,q_len,lens,tol", [
+    ("decode_h16", 16, 2, [2, 5, 64, 65, 300, 1000], 2e-2),
+    ("decode_h16", 32, 4, [4, 97, 700], 2e-2),
+    ("decode_h16", 40, 3, [3, 129], 2e-2),
+    ("tiny_f32", 16, 3, [3, 65, 200], None),
+    ("long_fp8", 16, 2, [2, 65, 333], 6e-2),
+])
+def test_multi_token_decode_matches_oracle(name, H, q_len, lens, tol):
+    wl = W.make_workload(name, B=len(lens), H=H, lens=lens)
+    _note(f"case multi-token {name} H={H} q_len={q_len} lens={lens}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    q_c, q_r, pos, hq_c, hq_r = DI.multi_query_inputs(dd, q_len)
+    ref = _oracle_multi(dd, hq_c, hq_r, q_len)
+    B = wl.B
+    q_abs = mla.absorb_q(q_c, q_r, pos, dd.w_uk).view(B, q_len, H, 576)
+    for S in (0, 1, 3):
+        z, lse = mla.decode_multi(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=S)
+        o = mla.upproj_v(z.view(B * q_len, H, 512), dd.w_uv).view(B, q_len, H, 128)
+        torch.cuda.synchronize()
+        zn, ln, on = z.cpu().numpy(), lse.cpu().numpy(), o.cpu().numpy()
+        if tol is None:  # fp32 path: absolute 1e-5
+            assert np.abs(zn - ref["z"]).max() <= 1e-5, S
+            assert np.abs(on - ref["o"]).max() <= 1e-5, S
+            assert np.abs(ln - ref["lse"]).max() <= 1e-5, S
+        else:
+            assert _rel(on, ref["o"]) <= tol, ("o", S)
+            assert _rel(zn, ref["z"]) <= tol, ("z", S)
+            assert np.abs(ln - ref["lse"]).max() <= tol, ("lse", S)
+
+
+def test_multi_token_decode_with_one_token_equals_decode():
+    wl = W.make_workload("decode_h16", B=3, H=16, lens=[3000, 77, 1])
+    _note("case multi-token q_len=1")
+    dd = DI.decode_inputs(wl, DEV)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    z1, l1 = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens)
+    z2, l2 = mla.decode_multi(q_abs.view(3, 1, 16, 576), dd.cache, dd.block_table, dd.seq_lens)
+    torch.cuda.synchronize()
+    assert torch.equal(z1, z2.view(3, 16, 512)) and torch.equal(l1, l2.view(3, 16))
+
+
 # --------------------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("H,T", [(16, 200), (128, 130)])
