@@ -83,18 +83,52 @@ def rope_frequencies(dim: int = D_R, base: float = 10000.0) -> np.ndarray:
     return np.power(float(base), -2.0 * m / dim)
 
 
-def rope(x: np.ndarray, positions, base: float = 10000.0) -> np.ndarray:
+YARN_FACTOR = 40.0    # s       ("DeepSeek-V3 Technical Report", §Long Context Extension)
+YARN_ALPHA = 1.0      # alpha
+YARN_BETA = 32.0      # beta
+YARN_ORIG_LEN = 4096  # context length before the extension (4K -> 32K -> 128K)
+
+
+def yarn_frequencies(dim: int = D_R, base: float = 10000.0, factor: float = YARN_FACTOR,
+                     alpha: float = YARN_ALPHA, beta: float = YARN_BETA, orig_len: int = YARN_ORIG_LEN) -> np.ndarray:
+    """YaRN frequencies of the decoupled RoPE path ("DeepSeek-V3" notes, §YaRN 扩展):
+
+        theta'_j = (1 - gamma_j) * theta_j / s + gamma_j * theta_j,
+
+    gamma_j = 1 for the high-frequency groups (frequency kept), 0 for the
+    low-frequency ones (divided by s), in between a smooth transition.  The
+    pages fix s, alpha, beta ("DeepSeek-V3 Technical Report", §Long Context
+    Extension) but only sketch the ramp.  Reading taken: gamma_j is linear in
+    the number of full turns r_j = orig_len * theta_j / (2 pi) that group j
+    makes over the pre-extension context (4K), 0 for r_j <= alpha and 1 for
+    r_j >= beta.
+    """
+    theta = rope_frequencies(dim, base)
+    r = orig_len * theta / (2.0 * math.pi)
+    gamma = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / factor + gamma * theta
+
+
+def yarn_attention_factor(factor: float = YARN_FACTOR) -> float:
+    """0.1 ln s + 1 ("DeepSeek-V3 Technical Report", §Long Context Extension).
+    Reading taken: it multiplies the attention scores once, i.e. the softmax
+    scale becomes (0.1 ln s + 1) / sqrt(192)."""
+    return 0.1 * math.log(factor) + 1.0
+
+
+def rope(x: np.ndarray, positions, base: float = 10000.0, theta=None) -> np.ndarray:
     """Rotate the last axis of x (length 64) at the given positions.
 
     Group m is the interleaved pair (x[2m], x[2m+1]); it is rotated
     counter-clockwise by the angle pos * theta_m (§YaRN 扩展: phi = m*theta_j):
         x'[2m]   = x[2m] cos(phi) - x[2m+1] sin(phi)
         x'[2m+1] = x[2m] sin(phi) + x[2m+1] cos(phi)
-    `positions` broadcasts against x[..., 0].
+    `positions` broadcasts against x[..., 0].  theta: the per-group
+    frequencies (default base^(-2m/64); yarn_frequencies() for YaRN).
     """
     x = np.asarray(x, dtype=np.float64)
     dim = x.shape[-1]
-    theta = rope_frequencies(dim, base)
+    theta = rope_frequencies(dim, base) if theta is None else np.asarray(theta, dtype=np.float64)
     pos = np.asarray(positions, dtype=np.float64)[..., None]
     phi = pos * theta  # [..., dim/2]
     c, s = np.cos(phi), np.sin(phi)
@@ -146,7 +180,7 @@ def absorb_query(q_c, w_uk):
 
 
 def decode_sequence(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, softmax_scale=None, rope_base=10000.0,
-                    query_pos=None, return_probs=False):
+                    query_pos=None, return_probs=False, rope_theta=None):
     """One decode token of one sequence attending to its L cached tokens.
 
     Keys sit at positions 0..L-1 and the query at L-1 unless `query_pos` is
@@ -165,8 +199,8 @@ def decode_sequence(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, softmax_scale=None, rope
         raise ValueError("softmax over an empty set of cached tokens has no value")
     scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
     p = L - 1 if query_pos is None else int(query_pos)
-    k_r_rot = rope(k_r, np.arange(L), rope_base)
-    q_r_rot = rope(q_r, p, rope_base)
+    k_r_rot = rope(k_r, np.arange(L), rope_base, rope_theta)
+    q_r_rot = rope(q_r, p, rope_base, rope_theta)
     o, z, lse, probs = _attend_expanded(q_c, q_r_rot, c_kv, k_r_rot, w_uk, w_uv, scale)
     q_t = absorb_query(q_c, w_uk)
     out = {"o": o, "z": z, "lse": lse, "q_tilde": q_t,
@@ -193,7 +227,7 @@ def decode_batch(q_c, q_r, c_kv_list, k_r_list, w_uk, w_uv, heads=None, **kw):
 
 
 def prefill_causal(q_c, q_r, c_kv, k_r, w_uk, w_uv, rows=None, *, softmax_scale=None,
-                   rope_base=10000.0):
+                   rope_base=10000.0, rope_theta=None):
     """Causal prefill of one sequence of T tokens at positions 0..T-1.
 
     Query row t attends to keys j <= t (the softmax sum of §注意力计算 runs
@@ -211,11 +245,11 @@ def prefill_causal(q_c, q_r, c_kv, k_r, w_uk, w_uv, rows=None, *, softmax_scale=
     T = c_kv.shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
-    k_r_rot = rope(k_r, np.arange(T), rope_base)
+    k_r_rot = rope(k_r, np.arange(T), rope_base, rope_theta)
     res = {"o": [], "z": [], "lse": [], "q_abs": []}
     for t in rows:
         t = int(t)
-        q_r_rot = rope(q_r[t], t, rope_base)
+        q_r_rot = rope(q_r[t], t, rope_base, rope_theta)
         o, z, lse, _ = _attend_expanded(q_c[t], q_r_rot, c_kv[: t + 1], k_r_rot[: t + 1], w_uk, w_uv, scale)
         res["o"].append(o)
         res["z"].append(z)
@@ -231,7 +265,7 @@ def prefill_causal(q_c, q_r, c_kv, k_r, w_uk, w_uv, rows=None, *, softmax_scale=
 # ----------------------------------------------------------------------------
 
 def decode_sequence_absorbed(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, softmax_scale=None,
-                             rope_base=10000.0):
+                             rope_base=10000.0, rope_theta=None):
     """The same decode through the absorbed equations of §潜在向量的作用:
 
     s_{j,i} = (q~_i . c_j + q_i^R . k^R_j) * scale,  z_i = sum_j a c_j,
@@ -242,8 +276,8 @@ def decode_sequence_absorbed(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, softmax_scale=N
     L = c_kv.shape[0]
     scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
     q_t = absorb_query(q_c, w_uk)  # [H,512]
-    k_r_rot = rope(k_r, np.arange(L), rope_base)
-    q_r_rot = rope(q_r, L - 1, rope_base)
+    k_r_rot = rope(k_r, np.arange(L), rope_base, rope_theta)
+    q_r_rot = rope(q_r, L - 1, rope_base, rope_theta)
     s = (q_t @ c_kv.T + q_r_rot @ k_r_rot.T) * scale  # [H,L]
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)

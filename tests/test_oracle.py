@@ -93,6 +93,46 @@ def test_rope_identity_norm_and_relative_position():
     assert abs(orc.rope(x, 0) @ orc.rope(y, 1) - orc.rope(x, 0) @ orc.rope(y, 2)) > 1e-3
 
 
+def test_yarn_constants_match_pages():
+    g = json.load(open(GOLDEN))
+    assert orc.YARN_FACTOR == g["yarn_factor"]["value"]
+    assert orc.YARN_ALPHA == g["yarn_alpha"]["value"]
+    assert orc.YARN_BETA == g["yarn_beta"]["value"]
+    assert orc.YARN_ORIG_LEN == g["context_before_extension"]["value"]
+
+
+def test_yarn_frequencies_regions():
+    """theta'_j = (1-gamma_j) theta_j / s + gamma_j theta_j (§YaRN 扩展).  With
+    s = 1 it is plain RoPE.  With the pages' s = 40, alpha = 1, beta = 32 and a
+    4K original context, group j makes r_j = (4096 / 2 pi) 10^(-j/8) turns:
+    r_10 = 36.6 >= 32 and r_11 = 27.5, r_22 = 1.16 > 1 and r_23 = 0.87 (worked
+    by hand), so groups 0..10 keep their frequency exactly, 23..31 are divided
+    by 40 exactly and 11..22 lie strictly between."""
+    theta = orc.rope_frequencies()
+    np.testing.assert_allclose(orc.yarn_frequencies(factor=1.0), theta, rtol=1e-15)  # up to one rounding
+    y = orc.yarn_frequencies()
+    np.testing.assert_array_equal(y[:11], theta[:11])
+    np.testing.assert_allclose(y[23:], theta[23:] / 40.0, rtol=1e-15)
+    assert np.all(y[11:23] < theta[11:23]) and np.all(y[11:23] > theta[11:23] / 40.0)
+    assert np.all(np.diff(y) < 0)  # frequencies keep their order
+    # still a rotation: relative positions only (§RoPE 数据流)
+    rng = np.random.default_rng(11)
+    x, v = rng.standard_normal(64), rng.standard_normal(64)
+    for m, n, k in [(3, 10, 5), (0, 100000, 30000)]:
+        a = orc.rope(x, m, theta=y) @ orc.rope(v, n, theta=y)
+        b = orc.rope(x, m + k, theta=y) @ orc.rope(v, n + k, theta=y)
+        assert math.isclose(a, b, rel_tol=1e-9, abs_tol=1e-9)
+    # the long-wavelength groups now turn 40x slower: angle at position 40 p
+    # equals plain RoPE's angle at p for those groups
+    np.testing.assert_allclose(orc.rope(x, 4000, theta=y)[46:], orc.rope(x, 100)[46:], rtol=1e-9, atol=1e-12)
+
+
+def test_yarn_attention_factor():
+    assert orc.yarn_attention_factor(1.0) == 1.0
+    assert math.isclose(orc.yarn_attention_factor(40.0), 1.0 + 0.1 * math.log(40.0), rel_tol=1e-15)
+    assert 1.36 < orc.yarn_attention_factor(40.0) < 1.37  # "about 1.369"
+
+
 # --------------------------------------------------------------------------- attention
 
 def test_absorbed_equals_expanded():
