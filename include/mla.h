@@ -94,6 +94,30 @@ typedef struct {
   void* kr;
 } mla_cache;
 
+/*
+ * Rotary frequencies of the decoupled RoPE path (q^R, k^R).  Plain RoPE:
+ * theta_j = base^(-2j/64).  YaRN ("DeepSeek-V3" notes, §YaRN 扩展; the
+ * Technical Report, §Long Context Extension: s = 40, alpha = 1, beta = 32):
+ *   theta'_j = (1 - gamma_j) theta_j / s + gamma_j theta_j,
+ * gamma_j = clamp((r_j - alpha) / (beta - alpha), 0, 1) with r_j =
+ * orig_len * theta_j / (2 pi) the turns group j makes over the context the
+ * model was trained on before the extension (4096).  yarn_factor = 1 is plain
+ * RoPE.  The same frequencies must rotate q^R (mla_absorb_q_rope) and k^R
+ * (mla_cache_write_rope / mla_prefill_causal_rope).  YaRN's attention factor
+ * (mla_yarn_attention_factor) multiplies the softmax scale the caller passes.
+ */
+typedef struct {
+  float base;         /* 10000 */
+  float yarn_factor;  /* s >= 1 */
+  float yarn_alpha;   /* > 0 */
+  float yarn_beta;    /* > yarn_alpha */
+  int32_t orig_len;   /* >= 1 */
+} mla_rope;
+
+/* 0.1 ln s + 1 (the Technical Report, §Long Context Extension): the factor
+ * YaRN applies to the attention scores; s <= 1 gives 1. */
+double mla_yarn_attention_factor(double s);
+
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int32_t status);
 
@@ -113,6 +137,12 @@ mla_status mla_absorb_q(const void* q_c, const void* q_r, const int32_t* pos, co
                         void* q_abs, int32_t N, int32_t H, int32_t dtype, float rope_base,
                         void* stream);
 
+/* mla_absorb_q with the rotary frequencies of `rope` (NULL: base 10000,
+ * no YaRN).  Errors: as mla_absorb_q, and MLA_ERR_INVALID_ARG for a rope
+ * outside the ranges stated at mla_rope. */
+mla_status mla_absorb_q_rope(const void* q_c, const void* q_r, const int32_t* pos, const void* w_uk, void* q_abs,
+                             int32_t N, int32_t H, int32_t dtype, const mla_rope* rope, void* stream);
+
 /*
  * mla_cache_write — store T tokens' (c^KV, RoPE_pos(k^R)) into the pool
  * (§KeyValue: only c^KV and the rotated k^R are cached).
@@ -126,6 +156,11 @@ mla_status mla_absorb_q(const void* q_c, const void* q_r, const int32_t* pos, co
 mla_status mla_cache_write(const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* slot,
                            int32_t T, int32_t in_dtype, const mla_cache* cache, float rope_base,
                            void* stream);
+
+/* mla_cache_write with the rotary frequencies of `rope` (as mla_absorb_q_rope). */
+mla_status mla_cache_write_rope(const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* slot,
+                                int32_t T, int32_t in_dtype, const mla_cache* cache, const mla_rope* rope,
+                                void* stream);
 
 /*
  * Workspace bytes mla_decode needs for B sequences, H heads and
@@ -249,6 +284,11 @@ mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k
                               const mla_cache* cache, const int32_t* block_table_row, int32_t T,
                               int32_t H, float softmax_scale, float rope_base, float* z, float* lse,
                               void* stream);
+
+/* mla_prefill_causal with the rotary frequencies of `rope` (as mla_absorb_q_rope). */
+mla_status mla_prefill_causal_rope(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
+                                   const mla_cache* cache, const int32_t* block_table_row, int32_t T, int32_t H,
+                                   float softmax_scale, const mla_rope* rope, float* z, float* lse, void* stream);
 
 /*
  * mla_upproj_v — o_i = W_i^UV z_i (§潜在向量的作用, value up-projection).

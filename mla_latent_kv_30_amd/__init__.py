@@ -9,5 +9,6 @@ from ._lib import (  # noqa: F401
     D_C, D_NOPE, D_R, D_V, MLA_BF16, MLA_ERR_HIP, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE,
     MLA_F32, MLA_FP8_E4M3, MLA_OK, PAGE, ROW, MLAError, PagedCache, absorb_q, cache_write, decode, decode_merge,
     decode_merge_upproj, decode_multi, decode_partial, decode_workspace,
-    decode_workspace_size, default_softmax_scale, lib, prefill_causal, status_string, upproj_v,
+    decode_workspace_size, default_softmax_scale, lib, prefill_causal, status_string, upproj_v, MlaRope, yarn_rope,
+    yarn_attention_factor,
 )

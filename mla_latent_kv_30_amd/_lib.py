@@ -34,6 +34,23 @@ class MlaCache(ctypes.Structure):
                 ("rows", _vp), ("ckv_fp8", _vp), ("ckv_scale", _vp), ("kr", _vp)]
 
 
+class MlaRope(ctypes.Structure):
+    """mla_rope: rotary frequencies of the decoupled RoPE path (plain or YaRN)."""
+    _fields_ = [("base", _f32), ("yarn_factor", _f32), ("yarn_alpha", _f32), ("yarn_beta", _f32),
+                ("orig_len", _i32)]
+
+
+def yarn_rope(factor: float = 40.0, alpha: float = 1.0, beta: float = 32.0, orig_len: int = 4096,
+              base: float = 10000.0) -> MlaRope:
+    """YaRN frequencies with the long-context configuration (s = 40, alpha = 1, beta = 32, 4K original)."""
+    return MlaRope(base, factor, alpha, beta, orig_len)
+
+
+def yarn_attention_factor(factor: float = 40.0) -> float:
+    """0.1 ln s + 1: multiply the softmax scale by it when the keys use YaRN (mla_yarn_attention_factor)."""
+    return float(lib().mla_yarn_attention_factor(float(factor)))
+
+
 class MLAError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -66,6 +83,16 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_partial.argtypes = list(L.mla_decode.argtypes)
     L.mla_decode_merge.restype = _i32
     L.mla_decode_merge.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_absorb_q_rope.restype = _i32
+    L.mla_absorb_q_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.POINTER(MlaRope), _vp]
+    L.mla_cache_write_rope.restype = _i32
+    L.mla_cache_write_rope.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(MlaCache),
+                                       ctypes.POINTER(MlaRope), _vp]
+    L.mla_prefill_causal_rope.restype = _i32
+    L.mla_prefill_causal_rope.argtypes = [_vp, _vp, _vp, _i32, ctypes.POINTER(MlaCache), _vp, _i32, _i32, _f32,
+                                          ctypes.POINTER(MlaRope), _vp, _vp, _vp]
+    L.mla_yarn_attention_factor.restype = ctypes.c_double
+    L.mla_yarn_attention_factor.argtypes = [ctypes.c_double]
     L.mla_decode_multi.restype = _i32
     L.mla_decode_multi.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                    ctypes.c_size_t, _vp, _vp, _vp]
@@ -174,8 +201,9 @@ class PagedCache:
 
 
 def absorb_q(q_c: torch.Tensor, q_r: torch.Tensor, pos: torch.Tensor, w_uk: torch.Tensor,
-             out: Optional[torch.Tensor] = None, rope_base: float = 10000.0) -> torch.Tensor:
-    """q_abs[N,H,576] = [W_UK^T q_C | RoPE_pos(q_R)] (mla_absorb_q)."""
+             out: Optional[torch.Tensor] = None, rope_base: float = 10000.0,
+             rope: Optional[MlaRope] = None) -> torch.Tensor:
+    """q_abs[N,H,576] = [W_UK^T q_C | RoPE_pos(q_R)] (mla_absorb_q; mla_absorb_q_rope if `rope` is given)."""
     N, H = q_c.shape[0], q_c.shape[1]
     dt = q_c.dtype
     _need(q_c, "q_c", dt, (N, H, D_NOPE))
@@ -185,13 +213,17 @@ def absorb_q(q_c: torch.Tensor, q_r: torch.Tensor, pos: torch.Tensor, w_uk: torc
     if out is None:
         out = torch.empty((N, H, ROW), dtype=dt, device=q_c.device)
     _need(out, "out", dt, (N, H, ROW))
+    if rope is not None:
+        _check(lib().mla_absorb_q_rope(_ptr(q_c), _ptr(q_r), _ptr(pos), _ptr(w_uk), _ptr(out), N, H, _dt_code(dt),
+                                       ctypes.byref(rope), _stream(q_c.device)), "mla_absorb_q_rope")
+        return out
     _check(lib().mla_absorb_q(_ptr(q_c), _ptr(q_r), _ptr(pos), _ptr(w_uk), _ptr(out), N, H, _dt_code(dt),
                               float(rope_base), _stream(q_c.device)), "mla_absorb_q")
     return out
 
 
 def cache_write(cache: PagedCache, c_kv: torch.Tensor, k_r: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor,
-                rope_base: float = 10000.0) -> None:
+                rope_base: float = 10000.0, rope: Optional[MlaRope] = None) -> None:
     """Store T tokens' (c_KV, RoPE_pos(k_R)) at pool rows `slot` (mla_cache_write)."""
     T = c_kv.shape[0]
     dt = cache.input_dtype
@@ -200,6 +232,11 @@ def cache_write(cache: PagedCache, c_kv: torch.Tensor, k_r: torch.Tensor, pos: t
     _need(pos, "pos", torch.int32, (T,))
     _need(slot, "slot", torch.int32, (T,))
     desc = cache.descriptor()
+    if rope is not None:
+        _check(lib().mla_cache_write_rope(_ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(slot), T, _dt_code(dt),
+                                          ctypes.byref(desc), ctypes.byref(rope), _stream(c_kv.device)),
+               "mla_cache_write_rope")
+        return
     _check(lib().mla_cache_write(_ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(slot), T, _dt_code(dt), ctypes.byref(desc),
                                  float(rope_base), _stream(c_kv.device)), "mla_cache_write")
 
@@ -320,7 +357,7 @@ def decode_merge_upproj(seq_lens: torch.Tensor, H: int, workspace: Optional[torc
 def prefill_causal(q_abs: torch.Tensor, c_kv: torch.Tensor, k_r: torch.Tensor, cache: PagedCache,
                    block_table_row: torch.Tensor, pos0: int = 0, softmax_scale: Optional[float] = None,
                    rope_base: float = 10000.0, z: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   want_lse: bool = True):
+                   want_lse: bool = True, rope: Optional[MlaRope] = None):
     """Append T tokens at positions pos0.. and attend causally (mla_prefill_causal)."""
     T, H = q_abs.shape[0], q_abs.shape[1]
     dt = cache.input_dtype
@@ -338,6 +375,11 @@ def prefill_causal(q_abs: torch.Tensor, c_kv: torch.Tensor, k_r: torch.Tensor, c
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
     desc = cache.descriptor()
+    if rope is not None:
+        _check(lib().mla_prefill_causal_rope(_ptr(q_abs), _ptr(c_kv), _ptr(k_r), int(pos0), ctypes.byref(desc),
+                                             _ptr(block_table_row), T, H, scale, ctypes.byref(rope), _ptr(z),
+                                             _ptr(lse), _stream(dev)), "mla_prefill_causal_rope")
+        return z, lse
     _check(lib().mla_prefill_causal(_ptr(q_abs), _ptr(c_kv), _ptr(k_r), int(pos0), ctypes.byref(desc),
                                     _ptr(block_table_row), T, H, scale, float(rope_base), _ptr(z), _ptr(lse),
                                     _stream(dev)), "mla_prefill_causal")

@@ -34,6 +34,28 @@ RopeTable rope_table(float base) {
   return t;
 }
 
+bool rope_ok(const mla_rope& r) {
+  return r.base > 1.0f && isfinite(r.base) && r.yarn_factor >= 1.0f && isfinite(r.yarn_factor) &&
+         r.yarn_alpha > 0.0f && r.yarn_beta > r.yarn_alpha && isfinite(r.yarn_beta) && r.orig_len >= 1;
+}
+
+// Plain frequencies, then the YaRN blend per group: gamma ramps from 0 at
+// alpha turns to 1 at beta turns over the original context.
+RopeTable rope_table(const mla_rope& r) {
+  RopeTable t = rope_table(r.base);
+  if (r.yarn_factor == 1.0f) return t;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int m = 0; m < 32; ++m) {
+    const double turns = (double)r.orig_len * t.theta[m] / two_pi;
+    double gamma = (turns - (double)r.yarn_alpha) / ((double)r.yarn_beta - (double)r.yarn_alpha);
+    gamma = gamma < 0.0 ? 0.0 : (gamma > 1.0 ? 1.0 : gamma);
+    t.theta[m] = (1.0 - gamma) * t.theta[m] / (double)r.yarn_factor + gamma * t.theta[m];
+  }
+  return t;
+}
+
+mla_rope plain_rope(float base) { return mla_rope{base, 1.0f, 1.0f, 32.0f, 4096}; }
+
 bool dtype_ok(int32_t d) { return d == MLA_F32 || d == MLA_BF16; }
 
 mla_status launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -121,27 +143,46 @@ const char* mla_status_string(int32_t s) {
   }
 }
 
-mla_status mla_absorb_q(const void* q_c, const void* q_r, const int32_t* pos, const void* w_uk, void* q_abs,
-                        int32_t N, int32_t H, int32_t dtype, float rope_base, void* stream) {
+double mla_yarn_attention_factor(double s) { return s <= 1.0 ? 1.0 : 0.1 * log(s) + 1.0; }
+
+mla_status mla_absorb_q_rope(const void* q_c, const void* q_r, const int32_t* pos, const void* w_uk, void* q_abs,
+                             int32_t N, int32_t H, int32_t dtype, const mla_rope* rope, void* stream) {
+  const mla_rope r = rope ? *rope : plain_rope(10000.0f);
   if (!q_c || !q_r || !pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
   if (N < 1 || H < 1 || H > MLA_MAX_HEADS || !dtype_ok(dtype)) return MLA_ERR_INVALID_ARG;
-  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  if (!rope_ok(r)) return MLA_ERR_INVALID_ARG;
   if ((long long)N * H > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
-  AbsorbArgs a{q_c, q_r, pos, w_uk, q_abs, N, H, rope_table(rope_base)};
+  AbsorbArgs a{q_c, q_r, pos, w_uk, q_abs, N, H, rope_table(r)};
   return launched(launch_absorb(a, dtype == MLA_F32 ? kKindF32 : kKindBf16, (hipStream_t)stream));
 }
 
-mla_status mla_cache_write(const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* slot, int32_t T,
-                           int32_t in_dtype, const mla_cache* cache, float rope_base, void* stream) {
-  if (!c_kv || !k_r || !pos || !slot || T < 1 || !dtype_ok(in_dtype)) return MLA_ERR_INVALID_ARG;
+mla_status mla_absorb_q(const void* q_c, const void* q_r, const int32_t* pos, const void* w_uk, void* q_abs,
+                        int32_t N, int32_t H, int32_t dtype, float rope_base, void* stream) {
   if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  const mla_rope r = plain_rope(rope_base);
+  return mla_absorb_q_rope(q_c, q_r, pos, w_uk, q_abs, N, H, dtype, &r, stream);
+}
+
+mla_status mla_cache_write_rope(const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* slot,
+                                int32_t T, int32_t in_dtype, const mla_cache* cache, const mla_rope* rope,
+                                void* stream) {
+  const mla_rope r = rope ? *rope : plain_rope(10000.0f);
+  if (!c_kv || !k_r || !pos || !slot || T < 1 || !dtype_ok(in_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!rope_ok(r)) return MLA_ERR_INVALID_ARG;
   const int kind = cache_kind(cache);
   if (kind < 0) return MLA_ERR_INVALID_ARG;
   if (in_dtype == MLA_F32 && kind != kKindF32) return MLA_ERR_INVALID_ARG;
   if (in_dtype == MLA_BF16 && kind == kKindF32) return MLA_ERR_INVALID_ARG;
   CacheWriteArgs a{c_kv, k_r, pos, slot, nullptr, 0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
-                   cache->ckv_scale, cache->kr, rope_table(rope_base)};
+                   cache->ckv_scale, cache->kr, rope_table(r)};
   return launched(launch_cache_write(a, kind, (hipStream_t)stream));
+}
+
+mla_status mla_cache_write(const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* slot, int32_t T,
+                           int32_t in_dtype, const mla_cache* cache, float rope_base, void* stream) {
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  const mla_rope r = plain_rope(rope_base);
+  return mla_cache_write_rope(c_kv, k_r, pos, slot, T, in_dtype, cache, &r, stream);
 }
 
 size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits) {
@@ -295,18 +336,28 @@ mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int
 mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
                               const mla_cache* cache, const int32_t* block_table_row, int32_t T, int32_t H,
                               float softmax_scale, float rope_base, float* z, float* lse, void* stream) {
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  const mla_rope r = plain_rope(rope_base);
+  return mla_prefill_causal_rope(q_abs, c_kv, k_r, pos0, cache, block_table_row, T, H, softmax_scale, &r, z, lse,
+                                 stream);
+}
+
+mla_status mla_prefill_causal_rope(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,
+                                   const mla_cache* cache, const int32_t* block_table_row, int32_t T, int32_t H,
+                                   float softmax_scale, const mla_rope* rope, float* z, float* lse, void* stream) {
+  const mla_rope rp = rope ? *rope : plain_rope(10000.0f);
   if (!q_abs || !block_table_row || !z || !c_kv || !k_r) return MLA_ERR_INVALID_ARG;
   if (T < 1 || H < 1 || H > MLA_MAX_HEADS || pos0 < 0) return MLA_ERR_INVALID_ARG;
   if ((long long)pos0 + T > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
-  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  if (!rope_ok(rp)) return MLA_ERR_INVALID_ARG;
   const int kind = cache_kind(cache);
   if (kind < 0) return MLA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   // 1. append the T new tokens: position pos0 + t, slot from the block-table row
   CacheWriteArgs w{c_kv,         k_r, nullptr, nullptr, block_table_row, pos0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
-                   cache->ckv_scale, cache->kr, rope_table(rope_base)};
+                   cache->ckv_scale, cache->kr, rope_table(rp)};
   mla_status st = launched(launch_cache_write(w, kind, s));
   if (st != MLA_OK) return st;
   // 2. causal attention: query row t sees cached tokens 0 .. pos0 + t

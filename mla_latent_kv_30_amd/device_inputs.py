@@ -37,7 +37,7 @@ def _t(x: np.ndarray, dtype, device) -> torch.Tensor:
 
 
 def decode_inputs(wl: W.Workload, device="cuda", spare_pages: int = 0, poison: bool = False,
-                  keep_host: bool = True, latents: Optional[tuple] = None) -> DeviceDecode:
+                  keep_host: bool = True, latents: Optional[tuple] = None, rope=None) -> DeviceDecode:
     """All inputs of a decode workload on `device`, cache filled through
     mla_cache_write (so k_R is rotated by the library at its position)."""
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
@@ -54,7 +54,7 @@ def decode_inputs(wl: W.Workload, device="cuda", spare_pages: int = 0, poison: b
     for s0 in range(0, c_all.shape[0], step):
         s1 = min(s0 + step, c_all.shape[0])
         _lib.cache_write(cache, _t(c_all[s0:s1], dt, device), _t(k_all[s0:s1], dt, device), pos_tok[s0:s1],
-                         slots[s0:s1])
+                         slots[s0:s1], rope=rope)
     host = {}
     if keep_host:
         host = dict(q_c=q_c, q_r=q_r, w_uk=w_uk, w_uv=w_uv, c_kv=c_all, k_r=k_all, offsets=layout.offsets)

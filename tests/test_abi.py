@@ -3,6 +3,7 @@ every function include/mla.h declares, and rejects bad arguments on the host
 before any HIP call (status codes, no launch)."""
 
 import ctypes
+import math
 
 import pytest
 
@@ -108,3 +109,27 @@ def test_prefill_and_upproj_reject_bad_arguments():
     assert L.mla_upproj_v(NULL, P, P, 1, 16, 1, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
     assert L.mla_upproj_v(P, P, P, 1, 16, 2, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
     assert L.mla_upproj_v(P, P, P, 1, 0, 1, 0, NULL) == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_yarn_attention_factor_host_helper():
+    """The library's 0.1 ln s + 1 (a host function, no GPU) against the oracle's."""
+    from oracle import mla_oracle as orc
+    assert _lib.yarn_attention_factor(1.0) == 1.0
+    assert math.isclose(_lib.yarn_attention_factor(40.0), orc.yarn_attention_factor(40.0), rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("rope", [
+    (10000.0, 0.5, 1.0, 32.0, 4096),   # s < 1
+    (10000.0, 40.0, 32.0, 32.0, 4096),  # beta <= alpha
+    (10000.0, 40.0, 0.0, 32.0, 4096),   # alpha <= 0
+    (10000.0, 40.0, 1.0, 32.0, 0),      # no original context
+    (1.0, 40.0, 1.0, 32.0, 4096),       # base <= 1
+])
+def test_rope_variants_reject_bad_frequency_settings(rope):
+    r = _lib.MlaRope(*rope)
+    assert L.mla_absorb_q_rope(P, P, P, P, P, 1, 16, _lib.MLA_BF16, ctypes.byref(r), NULL) == _lib.MLA_ERR_INVALID_ARG
+    desc = _lib.MlaCache(_lib.MLA_BF16, 4, 64, 0, P, None, None, None)
+    assert L.mla_cache_write_rope(P, P, P, P, 1, _lib.MLA_BF16, ctypes.byref(desc), ctypes.byref(r),
+                                  NULL) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_prefill_causal_rope(P, P, P, 0, ctypes.byref(desc), P, 4, 16, 0.07, ctypes.byref(r), P, None,
+                                     NULL) == _lib.MLA_ERR_INVALID_ARG

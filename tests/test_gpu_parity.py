@@ -444,6 +444,77 @@ def test_multi_token_decode_with_one_token_equals_decode():
     assert torch.equal(z1, z2.view(3, 16, 512)) and torch.equal(l1, l2.view(3, 16))
 
 
+# --------------------------------------------------------------------------- YaRN
+
+@pytest.mark.parametrize("name,lens,tol", [
+    ("decode_h16", [70, 1000, 5000], 2e-2),
+    ("tiny_f32", [64, 300], None),
+])
+def test_yarn_decode_matches_oracle(name, lens, tol):
+    """k^R written and q^R rotated with YaRN frequencies (s = 40, alpha = 1,
+    beta = 32, 4K original context), softmax scale times 0.1 ln s + 1."""
+    wl = W.make_workload(name, B=len(lens), H=16, lens=lens)
+    _note(f"case YaRN decode {name} lens={lens}")
+    rope = mla.yarn_rope()
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=1, rope=rope)
+    scale = mla.default_softmax_scale() * mla.yarn_attention_factor(40.0)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk, rope=rope)
+    z, lse = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, softmax_scale=scale)
+    o = mla.upproj_v(z, dd.w_uv)
+    torch.cuda.synchronize()
+    h = dd.host
+    off = h["offsets"]
+    theta = orc.yarn_frequencies()
+    oscale = orc.default_softmax_scale() * orc.yarn_attention_factor(40.0)
+    for b in range(wl.B):
+        r = orc.decode_sequence(h["q_c"][b], h["q_r"][b], h["c_kv"][off[b]:off[b + 1]], h["k_r"][off[b]:off[b + 1]],
+                                h["w_uk"], h["w_uv"], softmax_scale=oscale, rope_theta=theta)
+        if tol is None:
+            assert np.abs(o[b].cpu().numpy() - r["o"]).max() <= 1e-5, b
+            assert np.abs(q_abs[b].cpu().numpy() - r["q_abs"]).max() <= 1e-5, b
+        else:
+            assert _rel(o[b].cpu().numpy(), r["o"]) <= tol, b
+            assert _rel(z[b].cpu().numpy(), r["z"]) <= tol, b
+            assert np.abs(lse[b].cpu().numpy() - r["lse"]).max() <= tol, b
+            assert _rel(q_abs[b].float().cpu().numpy(), r["q_abs"]) <= 1e-2, b
+    # the rotated keys in the cache are the oracle's YaRN rotation
+    rows = dd.cache.rows.float().cpu().numpy().reshape(-1, 576)[dd.layout.slots]
+    kr_ref = orc.rope(h["k_r"], dd.layout.positions, theta=theta)
+    assert np.abs(rows[:, 512:] - kr_ref).max() <= (2 ** -8 if tol else 1e-6) * np.abs(kr_ref).max()
+
+
+def test_yarn_prefill_matches_oracle():
+    T, H = 150, 16
+    wl = W.make_workload("prefill_h128", H=H, lens=[T])
+    _note("case YaRN prefill")
+    dt = torch.bfloat16
+    w_uk, w_uv = W.weights(wl)
+    q_c, q_r = W.queries(wl)
+    c, k = W.sequence_latents(wl, 0)
+    npg = (T + 63) // 64
+    cache = mla.PagedCache(npg, dt, DEV, fill=float("nan"))
+    bt = torch.arange(npg, dtype=torch.int32, device=DEV)
+    td = lambda x: torch.from_numpy(x).to(DEV, dt)
+    rope = mla.yarn_rope()
+    scale = mla.default_softmax_scale() * mla.yarn_attention_factor(40.0)
+    q_abs = mla.absorb_q(td(q_c), td(q_r), torch.arange(T, dtype=torch.int32, device=DEV), td(w_uk), rope=rope)
+    z, lse = mla.prefill_causal(q_abs, td(c), td(k), cache, bt, softmax_scale=scale, rope=rope)
+    torch.cuda.synchronize()
+    ref = orc.prefill_causal(q_c, q_r, c, k, w_uk, w_uv, softmax_scale=orc.default_softmax_scale() *
+                             orc.yarn_attention_factor(40.0), rope_theta=orc.yarn_frequencies())
+    assert _rel(z.cpu().numpy(), ref["z"]) <= 2e-2
+    assert np.abs(lse.cpu().numpy() - ref["lse"]).max() <= 2e-2
+
+
+def test_yarn_with_factor_one_is_plain_rope():
+    wl = W.make_workload("decode_h16", B=2, H=16, lens=[300, 65])
+    dd = DI.decode_inputs(wl, DEV)
+    plain = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    one = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk, rope=mla.MlaRope(10000.0, 1.0, 1.0, 32.0, 4096))
+    torch.cuda.synchronize()
+    assert torch.equal(plain, one)
+
+
 # --------------------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("H,T", [(16, 200), (128, 130)])
