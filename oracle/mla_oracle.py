@@ -28,6 +28,11 @@ d_h^R = 64 (qk_rope_head_dim), d_v = 128 (v_head_dim).
     w_uk  [H, 128, 512]   head i's row block of the key up-projection
     w_uv  [H, 128, 512]   head i's row block of the value up-projection
 
+Around the attention it also gives the projections the pages define: the
+cache append c^KV = W^DKV h, k^R = RoPE(W^KR h) (§KeyValue), the query path
+c^Q = W^DQ h, q_i^C = W_i^UQ c^Q, q_i^R = RoPE(W_i^QR c^Q) (§Query), the
+output u = W^O [o_1; ...; o_H] (§注意力计算) and W^O with W^UV folded into it.
+
 Readings of points the pages leave open (each is restated where it is used):
   * RoPE rotates interleaved pairs (2m, 2m+1) counter-clockwise by pos*theta_m,
     theta_m = base^(-2m/64).  The pages give the per-pair angle (§YaRN 扩展)
@@ -42,6 +47,9 @@ Readings of points the pages leave open (each is restated where it is used):
     tile rule of "DeepSeek-V3 Technical Report", process-cxr.github.io,
     §Fine-grained quantization), scale = amax/448 computed in fp32, 1.0 for an
     all-zero tile; codes are round-to-nearest-even with saturation.
+  * No normalisation sits between a down-projection and its up-projection:
+    the equations of §KeyValue and §Query show none.  The model width d is
+    not given by the pages; every function here takes it from its inputs.
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle.py (closed forms, identities, a textbook attention routine,
@@ -374,3 +382,107 @@ def dequantize_latent_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """c~ = value(code) * scale of its (token, 128-channel) tile, in fp64."""
     vals = e4m3_decode(codes).reshape(codes.shape[0], D_C // FP8_TILE, FP8_TILE)
     return (vals * np.asarray(scales, dtype=np.float64)[:, :, None]).reshape(codes.shape[0], D_C)
+
+
+# ----------------------------------------------------------------------------
+# Projections before and after the attention
+# ----------------------------------------------------------------------------
+# Shapes are generic (the tests also run them at toy widths).  Head i's
+# blocks of the stacked matrices are contiguous row (or column) ranges:
+#   w_uq [H*d_h,  d_c'], rows i*d_h   .. (i+1)*d_h   - 1 are W_i^UQ
+#   w_qr [H*d_hR, d_c'], rows i*d_hR  .. (i+1)*d_hR  - 1 are W_i^QR
+#   w_o  [d, H*d_v],     columns i*d_v .. (i+1)*d_v - 1 meet o_i
+# Readings: the equations of §KeyValue and §Query carry no normalisation
+# between the down- and up-projections, so none is applied here.
+
+def kv_projection(h, w_dkv, w_kr, positions, *, rope_base=10000.0, rope_theta=None):
+    """What one token appends to the cache (§KeyValue):
+
+        c_t^KV = W^DKV h_t,    k_t^R = RoPE_t(W^KR h_t).
+
+    h [T, d] (row t is h_t), w_dkv [d_c, d], w_kr [d_hR, d], positions [T].
+    Returns c_kv [T, d_c], k_r [T, d_hR] before rotation and k_r_rot after.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    c_kv = h @ np.asarray(w_dkv, dtype=np.float64).T
+    k_r = h @ np.asarray(w_kr, dtype=np.float64).T
+    k_r_rot = rope(k_r, np.asarray(positions), rope_base, rope_theta)
+    return {"c_kv": c_kv, "k_r": k_r, "k_r_rot": k_r_rot}
+
+
+def query_projection(h, w_dq, w_uq, w_qr, positions, heads, *, rope_base=10000.0, rope_theta=None):
+    """The per-head queries of a token (§Query):
+
+        c_t^Q = W^DQ h_t,  q_{t,i}^C = W_i^UQ c_t^Q,  q_{t,i}^R = RoPE_t(W_i^QR c_t^Q).
+
+    h [T, d], w_dq [d_c', d], w_uq [H*d_h, d_c'], w_qr [H*d_hR, d_c'].
+    Returns c_q [T, d_c'], q_c [T, H, d_h], q_r [T, H, d_hR] before rotation
+    and q_r_rot after.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    w_uq = np.asarray(w_uq, dtype=np.float64)
+    w_qr = np.asarray(w_qr, dtype=np.float64)
+    T, H = h.shape[0], int(heads)
+    dh, dhr = w_uq.shape[0] // H, w_qr.shape[0] // H
+    c_q = h @ np.asarray(w_dq, dtype=np.float64).T
+    q_c = np.empty((T, H, dh))
+    q_r = np.empty((T, H, dhr))
+    for i in range(H):
+        q_c[:, i] = c_q @ w_uq[i * dh:(i + 1) * dh].T
+        q_r[:, i] = c_q @ w_qr[i * dhr:(i + 1) * dhr].T
+    pos = np.asarray(positions)[:, None]  # the same angle for every head of a token
+    q_r_rot = rope(q_r, pos, rope_base, rope_theta)
+    return {"c_q": c_q, "q_c": q_c, "q_r": q_r, "q_r_rot": q_r_rot}
+
+
+def output_projection(o, w_o):
+    """u_t = W^O [o_{t,1}; ...; o_{t,H}] (§注意力计算): the head outputs are
+    concatenated in head order and projected back to the model width.
+
+    o [T, H, d_v], w_o [d, H*d_v] -> u [T, d].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    T, H, dv = o.shape
+    cat = o.reshape(T, H * dv)
+    return cat @ np.asarray(w_o, dtype=np.float64).T
+
+
+def fold_wuv_into_wo(w_uv, w_o):
+    """The output matrix with the value up-projection absorbed into it
+    ("DeepSeek-V3 技术报告精读", §一 MLA, KV 权重吸收; o_i = W_i^UV z_i from
+    §潜在向量的作用):
+
+        W' = W^O blockdiag(W_1^UV, ..., W_H^UV),   u = W' [z_1; ...; z_H].
+
+    w_uv [H, d_v, d_c], w_o [d, H*d_v] -> W' [d, H*d_c]; column block i is
+    (columns i*d_v.. of W^O) @ W_i^UV.
+    """
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    w_o = np.asarray(w_o, dtype=np.float64)
+    H, dv, dc = w_uv.shape
+    out = np.zeros((w_o.shape[0], H * dc))
+    for i in range(H):
+        out[:, i * dc:(i + 1) * dc] = w_o[:, i * dv:(i + 1) * dv] @ w_uv[i]
+    return out
+
+
+def layer_decode_from_hidden(h_seq, w_dkv, w_kr, w_dq, w_uq, w_qr, w_uk, w_uv, w_o, *,
+                             softmax_scale=None, rope_base=10000.0, rope_theta=None):
+    """The attention layer's output for the newest token of one sequence,
+    from the hidden states h_0 .. h_{L-1} of all its tokens (positions
+    0..L-1): every token's (c^KV, k^R) from kv_projection, the newest token's
+    queries from query_projection, the expanded attention of decode_sequence,
+    and output_projection.  Returns a dict with u [d], o [H, d_v], z [H, d_c],
+    and the pieces c_kv, k_r (before rotation), q_c, q_r (before rotation).
+    """
+    h_seq = np.asarray(h_seq, dtype=np.float64)
+    L = h_seq.shape[0]
+    H = np.asarray(w_uk).shape[0]
+    kv = kv_projection(h_seq, w_dkv, w_kr, np.arange(L), rope_base=rope_base, rope_theta=rope_theta)
+    q = query_projection(h_seq[L - 1:], w_dq, w_uq, w_qr, [L - 1], H, rope_base=rope_base,
+                         rope_theta=rope_theta)
+    att = decode_sequence(q["q_c"][0], q["q_r"][0], kv["c_kv"], kv["k_r"], w_uk, w_uv,
+                          softmax_scale=softmax_scale, rope_base=rope_base, rope_theta=rope_theta)
+    u = output_projection(att["o"][None], w_o)[0]
+    return {"u": u, "o": att["o"], "z": att["z"], "c_kv": kv["c_kv"], "k_r": kv["k_r"],
+            "q_c": q["q_c"][0], "q_r": q["q_r"][0]}

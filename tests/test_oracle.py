@@ -333,3 +333,146 @@ def test_quantiser_error_bound():
     rel = np.abs(dq - c)[normal] / np.abs(c)[normal]
     assert rel.max() <= 2.0 ** -4 + 1e-12  # half a unit in the last place of a 3-bit mantissa
     assert np.abs(dq - c)[~normal].max() <= (2.0 ** -10 * s[~normal]).max() * (1 + 1e-9)
+
+
+# --------------------------------------------------------------------------- projections
+
+def _rot_loop(vec, pos, base=10000.0):
+    """Interleaved-pair rotation written out with scalar cos/sin."""
+    n = len(vec)
+    out = [0.0] * n
+    for m in range(n // 2):
+        ang = pos * base ** (-2.0 * m / n)
+        out[2 * m] = vec[2 * m] * math.cos(ang) - vec[2 * m + 1] * math.sin(ang)
+        out[2 * m + 1] = vec[2 * m] * math.sin(ang) + vec[2 * m + 1] * math.cos(ang)
+    return out
+
+
+def test_projections_bruteforce_loops():
+    """§KeyValue, §Query, §注意力计算 and the W^O fold at toy widths, against
+    scalar index loops (no NumPy linear algebra in the expected values)."""
+    rng = np.random.default_rng(21)
+    T, d, dc, dhr, dcq, H, dh, dv = 3, 7, 6, 4, 5, 3, 2, 3
+    h = _rand(rng, T, d)
+    w_dkv, w_kr = _rand(rng, dc, d), _rand(rng, dhr, d)
+    w_dq, w_uq, w_qr = _rand(rng, dcq, d), _rand(rng, H * dh, dcq), _rand(rng, H * dhr, dcq)
+    pos = np.array([0, 5, 17])
+    kv = orc.kv_projection(h, w_dkv, w_kr, pos)
+    q = orc.query_projection(h, w_dq, w_uq, w_qr, pos, H)
+    for t in range(T):
+        c = [sum(w_dkv[a][k] * h[t][k] for k in range(d)) for a in range(dc)]
+        kr = [sum(w_kr[a][k] * h[t][k] for k in range(d)) for a in range(dhr)]
+        np.testing.assert_allclose(kv["c_kv"][t], c, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(kv["k_r_rot"][t], _rot_loop(kr, pos[t]), rtol=1e-12, atol=1e-12)
+        cq = [sum(w_dq[a][k] * h[t][k] for k in range(d)) for a in range(dcq)]
+        np.testing.assert_allclose(q["c_q"][t], cq, rtol=1e-13, atol=1e-13)
+        for i in range(H):
+            qc = [sum(w_uq[i * dh + a][k] * cq[k] for k in range(dcq)) for a in range(dh)]
+            qr = [sum(w_qr[i * dhr + a][k] * cq[k] for k in range(dcq)) for a in range(dhr)]
+            np.testing.assert_allclose(q["q_c"][t, i], qc, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(q["q_r"][t, i], qr, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(q["q_r_rot"][t, i], _rot_loop(qr, pos[t]), rtol=1e-12, atol=1e-12)
+    o = _rand(rng, T, H, dv)
+    w_o = _rand(rng, d, H * dv)
+    u = orc.output_projection(o, w_o)
+    for t in range(T):
+        ref = [sum(w_o[r][i * dv + j] * o[t][i][j] for i in range(H) for j in range(dv)) for r in range(d)]
+        np.testing.assert_allclose(u[t], ref, rtol=1e-12, atol=1e-12)
+    w_uv = _rand(rng, H, dv, dc)
+    wf = orc.fold_wuv_into_wo(w_uv, w_o)
+    for r in range(d):
+        for i in range(H):
+            for c in range(dc):
+                ref = sum(w_o[r][i * dv + j] * w_uv[i][j][c] for j in range(dv))
+                assert abs(wf[r, i * dc + c] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_projection_selection_matrices():
+    """Selection matrices make every projection an exact gather, so a
+    transposed operand or a misplaced head block shows as a wrong index."""
+    rng = np.random.default_rng(22)
+    d, H = 1024, 4
+    h = _rand(rng, 2, d)
+    sel_c = rng.permutation(d)[:512]
+    sel_r = rng.permutation(d)[:64]
+    w_dkv = np.eye(d)[sel_c]
+    w_kr = np.eye(d)[sel_r]
+    kv = orc.kv_projection(h, w_dkv, w_kr, [0, 0])
+    np.testing.assert_array_equal(kv["c_kv"], h[:, sel_c])
+    np.testing.assert_array_equal(kv["k_r_rot"], h[:, sel_r])  # RoPE at position 0 is the identity
+    # W^DQ picks 1536 entries; head i's W^UQ block picks 128 of c^Q and scales by i+1
+    sel_q = rng.permutation(d)[:768]
+    w_dq = np.eye(d)[sel_q]
+    blk = [rng.permutation(768)[:128] for _ in range(H)]
+    w_uq = np.concatenate([(i + 1) * np.eye(768)[blk[i]] for i in range(H)])
+    w_qr = np.concatenate([np.eye(768)[blk[i][:64]] for i in range(H)])
+    q = orc.query_projection(h, w_dq, w_uq, w_qr, [0, 0], H)
+    for i in range(H):
+        np.testing.assert_array_equal(q["q_c"][:, i], (i + 1) * h[:, sel_q][:, blk[i]])
+        np.testing.assert_array_equal(q["q_r_rot"][:, i], h[:, sel_q][:, blk[i][:64]])
+    # W^O = identity: u is the concatenation of the heads in head order
+    o = _rand(rng, 2, H, 128)
+    np.testing.assert_array_equal(orc.output_projection(o, np.eye(H * 128)), o.reshape(2, -1))
+    # W^O that reads only head 2's block
+    w_o = np.zeros((128, H * 128))
+    w_o[:, 2 * 128:3 * 128] = np.eye(128)
+    np.testing.assert_array_equal(orc.output_projection(o, w_o), o[:, 2])
+    # the fold of W_UV into an identity W^O is blockdiag(W_UV)
+    w_uv = _rand(rng, H, 128, 512)
+    wf = orc.fold_wuv_into_wo(w_uv, np.eye(H * 128))
+    for i in range(H):
+        for k in range(H):
+            blockv = wf[i * 128:(i + 1) * 128, k * 512:(k + 1) * 512]
+            np.testing.assert_array_equal(blockv, w_uv[i] if i == k else np.zeros((128, 512)))
+
+
+def test_query_rotation_uses_the_token_position():
+    """q^R of every head of token t turns by t * theta; moving the token and
+    a key by the same offset keeps their position score (RoPE relative
+    property through the projections)."""
+    rng = np.random.default_rng(23)
+    d, H = 96, 2
+    h = _rand(rng, 1, d)
+    w = dict(w_dq=_rand(rng, 40, d), w_uq=_rand(rng, H * 128, 40), w_qr=_rand(rng, H * 64, 40))
+    w_kr = _rand(rng, 64, d)
+    hk = _rand(rng, 1, d)
+    s = []
+    for shift in (0, 37):
+        q = orc.query_projection(h, **w, positions=[100 + shift], heads=H)
+        k = orc.kv_projection(hk, np.zeros((512, d)), w_kr, [60 + shift])
+        s.append(q["q_r_rot"][0] @ k["k_r_rot"][0])
+    np.testing.assert_allclose(s[0], s[1], rtol=1e-10)
+
+
+def test_fold_equals_two_step_output():
+    """u = W^O [W_i^UV z_i] equals the folded W' [z_i] (associativity, the
+    absorption the pages state for W^UV)."""
+    rng = np.random.default_rng(24)
+    H, d, T = 3, 200, 4
+    w_uv = _rand(rng, H, 128, 512, std=512 ** -0.5)
+    w_o = _rand(rng, d, H * 128, std=(H * 128) ** -0.5)
+    z = _rand(rng, T, H, 512)
+    o = np.einsum("hdc,thc->thd", w_uv, z)
+    u2 = orc.output_projection(o, w_o)
+    u1 = z.reshape(T, H * 512) @ orc.fold_wuv_into_wo(w_uv, w_o).T
+    np.testing.assert_allclose(u1, u2, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_from_hidden_expanded_equals_absorbed_and_folded():
+    """The layer output of the newest token from hidden states, expanded
+    form (per-head keys and values), equals the absorbed form (q~, latent z)
+    followed by the folded output matrix W^O blockdiag(W^UV)."""
+    rng = np.random.default_rng(25)
+    L, d, H = 13, 160, 3
+    h = _rand(rng, L, d)
+    W = dict(w_dkv=_rand(rng, 512, d, std=d ** -0.5), w_kr=_rand(rng, 64, d, std=d ** -0.5),
+             w_dq=_rand(rng, 96, d, std=d ** -0.5), w_uq=_rand(rng, H * 128, 96, std=96 ** -0.5),
+             w_qr=_rand(rng, H * 64, 96, std=96 ** -0.5), w_uk=_rand(rng, H, 128, 512, std=512 ** -0.5),
+             w_uv=_rand(rng, H, 128, 512, std=512 ** -0.5), w_o=_rand(rng, d, H * 128, std=(H * 128) ** -0.5))
+    r = orc.layer_decode_from_hidden(h, **W)
+    ab = orc.decode_sequence_absorbed(r["q_c"], r["q_r"], r["c_kv"], r["k_r"], W["w_uk"], W["w_uv"])
+    u = orc.fold_wuv_into_wo(W["w_uv"], W["w_o"]) @ ab["z"].reshape(-1)
+    np.testing.assert_allclose(r["u"], u, rtol=1e-10, atol=1e-12)
+    # a one-token sequence attends only to itself: o_i = W_i^UV c^KV_0
+    r1 = orc.layer_decode_from_hidden(h[:1], **W)
+    np.testing.assert_allclose(r1["o"], np.einsum("hdc,c->hd", W["w_uv"], h[0] @ W["w_dkv"].T), atol=1e-12)
