@@ -266,7 +266,6 @@ mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H
                                    int32_t w_dtype, void* o, int32_t o_dtype, void* stream);
 
 /*
- * mla_prefill_causal/*
  * mla_prefill_causal — T new tokens of one sequence, at positions
  * pos0 .. pos0+T-1, are written into the cache and attend causally: query t
  * sees cached tokens 0 .. pos0+t inclusive (§注意力计算 sums up to the
@@ -300,6 +299,103 @@ mla_status mla_prefill_causal_rope(const void* q_abs, const void* c_kv, const vo
  */
 mla_status mla_upproj_v(const float* z, const void* w_uv, void* o, int32_t N, int32_t H, int32_t w_dtype,
                         int32_t o_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Projections around the attention.  All take bf16 operands stored K-major
+ * (each row contiguous along the contraction) and accumulate in fp32 on the
+ * matrix cores.  The model width d is the caller's (the pages do not fix
+ * it); it must be a multiple of 64.  A workspace is device memory the caller
+ * owns, at least the size the matching *_workspace_size function returns
+ * (that size depends on the arguments and the current device's compute-unit
+ * count only); it is scratch that the call overwrites.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes mla_linear needs for an N x M output with contraction K
+ * (0: none; also 0 for shapes mla_linear rejects). */
+size_t mla_linear_workspace_size(int32_t N, int32_t M, int32_t K);
+
+/*
+ * mla_linear — Y = X W^T, the projection every equation of §KeyValue,
+ * §Query and §注意力计算 applies to a token's vector (y = W x per row of X).
+ * W is given as two row blocks and Y is written as the matching two column
+ * blocks, so that a pair of projections that read the same input (W^DKV and
+ * W^KR, or W^UQ and W^QR) runs as one product:
+ *   x   [N][K] bf16
+ *   w0  [M0][K] bf16, w1 [M1][K] bf16 (M1 = 0: w1 and y1 are ignored)
+ *   y0  [N][M0], y1 [N][M1] out, in out_dtype (MLA_F32 or MLA_BF16)
+ * Shapes: N >= 1; K >= 64, K % 64 == 0; M0 >= 32, M0 % 32 == 0; M1 >= 0,
+ * M1 % 32 == 0; each operand under 2 GiB.  The workspace needs
+ * mla_linear_workspace_size(N, M0 + M1, K) bytes.
+ * Errors: MLA_ERR_INVALID_ARG (NULL pointer, a shape outside the above,
+ * another dtype); MLA_ERR_WORKSPACE.
+ */
+mla_status mla_linear(const void* x, const void* w0, int32_t M0, const void* w1, int32_t M1, void* y0, void* y1,
+                      int32_t N, int32_t K, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Workspace bytes of mla_kv_append (cache_dtype: the cache's dtype). */
+size_t mla_kv_append_workspace_size(int32_t T, int32_t d, int32_t cache_dtype);
+
+/*
+ * mla_kv_append — what T new tokens add to the cache (§KeyValue):
+ * c^KV = W^DKV h and k^R = RoPE_pos(W^KR h), stored (and quantised for an
+ * fp8 cache) exactly as mla_cache_write_rope stores them.
+ *   h      [T][d] bf16 hidden states
+ *   w_dkv  [512][d] bf16, w_kr [64][d] bf16
+ *   pos, slot, cache, rope: as mla_cache_write_rope (rope NULL: base 10000)
+ * c^KV and k^R pass through the workspace in the cache's input precision
+ * (fp32 for an fp32 cache, bf16 otherwise).
+ * Errors: MLA_ERR_INVALID_ARG (NULL, d % 64 != 0, a bad cache or rope);
+ * MLA_ERR_WORKSPACE.
+ */
+mla_status mla_kv_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, const int32_t* slot,
+                         int32_t T, int32_t d, const mla_cache* cache, const mla_rope* rope, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of mla_q_project. */
+size_t mla_q_project_workspace_size(int32_t T, int32_t d, int32_t dcq, int32_t H);
+
+/*
+ * mla_q_project — the queries of T tokens (§Query): c^Q = W^DQ h, then for
+ * every head q_i^C = W_i^UQ c^Q and the position query W_i^QR c^Q before its
+ * rotation (mla_absorb_q applies RoPE_pos and the absorption).
+ *   h     [T][d] bf16
+ *   w_dq  [dcq][d] bf16          (dcq = d_c', 1536 in the pages' model)
+ *   w_uq  [H*128][dcq] bf16      rows 128 i .. 128 i + 127 are W_i^UQ
+ *   w_qr  [H*64][dcq] bf16       rows 64 i .. 64 i + 63 are W_i^QR
+ *   q_c   [T][H][128], q_r [T][H][64] out, in out_dtype
+ * c^Q is kept in the workspace in bf16.  dcq % 64 == 0, H in [1,128].
+ * Errors: MLA_ERR_INVALID_ARG; MLA_ERR_WORKSPACE.
+ */
+mla_status mla_q_project(const void* h, const void* w_dq, const void* w_uq, const void* w_qr, void* q_c, void* q_r,
+                         int32_t T, int32_t d, int32_t dcq, int32_t H, int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * mla_output_proj — u = W^O [o_1; ...; o_H] (§注意力计算), N tokens.
+ *   x  [N][K] bf16: the head outputs o [N][H][128] (K = 128 H), or the
+ *      latent outputs z [N][H][512] in bf16 (K = 512 H) with the folded
+ *      matrix of mla_fold_wuv_wo
+ *   w  [d][K] bf16: W^O, or the folded matrix
+ *   u  [N][d] out, in out_dtype
+ * Workspace: mla_linear_workspace_size(N, d, K) bytes.  K % 128 == 0 and
+ * d % 32 == 0, otherwise as mla_linear.
+ */
+mla_status mla_output_proj(const void* x, const void* w, void* u, int32_t N, int32_t K, int32_t d, int32_t out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_fold_wuv_wo — W' = W^O blockdiag(W_1^UV, ..., W_H^UV), the output
+ * matrix with the value up-projection absorbed into it ("DeepSeek-V3
+ * 技术报告精读", §一 MLA, KV 权重吸收), so that u = W' [z_1; ...; z_H].
+ *   w_uv   [H][128][512] bf16, w_o [d][128 H] bf16
+ *   w_fold [d][512 H] bf16 out (fp32 sums, rounded once)
+ * A one-time weight transform.  W' holds four times the elements of W^O, so
+ * for decode the two-step order (mla_decode_merge_upproj, then
+ * mla_output_proj with W^O) moves fewer bytes.
+ * Errors: MLA_ERR_INVALID_ARG (NULL, H not in [1,128], d < 1).
+ */
+mla_status mla_fold_wuv_wo(const void* w_uv, const void* w_o, void* w_fold, int32_t H, int32_t d, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,5 +10,6 @@ from ._lib import (  # noqa: F401
     MLA_F32, MLA_FP8_E4M3, MLA_OK, PAGE, ROW, MLAError, PagedCache, absorb_q, cache_write, decode, decode_merge,
     decode_merge_upproj, decode_multi, decode_partial, decode_workspace,
     decode_workspace_size, default_softmax_scale, lib, prefill_causal, status_string, upproj_v, MlaRope, yarn_rope,
-    yarn_attention_factor,
+    yarn_attention_factor, linear, linear_workspace_size, kv_append, kv_append_workspace_size, q_project,
+    q_project_workspace_size, output_proj, fold_wuv_wo,
 )

@@ -104,6 +104,24 @@ def lib() -> ctypes.CDLL:
                                      _vp, _vp, _vp]
     L.mla_upproj_v.restype = _i32
     L.mla_upproj_v.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+    _sz = ctypes.c_size_t
+    L.mla_linear_workspace_size.restype = _sz
+    L.mla_linear_workspace_size.argtypes = [_i32, _i32, _i32]
+    L.mla_linear.restype = _i32
+    L.mla_linear.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]
+    L.mla_kv_append_workspace_size.restype = _sz
+    L.mla_kv_append_workspace_size.argtypes = [_i32, _i32, _i32]
+    L.mla_kv_append.restype = _i32
+    L.mla_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(MlaCache),
+                                ctypes.POINTER(MlaRope), _vp, _sz, _vp]
+    L.mla_q_project_workspace_size.restype = _sz
+    L.mla_q_project_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
+    L.mla_q_project.restype = _i32
+    L.mla_q_project.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+    L.mla_output_proj.restype = _i32
+    L.mla_output_proj.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+    L.mla_fold_wuv_wo.restype = _i32
+    L.mla_fold_wuv_wo.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
     _LIB = L
     return L
 
@@ -397,4 +415,113 @@ def upproj_v(z: torch.Tensor, w_uv: torch.Tensor, out_dtype=torch.float32,
     _need(out, "out", out_dtype, (N, H, D_V))
     _check(lib().mla_upproj_v(_ptr(z), _ptr(w_uv), _ptr(out), N, H, _dt_code(w_uv.dtype), _dt_code(out_dtype),
                               _stream(z.device)), "mla_upproj_v")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Projections around the attention
+# ---------------------------------------------------------------------------
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device) if nbytes > 0 else None
+
+
+def _ws_args(ws: Optional[torch.Tensor]):
+    return (_ptr(ws), 0 if ws is None else ws.numel())
+
+
+def linear_workspace_size(N: int, M: int, K: int) -> int:
+    return int(lib().mla_linear_workspace_size(int(N), int(M), int(K)))
+
+
+def linear(x: torch.Tensor, w0: torch.Tensor, w1: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+           workspace: Optional[torch.Tensor] = None):
+    """Y = X W^T with W = [w0; w1] (mla_linear).  Returns y0 [N, M0], or
+    (y0, y1) when w1 is given."""
+    N, K = x.shape
+    M0 = w0.shape[0]
+    M1 = 0 if w1 is None else w1.shape[0]
+    _need(x, "x", torch.bfloat16, (N, K))
+    _need(w0, "w0", torch.bfloat16, (M0, K))
+    if w1 is not None:
+        _need(w1, "w1", torch.bfloat16, (M1, K))
+    y0 = torch.empty((N, M0), dtype=out_dtype, device=x.device)
+    y1 = torch.empty((N, M1), dtype=out_dtype, device=x.device) if M1 else None
+    if workspace is None:
+        workspace = _workspace(linear_workspace_size(N, M0 + M1, K), x.device)
+    _check(lib().mla_linear(_ptr(x), _ptr(w0), M0, _ptr(w1), M1, _ptr(y0), _ptr(y1), N, K, _dt_code(out_dtype),
+                            *_ws_args(workspace), _stream(x.device)), "mla_linear")
+    return y0 if w1 is None else (y0, y1)
+
+
+def kv_append_workspace_size(T: int, d: int, cache_dtype: int) -> int:
+    return int(lib().mla_kv_append_workspace_size(int(T), int(d), int(cache_dtype)))
+
+
+def kv_append(cache: PagedCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor, pos: torch.Tensor,
+              slot: torch.Tensor, rope: Optional[MlaRope] = None, workspace: Optional[torch.Tensor] = None) -> None:
+    """c^KV = W^DKV h and RoPE_pos(W^KR h) of T tokens into the cache (mla_kv_append)."""
+    T, d = h.shape
+    _need(h, "h", torch.bfloat16, (T, d))
+    _need(w_dkv, "w_dkv", torch.bfloat16, (D_C, d))
+    _need(w_kr, "w_kr", torch.bfloat16, (D_R, d))
+    _need(pos, "pos", torch.int32, (T,))
+    _need(slot, "slot", torch.int32, (T,))
+    desc = cache.descriptor()
+    if workspace is None:
+        workspace = _workspace(kv_append_workspace_size(T, d, desc.dtype), h.device)
+    _check(lib().mla_kv_append(_ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(pos), _ptr(slot), T, d, ctypes.byref(desc),
+                               None if rope is None else ctypes.byref(rope), *_ws_args(workspace),
+                               _stream(h.device)), "mla_kv_append")
+
+
+def q_project_workspace_size(T: int, d: int, dcq: int, H: int) -> int:
+    return int(lib().mla_q_project_workspace_size(int(T), int(d), int(dcq), int(H)))
+
+
+def q_project(h: torch.Tensor, w_dq: torch.Tensor, w_uq: torch.Tensor, w_qr: torch.Tensor, H: int,
+              out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None):
+    """(q_c [T,H,128], q_r [T,H,64] before rotation) from hidden states (mla_q_project)."""
+    T, d = h.shape
+    dcq = w_dq.shape[0]
+    _need(h, "h", torch.bfloat16, (T, d))
+    _need(w_dq, "w_dq", torch.bfloat16, (dcq, d))
+    _need(w_uq, "w_uq", torch.bfloat16, (H * D_NOPE, dcq))
+    _need(w_qr, "w_qr", torch.bfloat16, (H * D_R, dcq))
+    q_c = torch.empty((T, H, D_NOPE), dtype=out_dtype, device=h.device)
+    q_r = torch.empty((T, H, D_R), dtype=out_dtype, device=h.device)
+    if workspace is None:
+        workspace = _workspace(q_project_workspace_size(T, d, dcq, H), h.device)
+    _check(lib().mla_q_project(_ptr(h), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(q_c), _ptr(q_r), T, d, dcq, H,
+                               _dt_code(out_dtype), *_ws_args(workspace), _stream(h.device)), "mla_q_project")
+    return q_c, q_r
+
+
+def output_proj(x: torch.Tensor, w: torch.Tensor, out_dtype=torch.float32,
+                workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """u = W x per token (mla_output_proj): x = o [N,H,128] with W^O, or the
+    bf16 latent z [N,H,512] with the folded matrix."""
+    N = x.shape[0]
+    K = x[0].numel()
+    d = w.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, (d, K))
+    if out is None:
+        out = torch.empty((N, d), dtype=out_dtype, device=x.device)
+    _need(out, "out", out_dtype, (N, d))
+    if workspace is None:
+        workspace = _workspace(linear_workspace_size(N, d, K), x.device)
+    _check(lib().mla_output_proj(_ptr(x), _ptr(w), _ptr(out), N, K, d, _dt_code(out_dtype), *_ws_args(workspace),
+                                 _stream(x.device)), "mla_output_proj")
+    return out
+
+
+def fold_wuv_wo(w_uv: torch.Tensor, w_o: torch.Tensor) -> torch.Tensor:
+    """W^O blockdiag(W^UV) [d, H*512] bf16 (mla_fold_wuv_wo)."""
+    H = w_uv.shape[0]
+    d = w_o.shape[0]
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_V, D_C))
+    _need(w_o, "w_o", torch.bfloat16, (d, H * D_V))
+    out = torch.empty((d, H * D_C), dtype=torch.bfloat16, device=w_o.device)
+    _check(lib().mla_fold_wuv_wo(_ptr(w_uv), _ptr(w_o), _ptr(out), H, d, _stream(w_o.device)), "mla_fold_wuv_wo")
     return out

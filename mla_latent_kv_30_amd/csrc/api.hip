@@ -394,3 +394,130 @@ mla_status mla_upproj_v(const float* z, const void* w_uv, void* o, int32_t N, in
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Projections around the attention
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr long long kMaxOperandBytes = 0x7fffffffLL;   // buffer offsets are 31-bit
+
+bool rows_fit(long long rows, int K) { return (rows + 256) * (long long)K * 2 <= kMaxOperandBytes; }
+
+bool linear_shape_ok(int N, int M0, int M1, int K) {
+  if (N < 1 || K < 64 || K % 64 != 0 || M0 < 32 || M0 % 32 != 0 || M1 < 0 || M1 % 32 != 0) return false;
+  return rows_fit(N, K) && rows_fit(M0, K) && rows_fit(M1, K) &&
+         (long long)N * (M0 + M1) * 4 <= kMaxOperandBytes;
+}
+
+mla_status run_linear(const void* x, const void* w0, int M0, const void* w1, int M1, void* y0, void* y1, int N, int K,
+                      int out_bf16, uint8_t* ws, size_t ws_bytes, hipStream_t st) {
+  const LinearPlan p = plan_linear(N, M0 + M1, K, device_cus());
+  if (p.part_bytes > 0 && (ws == nullptr || ws_bytes < p.part_bytes)) return MLA_ERR_WORKSPACE;
+  LinearArgs a{};
+  a.x = (const bf16*)x;
+  a.w0 = (const bf16*)w0;
+  a.w1 = (const bf16*)w1;
+  a.y0 = y0;
+  a.y1 = y1;
+  a.part = (float*)ws;
+  a.N = N;
+  a.K = K;
+  a.M0 = M0;
+  a.M1 = M1;
+  a.out_bf16 = out_bf16;
+  return launched(launch_linear(a, p, st));
+}
+
+size_t linear_ws(int N, int M, int K) { return plan_linear(N, M, K, device_cus()).part_bytes; }
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_linear_workspace_size(int32_t N, int32_t M, int32_t K) {
+  if (!linear_shape_ok(N, M, 0, K)) return 0;
+  return linear_ws(N, M, K);
+}
+
+mla_status mla_linear(const void* x, const void* w0, int32_t M0, const void* w1, int32_t M1, void* y0, void* y1,
+                      int32_t N, int32_t K, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!x || !w0 || !y0 || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!linear_shape_ok(N, M0, M1, K)) return MLA_ERR_INVALID_ARG;
+  if (M1 > 0 && (!w1 || !y1)) return MLA_ERR_INVALID_ARG;
+  return run_linear(x, w0, M0, M1 > 0 ? w1 : nullptr, M1, y0, M1 > 0 ? y1 : nullptr, N, K,
+                    out_dtype == MLA_BF16, (uint8_t*)workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+size_t mla_kv_append_workspace_size(int32_t T, int32_t d, int32_t cache_dtype) {
+  if (!linear_shape_ok(T, MLA_D_C, MLA_D_R, d)) return 0;
+  const size_t el = cache_dtype == MLA_F32 ? 4 : 2;
+  return align256((size_t)T * MLA_ROW * el) + linear_ws(T, MLA_ROW, d);
+}
+
+mla_status mla_kv_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, const int32_t* slot,
+                         int32_t T, int32_t d, const mla_cache* cache, const mla_rope* rope, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!h || !w_dkv || !w_kr || !pos || !slot) return MLA_ERR_INVALID_ARG;
+  if (!linear_shape_ok(T, MLA_D_C, MLA_D_R, d)) return MLA_ERR_INVALID_ARG;
+  const mla_rope r = rope ? *rope : plain_rope(10000.0f);
+  if (!rope_ok(r)) return MLA_ERR_INVALID_ARG;
+  const int kind = cache_kind(cache);
+  if (kind < 0) return MLA_ERR_INVALID_ARG;
+  const bool f32 = kind == kKindF32;
+  const size_t inter = align256((size_t)T * MLA_ROW * (f32 ? 4 : 2));
+  if (workspace == nullptr || workspace_bytes < mla_kv_append_workspace_size(T, d, cache->dtype))
+    return MLA_ERR_WORKSPACE;
+  uint8_t* ws = (uint8_t*)workspace;
+  void* c_kv = ws;
+  void* k_r = ws + (size_t)T * MLA_D_C * (f32 ? 4 : 2);
+  const hipStream_t st = (hipStream_t)stream;
+  mla_status e = run_linear(h, w_dkv, MLA_D_C, w_kr, MLA_D_R, c_kv, k_r, T, d, f32 ? 0 : 1, ws + inter,
+                            workspace_bytes - inter, st);
+  if (e != MLA_OK) return e;
+  CacheWriteArgs a{c_kv, k_r, pos, slot, nullptr, 0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
+                   cache->ckv_scale, cache->kr, rope_table(r)};
+  return launched(launch_cache_write(a, kind, st));
+}
+
+size_t mla_q_project_workspace_size(int32_t T, int32_t d, int32_t dcq, int32_t H) {
+  if (H < 1 || H > MLA_MAX_HEADS || !linear_shape_ok(T, dcq, 0, d)) return 0;
+  if (!linear_shape_ok(T, H * MLA_D_NOPE, H * MLA_D_R, dcq)) return 0;
+  const size_t a = linear_ws(T, dcq, d), b = linear_ws(T, H * (MLA_D_NOPE + MLA_D_R), dcq);
+  return align256((size_t)T * dcq * 2) + (a > b ? a : b);
+}
+
+mla_status mla_q_project(const void* h, const void* w_dq, const void* w_uq, const void* w_qr, void* q_c, void* q_r,
+                         int32_t T, int32_t d, int32_t dcq, int32_t H, int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!h || !w_dq || !w_uq || !w_qr || !q_c || !q_r || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (H < 1 || H > MLA_MAX_HEADS || !linear_shape_ok(T, dcq, 0, d)) return MLA_ERR_INVALID_ARG;
+  if (!linear_shape_ok(T, H * MLA_D_NOPE, H * MLA_D_R, dcq)) return MLA_ERR_INVALID_ARG;
+  const size_t need = mla_q_project_workspace_size(T, d, dcq, H);
+  if (workspace == nullptr || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  uint8_t* ws = (uint8_t*)workspace;
+  const size_t inter = align256((size_t)T * dcq * 2);
+  const hipStream_t st = (hipStream_t)stream;
+  mla_status e = run_linear(h, w_dq, dcq, nullptr, 0, ws, nullptr, T, d, 1, ws + inter, workspace_bytes - inter, st);
+  if (e != MLA_OK) return e;
+  return run_linear(ws, w_uq, H * MLA_D_NOPE, w_qr, H * MLA_D_R, q_c, q_r, T, dcq, out_dtype == MLA_BF16,
+                    ws + inter, workspace_bytes - inter, st);
+}
+
+mla_status mla_output_proj(const void* x, const void* w, void* u, int32_t N, int32_t K, int32_t d, int32_t out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w || !u || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (K % MLA_D_V != 0 || !linear_shape_ok(N, d, 0, K)) return MLA_ERR_INVALID_ARG;
+  return run_linear(x, w, d, nullptr, 0, u, nullptr, N, K, out_dtype == MLA_BF16, (uint8_t*)workspace,
+                    workspace_bytes, (hipStream_t)stream);
+}
+
+mla_status mla_fold_wuv_wo(const void* w_uv, const void* w_o, void* w_fold, int32_t H, int32_t d, void* stream) {
+  if (!w_uv || !w_o || !w_fold || H < 1 || H > MLA_MAX_HEADS || d < 1) return MLA_ERR_INVALID_ARG;
+  if ((long long)d * H * MLA_D_C * 2 > kMaxOperandBytes * 2) return MLA_ERR_INVALID_ARG;
+  return launched(launch_fold_wuv_wo((const bf16*)w_uv, (const bf16*)w_o, (bf16*)w_fold, H, d, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -88,4 +88,31 @@ struct UpprojArgs {
 };
 hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s);
 
+// Y = X W^T (bf16 operands, fp32 accumulate); W is the row concatenation
+// [w0 (M0 rows); w1 (M1 rows)] and Y the column concatenation [y0 | y1].
+struct LinearArgs {
+  const bf16* x;    // [N][K]
+  const bf16* w0;   // [M0][K]
+  const bf16* w1;   // [M1][K] (M1 == 0: unused)
+  void* y0;         // [N][M0]
+  void* y1;         // [N][M1]
+  float* part;      // [splits][N][M0+M1] fp32 partials (splits > 1)
+  int32_t N, K, M0, M1;
+  int32_t out_bf16;
+  int32_t mt, nt, splits, kt_split;   // filled from the plan
+};
+constexpr int kLinSmall = 0;   // 64 x 64 tiles (N <= 64)
+constexpr int kLinMid = 1;     // 128 x 128
+constexpr int kLinLarge = 2;   // 256 x 256
+struct LinearPlan {
+  int cfg, tm, tn, mt, nt, splits, kt_split;
+  size_t part_bytes;
+};
+LinearPlan plan_linear(int N, int M, int K, int cus);
+hipError_t launch_linear(LinearArgs a, const LinearPlan& p, hipStream_t s);
+
+// W' = W^O blockdiag(W_1^UV .. W_H^UV): [d][H*512] bf16 from W^O [d][H*128]
+// and W^UV [H][128][512], both bf16.
+hipError_t launch_fold_wuv_wo(const bf16* w_uv, const bf16* w_o, bf16* w_fold, int H, int d, hipStream_t s);
+
 }  // namespace mla

@@ -218,3 +218,42 @@ def all_latents(wl: Workload):
         cs.append(c)
         ks.append(k)
     return np.concatenate(cs, axis=0), np.concatenate(ks, axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the projections around the attention
+# ---------------------------------------------------------------------------
+# The pages fix d_c' = 1536 (q_lora_rank, §维度分解详解) but not the model
+# width d; D_MODEL is a synthetic choice (a multiple of 128, as the 128-wide
+# block quantisation tiles of the FP8 scheme assume).
+D_MODEL = 7168
+D_CQ = 1536
+
+
+def projection_weights(wl: Workload, d: int = D_MODEL, dcq: int = D_CQ):
+    """bf16 weights of the projections, each ~ N(0, 1/fan_in) so that every
+    projected vector has unit variance for unit-variance inputs:
+    W^DKV [512, d], W^KR [64, d], W^DQ [dcq, d], W^UQ [H*128, dcq],
+    W^QR [H*64, dcq], W^O [d, H*128]."""
+    def w(tag, shape, fan_in):
+        return round_bf16(_normal(stream(wl.seed, wl.name, tag, d), shape, float(np.sqrt(1.0 / fan_in))))
+    return {
+        "w_dkv": w("W_DKV", (D_C, d), d),
+        "w_kr": w("W_KR", (D_R, d), d),
+        "w_dq": w("W_DQ", (dcq, d), d),
+        "w_uq": w("W_UQ", (wl.H * D_H, dcq), dcq),
+        "w_qr": w("W_QR", (wl.H * D_R, dcq), dcq),
+        "w_o": w("W_O", (d, wl.H * D_H), wl.H * D_H),
+    }
+
+
+def hidden_states(wl: Workload, b: int, d: int = D_MODEL, rows: Optional[int] = None) -> np.ndarray:
+    """h [rows, d] ~ N(0, 1) in bf16: the hidden states of sequence b's
+    tokens (rows defaults to its length)."""
+    n = int(wl.lens[b]) if rows is None else int(rows)
+    return round_bf16(_normal(stream(wl.seed, wl.name, "h", b * 1_000_003 + d), (n, d)))
+
+
+def new_token_hidden(wl: Workload, d: int = D_MODEL) -> np.ndarray:
+    """h [B, d] ~ N(0, 1) bf16: the hidden state of each sequence's new token."""
+    return round_bf16(_normal(stream(wl.seed, wl.name, "h_new", d), (wl.B, d)))

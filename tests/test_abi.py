@@ -133,3 +133,52 @@ def test_rope_variants_reject_bad_frequency_settings(rope):
                                   NULL) == _lib.MLA_ERR_INVALID_ARG
     assert L.mla_prefill_causal_rope(P, P, P, 0, ctypes.byref(desc), P, 4, 16, 0.07, ctypes.byref(r), P, None,
                                      NULL) == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_projection_entry_points_reject_bad_arguments():
+    bf, f32, fp8 = _lib.MLA_BF16, _lib.MLA_F32, _lib.MLA_FP8_E4M3
+    bad = _lib.MLA_ERR_INVALID_ARG
+
+    def lin(N=64, K=512, M0=512, M1=64, w1=P, y1=P, dt=bf, ws=P, wsb=1 << 30, x=P):
+        return L.mla_linear(x, P, M0, w1, M1, P, y1, N, K, dt, ws, wsb, NULL)
+    assert lin(K=96) == bad            # K % 64
+    assert lin(K=0) == bad
+    assert lin(M0=48) == bad           # M0 % 32
+    assert lin(M0=0) == bad
+    assert lin(M1=40) == bad           # M1 % 32
+    assert lin(N=0) == bad
+    assert lin(w1=NULL) == bad         # second block without its pointers
+    assert lin(y1=NULL) == bad
+    assert lin(x=NULL) == bad
+    assert lin(dt=fp8) == bad
+    assert lin(N=1 << 20, K=4096) == bad   # X over 2 GiB
+    # a split contraction needs its partials
+    assert lin(N=64, K=7168, M0=512, M1=64, ws=NULL, wsb=0) == _lib.MLA_ERR_WORKSPACE
+    need = _lib.linear_workspace_size(64, 576, 7168)
+    assert lin(N=64, K=7168, M0=512, M1=64, ws=P, wsb=need - 1) == _lib.MLA_ERR_WORKSPACE
+
+    c = _cache()
+    r = _lib.MlaRope(10000.0, 1.0, 1.0, 32.0, 4096)
+    assert L.mla_kv_append(P, P, P, P, P, 4, 100, ctypes.byref(c), ctypes.byref(r), P, 1 << 30, NULL) == bad
+    assert L.mla_kv_append(P, P, P, P, P, 4, 128, ctypes.byref(_cache(page=32)), NULL, P, 1 << 30, NULL) == bad
+    assert L.mla_kv_append(P, P, NULL, P, P, 4, 128, ctypes.byref(c), NULL, P, 1 << 30, NULL) == bad
+    assert L.mla_kv_append(P, P, P, P, P, 4, 128, ctypes.byref(c), NULL, NULL, 0, NULL) == _lib.MLA_ERR_WORKSPACE
+    assert L.mla_q_project(P, P, P, P, P, P, 4, 256, 1536, 0, bf, P, 1 << 30, NULL) == bad
+    assert L.mla_q_project(P, P, P, P, P, P, 4, 256, 1500, 16, bf, P, 1 << 30, NULL) == bad
+    assert L.mla_q_project(P, P, P, P, P, P, 4, 256, 1536, 16, bf, NULL, 0, NULL) == _lib.MLA_ERR_WORKSPACE
+    assert L.mla_output_proj(P, P, P, 8, 64 * 3, 256, f32, P, 1 << 30, NULL) == bad   # K % 128
+    assert L.mla_output_proj(P, P, P, 8, 2048, 100, f32, P, 1 << 30, NULL) == bad     # d % 32
+    assert L.mla_fold_wuv_wo(P, P, P, 0, 256, NULL) == bad
+    assert L.mla_fold_wuv_wo(P, NULL, P, 16, 256, NULL) == bad
+
+
+def test_projection_workspace_sizes():
+    # few output tiles and a long contraction: split, partials in fp32
+    assert _lib.linear_workspace_size(64, 576, 7168) >= 2 * 64 * 576 * 4
+    # enough output tiles to fill the device: no split, no workspace
+    assert _lib.linear_workspace_size(4096, 7168, 16384) == 0
+    assert _lib.linear_workspace_size(64, 576, 100) == 0          # rejected shape
+    assert _lib.kv_append_workspace_size(64, 7168, _lib.MLA_BF16) >= 64 * 576 * 2
+    assert _lib.kv_append_workspace_size(64, 7168, _lib.MLA_F32) >= 64 * 576 * 4
+    assert _lib.q_project_workspace_size(64, 7168, 1536, 16) >= 64 * 1536 * 2
+    assert _lib.q_project_workspace_size(64, 7168, 1536, 0) == 0

@@ -1,0 +1,246 @@
+"""GPU parity of the projections around the attention (through the C-ABI)
+against the fp64 CPU oracle: the cache append from hidden states, the query
+path, the output projection, the W^O fold, and the whole layer from hidden
+states to u for the newest token of each sequence.
+
+Tolerances:
+  bf16 outputs, and every result that passes through a bf16 intermediate:
+      max |gpu - oracle| / max |oracle| <= 2e-2
+  fp32 outputs of one product of bf16 operands: the operands are exact in
+      both, the products are exact in fp32 and only the fp32 accumulation
+      rounds (random-walk error about sqrt(K) 2^-24 of the row scale), so
+      the same ratio is held to 1e-4
+  fp8 cache: <= 6e-2 against the oracle's unquantised values
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_30_amd as mla
+from mla_latent_kv_30_amd import workload as W
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+FP8_TOL = 6e-2
+
+
+def _rel(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), "non-finite GPU output"
+    return float(np.abs(gpu - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bf(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV, torch.bfloat16)
+
+
+def _host(t):
+    return t.float().cpu().numpy()
+
+
+def _randn(seed, tag, shape, std=1.0):
+    return W.round_bf16(W._normal(W.stream(seed, "projection_cases", tag), shape, std))
+
+
+# --------------------------------------------------------------------------- the product Y = X W^T
+
+# (N, K, M0, M1): each tile configuration (N <= 64, <= 512, larger), a split
+# contraction, ragged N and M, a W block boundary inside a tile (96 + 32 in a
+# 64-row tile), and the smallest shape.
+LINEAR_CASES = [
+    (5, 192, 96, 32),
+    (1, 64, 32, 0),
+    (64, 7168, 512, 64),
+    (77, 1536, 2048, 1024),
+    (600, 512, 800, 0),
+    (300, 1024, 160, 96),
+]
+
+
+@pytest.mark.parametrize("N,K,M0,M1", LINEAR_CASES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_linear_matches_oracle(N, K, M0, M1, out):
+    _note(f"case linear N={N} K={K} M0={M0} M1={M1} out={out}")
+    x = _randn(1, f"x{N}_{K}", (N, K))
+    w0 = _randn(2, f"w0{M0}_{K}", (M0, K), K ** -0.5)
+    w1 = _randn(3, f"w1{M1}_{K}", (M1, K), K ** -0.5)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    res = mla.linear(_bf(x), _bf(w0), _bf(w1) if M1 else None, out_dtype=dt)
+    torch.cuda.synchronize()
+    y0, y1 = (res, None) if M1 == 0 else res
+    # the oracle's two-block projection (h -> W^DKV h, W^KR h) at these widths
+    ref = orc.kv_projection(x, w0, w1, np.zeros(N))
+    tol = F32_TOL if out == "f32" else BF16_TOL
+    assert _rel(_host(y0), ref["c_kv"]) <= tol
+    if M1:
+        assert _rel(_host(y1), ref["k_r"]) <= tol
+
+
+def test_linear_repeated_calls_are_identical():
+    """Split partials are summed in a fixed order: two calls agree bit for bit."""
+    x = _bf(_randn(4, "rep_x", (64, 7168)))
+    w = _bf(_randn(5, "rep_w", (576, 7168), 7168 ** -0.5))
+    a = mla.linear(x, w, out_dtype=torch.float32)
+    b = mla.linear(x, w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------- cache append
+
+def _cache_rows(cache, slots):
+    """(c_kv [T,512], rotated k_r [T,64]) stored at `slots`, as fp64 on the host."""
+    s = torch.as_tensor(slots, dtype=torch.long, device=DEV)
+    if cache.is_fp8:
+        codes = cache.ckv.view(-1, 512)[s].cpu().numpy()
+        scales = cache.scale.view(-1, 4)[s].cpu().numpy()
+        c = orc.dequantize_latent_e4m3(codes, scales)
+        k = cache.kr.view(-1, 64)[s].float().cpu().numpy()
+        return c, k
+    rows = cache.rows.view(-1, 576)[s].double().cpu().numpy()
+    return rows[:, :512], rows[:, 512:]
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8", "f32"])
+def test_kv_append_matches_oracle(cache_dtype):
+    wl = W.make_workload("decode_h16", B=2, H=16, lens=[37, 70])
+    d = 1024
+    _note(f"case kv_append cache={cache_dtype} lens={list(wl.lens)} d={d}")
+    lay = W.paged_layout(wl, spare_pages=1)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": "fp8"}[cache_dtype]
+    cache = mla.PagedCache(lay.num_pages, dt, device=DEV, fill=float("nan"))
+    wts = W.projection_weights(wl, d=d)
+    h = np.concatenate([W.hidden_states(wl, b, d) for b in range(wl.B)])
+    pos = lay.positions
+    mla.kv_append(cache, _bf(h), _bf(wts["w_dkv"]), _bf(wts["w_kr"]), torch.as_tensor(pos, device=DEV),
+                  torch.as_tensor(lay.slots, device=DEV))
+    torch.cuda.synchronize()
+    ref = orc.kv_projection(h, wts["w_dkv"], wts["w_kr"], pos)
+    c, k = _cache_rows(cache, lay.slots)
+    tol = {"bf16": BF16_TOL, "f32": F32_TOL, "fp8": FP8_TOL}[cache_dtype]
+    assert _rel(c, ref["c_kv"]) <= tol
+    assert _rel(k, ref["k_r_rot"]) <= (BF16_TOL if cache_dtype == "fp8" else tol)
+
+
+def test_kv_append_yarn_rotation():
+    wl = W.make_workload("decode_h16", B=1, H=16, lens=[300])
+    d = 512
+    _note("case kv_append yarn")
+    lay = W.paged_layout(wl)
+    cache = mla.PagedCache(lay.num_pages, torch.bfloat16, device=DEV, fill=float("nan"))
+    wts = W.projection_weights(wl, d=d)
+    h = W.hidden_states(wl, 0, d)
+    pos = lay.positions + 5000   # positions past the original context
+    mla.kv_append(cache, _bf(h), _bf(wts["w_dkv"]), _bf(wts["w_kr"]), torch.as_tensor(pos, device=DEV),
+                  torch.as_tensor(lay.slots, device=DEV), rope=mla.yarn_rope())
+    torch.cuda.synchronize()
+    ref = orc.kv_projection(h, wts["w_dkv"], wts["w_kr"], pos, rope_theta=orc.yarn_frequencies())
+    c, k = _cache_rows(cache, lay.slots)
+    assert _rel(k, ref["k_r_rot"]) <= BF16_TOL
+    assert _rel(c, ref["c_kv"]) <= BF16_TOL
+
+
+# --------------------------------------------------------------------------- query path
+
+@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_q_project_matches_oracle(H, out):
+    wl = W.make_workload("decode_h16", B=19, H=H)
+    d = 1024
+    _note(f"case q_project H={H} T={wl.B} d={d} out={out}")
+    wts = W.projection_weights(wl, d=d)
+    h = W.new_token_hidden(wl, d)
+    pos = np.asarray(wl.lens) - 1
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    q_c, q_r = mla.q_project(_bf(h), _bf(wts["w_dq"]), _bf(wts["w_uq"]), _bf(wts["w_qr"]), H, out_dtype=dt)
+    torch.cuda.synchronize()
+    ref = orc.query_projection(h, wts["w_dq"], wts["w_uq"], wts["w_qr"], pos, H)
+    # c^Q passes through bf16 between the two products
+    assert _rel(_host(q_c), ref["q_c"]) <= BF16_TOL
+    assert _rel(_host(q_r), ref["q_r"]) <= BF16_TOL
+
+
+# --------------------------------------------------------------------------- output projection and fold
+
+def test_output_proj_matches_oracle():
+    N, H, d = 37, 16, 1024
+    _note(f"case output_proj N={N} H={H} d={d}")
+    o = _randn(6, "o", (N, H, 128))
+    w_o = _randn(7, "w_o", (d, H * 128), (H * 128) ** -0.5)
+    u32 = mla.output_proj(_bf(o), _bf(w_o), out_dtype=torch.float32)
+    u16 = mla.output_proj(_bf(o), _bf(w_o), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = orc.output_projection(o, w_o)
+    assert _rel(_host(u32), ref) <= F32_TOL
+    assert _rel(_host(u16), ref) <= BF16_TOL
+
+
+def test_fold_and_folded_output_match_oracle():
+    N, H, d = 9, 16, 512
+    _note(f"case fold H={H} d={d}")
+    w_uv = _randn(8, "w_uv", (H, 128, 512), 512 ** -0.5)
+    w_o = _randn(9, "w_o2", (d, H * 128), (H * 128) ** -0.5)
+    z = _randn(10, "z", (N, H, 512))
+    wf = mla.fold_wuv_wo(_bf(w_uv), _bf(w_o))
+    torch.cuda.synchronize()
+    ref_wf = orc.fold_wuv_into_wo(w_uv, w_o)
+    # each element is one fp32 sum of 128 exact products, rounded once to bf16
+    got = _host(wf).astype(np.float64)
+    assert np.all(np.abs(got - ref_wf) <= 2.0 ** -8 * np.abs(ref_wf) + 1e-6)
+    u = mla.output_proj(_bf(z), wf, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_u = orc.output_projection(np.einsum("hdc,nhc->nhd", w_uv, z), w_o)
+    assert _rel(_host(u), ref_u) <= BF16_TOL
+
+
+# --------------------------------------------------------------------------- the layer from hidden states
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
+def test_layer_from_hidden_matches_oracle(cache_dtype):
+    """Cache append of every token, the newest token's queries, absorbed
+    decode, merge + value up-projection and W^O: u for the newest token of
+    each sequence, against the oracle's expanded layer."""
+    wl = W.make_workload("decode_h16", B=3, H=16, lens=[1, 65, 200])
+    d, dcq = 512, 1536
+    _note(f"case layer cache={cache_dtype} lens={list(wl.lens)} d={d}")
+    lay = W.paged_layout(wl, spare_pages=1)
+    cache = mla.PagedCache(lay.num_pages, torch.bfloat16 if cache_dtype == "bf16" else "fp8", device=DEV,
+                           fill=float("nan"))
+    wts = W.projection_weights(wl, d=d, dcq=dcq)
+    w_uk, w_uv = W.weights(wl)
+    hs = [W.hidden_states(wl, b, d) for b in range(wl.B)]
+    h_all = np.concatenate(hs)
+    mla.kv_append(cache, _bf(h_all), _bf(wts["w_dkv"]), _bf(wts["w_kr"]),
+                  torch.as_tensor(lay.positions, device=DEV), torch.as_tensor(lay.slots, device=DEV))
+    h_new = np.stack([hb[-1] for hb in hs])
+    pos = torch.as_tensor(np.asarray(wl.lens) - 1, dtype=torch.int32, device=DEV)
+    q_c, q_r = mla.q_project(_bf(h_new), _bf(wts["w_dq"]), _bf(wts["w_uq"]), _bf(wts["w_qr"]), wl.H)
+    q_abs = mla.absorb_q(q_c, q_r, pos, _bf(w_uk))
+    bt = torch.as_tensor(np.where(lay.block_table < 0, 0, lay.block_table), dtype=torch.int32, device=DEV)
+    seq_lens = torch.as_tensor(wl.lens, dtype=torch.int32, device=DEV)
+    z = torch.empty((wl.B, wl.H, 512), dtype=torch.float32, device=DEV)
+    ws = mla.decode_partial(q_abs, cache, bt, seq_lens, mla.decode_workspace(wl.B, wl.H, 0), z)
+    o = mla.decode_merge_upproj(seq_lens, wl.H, ws, z, _bf(w_uv), out_dtype=torch.bfloat16)
+    u = mla.output_proj(o, _bf(wts["w_o"]), out_dtype=torch.float32)
+    wf = mla.fold_wuv_wo(_bf(w_uv), _bf(wts["w_o"]))
+    u_fold = mla.output_proj(z.to(torch.bfloat16), wf, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = np.stack([orc.layer_decode_from_hidden(hs[b], wts["w_dkv"], wts["w_kr"], wts["w_dq"], wts["w_uq"],
+                                                 wts["w_qr"], w_uk, w_uv, wts["w_o"])["u"] for b in range(wl.B)])
+    tol = BF16_TOL if cache_dtype == "bf16" else FP8_TOL
+    assert _rel(_host(u), ref) <= tol
+    assert _rel(_host(u_fold), ref) <= tol
