@@ -11,6 +11,13 @@ keep the 256 MB last-level cache from serving repeated reads, the step
 rotates over enough replicas of its inputs (cache, weights, queries) to
 exceed 600 MB.
 
+With --layer the step starts from hidden states instead: the query path
+(mla_q_project: c^Q, q^C, q^R), the new token's cache append
+(mla_kv_append: c^KV and the rotated k^R), the same decode path, and the
+output projection (mla_output_proj: u = W^O [o_1..o_H]), with synthetic
+bf16 weights at model width --d-model; each projection is also timed alone
+against its HBM roofline.
+
 Prints one JSON line: value = cached tokens per second over the whole step,
 plus the decode kernel's achieved HBM bandwidth and matrix-core rate against
 MI355X's published peaks, and the CPU oracle timed on a bounded sample.
@@ -51,6 +58,9 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layer", action="store_true",
+                    help="step from hidden states to u: query path, cache append, decode, output projection")
+    ap.add_argument("--d-model", type=int, default=7168, help="model width d for --layer (not fixed by the pages)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence (multi-token decode, mla_decode_multi); decode workloads only")
     return ap.parse_args()
@@ -188,32 +198,66 @@ def main():
 
     # ---- replicas of everything a step reads
     per_rep = dd.cache.nbytes() + sum(t.numel() * t.element_size() for t in (dd.q_c, dd.q_r, dd.w_uk, dd.w_uv))
-    R = args.replicas or max(1, min(16, math.ceil(REPLICA_TARGET_BYTES / per_rep)))
     QL = max(1, args.q_len)
     if QL * H > 128:
         sys.exit(f"--q-len {QL} with {H} heads: multi-token decode takes q_len * H <= 128")
+    LAYER = args.layer
+    lw0 = None
+    if LAYER:
+        if QL > 1 or wl.dtype == "f32":
+            sys.exit("--layer: one-token decode over a bf16 or fp8 cache only")
+        D = args.d_model
+        lw0 = {k: torch.from_numpy(v).to(dev, torch.bfloat16) for k, v in W.projection_weights(wl, d=D).items()}
+        lw0["h"] = torch.from_numpy(W.new_token_hidden(wl, D)).to(dev, torch.bfloat16)
+        per_rep += sum(t.numel() * t.element_size() for t in lw0.values())
+        last = (wl.lens - 1).astype(np.int64)
+        slot_new = torch.from_numpy((dd.layout.block_table[np.arange(B), last // 64].astype(np.int64) * 64
+                                     + last % 64).astype(np.int32)).to(dev)
+        dcq = lw0["w_dq"].shape[0]
+        ws_q = torch.empty(max(1, mla.q_project_workspace_size(B, D, dcq, H)), dtype=torch.uint8, device=dev)
+        ws_kv = torch.empty(max(1, mla.kv_append_workspace_size(B, D, dd.cache.code)), dtype=torch.uint8,
+                            device=dev)
+        ws_o = torch.empty(max(1, mla.linear_workspace_size(B, D, H * 128)), dtype=torch.uint8, device=dev)
+        u = torch.empty((B, D), dtype=torch.float32, device=dev)
+    R = args.replicas or max(1, min(16, math.ceil(REPLICA_TARGET_BYTES / per_rep)))
     if QL > 1:  # q_len new tokens per sequence at positions L - q_len + t
         q_c0, q_r0, pos_q, _, _ = DI.multi_query_inputs(dd, QL)
     else:
         q_c0, q_r0, pos_q = dd.q_c, dd.q_r, dd.pos
-    reps = [(dd.cache, q_c0, q_r0, dd.w_uk, dd.w_uv)]
+    reps = [(dd.cache, q_c0, q_r0, dd.w_uk, dd.w_uv, lw0)]
     for _ in range(R - 1):
         c = mla.PagedCache.__new__(mla.PagedCache)
         c.__dict__.update(dd.cache.__dict__)
         for name in ("rows", "ckv", "scale", "kr"):
             t = getattr(dd.cache, name)
             setattr(c, name, None if t is None else t.clone())
-        reps.append((c, q_c0.clone(), q_r0.clone(), dd.w_uk.clone(), dd.w_uv.clone()))
+        lw = None if lw0 is None else {k: v.clone() for k, v in lw0.items()}
+        reps.append((c, q_c0.clone(), q_r0.clone(), dd.w_uk.clone(), dd.w_uv.clone(), lw))
     q_abs = torch.empty((B * QL, H, 576), dtype=dt, device=dev)
     z = torch.empty((B * QL, H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((B * QL, H), dtype=torch.float32, device=dev)
-    o = torch.empty((B * QL, H, 128), dtype=torch.float32, device=dev)
+    o = torch.empty((B * QL, H, 128), dtype=torch.bfloat16 if LAYER else torch.float32, device=dev)
     ws = mla.decode_workspace(B, QL * H, splits, dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
+    def q_proj(r):
+        _, q_c, q_r, _, _, lw = reps[r]
+        mla.q_project(lw["h"], lw["w_dq"], lw["w_uq"], lw["w_qr"], H, workspace=ws_q, q_c=q_c, q_r=q_r)
+
+    def kv_app(r):
+        cache, *_, lw = reps[r]
+        mla.kv_append(cache, lw["h"], lw["w_dkv"], lw["w_kr"], pos_q, slot_new, workspace=ws_kv)
+
+    def out_proj(r):
+        lw = reps[r][-1]
+        mla.output_proj(o, lw["w_o"], workspace=ws_o, out=u)
+
     def step(r):
-        cache, q_c, q_r, w_uk, w_uv = reps[r]
+        cache, q_c, q_r, w_uk, w_uv, lw = reps[r]
+        if LAYER:
+            q_proj(r)
+            kv_app(r)
         mla.absorb_q(q_c, q_r, pos_q, w_uk, out=q_abs)
         if QL > 1:
             mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
@@ -221,7 +265,9 @@ def main():
             mla.upproj_v(z, w_uv, out=o)
         else:
             mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
-            mla.decode_merge_upproj(dd.seq_lens, H, ws, z, w_uv, lse=lse, num_splits=splits, out=o)
+            mla.decode_merge_upproj(dd.seq_lens, H, ws, z, w_uv, lse=lse, num_splits=splits, out=o, out_dtype=o.dtype)
+        if LAYER:
+            out_proj(r)
 
     for k in range(max(1, args.warmup)):
         step(k % R)
@@ -267,27 +313,50 @@ def main():
     # between two events on the stream it runs on, three times; a GPU sleep
     # first lets the host enqueue every launch ahead of the device, so no host
     # latency lands inside the timed batch
-    kern_ms = []
-    for _rep in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        try:
-            torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * K)))
-        except Exception:  # no device sleep available: host latency may inflate the kernel time
-            pass
-        e0.record()
-        for k in range(K):
-            cache, *_ = reps[k % R]
-            if QL > 1:  # the multi-token entry point is decode + merge
-                mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
-                                 workspace=ws, z=z.view(B, QL, H, 512), lse=lse.view(B, QL, H))
-            else:
-                mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
-        e1.record()
-        torch.cuda.synchronize()
-        kern_ms.append(e0.elapsed_time(e1) / K)
-    kern_ms.sort()
+    def timed_batches(call):
+        out_ms = []
+        for _rep in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            try:
+                torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * K)))
+            except Exception:  # no device sleep available: host latency may inflate the kernel time
+                pass
+            e0.record()
+            for k in range(K):
+                call(k % R)
+            e1.record()
+            torch.cuda.synchronize()
+            out_ms.append(e0.elapsed_time(e1) / K)
+        out_ms.sort()
+        return out_ms
+
+    def decode_only(r):
+        cache = reps[r][0]
+        if QL > 1:  # the multi-token entry point is decode + merge
+            mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
+                             workspace=ws, z=z.view(B, QL, H, 512), lse=lse.view(B, QL, H))
+        else:
+            mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
+
+    kern_ms = timed_batches(decode_only)
     kern_avg_ms = kern_ms[1]  # median of the three batches
+
+    layer = None
+    if LAYER:
+        # each projection alone, against the bytes it must move (weights,
+        # activations in and out, intermediates written and read once)
+        tok_b = {"bf16": 1152, "fp8": 656}[wl.dtype]
+        nbytes = {
+            "q_project": 2 * (dcq * D + H * 192 * dcq + B * D + 2 * B * dcq + B * H * 192),
+            "kv_append": 2 * (576 * D + B * D + 2 * B * 576) + B * tok_b,
+            "output_proj": 2 * (D * H * 128 + B * H * 128) + 4 * B * D,
+        }
+        layer = {"d_model": D, "d_cq": dcq}
+        for name, call in (("q_project", q_proj), ("kv_append", kv_app), ("output_proj", out_proj)):
+            ms = timed_batches(call)[1]
+            gbs_p = nbytes[name] / (ms * 1e-3) / 1e9
+            layer[name] = {"us": ms * 1e3, "alg_bytes": nbytes[name], "GB/s": gbs_p, "hbm_frac": gbs_p / PEAK_HBM_GBS}
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -333,13 +402,16 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": wl.name, "batch": B, "heads": H, "cached_tokens": total,
+            "workload": wl.name + (f"+layer(d={D})" if LAYER else ""), "batch": B, "heads": H, "cached_tokens": total,
             "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
             "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
-            "step": ("absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)" if QL == 1
+            "step": ("q_project + kv_append + absorb_q + decode_partial + decode_merge_upproj + output_proj"
+                     if LAYER else
+                     "absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)" if QL == 1
                      else "absorb_q + decode_multi (decode + split merge) + upproj_v"),
             "q_len": QL, "query_tokens_per_s": B * QL / (ms_per_step * 1e-3),
         },
+        "layer": layer,
         "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
             "traffic": None if tr is None else tr["traffic_bytes"], "kernel": kname,

@@ -480,7 +480,8 @@ def q_project_workspace_size(T: int, d: int, dcq: int, H: int) -> int:
 
 
 def q_project(h: torch.Tensor, w_dq: torch.Tensor, w_uq: torch.Tensor, w_qr: torch.Tensor, H: int,
-              out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None):
+              out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None,
+              q_c: Optional[torch.Tensor] = None, q_r: Optional[torch.Tensor] = None):
     """(q_c [T,H,128], q_r [T,H,64] before rotation) from hidden states (mla_q_project)."""
     T, d = h.shape
     dcq = w_dq.shape[0]
@@ -488,8 +489,12 @@ def q_project(h: torch.Tensor, w_dq: torch.Tensor, w_uq: torch.Tensor, w_qr: tor
     _need(w_dq, "w_dq", torch.bfloat16, (dcq, d))
     _need(w_uq, "w_uq", torch.bfloat16, (H * D_NOPE, dcq))
     _need(w_qr, "w_qr", torch.bfloat16, (H * D_R, dcq))
-    q_c = torch.empty((T, H, D_NOPE), dtype=out_dtype, device=h.device)
-    q_r = torch.empty((T, H, D_R), dtype=out_dtype, device=h.device)
+    if q_c is None:
+        q_c = torch.empty((T, H, D_NOPE), dtype=out_dtype, device=h.device)
+    if q_r is None:
+        q_r = torch.empty((T, H, D_R), dtype=out_dtype, device=h.device)
+    _need(q_c, "q_c", out_dtype, (T, H, D_NOPE))
+    _need(q_r, "q_r", out_dtype, (T, H, D_R))
     if workspace is None:
         workspace = _workspace(q_project_workspace_size(T, d, dcq, H), h.device)
     _check(lib().mla_q_project(_ptr(h), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(q_c), _ptr(q_r), T, d, dcq, H,

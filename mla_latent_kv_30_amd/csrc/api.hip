@@ -474,11 +474,19 @@ mla_status mla_kv_append(const void* h, const void* w_dkv, const void* w_kr, con
   void* c_kv = ws;
   void* k_r = ws + (size_t)T * MLA_D_C * (f32 ? 4 : 2);
   const hipStream_t st = (hipStream_t)stream;
-  mla_status e = run_linear(h, w_dkv, MLA_D_C, w_kr, MLA_D_R, c_kv, k_r, T, d, f32 ? 0 : 1, ws + inter,
-                            workspace_bytes - inter, st);
+  // A split product leaves its fp32 partials for the cache write to sum (one
+  // launch less); otherwise the product writes c^KV and k^R in the input
+  // precision of the cache write.
+  const bool split = plan_linear(T, MLA_ROW, d, device_cus()).splits > 1;
+  mla_status e = run_linear(h, w_dkv, MLA_D_C, w_kr, MLA_D_R, split ? nullptr : c_kv, split ? nullptr : k_r, T, d,
+                            f32 ? 0 : 1, ws + inter, workspace_bytes - inter, st);
   if (e != MLA_OK) return e;
   CacheWriteArgs a{c_kv, k_r, pos, slot, nullptr, 0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
                    cache->ckv_scale, cache->kr, rope_table(r)};
+  if (split) {
+    a.part = (const float*)(ws + inter);
+    a.splits = plan_linear(T, MLA_ROW, d, device_cus()).splits;
+  }
   return launched(launch_cache_write(a, kind, st));
 }
 

@@ -4,6 +4,8 @@
 // E4M3 with one fp32 scale per token per 128 channels (the 1x128 tile rule of
 // "DeepSeek-V3 Technical Report", process-cxr.github.io, §Fine-grained
 // quantization; E4M3 max 448 from "DeepSeek-V3 技术报告精读", §FP8 混合精度训练).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -92,7 +94,78 @@ __global__ void __launch_bounds__(256) cache_write_fp8_kernel(CacheWriteArgs a) 
   }
 }
 
+// The same stores from fp32 partial sums: one workgroup per token, wave w
+// owning c^KV channels 128w .. 128w+127 (one fp8 tile; two channels per lane)
+// and k^R pairs 8w .. 8w+7 (lanes 0..7).  Each channel's partials are loaded
+// in batches of 8 and added in plane order, then rounded once to the input
+// precision T (what the unsplit product would have written).
+// Channels ch and ch+1 (a float2) summed over the planes in plane order,
+// 0 + p_0 + p_1 + ...: batches of 16 planes, every load issued before the
+// adds (indices past the last plane re-read it and add zero).
+template <typename T>
+__device__ __forceinline__ float2 sum_planes2(const CacheWriteArgs& a, int t, int ch) {
+  const size_t plane = (size_t)a.T * kRow;
+  const float* p = a.part + (size_t)t * kRow + ch;
+  float2 s = make_float2(0.f, 0.f);
+  for (int i0 = 0; i0 < a.splits; i0 += 16) {
+    float2 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = *(const float2*)(p + (size_t)min(i0 + j, a.splits - 1) * plane);
+    // planes past the last add zero (exact), so no load waits on a branch
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool in = i0 + j < a.splits;
+      s.x += in ? v[j].x : 0.f;
+      s.y += in ? v[j].y : 0.f;
+    }
+  }
+  return make_float2((float)(T)s.x, (float)(T)s.y);
+}
+
+template <int KIND>
+__global__ void __launch_bounds__(256) cache_write_partials_kernel(CacheWriteArgs a) {
+  using T = typename std::conditional<KIND == kKindF32, float, bf16>::type;
+  const int t = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pos = a.pos[t];
+  const int slot = a.slot[t];
+  const int ch = 128 * wave + 2 * lane;
+  const float2 vv = sum_planes2<T>(a, t, ch);
+  const float v0 = vv.x, v1 = vv.y;
+  if constexpr (KIND == kKindFp8) {
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+    const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    const float q0 = fminf(fmaxf(__fdiv_rn(v0, scale), -448.0f), 448.0f);
+    const float q1 = fminf(fmaxf(__fdiv_rn(v1, scale), -448.0f), 448.0f);
+    const uint16_t codes = (uint16_t)(e4m3_rne(q0) | (e4m3_rne(q1) << 8));
+    *(uint16_t*)(a.ckv8 + (size_t)slot * kDc + ch) = codes;
+    if (lane == 0) a.scale8[(size_t)slot * 4 + wave] = scale;
+  } else {
+    T* row = (T*)a.rows + (size_t)slot * kRow;
+    row[ch] = (T)v0;
+    row[ch + 1] = (T)v1;
+  }
+  if (lane < 8) {
+    const int m = 8 * wave + lane;   // RoPE pair
+    const float2 xx = sum_planes2<T>(a, t, kDc + 2 * m);
+    const float x0 = xx.x, x1 = xx.y;
+    float cs, sn;
+    rope_cs(pos, a.rope.theta[m], cs, sn);
+    T* kr = KIND == kKindFp8 ? (T*)a.kr8 + (size_t)slot * kDr : (T*)a.rows + (size_t)slot * kRow + kDc;
+    kr[2 * m] = (T)(x0 * cs - x1 * sn);
+    kr[2 * m + 1] = (T)(x0 * sn + x1 * cs);
+  }
+}
+
 hipError_t launch_cache_write(const CacheWriteArgs& a, int kind, hipStream_t s) {
+  if (a.part) {
+    if (kind == kKindF32) hipLaunchKernelGGL(cache_write_partials_kernel<kKindF32>, dim3(a.T), dim3(256), 0, s, a);
+    else if (kind == kKindBf16) hipLaunchKernelGGL(cache_write_partials_kernel<kKindBf16>, dim3(a.T), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(cache_write_partials_kernel<kKindFp8>, dim3(a.T), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((a.T + 3) / 4), blk(256);
   if (kind == kKindF32) {
     hipLaunchKernelGGL(cache_write_rows_kernel<float>, grid, blk, 0, s, a);

@@ -76,6 +76,9 @@ struct CacheWriteArgs {
   float* scale8;
   void* kr8;
   RopeTable rope;
+  const float* part;    // non-NULL: inputs are the sums of `splits` fp32 partial
+  int32_t splits;       // planes [splits][T][576] (c^KV | k^R), rounded once to
+                        // the input precision (c_kv, k_r unused)
 };
 hipError_t launch_cache_write(const CacheWriteArgs& a, int kind, hipStream_t s);
 
@@ -101,9 +104,10 @@ struct LinearArgs {
   int32_t out_bf16;
   int32_t mt, nt, splits, kt_split;   // filled from the plan
 };
-constexpr int kLinSmall = 0;   // 64 x 64 tiles (N <= 64)
-constexpr int kLinMid = 1;     // 128 x 128
-constexpr int kLinLarge = 2;   // 256 x 256
+constexpr int kLinSkinny32 = 0;  // 128 W rows x 32 tokens (N <= 32)
+constexpr int kLinSkinny64 = 1;  // 128 x 64 (N <= 64)
+constexpr int kLinMid = 2;       // 128 x 128
+constexpr int kLinLarge = 3;     // 256 x 256
 struct LinearPlan {
   int cfg, tm, tn, mt, nt, splits, kt_split;
   size_t part_bytes;

@@ -37,11 +37,23 @@ __device__ __forceinline__ int tile_row(int p) {
 }
 __device__ __forceinline__ int chunk_perm(int p) { return 2 * ((p >> 2) & 3); }
 
-// Wait until at most the copies of this wave's `later` (0..2) most recently
+// Wait until at most the copies of this wave's `later` (0..4) most recently
 // issued steps are in flight (P copies per step).
-template <int P>
+template <int P, int MAXL>
 __device__ __forceinline__ void wait_steps(int later) {
-  if (later >= 2) wait_vmcnt<2 * P>(); else if (later == 1) wait_vmcnt<P>(); else wait_vmcnt<0>();
+  if constexpr (MAXL >= 4) {
+    if (later >= 4) { wait_vmcnt<4 * P>(); return; }
+  }
+  if constexpr (MAXL >= 3) {
+    if (later == 3) { wait_vmcnt<3 * P>(); return; }
+  }
+  if constexpr (MAXL >= 2) {
+    if (later == 2) { wait_vmcnt<2 * P>(); return; }
+  }
+  if constexpr (MAXL >= 1) {
+    if (later == 1) { wait_vmcnt<P>(); return; }
+  }
+  wait_vmcnt<0>();
 }
 
 template <int WM, int WN, int FM, int FN, int STAGES>
@@ -56,7 +68,8 @@ struct Tile {
   static constexpr int kLdsBytes = STAGES * kStageBytes;
   static_assert(kWaves == 4, "the copy plan puts copy c of every wave in row group c");
   static_assert(kCopies % kWaves == 0, "copies must split evenly over the waves");
-  static_assert(STAGES >= 2 && STAGES <= 4 && 2 * kPerWave < 64, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 2) * kPerWave < 64, "vmcnt range");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
 // Output tile of workgroup b: consecutive tiles go to one XCD (the hardware
@@ -146,7 +159,7 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
 
   for (int i = 0; i < steps; ++i) {
     // copies of step i are done once at most those of the later issued steps remain
-    wait_steps<T::kPerWave>(min(STAGES - 2, steps - 1 - i));
+    wait_steps<T::kPerWave, STAGES - 2>(min(STAGES - 2, steps - 1 - i));
     __syncthreads();
     if (i + STAGES - 1 < steps) issue(i + STAGES - 1);
     const uint32_t stage = lds0 + (uint32_t)((i % STAGES) * T::kStageBytes);
@@ -218,10 +231,21 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearArgs a) {
   const int m = 4 * (int)(idx - (size_t)n * M4);
   const size_t plane = (size_t)a.N * M;
   const float* p = a.part + (size_t)n * M + m;
-  float4 v = *(const float4*)p;
-  for (int s = 1; s < a.splits; ++s) {
-    const float4 w = *(const float4*)(p + s * plane);
-    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  // 0 + p_0 + p_1 + ... in plane order: batches of 16 planes, all loads
+  // issued before the adds (indices past the last plane re-read it)
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < a.splits; s0 += 16) {
+    float4 w[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = *(const float4*)(p + (size_t)min(s0 + j, a.splits - 1) * plane);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {   // past the last plane: add zero (exact)
+      const bool in = s0 + j < a.splits;
+      v.x += in ? w[j].x : 0.f;
+      v.y += in ? w[j].y : 0.f;
+      v.z += in ? w[j].z : 0.f;
+      v.w += in ? w[j].w : 0.f;
+    }
   }
   const bool first = m < a.M0;
   const int ld = first ? a.M0 : a.M1;
@@ -279,7 +303,8 @@ hipError_t run(LinearArgs a, hipStream_t st) {
   }
   hipLaunchKernelGGL(k, dim3(a.mt * a.nt, a.splits), dim3(T::kThreads), T::kLdsBytes, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
+  // no outputs named: the caller consumes the partials itself
+  if (e != hipSuccess || a.splits == 1 || a.y0 == nullptr) return e;
   const size_t n4 = (size_t)a.N * ((a.M0 + a.M1) / 4);
   hipLaunchKernelGGL(linear_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
@@ -287,10 +312,19 @@ hipError_t run(LinearArgs a, hipStream_t st) {
 
 }  // namespace
 
+// Tile shape by token count: decode-sized products (N <= 64) stream W
+// through 128-row tiles with 5-6 stages (one workgroup per compute unit keeps
+// 64-80 KB of W in flight); larger N use square tiles.  A product with at
+// most half as many output tiles as compute units is split over k, about one
+// workgroup per compute unit, with S N / K <= 1/16 so that the fp32 partials
+// (written once, read once) stay within a quarter of the weight bytes, and
+// at least 8 k steps per split so that the copy ring fills.
 LinearPlan plan_linear(int N, int M, int K, int cus) {
   LinearPlan p;
-  if (N <= 64) {
-    p.cfg = kLinSmall; p.tm = 64; p.tn = 64;
+  if (N <= 32) {
+    p.cfg = kLinSkinny32; p.tm = 128; p.tn = 32;
+  } else if (N <= 64) {
+    p.cfg = kLinSkinny64; p.tm = 128; p.tn = 64;
   } else if (N <= 512) {
     p.cfg = kLinMid; p.tm = 128; p.tn = 128;
   } else {
@@ -301,8 +335,11 @@ LinearPlan plan_linear(int N, int M, int K, int cus) {
   const int nk = K / kTK;
   const int tiles = p.mt * p.nt;
   int splits = 1;
-  if (tiles < cus) splits = (cus + tiles / 2) / tiles;     // about one workgroup per compute unit
-  splits = max(1, min(splits, nk / 2 > 0 ? nk / 2 : 1));    // at least two k steps per split
+  if (tiles * 2 <= cus) {
+    splits = cus / tiles;                                  // one workgroup per compute unit
+    splits = min(splits, max(1, K / (16 * N)));            // partial bytes <= weight bytes / 4
+    splits = min(splits, max(1, nk / 8));                  // at least 8 k steps (a full ring) per split
+  }
   p.kt_split = (nk + splits - 1) / splits;
   p.splits = (nk + p.kt_split - 1) / p.kt_split;
   p.part_bytes = p.splits > 1 ? (size_t)p.splits * N * M * sizeof(float) : 0;
@@ -315,7 +352,8 @@ hipError_t launch_linear(LinearArgs a, const LinearPlan& p, hipStream_t st) {
   a.splits = p.splits;
   a.kt_split = p.kt_split;
   switch (p.cfg) {
-    case kLinSmall: return run<2, 2, 1, 1, 4>(a, st);
+    case kLinSkinny32: return run<4, 1, 1, 1, 6>(a, st);
+    case kLinSkinny64: return run<4, 1, 1, 2, 5>(a, st);
     case kLinMid: return run<2, 2, 2, 2, 3>(a, st);
     default: return run<2, 2, 4, 4, 2>(a, st);
   }

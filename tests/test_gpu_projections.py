@@ -136,6 +136,36 @@ def test_kv_append_matches_oracle(cache_dtype):
     assert _rel(k, ref["k_r_rot"]) <= (BF16_TOL if cache_dtype == "fp8" else tol)
 
 
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8", "f32"])
+def test_kv_append_new_tokens_split(cache_dtype):
+    """Decode shape: one new token per sequence (T = 16) and a long
+    contraction, so the product is split over k and the cache write sums
+    the partials itself."""
+    wl = W.make_workload("decode_h16", B=16, H=16, lens=list(range(40, 200, 10)))
+    d = 4096
+    assert mla.linear_workspace_size(wl.B, 576, d) > 0   # the split path
+    _note(f"case kv_append new tokens cache={cache_dtype} d={d}")
+    lay = W.paged_layout(wl)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": "fp8"}[cache_dtype]
+    cache = mla.PagedCache(lay.num_pages, dt, device=DEV, fill=float("nan"))
+    wts = W.projection_weights(wl, d=d)
+    h = W.new_token_hidden(wl, d)
+    last = lay.offsets[1:] - 1
+    pos, slots = lay.positions[last], lay.slots[last]
+    mla.kv_append(cache, _bf(h), _bf(wts["w_dkv"]), _bf(wts["w_kr"]), torch.as_tensor(pos, device=DEV),
+                  torch.as_tensor(slots, device=DEV))
+    torch.cuda.synchronize()
+    ref = orc.kv_projection(h, wts["w_dkv"], wts["w_kr"], pos)
+    c, k = _cache_rows(cache, slots)
+    tol = {"bf16": BF16_TOL, "f32": F32_TOL, "fp8": FP8_TOL}[cache_dtype]
+    assert _rel(c, ref["c_kv"]) <= tol
+    assert _rel(k, ref["k_r_rot"]) <= (BF16_TOL if cache_dtype == "fp8" else tol)
+    # the rows of the other tokens are untouched (still NaN)
+    other = np.setdiff1d(lay.slots, slots)[:50]
+    oc, _ = _cache_rows(cache, other)
+    assert np.isnan(oc).all()
+
+
 def test_kv_append_yarn_rotation():
     wl = W.make_workload("decode_h16", B=1, H=16, lens=[300])
     d = 512
