@@ -214,6 +214,8 @@ def main():
         slot_new = torch.from_numpy((dd.layout.block_table[np.arange(B), last // 64].astype(np.int64) * 64
                                      + last % 64).astype(np.int32)).to(dev)
         dcq = lw0["w_dq"].shape[0]
+        ws_qkv = torch.empty(max(1, mla.qkv_project_workspace_size(B, D, dcq, H, dd.cache.code)), dtype=torch.uint8,
+                             device=dev)
         ws_q = torch.empty(max(1, mla.q_project_workspace_size(B, D, dcq, H)), dtype=torch.uint8, device=dev)
         ws_kv = torch.empty(max(1, mla.kv_append_workspace_size(B, D, dd.cache.code)), dtype=torch.uint8,
                             device=dev)
@@ -249,6 +251,11 @@ def main():
         cache, *_, lw = reps[r]
         mla.kv_append(cache, lw["h"], lw["w_dkv"], lw["w_kr"], pos_q, slot_new, workspace=ws_kv)
 
+    def qkv_proj(r):
+        cache, q_c, q_r, *_, lw = reps[r]
+        mla.qkv_project(cache, lw["h"], lw["w_dq"], lw["w_dkv"], lw["w_kr"], lw["w_uq"], lw["w_qr"], pos_q, slot_new,
+                        H, workspace=ws_qkv, q_c=q_c, q_r=q_r)
+
     def out_proj(r):
         lw = reps[r][-1]
         mla.output_proj(o, lw["w_o"], workspace=ws_o, out=u)
@@ -256,8 +263,7 @@ def main():
     def step(r):
         cache, q_c, q_r, w_uk, w_uv, lw = reps[r]
         if LAYER:
-            q_proj(r)
-            kv_app(r)
+            qkv_proj(r)
         mla.absorb_q(q_c, q_r, pos_q, w_uk, out=q_abs)
         if QL > 1:
             mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
@@ -348,12 +354,14 @@ def main():
         # activations in and out, intermediates written and read once)
         tok_b = {"bf16": 1152, "fp8": 656}[wl.dtype]
         nbytes = {
+            "qkv_project": 2 * ((dcq + 576) * D + H * 192 * dcq + B * D + 2 * B * dcq + B * H * 192) + B * tok_b,
             "q_project": 2 * (dcq * D + H * 192 * dcq + B * D + 2 * B * dcq + B * H * 192),
             "kv_append": 2 * (576 * D + B * D + 2 * B * 576) + B * tok_b,
             "output_proj": 2 * (D * H * 128 + B * H * 128) + 4 * B * D,
         }
         layer = {"d_model": D, "d_cq": dcq}
-        for name, call in (("q_project", q_proj), ("kv_append", kv_app), ("output_proj", out_proj)):
+        for name, call in (("qkv_project", qkv_proj), ("q_project", q_proj), ("kv_append", kv_app),
+                           ("output_proj", out_proj)):
             ms = timed_batches(call)[1]
             gbs_p = nbytes[name] / (ms * 1e-3) / 1e9
             layer[name] = {"us": ms * 1e3, "alg_bytes": nbytes[name], "GB/s": gbs_p, "hbm_frac": gbs_p / PEAK_HBM_GBS}
@@ -405,7 +413,8 @@ def main():
             "workload": wl.name + (f"+layer(d={D})" if LAYER else ""), "batch": B, "heads": H, "cached_tokens": total,
             "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
             "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
-            "step": ("q_project + kv_append + absorb_q + decode_partial + decode_merge_upproj + output_proj"
+            "step": ("qkv_project (cache append + query path) + absorb_q + decode_partial + decode_merge_upproj"
+                     " + output_proj"
                      if LAYER else
                      "absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)" if QL == 1
                      else "absorb_q + decode_multi (decode + split merge) + upproj_v"),

@@ -371,6 +371,24 @@ mla_status mla_q_project(const void* h, const void* w_dq, const void* w_uq, cons
                          int32_t T, int32_t d, int32_t dcq, int32_t H, int32_t out_dtype, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of mla_qkv_project (cache_dtype: the cache's dtype). */
+size_t mla_qkv_project_workspace_size(int32_t T, int32_t d, int32_t dcq, int32_t H, int32_t cache_dtype);
+
+/*
+ * mla_qkv_project — mla_kv_append and mla_q_project of the same T tokens
+ * in one call: both start from h (§KeyValue, §Query), so c^Q, c^KV and the
+ * unrotated k^R come out of one product h [W^DQ; W^DKV; W^KR]^T; the cache
+ * rows are then stored as mla_kv_append stores them and q_c, q_r computed
+ * as mla_q_project computes them (rounded at the same points; the fp32 sums
+ * may be grouped differently when the two plans split the product
+ * differently).  Arguments as for those two calls.
+ * Errors: MLA_ERR_INVALID_ARG; MLA_ERR_WORKSPACE.
+ */
+mla_status mla_qkv_project(const void* h, const void* w_dq, const void* w_dkv, const void* w_kr, const void* w_uq,
+                           const void* w_qr, const int32_t* pos, const int32_t* slot, int32_t T, int32_t d,
+                           int32_t dcq, int32_t H, const mla_cache* cache, const mla_rope* rope, void* q_c,
+                           void* q_r, int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * mla_output_proj — u = W^O [o_1; ...; o_H] (§注意力计算), N tokens.
  *   x  [N][K] bf16: the head outputs o [N][H][128] (K = 128 H), or the

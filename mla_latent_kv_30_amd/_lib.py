@@ -118,6 +118,11 @@ def lib() -> ctypes.CDLL:
     L.mla_q_project_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
     L.mla_q_project.restype = _i32
     L.mla_q_project.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+    L.mla_qkv_project_workspace_size.restype = _sz
+    L.mla_qkv_project_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    L.mla_qkv_project.restype = _i32
+    L.mla_qkv_project.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                  ctypes.POINTER(MlaCache), ctypes.POINTER(MlaRope), _vp, _vp, _i32, _vp, _sz, _vp]
     L.mla_output_proj.restype = _i32
     L.mla_output_proj.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
     L.mla_fold_wuv_wo.restype = _i32
@@ -499,6 +504,42 @@ def q_project(h: torch.Tensor, w_dq: torch.Tensor, w_uq: torch.Tensor, w_qr: tor
         workspace = _workspace(q_project_workspace_size(T, d, dcq, H), h.device)
     _check(lib().mla_q_project(_ptr(h), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(q_c), _ptr(q_r), T, d, dcq, H,
                                _dt_code(out_dtype), *_ws_args(workspace), _stream(h.device)), "mla_q_project")
+    return q_c, q_r
+
+
+def qkv_project_workspace_size(T: int, d: int, dcq: int, H: int, cache_dtype: int) -> int:
+    return int(lib().mla_qkv_project_workspace_size(int(T), int(d), int(dcq), int(H), int(cache_dtype)))
+
+
+def qkv_project(cache: PagedCache, h: torch.Tensor, w_dq: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
+                w_uq: torch.Tensor, w_qr: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor, H: int,
+                out_dtype=torch.bfloat16, rope: Optional[MlaRope] = None, workspace: Optional[torch.Tensor] = None,
+                q_c: Optional[torch.Tensor] = None, q_r: Optional[torch.Tensor] = None):
+    """Cache append and query path of T tokens from h in one call
+    (mla_qkv_project); returns (q_c [T,H,128], q_r [T,H,64] before rotation)."""
+    T, d = h.shape
+    dcq = w_dq.shape[0]
+    _need(h, "h", torch.bfloat16, (T, d))
+    _need(w_dq, "w_dq", torch.bfloat16, (dcq, d))
+    _need(w_dkv, "w_dkv", torch.bfloat16, (D_C, d))
+    _need(w_kr, "w_kr", torch.bfloat16, (D_R, d))
+    _need(w_uq, "w_uq", torch.bfloat16, (H * D_NOPE, dcq))
+    _need(w_qr, "w_qr", torch.bfloat16, (H * D_R, dcq))
+    _need(pos, "pos", torch.int32, (T,))
+    _need(slot, "slot", torch.int32, (T,))
+    if q_c is None:
+        q_c = torch.empty((T, H, D_NOPE), dtype=out_dtype, device=h.device)
+    if q_r is None:
+        q_r = torch.empty((T, H, D_R), dtype=out_dtype, device=h.device)
+    _need(q_c, "q_c", out_dtype, (T, H, D_NOPE))
+    _need(q_r, "q_r", out_dtype, (T, H, D_R))
+    desc = cache.descriptor()
+    if workspace is None:
+        workspace = _workspace(qkv_project_workspace_size(T, d, dcq, H, desc.dtype), h.device)
+    _check(lib().mla_qkv_project(_ptr(h), _ptr(w_dq), _ptr(w_dkv), _ptr(w_kr), _ptr(w_uq), _ptr(w_qr), _ptr(pos),
+                                 _ptr(slot), T, d, dcq, H, ctypes.byref(desc),
+                                 None if rope is None else ctypes.byref(rope), _ptr(q_c), _ptr(q_r),
+                                 _dt_code(out_dtype), *_ws_args(workspace), _stream(h.device)), "mla_qkv_project")
     return q_c, q_r
 
 

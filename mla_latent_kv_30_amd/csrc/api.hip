@@ -411,22 +411,38 @@ bool linear_shape_ok(int N, int M0, int M1, int K) {
          (long long)N * (M0 + M1) * 4 <= kMaxOperandBytes;
 }
 
-mla_status run_linear(const void* x, const void* w0, int M0, const void* w1, int M1, void* y0, void* y1, int N, int K,
-                      int out_bf16, uint8_t* ws, size_t ws_bytes, hipStream_t st) {
-  const LinearPlan p = plan_linear(N, M0 + M1, K, device_cus());
+// One product's row blocks of W and column blocks of Y.
+struct Blocks {
+  const void* w[kLinBlocks] = {nullptr, nullptr, nullptr};
+  void* y[kLinBlocks] = {nullptr, nullptr, nullptr};
+  int M[kLinBlocks] = {0, 0, 0};
+  int bf16_mask = 0;   // bit b: y[b] in bf16
+  int rows() const { return M[0] + M[1] + M[2]; }
+  void add(const void* wb, int m, void* yb, bool bf) {
+    int b = M[0] == 0 ? 0 : (M[1] == 0 ? 1 : 2);
+    w[b] = wb;
+    y[b] = yb;
+    M[b] = m;
+    if (bf) bf16_mask |= 1 << b;
+  }
+};
+
+// Y = X W^T.  With y[0] == NULL the product is split or not as planned and,
+// if split, leaves its partials in `ws` for the caller (no reduction).
+mla_status run_linear(const void* x, const Blocks& bl, int N, int K, uint8_t* ws, size_t ws_bytes, hipStream_t st) {
+  const LinearPlan p = plan_linear(N, bl.rows(), K, device_cus());
   if (p.part_bytes > 0 && (ws == nullptr || ws_bytes < p.part_bytes)) return MLA_ERR_WORKSPACE;
   LinearArgs a{};
   a.x = (const bf16*)x;
-  a.w0 = (const bf16*)w0;
-  a.w1 = (const bf16*)w1;
-  a.y0 = y0;
-  a.y1 = y1;
+  for (int b = 0; b < kLinBlocks; ++b) {
+    a.w[b] = (const bf16*)bl.w[b];
+    a.y[b] = bl.y[b];
+    a.Mb[b] = bl.M[b];
+  }
   a.part = (float*)ws;
   a.N = N;
   a.K = K;
-  a.M0 = M0;
-  a.M1 = M1;
-  a.out_bf16 = out_bf16;
+  a.out_bf16 = bl.bf16_mask;
   return launched(launch_linear(a, p, st));
 }
 
@@ -447,8 +463,11 @@ mla_status mla_linear(const void* x, const void* w0, int32_t M0, const void* w1,
   if (!x || !w0 || !y0 || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
   if (!linear_shape_ok(N, M0, M1, K)) return MLA_ERR_INVALID_ARG;
   if (M1 > 0 && (!w1 || !y1)) return MLA_ERR_INVALID_ARG;
-  return run_linear(x, w0, M0, M1 > 0 ? w1 : nullptr, M1, y0, M1 > 0 ? y1 : nullptr, N, K,
-                    out_dtype == MLA_BF16, (uint8_t*)workspace, workspace_bytes, (hipStream_t)stream);
+  const bool bf = out_dtype == MLA_BF16;
+  Blocks bl;
+  bl.add(w0, M0, y0, bf);
+  if (M1 > 0) bl.add(w1, M1, y1, bf);
+  return run_linear(x, bl, N, K, (uint8_t*)workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 size_t mla_kv_append_workspace_size(int32_t T, int32_t d, int32_t cache_dtype) {
@@ -477,15 +496,19 @@ mla_status mla_kv_append(const void* h, const void* w_dkv, const void* w_kr, con
   // A split product leaves its fp32 partials for the cache write to sum (one
   // launch less); otherwise the product writes c^KV and k^R in the input
   // precision of the cache write.
-  const bool split = plan_linear(T, MLA_ROW, d, device_cus()).splits > 1;
-  mla_status e = run_linear(h, w_dkv, MLA_D_C, w_kr, MLA_D_R, split ? nullptr : c_kv, split ? nullptr : k_r, T, d,
-                            f32 ? 0 : 1, ws + inter, workspace_bytes - inter, st);
+  const int splits = plan_linear(T, MLA_ROW, d, device_cus()).splits;
+  Blocks bl;
+  bl.add(w_dkv, MLA_D_C, splits > 1 ? nullptr : c_kv, !f32);
+  bl.add(w_kr, MLA_D_R, splits > 1 ? nullptr : k_r, !f32);
+  mla_status e = run_linear(h, bl, T, d, ws + inter, workspace_bytes - inter, st);
   if (e != MLA_OK) return e;
   CacheWriteArgs a{c_kv, k_r, pos, slot, nullptr, 0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
                    cache->ckv_scale, cache->kr, rope_table(r)};
-  if (split) {
+  if (splits > 1) {
     a.part = (const float*)(ws + inter);
-    a.splits = plan_linear(T, MLA_ROW, d, device_cus()).splits;
+    a.splits = splits;
+    a.part_ld = MLA_ROW;
+    a.part_col = 0;
   }
   return launched(launch_cache_write(a, kind, st));
 }
@@ -508,18 +531,84 @@ mla_status mla_q_project(const void* h, const void* w_dq, const void* w_uq, cons
   uint8_t* ws = (uint8_t*)workspace;
   const size_t inter = align256((size_t)T * dcq * 2);
   const hipStream_t st = (hipStream_t)stream;
-  mla_status e = run_linear(h, w_dq, dcq, nullptr, 0, ws, nullptr, T, d, 1, ws + inter, workspace_bytes - inter, st);
+  Blocks b1;
+  b1.add(w_dq, dcq, ws, true);
+  mla_status e = run_linear(h, b1, T, d, ws + inter, workspace_bytes - inter, st);
   if (e != MLA_OK) return e;
-  return run_linear(ws, w_uq, H * MLA_D_NOPE, w_qr, H * MLA_D_R, q_c, q_r, T, dcq, out_dtype == MLA_BF16,
-                    ws + inter, workspace_bytes - inter, st);
+  const bool bf = out_dtype == MLA_BF16;
+  Blocks b2;
+  b2.add(w_uq, H * MLA_D_NOPE, q_c, bf);
+  b2.add(w_qr, H * MLA_D_R, q_r, bf);
+  return run_linear(ws, b2, T, dcq, ws + inter, workspace_bytes - inter, st);
+}
+
+size_t mla_qkv_project_workspace_size(int32_t T, int32_t d, int32_t dcq, int32_t H, int32_t cache_dtype) {
+  if (H < 1 || H > MLA_MAX_HEADS || !linear_shape_ok(T, dcq, MLA_ROW, d)) return 0;
+  if (!linear_shape_ok(T, H * MLA_D_NOPE, H * MLA_D_R, dcq)) return 0;
+  const size_t el = cache_dtype == MLA_F32 ? 4 : 2;
+  const size_t a = linear_ws(T, dcq + MLA_ROW, d), b = linear_ws(T, H * (MLA_D_NOPE + MLA_D_R), dcq);
+  return align256((size_t)T * dcq * 2) + align256((size_t)T * MLA_ROW * el) + (a > b ? a : b);
+}
+
+mla_status mla_qkv_project(const void* h, const void* w_dq, const void* w_dkv, const void* w_kr, const void* w_uq,
+                           const void* w_qr, const int32_t* pos, const int32_t* slot, int32_t T, int32_t d,
+                           int32_t dcq, int32_t H, const mla_cache* cache, const mla_rope* rope, void* q_c,
+                           void* q_r, int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h || !w_dq || !w_dkv || !w_kr || !w_uq || !w_qr || !pos || !slot || !q_c || !q_r || !dtype_ok(out_dtype))
+    return MLA_ERR_INVALID_ARG;
+  if (H < 1 || H > MLA_MAX_HEADS || !linear_shape_ok(T, dcq, MLA_ROW, d)) return MLA_ERR_INVALID_ARG;
+  if (!linear_shape_ok(T, H * MLA_D_NOPE, H * MLA_D_R, dcq)) return MLA_ERR_INVALID_ARG;
+  const mla_rope r = rope ? *rope : plain_rope(10000.0f);
+  if (!rope_ok(r)) return MLA_ERR_INVALID_ARG;
+  const int kind = cache_kind(cache);
+  if (kind < 0) return MLA_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < mla_qkv_project_workspace_size(T, d, dcq, H, cache->dtype))
+    return MLA_ERR_WORKSPACE;
+  const bool f32 = kind == kKindF32;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* cq = ws;
+  uint8_t* kv = cq + align256((size_t)T * dcq * 2);
+  uint8_t* part = kv + align256((size_t)T * MLA_ROW * (f32 ? 4 : 2));
+  const size_t part_bytes = workspace_bytes - (size_t)(part - ws);
+  void* c_kv = kv;
+  void* k_r = kv + (size_t)T * MLA_D_C * (f32 ? 4 : 2);
+  const hipStream_t st = (hipStream_t)stream;
+  // h [W^DQ; W^DKV; W^KR]^T in one product.  Split: one workgroup per token
+  // then sums the partials into c^Q and the cache rows; otherwise the
+  // product writes c^Q, c^KV, k^R and the cache write follows.
+  const int splits = plan_linear(T, dcq + MLA_ROW, d, device_cus()).splits;
+  Blocks b1;
+  b1.add(w_dq, dcq, splits > 1 ? nullptr : cq, true);
+  b1.add(w_dkv, MLA_D_C, splits > 1 ? nullptr : c_kv, !f32);
+  b1.add(w_kr, MLA_D_R, splits > 1 ? nullptr : k_r, !f32);
+  mla_status e = run_linear(h, b1, T, d, part, part_bytes, st);
+  if (e != MLA_OK) return e;
+  CacheWriteArgs a{c_kv, k_r, pos, slot, nullptr, 0, T, cache->rows, (uint8_t*)cache->ckv_fp8,
+                   cache->ckv_scale, cache->kr, rope_table(r)};
+  if (splits > 1) {
+    a.part = (const float*)part;
+    a.splits = splits;
+    a.part_ld = dcq + MLA_ROW;
+    a.part_col = dcq;
+    a.cq = (bf16*)cq;
+    a.cq_width = dcq;
+  }
+  e = launched(launch_cache_write(a, kind, st));
+  if (e != MLA_OK) return e;
+  const bool bf = out_dtype == MLA_BF16;
+  Blocks b2;
+  b2.add(w_uq, H * MLA_D_NOPE, q_c, bf);
+  b2.add(w_qr, H * MLA_D_R, q_r, bf);
+  return run_linear(cq, b2, T, dcq, part, part_bytes, st);
 }
 
 mla_status mla_output_proj(const void* x, const void* w, void* u, int32_t N, int32_t K, int32_t d, int32_t out_dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !w || !u || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
   if (K % MLA_D_V != 0 || !linear_shape_ok(N, d, 0, K)) return MLA_ERR_INVALID_ARG;
-  return run_linear(x, w, d, nullptr, 0, u, nullptr, N, K, out_dtype == MLA_BF16, (uint8_t*)workspace,
-                    workspace_bytes, (hipStream_t)stream);
+  Blocks bl;
+  bl.add(w, d, u, out_dtype == MLA_BF16);
+  return run_linear(x, bl, N, K, (uint8_t*)workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 mla_status mla_fold_wuv_wo(const void* w_uv, const void* w_o, void* w_fold, int32_t H, int32_t d, void* stream) {

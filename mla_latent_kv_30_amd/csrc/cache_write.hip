@@ -94,18 +94,19 @@ __global__ void __launch_bounds__(256) cache_write_fp8_kernel(CacheWriteArgs a) 
   }
 }
 
-// The same stores from fp32 partial sums: one workgroup per token, wave w
+// The same stores from fp32 partial sums (plane row stride part_ld, c^KV at
+// column part_col): one workgroup per token, wave w
 // owning c^KV channels 128w .. 128w+127 (one fp8 tile; two channels per lane)
 // and k^R pairs 8w .. 8w+7 (lanes 0..7).  Each channel's partials are loaded
 // in batches of 8 and added in plane order, then rounded once to the input
 // precision T (what the unsplit product would have written).
-// Channels ch and ch+1 (a float2) summed over the planes in plane order,
+// Plane columns col and col+1 (a float2) summed over the planes in plane order,
 // 0 + p_0 + p_1 + ...: batches of 16 planes, every load issued before the
 // adds (indices past the last plane re-read it and add zero).
 template <typename T>
-__device__ __forceinline__ float2 sum_planes2(const CacheWriteArgs& a, int t, int ch) {
-  const size_t plane = (size_t)a.T * kRow;
-  const float* p = a.part + (size_t)t * kRow + ch;
+__device__ __forceinline__ float2 sum_planes2(const CacheWriteArgs& a, int t, int col) {
+  const size_t plane = (size_t)a.T * a.part_ld;
+  const float* p = a.part + (size_t)t * a.part_ld + col;
   float2 s = make_float2(0.f, 0.f);
   for (int i0 = 0; i0 < a.splits; i0 += 16) {
     float2 v[16];
@@ -130,7 +131,7 @@ __global__ void __launch_bounds__(256) cache_write_partials_kernel(CacheWriteArg
   const int pos = a.pos[t];
   const int slot = a.slot[t];
   const int ch = 128 * wave + 2 * lane;
-  const float2 vv = sum_planes2<T>(a, t, ch);
+  const float2 vv = sum_planes2<T>(a, t, a.part_col + ch);
   const float v0 = vv.x, v1 = vv.y;
   if constexpr (KIND == kKindFp8) {
     float amax = fmaxf(fabsf(v0), fabsf(v1));
@@ -149,13 +150,23 @@ __global__ void __launch_bounds__(256) cache_write_partials_kernel(CacheWriteArg
   }
   if (lane < 8) {
     const int m = 8 * wave + lane;   // RoPE pair
-    const float2 xx = sum_planes2<T>(a, t, kDc + 2 * m);
+    const float2 xx = sum_planes2<T>(a, t, a.part_col + kDc + 2 * m);
     const float x0 = xx.x, x1 = xx.y;
     float cs, sn;
     rope_cs(pos, a.rope.theta[m], cs, sn);
     T* kr = KIND == kKindFp8 ? (T*)a.kr8 + (size_t)slot * kDr : (T*)a.rows + (size_t)slot * kRow + kDc;
     kr[2 * m] = (T)(x0 * cs - x1 * sn);
     kr[2 * m + 1] = (T)(x0 * sn + x1 * cs);
+  }
+  // the query's latent c^Q, when it shares the planes (columns 0 .. cq_width-1)
+  if (a.cq) {
+    for (int c2 = threadIdx.x; 2 * c2 < a.cq_width; c2 += 256) {
+      const float2 q = sum_planes2<bf16>(a, t, 2 * c2);
+      bf16x2 o;
+      o[0] = f2bf(q.x);
+      o[1] = f2bf(q.y);
+      *(bf16x2*)(a.cq + (size_t)t * a.cq_width + 2 * c2) = o;
+    }
   }
 }
 

@@ -77,8 +77,11 @@ struct CacheWriteArgs {
   void* kr8;
   RopeTable rope;
   const float* part;    // non-NULL: inputs are the sums of `splits` fp32 partial
-  int32_t splits;       // planes [splits][T][576] (c^KV | k^R), rounded once to
-                        // the input precision (c_kv, k_r unused)
+  int32_t splits;       // planes [splits][T][part_ld], c^KV | k^R at columns
+  int32_t part_ld;      // part_col .. part_col+575, rounded once to the input
+  int32_t part_col;     // precision (c_kv, k_r unused)
+  bf16* cq;             // optional: columns 0 .. cq_width-1 of the planes,
+  int32_t cq_width;     // summed and stored as bf16 [T][cq_width]
 };
 hipError_t launch_cache_write(const CacheWriteArgs& a, int kind, hipStream_t s);
 
@@ -91,17 +94,18 @@ struct UpprojArgs {
 };
 hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s);
 
-// Y = X W^T (bf16 operands, fp32 accumulate); W is the row concatenation
-// [w0 (M0 rows); w1 (M1 rows)] and Y the column concatenation [y0 | y1].
+// Y = X W^T (bf16 operands, fp32 accumulate); W is the row concatenation of
+// up to three blocks [w[0]; w[1]; w[2]] (Mb[b] rows each, multiples of 32)
+// and Y the matching column concatenation [y[0] | y[1] | y[2]].
+constexpr int kLinBlocks = 3;
 struct LinearArgs {
-  const bf16* x;    // [N][K]
-  const bf16* w0;   // [M0][K]
-  const bf16* w1;   // [M1][K] (M1 == 0: unused)
-  void* y0;         // [N][M0]
-  void* y1;         // [N][M1]
-  float* part;      // [splits][N][M0+M1] fp32 partials (splits > 1)
-  int32_t N, K, M0, M1;
-  int32_t out_bf16;
+  const bf16* x;                 // [N][K]
+  const bf16* w[kLinBlocks];     // [Mb[b]][K]
+  void* y[kLinBlocks];           // [N][Mb[b]]
+  int32_t Mb[kLinBlocks];        // 0: block absent
+  float* part;                   // [splits][N][M] fp32 partials (splits > 1)
+  int32_t N, K;
+  int32_t out_bf16;              // bit b: y[b] in bf16 (else fp32)
   int32_t mt, nt, splits, kt_split;   // filled from the plan
 };
 constexpr int kLinSkinny32 = 0;  // 128 W rows x 32 tokens (N <= 32)

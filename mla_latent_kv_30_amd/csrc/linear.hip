@@ -88,6 +88,22 @@ __device__ __forceinline__ void tile_of(int b, int mt, int nt, int& m, int& n) {
   m = g * gm + (r - n * width);
 }
 
+// Y[n][m .. m+3] (m % 4 == 0; the four features lie in one block of Y).
+__device__ __forceinline__ void store_out(const LinearArgs& a, int n, int m, float4 v) {
+  const int e1 = a.Mb[0], e2 = a.Mb[0] + a.Mb[1];
+  const int b = m < e1 ? 0 : (m < e2 ? 1 : 2);
+  const int mm = m - (b == 0 ? 0 : (b == 1 ? e1 : e2));
+  const size_t at = (size_t)n * a.Mb[b] + mm;
+  void* y = a.y[b];
+  if ((a.out_bf16 >> b) & 1) {
+    bf16x4 h;
+    h[0] = f2bf(v.x); h[1] = f2bf(v.y); h[2] = f2bf(v.z); h[3] = f2bf(v.w);
+    *(bf16x4*)((bf16*)y + at) = h;
+  } else {
+    *(float4*)((float*)y + at) = v;
+  }
+}
+
 template <int WM, int WN, int FM, int FN, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   using T = Tile<WM, WN, FM, FN, STAGES>;
@@ -110,15 +126,19 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   // LDS rows 8q .. 8q+7, i.e. rows 8 wave + l/8 of the stage's 32-row group
   // c.  The lane part of the offset is the same for every copy of a wave;
   // the group's first row is a scalar.  W groups come first (features), then
-  // X groups (tokens); the 32 rows of a W group sit in one of w0, w1.
+  // X groups (tokens); the 32 rows of a W group sit in one block of W (rows
+  // past the last block read as zeros).
   const uint32_t lds0 = lds_addr(lds);
   const uint32_t rowb = (uint32_t)a.K * 2;
   const int pr = 8 * wave + (lane >> 3);
   const uint32_t lane_vo = (uint32_t)tile_row(pr) * rowb + 16u * (uint32_t)((lane & 7) ^ chunk_perm(pr));
+  const int e1 = a.Mb[0], e2 = a.Mb[0] + a.Mb[1];
   const __amdgpu_buffer_rsrc_t rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(a.w0), (short)0, uniform((int)((uint32_t)a.M0 * rowb)), kRsrc3);
+      (void*)uniform_ptr(a.w[0]), (short)0, uniform((int)((uint32_t)a.Mb[0] * rowb)), kRsrc3);
   const __amdgpu_buffer_rsrc_t rs_w1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(a.w1), (short)0, uniform((int)((uint32_t)a.M1 * rowb)), kRsrc3);
+      (void*)uniform_ptr(a.w[1]), (short)0, uniform((int)((uint32_t)a.Mb[1] * rowb)), kRsrc3);
+  const __amdgpu_buffer_rsrc_t rs_w2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(a.w[2]), (short)0, uniform((int)((uint32_t)a.Mb[2] * rowb)), kRsrc3);
   const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
       (void*)uniform_ptr(a.x), (short)0, uniform((int)((uint32_t)a.N * rowb)), kRsrc3);
   auto issue = [&](int step) {
@@ -129,8 +149,9 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
       const uint32_t ldsq = stage + 1024u * (uint32_t)(wave + c * T::kWaves);
       if (32 * c < T::TM) {
         const int row0 = m0 + 32 * c;
-        if (row0 < a.M0) lds_dma16(rs_w0, ldsq, lane_vo + (uint32_t)row0 * rowb, koff);
-        else lds_dma16(rs_w1, ldsq, lane_vo + (uint32_t)(row0 - a.M0) * rowb, koff);
+        if (row0 < e1) lds_dma16(rs_w0, ldsq, lane_vo + (uint32_t)row0 * rowb, koff);
+        else if (row0 < e2) lds_dma16(rs_w1, ldsq, lane_vo + (uint32_t)(row0 - e1) * rowb, koff);
+        else lds_dma16(rs_w2, ldsq, lane_vo + (uint32_t)(row0 - e2) * rowb, koff);
       } else {
         lds_dma16(rs_x, ldsq, lane_vo + (uint32_t)(n0 + 32 * c - T::TM) * rowb, koff);
       }
@@ -185,7 +206,7 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   }
 
   // ---- epilogue: lane holds token (l % 32) and features 8q + 4hf + e ----
-  const int M = a.M0 + a.M1;
+  const int M = a.Mb[0] + a.Mb[1] + a.Mb[2];
 #pragma unroll
   for (int g = 0; g < FN; ++g) {
     const int n = n0 + (wn * FN + g) * 32 + (lane & 31);
@@ -205,17 +226,7 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
           *(float4*)(a.part + ((size_t)s * a.N + n) * M + m) = v;
           continue;
         }
-        const bool first = mg < a.M0;
-        const int ld = first ? a.M0 : a.M1;
-        const int mm = first ? m : m - a.M0;
-        void* y = first ? a.y0 : a.y1;
-        if (a.out_bf16) {
-          bf16x4 h;
-          h[0] = f2bf(v.x); h[1] = f2bf(v.y); h[2] = f2bf(v.z); h[3] = f2bf(v.w);
-          *(bf16x4*)((bf16*)y + (size_t)n * ld + mm) = h;
-        } else {
-          *(float4*)((float*)y + (size_t)n * ld + mm) = v;
-        }
+        store_out(a, n, m, v);
       }
     }
   }
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
 
 // Sum of the split partials (in split order) for 4 consecutive features.
 __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearArgs a) {
-  const int M = a.M0 + a.M1;
+  const int M = a.Mb[0] + a.Mb[1] + a.Mb[2];
   const int M4 = M / 4;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)a.N * M4) return;
@@ -247,17 +258,7 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearArgs a) {
       v.w += in ? w[j].w : 0.f;
     }
   }
-  const bool first = m < a.M0;
-  const int ld = first ? a.M0 : a.M1;
-  const int mm = first ? m : m - a.M0;
-  void* y = first ? a.y0 : a.y1;
-  if (a.out_bf16) {
-    bf16x4 h;
-    h[0] = f2bf(v.x); h[1] = f2bf(v.y); h[2] = f2bf(v.z); h[3] = f2bf(v.w);
-    *(bf16x4*)((bf16*)y + (size_t)n * ld + mm) = h;
-  } else {
-    *(float4*)((float*)y + (size_t)n * ld + mm) = v;
-  }
+  store_out(a, n, m, v);
 }
 
 // W'[r][512 i + c] = sum_j W^O[r][128 i + j] W_i^UV[j][c]: a one-time weight
@@ -304,8 +305,8 @@ hipError_t run(LinearArgs a, hipStream_t st) {
   hipLaunchKernelGGL(k, dim3(a.mt * a.nt, a.splits), dim3(T::kThreads), T::kLdsBytes, st, a);
   hipError_t e = hipGetLastError();
   // no outputs named: the caller consumes the partials itself
-  if (e != hipSuccess || a.splits == 1 || a.y0 == nullptr) return e;
-  const size_t n4 = (size_t)a.N * ((a.M0 + a.M1) / 4);
+  if (e != hipSuccess || a.splits == 1 || a.y[0] == nullptr) return e;
+  const size_t n4 = (size_t)a.N * ((a.Mb[0] + a.Mb[1] + a.Mb[2]) / 4);
   hipLaunchKernelGGL(linear_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -204,6 +204,47 @@ def test_q_project_matches_oracle(H, out):
     assert _rel(_host(q_r), ref["q_r"]) <= BF16_TOL
 
 
+# --------------------------------------------------------------------------- fused cache append + query path
+
+@pytest.mark.parametrize("T,cache_dtype", [(16, "bf16"), (16, "fp8"), (16, "f32"), (100, "bf16"), (100, "fp8")])
+def test_qkv_project_matches_oracle_and_the_separate_calls(T, cache_dtype):
+    """mla_qkv_project against the oracle's query and cache-append
+    projections, and bit for bit against mla_q_project + mla_kv_append
+    (T = 16: split product, partials summed in the cache write; T = 100:
+    unsplit)."""
+    H, d = 16, 2048
+    wl = W.make_workload("decode_h16", B=T, H=H)
+    _note(f"case qkv_project T={T} cache={cache_dtype} d={d}")
+    lay = W.paged_layout(wl)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": "fp8"}[cache_dtype]
+    c1 = mla.PagedCache(lay.num_pages, dt, device=DEV, fill=float("nan"))
+    c2 = mla.PagedCache(lay.num_pages, dt, device=DEV, fill=float("nan"))
+    wts = W.projection_weights(wl, d=d)
+    g = {k: _bf(v) for k, v in wts.items()}
+    h = W.new_token_hidden(wl, d)
+    hd = _bf(h)
+    last = lay.offsets[1:] - 1
+    pos, slots = lay.positions[last], lay.slots[last]
+    pos_d, slot_d = torch.as_tensor(pos, device=DEV), torch.as_tensor(slots, device=DEV)
+    q_c, q_r = mla.qkv_project(c1, hd, g["w_dq"], g["w_dkv"], g["w_kr"], g["w_uq"], g["w_qr"], pos_d, slot_d, H)
+    q_c2, q_r2 = mla.q_project(hd, g["w_dq"], g["w_uq"], g["w_qr"], H)
+    mla.kv_append(c2, hd, g["w_dkv"], g["w_kr"], pos_d, slot_d)
+    torch.cuda.synchronize()
+    assert torch.equal(q_c, q_c2) and torch.equal(q_r, q_r2)
+    for name in ("rows", "ckv", "scale", "kr"):
+        a, b = getattr(c1, name), getattr(c2, name)
+        if a is not None:
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+    refq = orc.query_projection(h, wts["w_dq"], wts["w_uq"], wts["w_qr"], pos, H)
+    assert _rel(_host(q_c), refq["q_c"]) <= BF16_TOL
+    assert _rel(_host(q_r), refq["q_r"]) <= BF16_TOL
+    refk = orc.kv_projection(h, wts["w_dkv"], wts["w_kr"], pos)
+    c, k = _cache_rows(c1, slots)
+    tol = {"bf16": BF16_TOL, "f32": F32_TOL, "fp8": FP8_TOL}[cache_dtype]
+    assert _rel(c, refk["c_kv"]) <= tol
+    assert _rel(k, refk["k_r_rot"]) <= (BF16_TOL if cache_dtype == "fp8" else tol)
+
+
 # --------------------------------------------------------------------------- output projection and fold
 
 def test_output_proj_matches_oracle():
