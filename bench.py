@@ -117,10 +117,38 @@ def run_prefill(args, wl, dev):
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     o = torch.empty((T, H, 128), dtype=torch.float32, device=dev)
 
+    LAYER = args.layer
+    if LAYER:
+        D = args.d_model
+        lw = {kk: td(v) for kk, v in W.projection_weights(wl, d=D).items()}
+        h = td(W.hidden_states(wl, 0, D))
+        dcq = lw["w_dq"].shape[0]
+        ws_q = torch.empty(max(1, mla.q_project_workspace_size(T, D, dcq, H)), dtype=torch.uint8, device=dev)
+        ws_kv = torch.empty(max(1, mla.linear_workspace_size(T, 576, D)), dtype=torch.uint8, device=dev)
+        ws_o = torch.empty(max(1, mla.linear_workspace_size(T, D, H * 128)), dtype=torch.uint8, device=dev)
+        o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        u = torch.empty((T, D), dtype=torch.float32, device=dev)
+
+    def q_proj():
+        mla.q_project(h, lw["w_dq"], lw["w_uq"], lw["w_qr"], H, workspace=ws_q, q_c=q_c, q_r=q_r)
+
+    def kv_proj():
+        c2, k2 = mla.linear(h, lw["w_dkv"], lw["w_kr"], workspace=ws_kv)
+        c.copy_(c2)
+        k.copy_(k2)
+
+    def out_proj():
+        mla.output_proj(o.view(T, H * 128), lw["w_o"], workspace=ws_o, out=u)
+
     def step():
+        if LAYER:
+            q_proj()
+            kv_proj()
         mla.absorb_q(q_c, q_r, pos, w_uk, out=q_abs)
         mla.prefill_causal(q_abs, c, k, cache, bt, z=z, lse=lse)
-        mla.upproj_v(z, w_uv, out=o)
+        mla.upproj_v(z, w_uv, out=o, out_dtype=o.dtype)
+        if LAYER:
+            out_proj()
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -148,13 +176,34 @@ def run_prefill(args, wl, dev):
     attn_flops = pairs * H * FLOP_PER_TOKEN_HEAD
     proj_flops = 2 * T * H * 2 * 128 * 512
     tflops_kernel = attn_flops / (kern_avg_ms * 1e-3) / 1e12
+    layer = None
+    if LAYER:
+        flops = {"q_project": 2 * T * (D * dcq + dcq * H * 192), "kv_projection": 2 * T * D * 576,
+                 "output_proj": 2 * T * H * 128 * D}
+        layer = {"d_model": D, "d_cq": dcq}
+        for name, call in (("q_project", q_proj), ("kv_projection", kv_proj), ("output_proj", out_proj)):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a0.record()
+            for _ in range(K):
+                call()
+            a1.record()
+            torch.cuda.synchronize()
+            ms = a0.elapsed_time(a1) / K
+            tf = flops[name] / (ms * 1e-3) / 1e12
+            layer[name] = {"us": ms * 1e3, "alg_flops": flops[name], "TFLOP/s": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+        proj_flops += sum(flops.values())
     out = {
         "metric": "MLA causal prefill TFLOP/s (absorbed attention + absorb + up-projection)",
         "value": (attn_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
         "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": T, "heads": H, "causal_pairs": pairs,
-                   "step": "absorb_q + prefill_causal (cache append + causal attention) + upproj_v"},
+        "config": {"workload": wl.name + (f"+layer(d={D})" if LAYER else ""), "tokens": T, "heads": H,
+                   "causal_pairs": pairs,
+                   "step": ("q_project + kv projection + " if LAYER else "") +
+                           "absorb_q + prefill_causal (cache append + causal attention) + upproj_v" +
+                           (" + output_proj" if LAYER else "")},
+        "layer": layer,
         "roofline": {
             "bound": "mfma", "achieved": tflops_kernel, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops_kernel / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "decode_mfma_kernel (prefill)",

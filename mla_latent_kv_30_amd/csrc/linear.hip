@@ -133,12 +133,6 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   const int pr = 8 * wave + (lane >> 3);
   const uint32_t lane_vo = (uint32_t)tile_row(pr) * rowb + 16u * (uint32_t)((lane & 7) ^ chunk_perm(pr));
   const int e1 = a.Mb[0], e2 = a.Mb[0] + a.Mb[1];
-  const __amdgpu_buffer_rsrc_t rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(a.w[0]), (short)0, uniform((int)((uint32_t)a.Mb[0] * rowb)), kRsrc3);
-  const __amdgpu_buffer_rsrc_t rs_w1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(a.w[1]), (short)0, uniform((int)((uint32_t)a.Mb[1] * rowb)), kRsrc3);
-  const __amdgpu_buffer_rsrc_t rs_w2 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(a.w[2]), (short)0, uniform((int)((uint32_t)a.Mb[2] * rowb)), kRsrc3);
   const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
       (void*)uniform_ptr(a.x), (short)0, uniform((int)((uint32_t)a.N * rowb)), kRsrc3);
   auto issue = [&](int step) {
@@ -147,13 +141,17 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
 #pragma unroll
     for (int c = 0; c < T::kPerWave; ++c) {
       const uint32_t ldsq = stage + 1024u * (uint32_t)(wave + c * T::kWaves);
-      if (32 * c < T::TM) {
+      if (32 * c < T::TM) {   // W group: its block chosen by selects, not branches
         const int row0 = m0 + 32 * c;
-        if (row0 < e1) lds_dma16(rs_w0, ldsq, lane_vo + (uint32_t)row0 * rowb, koff);
-        else if (row0 < e2) lds_dma16(rs_w1, ldsq, lane_vo + (uint32_t)(row0 - e1) * rowb, koff);
-        else lds_dma16(rs_w2, ldsq, lane_vo + (uint32_t)(row0 - e2) * rowb, koff);
+        const bool b0 = row0 < e1, b1 = row0 < e2;
+        const bf16* base = uniform_ptr(b0 ? a.w[0] : (b1 ? a.w[1] : a.w[2]));
+        const int rows = uniform(b0 ? a.Mb[0] : (b1 ? a.Mb[1] : a.Mb[2]));
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)((uint32_t)rows * rowb), kRsrc3);
+        const int r = uniform(row0 - (b0 ? 0 : (b1 ? e1 : e2)));
+        lds_dma16(rs, uniform((int)ldsq), lane_vo + (uint32_t)r * rowb, koff);
       } else {
-        lds_dma16(rs_x, ldsq, lane_vo + (uint32_t)(n0 + 32 * c - T::TM) * rowb, koff);
+        lds_dma16(rs_x, uniform((int)ldsq), lane_vo + (uint32_t)(n0 + 32 * c - T::TM) * rowb, koff);
       }
     }
   };
@@ -184,24 +182,34 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
     __syncthreads();
     if (i + STAGES - 1 < steps) issue(i + STAGES - 1);
     const uint32_t stage = lds0 + (uint32_t)((i % STAGES) * T::kStageBytes);
+    // Fragments of the four 16-k substeps, double-buffered: the reads of
+    // substep j+1 are issued before the products of substep j (the fence
+    // keeps them there; the pins keep the products after it), so each wait
+    // covers only reads issued one substep earlier.
+    bf16x8 af[2][FM], bfr[2][FN];
+    auto read = [&](int j, int buf) {
+      const uint32_t co = 16u * (uint32_t)((2 * j + hf) ^ cp);
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+        af[buf][f] = __builtin_bit_cast(bf16x8, lds_read_b128_at(stage + a_off + f * 32 * kSlice + co));
+#pragma unroll
+      for (int g = 0; g < FN; ++g)
+        bfr[buf][g] = __builtin_bit_cast(bf16x8, lds_read_b128_at(stage + b_off + g * 32 * kSlice + co));
+    };
+    read(0, 0);
 #pragma unroll
     for (int j = 0; j < kTK / 16; ++j) {
-      const uint32_t co = 16u * (uint32_t)((2 * j + hf) ^ cp);
-      bf16x8 af[FM], bfr[FN];
+      const int cur = j & 1;
+      if (j + 1 < kTK / 16) read(j + 1, cur ^ 1);
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int4v v = lds_read_b128_at(stage + a_off + f * 32 * kSlice + co);
-        af[f] = *(const bf16x8*)&v;
-      }
+      for (int f = 0; f < FM; ++f) asm volatile("" : "+v"(af[cur][f]));
 #pragma unroll
-      for (int g = 0; g < FN; ++g) {
-        const int4v v = lds_read_b128_at(stage + b_off + g * 32 * kSlice + co);
-        bfr[g] = *(const bf16x8*)&v;
-      }
+      for (int g = 0; g < FN; ++g) asm volatile("" : "+v"(bfr[cur][g]));
 #pragma unroll
       for (int f = 0; f < FM; ++f)
 #pragma unroll
-        for (int g = 0; g < FN; ++g) acc[f][g] = mfma32(af[f], bfr[g], acc[f][g]);
+        for (int g = 0; g < FN; ++g) acc[f][g] = mfma32(af[cur][f], bfr[cur][g], acc[f][g]);
     }
   }
 
