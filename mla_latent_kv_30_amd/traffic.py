@@ -9,8 +9,8 @@ counter reads for a plain device copy of known size run in the same command
     python -m mla_latent_kv_30_amd.traffic summarize --fetch DIR --write DIR \\
         --kernel decode_mfma_kernel --workload decode_h16 --out profiles/X.json
 
-The summary records a digest of the kernel sources; bench.py reports the
-traffic only while the sources still have that digest.
+The summary records a digest of the sources the kernel is built from;
+bench.py reports the traffic only while those sources still have that digest.
 """
 
 from __future__ import annotations
@@ -28,12 +28,22 @@ COPY_BYTES = 256 << 20        # bench.py --calibrate-copy
 COPY_KERNEL = "copyBuffer"    # the runtime's device-to-device copy kernel
 
 
-def source_digest() -> str:
-    """Digest of every kernel source the library is built from."""
+# The sources each measured kernel is compiled from (its file and the headers
+# it includes); other kernels are digested over every source.
+KERNEL_SOURCES = {
+    "decode_mfma_kernel": ("decode.hip", "decode_common.h", "common.h", "kernels.h"),
+    "decode_f32_kernel": ("decode.hip", "decode_common.h", "common.h", "kernels.h"),
+}
+
+
+def source_digest(kernel: str = "") -> str:
+    """Digest of the sources `kernel` is built from (every kernel source if unknown)."""
+    names = KERNEL_SOURCES.get(kernel)
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
-        if path.endswith((".hip", ".h")):
-            h.update(os.path.basename(path).encode())
+        base = os.path.basename(path)
+        if path.endswith((".hip", ".h")) and (names is None or base in names):
+            h.update(base.encode())
             with open(path, "rb") as f:
                 h.update(f.read())
     return h.hexdigest()[:16]
@@ -73,7 +83,7 @@ def summarize(fetch_dir: str, write_dir: str, kernel: str, workload: str) -> dic
     fetch_b = fetch_kib * 1024.0 * f_scale
     write_b = write_kib * 1024.0 * w_scale
     return {
-        "workload": workload, "kernel": kernel, "source_digest": source_digest(),
+        "workload": workload, "kernel": kernel, "source_digest": source_digest(kernel),
         "dispatches": {"fetch": len(fk), "write": len(wk)},
         "fetch_kib_median": fetch_kib, "write_kib_median": write_kib,
         "copy_fetch_kib": max(fc), "copy_write_kib": max(wc),
@@ -89,7 +99,7 @@ def load(kernel: str, workload: str, profiles_dir: str):
         return None
     with open(path) as f:
         d = json.load(f)
-    return d if d.get("source_digest") == source_digest() else None
+    return d if d.get("source_digest") == source_digest(kernel) else None
 
 
 def main():
@@ -103,9 +113,10 @@ def main():
     s.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     s.add_argument("--out", required=True)
     d = sub.add_parser("digest")
+    d.add_argument("--kernel", default="")
     args = ap.parse_args()
     if args.cmd == "digest":
-        print(source_digest())
+        print(source_digest(args.kernel))
         return
     out = summarize(args.fetch, args.write, args.kernel, args.workload)
     out["command"] = args.command
