@@ -66,7 +66,7 @@ struct Tile {
   static constexpr int kPerWave = kCopies / kWaves;
   static constexpr int kStageBytes = (TM + TN) * kSlice;
   static constexpr int kLdsBytes = STAGES * kStageBytes;
-  static_assert(kWaves == 4, "the copy plan puts copy c of every wave in row group c");
+  static_assert(kWaves == 4 || kWaves == 8, "the copy plan takes 4 or 8 waves");
   static_assert(kCopies % kWaves == 0, "copies must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 2) * kPerWave < 64, "vmcnt range");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
@@ -122,37 +122,35 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   const int steps = kt1 - kt0;
 
   // ---- copy plan ----
-  // Copy q of a stage (q = wave + 4 c) fills LDS bytes [q KB, q KB + 1 KB):
-  // LDS rows 8q .. 8q+7, i.e. rows 8 wave + l/8 of the stage's 32-row group
-  // c.  The lane part of the offset is the same for every copy of a wave;
-  // the group's first row is a scalar.  W groups come first (features), then
-  // X groups (tokens); the 32 rows of a W group sit in one block of W (rows
-  // past the last block read as zeros).
+  // Copy q of a stage (q = wave + W c, W waves) fills LDS bytes
+  // [q KB, q KB + 1 KB): LDS rows 8q .. 8q+7, i.e. rows 8 (wave % 4) + l/8
+  // of the stage's 32-row group q / 4 = (W/4) c + wave / 4.  The lane part
+  // of the offset is the same for every copy of a wave; the group's first
+  // row is a scalar.  W groups come first (features), then X groups
+  // (tokens); the 32 rows of a W group sit in one block of W (rows past the
+  // last block read as zeros).
   const uint32_t lds0 = lds_addr(lds);
   const uint32_t rowb = (uint32_t)a.K * 2;
-  const int pr = 8 * wave + (lane >> 3);
+  const int pr = 8 * (wave & 3) + (lane >> 3);
   const uint32_t lane_vo = (uint32_t)tile_row(pr) * rowb + 16u * (uint32_t)((lane & 7) ^ chunk_perm(pr));
   const int e1 = a.Mb[0], e2 = a.Mb[0] + a.Mb[1];
-  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(a.x), (short)0, uniform((int)((uint32_t)a.N * rowb)), kRsrc3);
   auto issue = [&](int step) {
     const uint32_t stage = lds0 + (uint32_t)((step % STAGES) * T::kStageBytes);
     const uint32_t koff = (uint32_t)((kt0 + step) * kSlice);
 #pragma unroll
     for (int c = 0; c < T::kPerWave; ++c) {
       const uint32_t ldsq = stage + 1024u * (uint32_t)(wave + c * T::kWaves);
-      if (32 * c < T::TM) {   // W group: its block chosen by selects, not branches
-        const int row0 = m0 + 32 * c;
-        const bool b0 = row0 < e1, b1 = row0 < e2;
-        const bf16* base = uniform_ptr(b0 ? a.w[0] : (b1 ? a.w[1] : a.w[2]));
-        const int rows = uniform(b0 ? a.Mb[0] : (b1 ? a.Mb[1] : a.Mb[2]));
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)((uint32_t)rows * rowb), kRsrc3);
-        const int r = uniform(row0 - (b0 ? 0 : (b1 ? e1 : e2)));
-        lds_dma16(rs, uniform((int)ldsq), lane_vo + (uint32_t)r * rowb, koff);
-      } else {
-        lds_dma16(rs_x, uniform((int)ldsq), lane_vo + (uint32_t)(n0 + 32 * c - T::TM) * rowb, koff);
-      }
+      const int gq = (T::kWaves / 4) * c + (wave >> 2);   // row group of this copy
+      // W group (block chosen by selects) or X group, no branches
+      const bool is_w = 32 * gq < T::TM;
+      const int row0 = m0 + 32 * gq;
+      const bool b0 = row0 < e1, b1 = row0 < e2;
+      const bf16* base = uniform_ptr(is_w ? (b0 ? a.w[0] : (b1 ? a.w[1] : a.w[2])) : a.x);
+      const int rows = uniform(is_w ? (b0 ? a.Mb[0] : (b1 ? a.Mb[1] : a.Mb[2])) : a.N);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)((uint32_t)rows * rowb), kRsrc3);
+      const int r = uniform(is_w ? row0 - (b0 ? 0 : (b1 ? e1 : e2)) : n0 + 32 * gq - T::TM);
+      lds_dma16(rs, uniform((int)ldsq), lane_vo + (uint32_t)r * rowb, koff);
     }
   };
 
@@ -364,7 +362,7 @@ hipError_t launch_linear(LinearArgs a, const LinearPlan& p, hipStream_t st) {
     case kLinSkinny32: return run<4, 1, 1, 1, 6>(a, st);
     case kLinSkinny64: return run<4, 1, 1, 2, 5>(a, st);
     case kLinMid: return run<2, 2, 2, 2, 3>(a, st);
-    default: return run<2, 2, 4, 4, 2>(a, st);
+    default: return run<2, 4, 4, 2, 2>(a, st);
   }
 }
 
