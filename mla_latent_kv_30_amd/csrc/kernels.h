@@ -112,6 +112,7 @@ constexpr int kLinSkinny32 = 0;  // 128 W rows x 32 tokens (N <= 32)
 constexpr int kLinSkinny64 = 1;  // 128 x 64 (N <= 64)
 constexpr int kLinMid = 2;       // 128 x 128
 constexpr int kLinLarge = 3;     // 256 x 256
+constexpr int kLinNarrow = 4;    // 64 x 64 (N <= 64, few output rows)
 struct LinearPlan {
   int cfg, tm, tn, mt, nt, splits, kt_split;
   size_t part_bytes;

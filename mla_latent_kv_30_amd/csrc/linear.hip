@@ -326,17 +326,9 @@ hipError_t run(LinearArgs a, hipStream_t st) {
 // workgroup per compute unit, with S N / K <= 1/16 so that the fp32 partials
 // (written once, read once) stay within a quarter of the weight bytes, and
 // at least 8 k steps per split so that the copy ring fills.
-LinearPlan plan_linear(int N, int M, int K, int cus) {
-  LinearPlan p;
-  if (N <= 32) {
-    p.cfg = kLinSkinny32; p.tm = 128; p.tn = 32;
-  } else if (N <= 64) {
-    p.cfg = kLinSkinny64; p.tm = 128; p.tn = 64;
-  } else if (N <= 512) {
-    p.cfg = kLinMid; p.tm = 128; p.tn = 128;
-  } else {
-    p.cfg = kLinLarge; p.tm = 256; p.tn = 256;
-  }
+namespace {
+
+void plan_splits(LinearPlan& p, int N, int M, int K, int cus) {
   p.mt = (M + p.tm - 1) / p.tm;
   p.nt = (N + p.tn - 1) / p.tn;
   const int nk = K / kTK;
@@ -350,6 +342,30 @@ LinearPlan plan_linear(int N, int M, int K, int cus) {
   p.kt_split = (nk + splits - 1) / splits;
   p.splits = (nk + p.kt_split - 1) / p.kt_split;
   p.part_bytes = p.splits > 1 ? (size_t)p.splits * N * M * sizeof(float) : 0;
+}
+
+}  // namespace
+
+LinearPlan plan_linear(int N, int M, int K, int cus) {
+  LinearPlan p;
+  if (N <= 32) {
+    p.cfg = kLinSkinny32; p.tm = 128; p.tn = 32;
+  } else if (N <= 64) {
+    p.cfg = kLinSkinny64; p.tm = 128; p.tn = 64;
+  } else if (N <= 512) {
+    p.cfg = kLinMid; p.tm = 128; p.tn = 128;
+  } else {
+    p.cfg = kLinLarge; p.tm = 256; p.tn = 256;
+  }
+  plan_splits(p, N, M, K, cus);
+  // a decode-sized product that 128-row tiles cannot spread over half of
+  // the compute units (few output rows, short contraction) takes 64-row tiles
+  if (N <= 64 && p.mt * p.nt * p.splits * 2 < cus) {
+    LinearPlan q;
+    q.cfg = kLinNarrow; q.tm = 64; q.tn = 64;
+    plan_splits(q, N, M, K, cus);
+    if (q.mt * q.nt * q.splits > p.mt * p.nt * p.splits) p = q;
+  }
   return p;
 }
 
@@ -362,6 +378,7 @@ hipError_t launch_linear(LinearArgs a, const LinearPlan& p, hipStream_t st) {
     case kLinSkinny32: return run<4, 1, 1, 1, 6>(a, st);
     case kLinSkinny64: return run<4, 1, 1, 2, 5>(a, st);
     case kLinMid: return run<2, 2, 2, 2, 3>(a, st);
+    case kLinNarrow: return run<2, 2, 1, 1, 6>(a, st);
     default: return run<2, 4, 4, 2, 2>(a, st);
   }
 }
