@@ -315,9 +315,9 @@ def main():
             qkv_proj(r)
         mla.absorb_q(q_c, q_r, pos_q, w_uk, out=q_abs)
         if QL > 1:
-            mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
-                             workspace=ws, z=z.view(B, QL, H, 512), lse=lse.view(B, QL, H))
-            mla.upproj_v(z, w_uv, out=o)
+            mla.decode_multi_upproj(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, w_uv,
+                                    num_splits=splits, workspace=ws, z=z.view(B, QL, H, 512),
+                                    lse=lse.view(B, QL, H), out=o.view(B, QL, H, 128))
         else:
             mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
             mla.decode_merge_upproj(dd.seq_lens, H, ws, z, w_uv, lse=lse, num_splits=splits, out=o, out_dtype=o.dtype)
@@ -466,7 +466,7 @@ def main():
                      " + output_proj"
                      if LAYER else
                      "absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)" if QL == 1
-                     else "absorb_q + decode_multi (decode + split merge) + upproj_v"),
+                     else "absorb_q + decode_multi_upproj (decode, then split merge + W_UV up-projection)"),
             "q_len": QL, "query_tokens_per_s": B * QL / (ms_per_step * 1e-3),
         },
         "layer": layer,

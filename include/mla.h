@@ -253,6 +253,23 @@ mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int
                             float* lse, void* stream);
 
 /*
+ * mla_decode_multi_upproj: mla_decode_multi followed by the value
+ * up-projection o = W_i^UV z (§潜在向量的作用) of every query token's heads:
+ * o [B][q_len][H][128] in o_dtype.  With a bf16 weight and B <= 32 the
+ * split merge and the up-projection run as one launch (as in
+ * mla_decode_merge_upproj; z stays fp32 in that product), otherwise as
+ * the merge and mla_upproj_v with N = B*q_len.  z and lse are written as
+ * mla_decode_multi writes them.  Errors: those of mla_decode_multi, plus
+ * MLA_ERR_INVALID_ARG for a NULL w_uv or o, or a dtype outside
+ * {MLA_F32, MLA_BF16}.
+ */
+mla_status mla_decode_multi_upproj(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
+                                   float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes, float* z,
+                                   float* lse, const void* w_uv, int32_t w_dtype, void* o, int32_t o_dtype,
+                                   void* stream);
+
+/*
  * mla_decode_merge_upproj: mla_decode_merge followed by mla_upproj_v on its z
  * (o_i = W_i^UV z_i, §潜在向量的作用), with N = B.  Arguments as for those
  * two calls; z and lse are written as mla_decode_merge writes them.  With a

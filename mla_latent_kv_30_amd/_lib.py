@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_multi.restype = _i32
     L.mla_decode_multi.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                    ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_decode_multi_upproj.restype = _i32
+    L.mla_decode_multi_upproj.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                                          _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp, _i32, _vp]
     L.mla_decode_merge_upproj.restype = _i32
     L.mla_decode_merge_upproj.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp,
                                           _i32, _vp]
@@ -357,6 +360,40 @@ def decode_multi(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tens
                                   block_table.shape[1], scale, int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
                                   _ptr(lse), _stream(dev)), "mla_decode_multi")
     return z, lse
+
+
+def decode_multi_upproj(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                        w_uv: torch.Tensor, softmax_scale: Optional[float] = None, num_splits: int = 0,
+                        workspace: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, out_dtype=torch.float32,
+                        out: Optional[torch.Tensor] = None):
+    """(o[B,q_len,H,128], z, lse) of q_len new tokens per sequence (mla_decode_multi_upproj)."""
+    B, q_len, H = q_abs.shape[0], q_abs.shape[1], q_abs.shape[2]
+    _need(q_abs, "q_abs", cache.input_dtype, (B, q_len, H, ROW))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(w_uv, "w_uv", None, (H, D_V, D_C))
+    dev = q_abs.device
+    if z is None:
+        z = torch.empty((B, q_len, H, D_C), dtype=torch.float32, device=dev)
+    _need(z, "z", torch.float32, (B, q_len, H, D_C))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, q_len, H))
+    if out is None:
+        out = torch.empty((B, q_len, H, D_V), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, (B, q_len, H, D_V))
+    if workspace is None:
+        workspace = decode_workspace(B, q_len * H, num_splits, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
+    desc = cache.descriptor()
+    _check(lib().mla_decode_multi_upproj(_ptr(q_abs), ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), B,
+                                         q_len, H, block_table.shape[1], scale, int(num_splits), _ptr(workspace),
+                                         ws_bytes, _ptr(z), _ptr(lse), _ptr(w_uv), _dt_code(w_uv.dtype), _ptr(out),
+                                         _dt_code(out_dtype), _stream(dev)), "mla_decode_multi_upproj")
+    return out, z, lse
 
 
 def decode_merge_upproj(seq_lens: torch.Tensor, H: int, workspace: Optional[torch.Tensor], z: torch.Tensor,

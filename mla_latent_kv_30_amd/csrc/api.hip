@@ -284,6 +284,7 @@ mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H
     memset(&m, 0, sizeof(m));
     m.d.B = B;
     m.d.H = H;
+    m.d.hs = H;
     m.d.z = z;
     m.d.lse = lse;
     set_workspace(m.d, workspace, B, H, p);
@@ -331,6 +332,41 @@ mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int
   st = launched(launch_decode(a, kind, s));
   if (st != MLA_OK || p.slots == 0) return st;
   return launched(launch_merge(a, s));
+}
+
+mla_status mla_decode_multi_upproj(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
+                                   float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes, float* z,
+                                   float* lse, const void* w_uv, int32_t w_dtype, void* o, int32_t o_dtype,
+                                   void* stream) {
+  if (q_len < 1 || H < 1 || (long long)q_len * H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (!w_uv || !o || !dtype_ok(w_dtype) || !dtype_ok(o_dtype)) return MLA_ERR_INVALID_ARG;
+  DecodeArgs a;
+  int kind;
+  Plan p;
+  mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, q_len * H, max_pages, softmax_scale,
+                                 num_splits, workspace, ws_bytes, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
+  a.q_len = q_len;
+  a.hs = H;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  st = launched(launch_decode(a, kind, s));
+  if (st != MLA_OK) return st;
+  if (w_dtype == MLA_BF16 && B <= kFusedMaxB) {
+    MergeUpArgs m;
+    memset(&m, 0, sizeof(m));
+    m.d = a;
+    m.w_uv = w_uv;
+    m.o = o;
+    m.o_bf16 = o_dtype == MLA_BF16 ? 1 : 0;
+    return launched(launch_merge_upproj(m, s));
+  }
+  if (p.slots > 0) {
+    st = launched(launch_merge(a, s));
+    if (st != MLA_OK) return st;
+  }
+  return mla_upproj_v(z, w_uv, o, B * q_len, H, w_dtype, o_dtype, stream);
 }
 
 mla_status mla_prefill_causal(const void* q_abs, const void* c_kv, const void* k_r, int32_t pos0,

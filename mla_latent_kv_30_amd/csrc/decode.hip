@@ -539,7 +539,8 @@ __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeUpArgs m) {
   const int head = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ __attribute__((aligned(16))) float zs[kDc];
-  const int4v* wrow = (const int4v*)((const bf16*)m.w_uv + ((size_t)head * kDv + 32 * wave) * kDc) + lane;
+  // multi-token decode: head h' of the merge is head h' % hs of token h' / hs
+  const int4v* wrow = (const int4v*)((const bf16*)m.w_uv + ((size_t)(head % a.hs) * kDv + 32 * wave) * kDc) + lane;
   int4v wv[32];
 #pragma unroll
   for (int r = 0; r < 32; ++r) wv[r] = wrow[r * (kDc / 8)];

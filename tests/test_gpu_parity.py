@@ -433,6 +433,39 @@ def test_multi_token_decode_matches_oracle(name, H, q_len, lens, tol):
             assert np.abs(ln - ref["lse"]).max() <= tol, ("lse", S)
 
 
+@pytest.mark.parametrize("name,H,q_len,lens,o_dtype", [
+    ("decode_h16", 16, 2, [1500, 9, 700, 64], torch.float32),     # fused merge + W^UV (B <= 32)
+    ("decode_h16", 32, 4, [3000, 200], torch.bfloat16),
+    ("tiny_f32", 16, 3, [300, 64, 5], torch.float32),             # fp32 weights: merge, then upproj_v
+    ("long_fp8", 64, 2, [2048, 131], torch.float32),
+])
+def test_multi_token_decode_upproj_matches_oracle(name, H, q_len, lens, o_dtype):
+    """mla_decode_multi_upproj: the up-projected outputs of every query token
+    (head h' of the merge takes W^UV row block h' % H), for the automatic and
+    explicit splits."""
+    wl = W.make_workload(name, B=len(lens), H=H, lens=lens)
+    _note(f"case multi-token upproj {name} H={H} q_len={q_len} lens={lens}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    q_c, q_r, pos, hq_c, hq_r = DI.multi_query_inputs(dd, q_len)
+    ref = _oracle_multi(dd, hq_c, hq_r, q_len)
+    B = wl.B
+    q_abs = mla.absorb_q(q_c, q_r, pos, dd.w_uk).view(B, q_len, H, 576)
+    tol = {"decode_h16": 2e-2, "long_fp8": 6e-2}.get(name)
+    for S in (0, 1, 3):
+        lse = torch.empty((B, q_len, H), device=DEV)
+        o, z, lse = mla.decode_multi_upproj(q_abs, dd.cache, dd.block_table, dd.seq_lens, dd.w_uv, num_splits=S,
+                                            lse=lse, out_dtype=o_dtype)
+        torch.cuda.synchronize()
+        on, zn, ln = o.float().cpu().numpy(), z.cpu().numpy(), lse.cpu().numpy()
+        if tol is None:  # fp32 path
+            assert np.abs(on - ref["o"]).max() <= 1e-5, S
+            assert np.abs(zn - ref["z"]).max() <= 1e-5, S
+        else:
+            assert _rel(on, ref["o"]) <= tol, ("o", S)
+            assert _rel(zn, ref["z"]) <= tol, ("z", S)
+            assert np.abs(ln - ref["lse"]).max() <= tol, ("lse", S)
+
+
 def test_multi_token_decode_with_one_token_equals_decode():
     wl = W.make_workload("decode_h16", B=3, H=16, lens=[3000, 77, 1])
     _note("case multi-token q_len=1")
