@@ -118,6 +118,26 @@ typedef struct {
  * YaRN applies to the attention scores; s <= 1 gives 1. */
 double mla_yarn_attention_factor(double s);
 
+/*
+ * Checks of what the decode entry points take on trust (device data the
+ * host does not read): every seq_lens[b] in [q_len, 64*max_pages] (q_len = 1
+ * for one query token per sequence) and, when block_table is not NULL, every
+ * page a sequence uses (entries 0 .. ceil(L_b/64)-1 of its row) in
+ * [0, num_pages).
+ * mla_validate_decode_inputs checks host copies:
+ *   seq_lens [B], block_table [B][max_pages] or NULL (host memory)
+ *   returns MLA_OK or MLA_ERR_INVALID_ARG.
+ * mla_set_debug(1) (or MLA_DEBUG=1 in the environment) makes mla_decode,
+ * mla_decode_partial, mla_decode_multi and mla_decode_multi_upproj copy the
+ * lengths and the block table to the host in stream order, synchronise the
+ * stream and apply the same check before launching (MLA_ERR_INVALID_ARG,
+ * nothing launched).  A debugging aid: it blocks the caller and cannot run
+ * under stream capture.
+ */
+mla_status mla_validate_decode_inputs(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
+                                      int32_t max_pages, int32_t num_pages, int32_t q_len);
+void mla_set_debug(int32_t on);
+
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int32_t status);
 

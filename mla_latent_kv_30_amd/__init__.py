@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     decode_merge_upproj, decode_multi, decode_multi_upproj, decode_partial, decode_workspace,
     decode_workspace_size, default_softmax_scale, lib, prefill_causal, status_string, upproj_v, MlaRope, yarn_rope,
     yarn_attention_factor, linear, linear_workspace_size, kv_append, kv_append_workspace_size, q_project,
-    q_project_workspace_size, qkv_project, qkv_project_workspace_size, output_proj, fold_wuv_wo,
+    q_project_workspace_size, qkv_project, qkv_project_workspace_size, output_proj, fold_wuv_wo, set_debug, validate_decode_inputs,
 )

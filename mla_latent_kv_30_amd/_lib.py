@@ -96,6 +96,10 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_multi.restype = _i32
     L.mla_decode_multi.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                    ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_validate_decode_inputs.restype = _i32
+    L.mla_validate_decode_inputs.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32]
+    L.mla_set_debug.restype = None
+    L.mla_set_debug.argtypes = [_i32]
     L.mla_decode_multi_upproj.restype = _i32
     L.mla_decode_multi_upproj.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp, _i32, _vp]
@@ -608,3 +612,22 @@ def fold_wuv_wo(w_uv: torch.Tensor, w_o: torch.Tensor) -> torch.Tensor:
     out = torch.empty((d, H * D_C), dtype=torch.bfloat16, device=w_o.device)
     _check(lib().mla_fold_wuv_wo(_ptr(w_uv), _ptr(w_o), _ptr(out), H, d, _stream(w_o.device)), "mla_fold_wuv_wo")
     return out
+
+
+def set_debug(on: bool) -> None:
+    """Debug mode of the decode entry points (mla_set_debug): lengths and
+    block table are checked on the host before every launch."""
+    lib().mla_set_debug(1 if on else 0)
+
+
+def validate_decode_inputs(seq_lens, block_table, num_pages: int, q_len: int = 1) -> int:
+    """mla_validate_decode_inputs on host arrays (numpy or CPU tensors);
+    returns the status code."""
+    import numpy as _np
+    lens = _np.ascontiguousarray(_np.asarray(seq_lens, dtype=_np.int32))
+    bt = None if block_table is None else _np.ascontiguousarray(_np.asarray(block_table, dtype=_np.int32))
+    B = lens.shape[0]
+    max_pages = 1 if bt is None else bt.shape[1]
+    return int(lib().mla_validate_decode_inputs(lens.ctypes.data_as(_vp), None if bt is None else bt.ctypes.data_as(_vp),
+                                                B, max_pages if bt is not None else max(1, int(lens.max() + 63) // 64),
+                                                int(num_pages), int(q_len)))

@@ -1,6 +1,7 @@
 // C entry points of libmla: host-side validation, workspace sizing and
 // dispatch to the gfx950 kernels.  See include/mla.h for the contract.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -192,6 +193,57 @@ size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t num_splits) {
 
 namespace {
 
+// Debug mode (mla_set_debug, or MLA_DEBUG=1 in the environment): the decode
+// entry points copy the lengths and the block table to the host, in stream
+// order, and check them before launching.
+std::atomic<int> g_debug{-1};
+
+bool debug_on() {
+  int v = g_debug.load();
+  if (v < 0) {
+    const char* e = getenv("MLA_DEBUG");
+    v = (e != nullptr && e[0] == '1') ? 1 : 0;
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, v);
+    v = g_debug.load();
+  }
+  return v == 1;
+}
+
+// Every length in [q_len, 64 * max_pages]; with a block table, every page a
+// sequence uses in [0, num_pages).
+mla_status check_lengths(const int32_t* lens, const int32_t* bt, int32_t B, int32_t max_pages, int32_t num_pages,
+                         int32_t q_len) {
+  for (int b = 0; b < B; ++b) {
+    const long long L = lens[b];
+    if (L < q_len || L > (long long)MLA_PAGE * max_pages) return MLA_ERR_INVALID_ARG;
+    if (bt != nullptr) {
+      const long long used = (L + MLA_PAGE - 1) / MLA_PAGE;
+      for (long long k = 0; k < used; ++k) {
+        const int32_t pg = bt[(size_t)b * max_pages + k];
+        if (pg < 0 || pg >= num_pages) return MLA_ERR_INVALID_ARG;
+      }
+    }
+  }
+  return MLA_OK;
+}
+
+mla_status debug_check(const DecodeArgs& a, int32_t q_len, int32_t num_pages, hipStream_t s) {
+  if (!debug_on()) return MLA_OK;
+  int32_t* lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)a.B);
+  int32_t* bt = (int32_t*)malloc(sizeof(int32_t) * (size_t)a.B * a.max_pages);
+  mla_status st = MLA_ERR_HIP;
+  if (lens != nullptr && bt != nullptr &&
+      hipMemcpyAsync(lens, a.seq_lens, sizeof(int32_t) * a.B, hipMemcpyDeviceToHost, s) == hipSuccess &&
+      hipMemcpyAsync(bt, a.block_table, sizeof(int32_t) * (size_t)a.B * a.max_pages, hipMemcpyDeviceToHost, s) ==
+          hipSuccess &&
+      hipStreamSynchronize(s) == hipSuccess)
+    st = check_lengths(lens, bt, a.B, a.max_pages, num_pages, q_len);
+  free(lens);
+  free(bt);
+  return st;
+}
+
 // Validate a decode call and fill its launch arguments.
 mla_status prepare_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
                           const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
@@ -240,6 +292,8 @@ mla_status mla_decode_partial(const void* q_abs, const mla_cache* cache, const i
   Plan p;
   mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
                                  workspace, ws_bytes, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
+  st = debug_check(a, 1, cache->num_pages, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   (void)hipGetLastError();  // clear a stale error so a launch failure is reported as ours
   return launched(launch_decode(a, kind, (hipStream_t)stream));
@@ -307,6 +361,8 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
   mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
                                  workspace, ws_bytes, z, lse, a, kind, p);
   if (st != MLA_OK) return st;
+  st = debug_check(a, 1, cache->num_pages, (hipStream_t)stream);
+  if (st != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   st = launched(launch_decode(a, kind, s));
@@ -324,6 +380,8 @@ mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int
   Plan p;
   mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, q_len * H, max_pages, softmax_scale,
                                  num_splits, workspace, ws_bytes, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
+  st = debug_check(a, q_len, cache->num_pages, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   a.q_len = q_len;
   a.hs = H;
@@ -346,6 +404,8 @@ mla_status mla_decode_multi_upproj(const void* q_abs, const mla_cache* cache, co
   Plan p;
   mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, q_len * H, max_pages, softmax_scale,
                                  num_splits, workspace, ws_bytes, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
+  st = debug_check(a, q_len, cache->num_pages, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   a.q_len = q_len;
   a.hs = H;
@@ -487,6 +547,14 @@ size_t linear_ws(int N, int M, int K) { return plan_linear(N, M, K, device_cus()
 }  // namespace
 
 extern "C" {
+
+void mla_set_debug(int32_t on) { g_debug.store(on ? 1 : 0); }
+
+mla_status mla_validate_decode_inputs(const int32_t* seq_lens, const int32_t* block_table, int32_t B,
+                                      int32_t max_pages, int32_t num_pages, int32_t q_len) {
+  if (!seq_lens || B < 1 || max_pages < 1 || num_pages < 1 || q_len < 1) return MLA_ERR_INVALID_ARG;
+  return check_lengths(seq_lens, block_table, B, max_pages, num_pages, q_len);
+}
 
 size_t mla_linear_workspace_size(int32_t N, int32_t M, int32_t K) {
   if (!linear_shape_ok(N, M, 0, K)) return 0;

@@ -182,3 +182,20 @@ def test_projection_workspace_sizes():
     assert _lib.kv_append_workspace_size(64, 7168, _lib.MLA_F32) >= 64 * 576 * 4
     assert _lib.q_project_workspace_size(64, 7168, 1536, 16) >= 64 * 1536 * 2
     assert _lib.q_project_workspace_size(64, 7168, 1536, 0) == 0
+
+
+def test_validate_decode_inputs_host_check():
+    import numpy as np
+    ok = _lib.MLA_OK
+    bad = _lib.MLA_ERR_INVALID_ARG
+    bt = np.array([[3, 1, -1], [0, 2, 4]], dtype=np.int32)
+    assert _lib.validate_decode_inputs([100, 129], bt, num_pages=5) == ok
+    assert _lib.validate_decode_inputs([100, 192], bt, num_pages=5) == ok           # 3 full pages
+    assert _lib.validate_decode_inputs([0, 129], bt, num_pages=5) == bad            # empty softmax
+    assert _lib.validate_decode_inputs([100, 193], bt, num_pages=5) == bad          # past 64*max_pages
+    assert _lib.validate_decode_inputs([129, 10], bt, num_pages=5) == bad           # uses the -1 entry
+    assert _lib.validate_decode_inputs([100, 129], bt, num_pages=4) == bad          # page 4 not in the pool
+    assert _lib.validate_decode_inputs([100, 129], bt, num_pages=5, q_len=2) == ok
+    assert _lib.validate_decode_inputs([1, 129], bt, num_pages=5, q_len=2) == bad   # fewer tokens than queries
+    assert _lib.validate_decode_inputs([100, 129], None, num_pages=5) == ok         # lengths only
+    assert L.mla_validate_decode_inputs(NULL, NULL, 2, 3, 5, 1) == bad

@@ -625,3 +625,37 @@ def test_fp8_prefill_matches_oracle():
     slot = bt.cpu().numpy()[j // 64] * 64 + j % 64
     rc, _ = orc.quantize_latent_e4m3(c)
     np.testing.assert_array_equal(codes[slot], rc)
+
+
+# --------------------------------------------------------------------------- debug mode
+
+def test_debug_mode_rejects_bad_lengths_and_pages_before_launch():
+    """With mla_set_debug(1) the decode entry points check the device-side
+    lengths and block table on the host and return MLA_ERR_INVALID_ARG
+    (nothing launched) for a length of 0, a length past the block table, a
+    page outside the pool, or fewer tokens than query tokens."""
+    wl = W.make_workload("decode_h16", B=3, H=16, lens=[100, 65, 1])
+    _note("case debug mode")
+    dd = DI.decode_inputs(wl, DEV)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    mla.set_debug(True)
+    try:
+        z, lse = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens)   # valid inputs still run
+        torch.cuda.synchronize()
+        assert torch.isfinite(z).all()
+        maxp = dd.block_table.shape[1]
+        for b, L in ((1, 0), (0, 64 * maxp + 1)):
+            bad = dd.seq_lens.clone()
+            bad[b] = L
+            with pytest.raises(mla.MLAError) as e:
+                mla.decode(q_abs, dd.cache, dd.block_table, bad)
+            assert e.value.status == mla.MLA_ERR_INVALID_ARG
+        bt = dd.block_table.clone()
+        bt[0, 0] = dd.cache.num_pages
+        with pytest.raises(mla.MLAError):
+            mla.decode(q_abs, dd.cache, bt, dd.seq_lens)
+        q2 = torch.zeros((3, 2, 16, 576), dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(mla.MLAError):   # sequence 2 holds 1 token, 2 query tokens
+            mla.decode_multi(q2, dd.cache, dd.block_table, dd.seq_lens)
+    finally:
+        mla.set_debug(False)
