@@ -315,3 +315,37 @@ def test_layer_from_hidden_matches_oracle(cache_dtype):
     tol = BF16_TOL if cache_dtype == "bf16" else FP8_TOL
     assert _rel(_host(u), ref) <= tol
     assert _rel(_host(u_fold), ref) <= tol
+
+
+# One shape per (tile configuration, split or not) of the host plan:
+#   (16, 256, 16384, 0)   32-token tiles, unsplit    (16, 7168, 4096, 0)  split
+#   (64, 512, 16384, 0)   64-token tiles, unsplit    (48, 7168, 4096, 32) split
+#   (200, 1024, 768, 32)  128 x 128 tiles, unsplit   (65, 4096, 1024, 0)  split
+#   (700, 576, 800, 0)    256 x 256 tiles, unsplit   (513, 32768, 256, 0) split
+#   (3, 128, 96, 0)       64 x 64 tiles, unsplit     (16, 7168, 512, 64)  split
+PLAN_SHAPES = [(16, 256, 16384, 0), (16, 7168, 4096, 0), (64, 512, 16384, 0), (48, 7168, 4096, 32),
+               (200, 1024, 768, 32), (65, 4096, 1024, 0), (700, 576, 800, 0), (513, 32768, 256, 0),
+               (3, 128, 96, 0), (16, 7168, 512, 64)]
+
+
+def test_linear_every_plan_and_random_shapes():
+    """Every tile configuration and split of the host plan, plus a seeded
+    sweep of random shapes, against the oracle's two-block projection
+    (fp32 output)."""
+    rng = np.random.default_rng(31)
+    shapes = list(PLAN_SHAPES)
+    for _ in range(6):
+        shapes.append((int(rng.choice([1, 3, 16, 31, 33, 64, 65, 200, 513, 700])), 64 * int(rng.integers(1, 48)),
+                       32 * int(rng.integers(1, 24)), 32 * int(rng.integers(0, 6))))
+    for case, (N, K, M0, M1) in enumerate(shapes):
+        _note(f"case linear plan/random {case}: N={N} K={K} M0={M0} M1={M1}")
+        x = _randn(40 + case, f"rx{case}", (N, K))
+        w0 = _randn(60 + case, f"rw0{case}", (M0, K), K ** -0.5)
+        w1 = _randn(80 + case, f"rw1{case}", (M1, K), K ** -0.5)
+        res = mla.linear(_bf(x), _bf(w0), _bf(w1) if M1 else None, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        y0, y1 = (res, None) if M1 == 0 else res
+        ref = orc.kv_projection(x, w0, w1, np.zeros(N))
+        assert _rel(_host(y0), ref["c_kv"]) <= F32_TOL, case
+        if M1:
+            assert _rel(_host(y1), ref["k_r"]) <= F32_TOL, case
