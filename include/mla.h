@@ -344,7 +344,8 @@ mla_status mla_upproj_v(const float* z, const void* w_uv, void* o, int32_t N, in
  * it); it must be a multiple of 64.  A workspace is device memory the caller
  * owns, at least the size the matching *_workspace_size function returns
  * (that size depends on the arguments and the current device's compute-unit
- * count only); it is scratch that the call overwrites.
+ * count only); it is scratch that the call overwrites.  Every matrix and
+ * workspace pointer must be 16-byte aligned (MLA_ERR_INVALID_ARG otherwise).
  * ------------------------------------------------------------------------ */
 
 /* Workspace bytes mla_linear needs for an N x M output with contraction K

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/mla.h"
@@ -102,6 +103,14 @@ Plan make_plan(int32_t B, int32_t num_splits) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Every pointer the projection kernels read or write with 16-byte vectors.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return false;
+  return true;
+}
 
 // Workspace layout: [per-sequence piece record: B x (first slot, count) int32]
 //                   [partial z: slots x H x 512 fp32][partial lse: slots x H fp32]
@@ -567,6 +576,7 @@ mla_status mla_linear(const void* x, const void* w0, int32_t M0, const void* w1,
   if (!x || !w0 || !y0 || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
   if (!linear_shape_ok(N, M0, M1, K)) return MLA_ERR_INVALID_ARG;
   if (M1 > 0 && (!w1 || !y1)) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({x, w0, w1, y0, y1, workspace})) return MLA_ERR_INVALID_ARG;
   const bool bf = out_dtype == MLA_BF16;
   Blocks bl;
   bl.add(w0, M0, y0, bf);
@@ -584,6 +594,7 @@ mla_status mla_kv_append(const void* h, const void* w_dkv, const void* w_kr, con
                          int32_t T, int32_t d, const mla_cache* cache, const mla_rope* rope, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (!h || !w_dkv || !w_kr || !pos || !slot) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({h, w_dkv, w_kr, workspace})) return MLA_ERR_INVALID_ARG;
   if (!linear_shape_ok(T, MLA_D_C, MLA_D_R, d)) return MLA_ERR_INVALID_ARG;
   const mla_rope r = rope ? *rope : plain_rope(10000.0f);
   if (!rope_ok(r)) return MLA_ERR_INVALID_ARG;
@@ -628,6 +639,7 @@ mla_status mla_q_project(const void* h, const void* w_dq, const void* w_uq, cons
                          int32_t T, int32_t d, int32_t dcq, int32_t H, int32_t out_dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (!h || !w_dq || !w_uq || !w_qr || !q_c || !q_r || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({h, w_dq, w_uq, w_qr, q_c, q_r, workspace})) return MLA_ERR_INVALID_ARG;
   if (H < 1 || H > MLA_MAX_HEADS || !linear_shape_ok(T, dcq, 0, d)) return MLA_ERR_INVALID_ARG;
   if (!linear_shape_ok(T, H * MLA_D_NOPE, H * MLA_D_R, dcq)) return MLA_ERR_INVALID_ARG;
   const size_t need = mla_q_project_workspace_size(T, d, dcq, H);
@@ -660,6 +672,7 @@ mla_status mla_qkv_project(const void* h, const void* w_dq, const void* w_dkv, c
                            void* q_r, int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!h || !w_dq || !w_dkv || !w_kr || !w_uq || !w_qr || !pos || !slot || !q_c || !q_r || !dtype_ok(out_dtype))
     return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({h, w_dq, w_dkv, w_kr, w_uq, w_qr, q_c, q_r, workspace})) return MLA_ERR_INVALID_ARG;
   if (H < 1 || H > MLA_MAX_HEADS || !linear_shape_ok(T, dcq, MLA_ROW, d)) return MLA_ERR_INVALID_ARG;
   if (!linear_shape_ok(T, H * MLA_D_NOPE, H * MLA_D_R, dcq)) return MLA_ERR_INVALID_ARG;
   const mla_rope r = rope ? *rope : plain_rope(10000.0f);
@@ -709,6 +722,7 @@ mla_status mla_qkv_project(const void* h, const void* w_dq, const void* w_dkv, c
 mla_status mla_output_proj(const void* x, const void* w, void* u, int32_t N, int32_t K, int32_t d, int32_t out_dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !w || !u || !dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({x, w, u, workspace})) return MLA_ERR_INVALID_ARG;
   if (K % MLA_D_V != 0 || !linear_shape_ok(N, d, 0, K)) return MLA_ERR_INVALID_ARG;
   Blocks bl;
   bl.add(w, d, u, out_dtype == MLA_BF16);

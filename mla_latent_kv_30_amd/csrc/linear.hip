@@ -107,7 +107,7 @@ __device__ __forceinline__ void store_out(const LinearArgs& a, int n, int m, flo
 template <int WM, int WN, int FM, int FN, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   using T = Tile<WM, WN, FM, FN, STAGES>;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::kLdsBytes];
   const int wave = uniform((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int mtile, ntile;
@@ -300,15 +300,8 @@ __global__ __launch_bounds__(256) void fold_kernel(const bf16* __restrict__ w_uv
 template <int WM, int WN, int FM, int FN, int STAGES>
 hipError_t run(LinearArgs a, hipStream_t st) {
   using T = Tile<WM, WN, FM, FN, STAGES>;
-  auto k = linear_kernel<WM, WN, FM, FN, STAGES>;
-  static bool attr = false;   // the dynamic-LDS limit is set once per process
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             T::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  hipLaunchKernelGGL(k, dim3(a.mt * a.nt, a.splits), dim3(T::kThreads), T::kLdsBytes, st, a);
+  hipLaunchKernelGGL((linear_kernel<WM, WN, FM, FN, STAGES>), dim3(a.mt * a.nt, a.splits), dim3(T::kThreads), 0, st,
+                     a);
   hipError_t e = hipGetLastError();
   // no outputs named: the caller consumes the partials itself
   if (e != hipSuccess || a.splits == 1 || a.y[0] == nullptr) return e;

@@ -199,3 +199,12 @@ def test_validate_decode_inputs_host_check():
     assert _lib.validate_decode_inputs([1, 129], bt, num_pages=5, q_len=2) == bad   # fewer tokens than queries
     assert _lib.validate_decode_inputs([100, 129], None, num_pages=5) == ok         # lengths only
     assert L.mla_validate_decode_inputs(NULL, NULL, 2, 3, 5, 1) == bad
+
+
+def test_projections_reject_misaligned_pointers():
+    bad = _lib.MLA_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    assert L.mla_linear(odd, P, 64, NULL, 0, P, NULL, 8, 128, _lib.MLA_F32, NULL, 0, NULL) == bad
+    assert L.mla_linear(P, P, 64, NULL, 0, odd, NULL, 8, 128, _lib.MLA_F32, NULL, 0, NULL) == bad
+    assert L.mla_output_proj(P, odd, P, 8, 2048, 256, _lib.MLA_F32, P, 1 << 30, NULL) == bad
+    assert L.mla_q_project(P, P, P, P, P, P, 4, 256, 1536, 16, _lib.MLA_BF16, odd, 1 << 30, NULL) == bad
