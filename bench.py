@@ -442,6 +442,7 @@ def main():
     from mla_latent_kv_30_amd import traffic as TR
     kname = "decode_mfma_kernel" if wl.dtype != "f32" else "decode_f32_kernel"
     tr = TR.load(kname, wl.name, os.path.join(ROOT, "profiles")) if QL == 1 else None
+    mc = TR.load(kname, wl.name, os.path.join(ROOT, "profiles"), "mfma") if QL == 1 else None
     if QL > 1:
         kname += " + merge_kernel"
 
@@ -479,6 +480,10 @@ def main():
             "alg_bytes_per_launch": alg_bytes,
             "alg_flops_per_launch": alg_flops, "tflops": tflops, "mfma_peak_tflops": mfma_peak,
             "mfma_frac": tflops / mfma_peak,
+            # matrix-core counters of the same kernel (stored run on the current sources)
+            "mfma_counters": None if mc is None else {
+                "issued_tflops": mc["issued_tflops"], "busy_frac": mc["busy_frac"],
+                "issued_over_algorithmic": mc["mfma_flops_issued"] / alg_flops},
         },
         "cpu_baseline": cpu,
         "wall_s_timed": wall,

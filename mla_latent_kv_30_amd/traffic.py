@@ -9,6 +9,9 @@ counter reads for a plain device copy of known size run in the same command
     python -m mla_latent_kv_30_amd.traffic summarize --fetch DIR --write DIR \\
         --kernel decode_mfma_kernel --workload decode_h16 --out profiles/X.json
 
+The same module summarises a matrix-core counter run (mfma subcommand:
+SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE).
+
 The summary records a digest of the sources the kernel is built from;
 bench.py reports the traffic only while those sources still have that digest.
 """
@@ -92,9 +95,46 @@ def summarize(fetch_dir: str, write_dir: str, kernel: str, workload: str) -> dic
     }
 
 
-def load(kernel: str, workload: str, profiles_dir: str):
-    """The stored traffic summary for (kernel, workload) if it matches the current sources, else None."""
-    path = os.path.join(profiles_dir, f"{kernel}_{workload}_traffic.json")
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 matrix cores
+CLOCK_HZ = 2.4e9           # MI355X peak engine clock
+
+
+def summarize_mfma(run_dir: str, kernel: str, workload: str, simds: int = 1024, largest: bool = False) -> dict:
+    """Matrix-core counters of `kernel` (median over its dispatches):
+    bf16 MFMA ops issued (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = FLOPs), MFMA
+    busy cycles summed over the SIMDs, and the dispatch duration.  Derived:
+    the issued rate against the bf16 peak, and the busy fraction of the
+    SIMDs' cycles at the peak clock over the dispatch."""
+    path = _counter_csv(run_dir)
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    rows = [d for d in per.values() if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in d and "SQ_VALU_MFMA_BUSY_CYCLES" in d]
+    if not rows:
+        raise RuntimeError(f"no dispatches of {kernel} with MFMA counters in {run_dir}")
+    if largest:  # one kernel serving several products: keep the largest product's dispatches
+        top = max(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in rows)
+        rows = [d for d in rows if d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] == top]
+    flops = statistics.median(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0 for d in rows)
+    busy = statistics.median(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in rows)
+    ns = statistics.median(d["ns"] for d in rows)
+    return {
+        "workload": workload, "kernel": kernel, "source_digest": source_digest(kernel), "dispatches": len(rows),
+        "mfma_flops_issued": flops, "mfma_busy_cycles": busy, "duration_ns": ns,
+        "issued_tflops": flops / (ns * 1e-9) / 1e12, "issued_frac": flops / (ns * 1e-9) / PEAK_BF16_FLOPS,
+        "busy_frac": busy / (simds * ns * 1e-9 * CLOCK_HZ),
+    }
+
+
+def load(kernel: str, workload: str, profiles_dir: str, what: str = "traffic"):
+    """The stored summary (traffic or mfma) for (kernel, workload) if it
+    matches the current sources, else None."""
+    path = os.path.join(profiles_dir, f"{kernel}_{workload}_{what}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -112,11 +152,25 @@ def main():
     s.add_argument("--workload", required=True)
     s.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     s.add_argument("--out", required=True)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("--dir", required=True)
+    mf.add_argument("--kernel", required=True)
+    mf.add_argument("--workload", required=True)
+    mf.add_argument("--command", default="")
+    mf.add_argument("--largest", action="store_true", help="only the dispatches of the largest product")
+    mf.add_argument("--out", required=True)
     d = sub.add_parser("digest")
     d.add_argument("--kernel", default="")
     args = ap.parse_args()
     if args.cmd == "digest":
         print(source_digest(args.kernel))
+        return
+    if args.cmd == "mfma":
+        out = summarize_mfma(args.dir, args.kernel, args.workload, largest=args.largest)
+        out["command"] = args.command
+        with open(args.out, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out))
         return
     out = summarize(args.fetch, args.write, args.kernel, args.workload)
     out["command"] = args.command
