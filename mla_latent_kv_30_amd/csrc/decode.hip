@@ -41,15 +41,15 @@ namespace mla {
 // Per-wave state: 16 heads and NT tiles of 16 latent channels.  Lane l serves
 // head h0 + l%16; its lane group g = l/16 picks which channels / tokens of
 // each matrix-core operand it holds.
-template <int NT>
+template <int NT, int NQ = 18>
 struct WaveState {
-  bf16x8 q[18];      // absorbed query, B operand of S^T = R Q^T: channels 32kk + 8g + j
+  bf16x8 q[NQ];      // absorbed query, B operand of S^T = R Q^T: channels 32(k0 + kk) + 8g + j
   floatx4 zacc[NT];  // Z^T tile j: channels c0 + 16j + 4g + r, column = head
   float m, l;        // running max (log2 units) and this lane's partial sum
 };
 
-template <int NT>
-__device__ __forceinline__ void reset_state(WaveState<NT>& st) {
+template <int NT, int NQ>
+__device__ __forceinline__ void reset_state(WaveState<NT, NQ>& st) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) st.zacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
@@ -60,8 +60,8 @@ __device__ __forceinline__ void reset_state(WaveState<NT>& st) {
 // -inf where masked; p: probabilities relative to the running maximum.  The
 // maximum is only moved when it grows by more than kLazyRescale, so the
 // accumulator is rescaled rarely; p stays <= 2^kLazyRescale.
-template <int NT, int NV>
-__device__ __forceinline__ void softmax_update(WaveState<NT>& st, float (&x)[NV], float (&p)[NV]) {
+template <int NT, int NQ, int NV>
+__device__ __forceinline__ void softmax_update(WaveState<NT, NQ>& st, float (&x)[NV], float (&p)[NV]) {
   float mx = x[0];
 #pragma unroll
   for (int r = 1; r < NV; ++r) mx = fmaxf(mx, x[r]);
@@ -132,6 +132,36 @@ __device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int
   }
 }
 
+// One 16-token subtile u of a block buffer over the nine K-steps k0 .. k0+8
+// (k0 = 0 or 9): the partial product S^T of those 288 channels, in the
+// register layout of score32.  dma(t) is called after steps 1, 3, 5, 7 and 8.
+template <int D, class Dma>
+__device__ __forceinline__ floatx4 score_half(const bf16x8 (&q)[9], uint32_t buf, int lane, int u, int k0,
+                                              Dma&& dma) {
+  const int g = lane >> 4, m = lane & 15;
+  const int r = 4 * (m & 3) + (m >> 2) + 16 * u;
+  // step j reads bf[j & 1] + 128 (j >> 1): steps of equal parity differ by
+  // whole 128-byte strides, which the permutation (bits 4..6) leaves alone
+  uint32_t bf[2];
+  bf[0] = buf + lds_off(r, 64 * k0 + 16 * g);
+  bf[1] = buf + lds_off(r, 64 * (k0 + 1) + 16 * g);
+  asm volatile("" : "+v"(bf[0]), "+v"(bf[1]));
+  auto rd = [&](int j) { return lds_read_b128_at(bf[j & 1] + 128 * (j >> 1)); };
+  floatx4 S = floatx4{};
+  int4v a[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) a[i] = rd(i);
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int4v c = a[j % D];
+    if (j + D < 9) a[j % D] = rd(j + D);
+    S = mfma16(__builtin_bit_cast(bf16x8, c), q[j], S);
+    if (j % 2 == 1) dma(j / 2);
+  }
+  dma(4);
+  return S;
+}
+
 // One block buffer (32 rows); rows at or past `hi` (per lane: it may differ
 // between the query tokens of multi-token decode) are masked.  Scores for
 // the wave's 16 heads over the 32 tokens, then the value product
@@ -139,17 +169,54 @@ __device__ __forceinline__ void score32(const bf16x8 (&q)[18], uint32_t buf, int
 // multiple of 4): A = C^T (16 channels x 32 tokens) through transposing LDS
 // reads, B = P^T.  The K = 32 slots of lane group g are tokens 4j + g
 // (j < 4) and 16 + 4(j-4) + g.
+template <int NT, int NQ>
+__device__ __forceinline__ void softmax_value(WaveState<NT, NQ>& st, const floatx4 (&S)[2], uint32_t buf, int hi,
+                                              int lane, int mt0, float scale_log2);
+
 template <int NT, class Dma>
 __device__ __forceinline__ void block_compute(WaveState<NT>& st, uint32_t buf, int hi, int lane, int mt0,
                                               float scale_log2, Dma&& dma) {
   // Recompute the lane's operand offsets in every call rather than let the
   // compiler keep one set per buffer live across the block loop.
   lane = lane_id_fresh();
-  const int g = lane >> 4;
-  float x[8], p[8];
   floatx4 S[2];
   // deeper operand prefetch where the accumulator leaves registers for it
   score32<NT <= 16 ? 4 : 1>(st.q, buf, lane, S[0], S[1], dma);
+  softmax_value(st, S, buf, hi, lane, mt0, scale_log2);
+}
+
+// The scores of one 16-head group split over its four computing waves
+// (channel groups): wave w multiplies subtile w & 1 over K-steps
+// 9 (w >> 1) .. +8, the four partial products meet in LDS (`exch`, 4 KB:
+// [wave][lane] x 16 bytes) across one barrier, and every wave adds the two
+// halves of each subtile in the same order, so all four hold the same
+// scores and the same softmax state.  The barrier is reached by every wave
+// of the workgroup exactly once per call; the waves that do not compute
+// meet it from the block loop.
+template <int NT, class Dma>
+__device__ __forceinline__ void block_compute_ksplit(WaveState<NT, 9>& st, uint32_t buf, uint32_t exch, int wave,
+                                                     int hi, int lane, int mt0, float scale_log2, Dma&& dma) {
+  lane = lane_id_fresh();
+  const floatx4 part = score_half<4>(st.q, buf, lane, wave & 1, 9 * (wave >> 1), dma);
+  *(MLA_LDS floatx4*)(uintptr_t)(exch + (64 * wave + lane) * 16) = part;
+  __syncthreads();
+  floatx4 S[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const floatx4 lo = *(const MLA_LDS floatx4*)(uintptr_t)(exch + (64 * u + lane) * 16);
+    const floatx4 hi2 = *(const MLA_LDS floatx4*)(uintptr_t)(exch + (64 * (u + 2) + lane) * 16);
+    S[u] = lo + hi2;
+  }
+  softmax_value(st, S, buf, hi, lane, mt0, scale_log2);
+}
+
+// Softmax of the block's scores S (the two subtiles of score32's layout) and
+// the value product Z^T += C^T P^T for the wave's NT channel tiles.
+template <int NT, int NQ>
+__device__ __forceinline__ void softmax_value(WaveState<NT, NQ>& st, const floatx4 (&S)[2], uint32_t buf, int hi,
+                                              int lane, int mt0, float scale_log2) {
+  const int g = lane >> 4;
+  float x[8], p[8];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -158,7 +225,7 @@ __device__ __forceinline__ void block_compute(WaveState<NT>& st, uint32_t buf, i
       x[4 * u + r] = 16 * u + 4 * r + g < hi ? v : -INFINITY;
     }
   }
-  softmax_update<NT, 8>(st, x, p);
+  softmax_update(st, x, p);
   // Source lane s' of each 16-lane group points at row 4(s'/4) + g,
   // channels 16mt + 4(s'%4) .. +3, i.e. row byte 32mt + 8(s'%4); the
   // permutation leaves a base per mt%4 (and per row half) and a stride of
@@ -195,8 +262,8 @@ __device__ __forceinline__ void block_compute(WaveState<NT>& st, uint32_t buf, i
 
 // Normalise and write one wave's part: z rows [head][512] at channels
 // c0 .. c0 + 16 NT, and lse[head] if with_lse.
-template <int NT>
-__device__ __forceinline__ void store_state(const WaveState<NT>& st, float l_tot, float* zdst, float* ldst, int h0,
+template <int NT, int NQ>
+__device__ __forceinline__ void store_state(const WaveState<NT, NQ>& st, float l_tot, float* zdst, float* ldst, int h0,
                                             int H, int lane, int c0, bool with_lse) {
   constexpr float kLn2 = 0.69314718055994530942f;
   const int head = h0 + (lane & 15);
@@ -240,10 +307,18 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   constexpr int kSmem = FP8 ? kNBuf * kStageBytes + kBlockBytes : kNBuf * kBlockBytes;
   constexpr int kCopyLo = FP8 ? kFp8Copies : kCopiesLo;  // copies per block of waves 0..3
   constexpr int kCopyHi = FP8 ? kFp8Copies : kCopiesHi;  // and of waves 4..7
+  // one head group: its four computing waves split the scores (K halves x
+  // subtiles) and exchange the partial products
+  constexpr bool kKSplit = HG == 1 && CG == 4;
+  constexpr int NQ = kKSplit ? 9 : 18;
+  // the exchange area comes out of the block-table copy, so that the
+  // workgroup still fits the 160 KB of LDS
+  constexpr int kBt = kKSplit ? kBtLds - 64 : kBtLds;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   __shared__ int pfx[kMaxSchedB + 1];
   __shared__ int lens[kMaxSchedB];
-  __shared__ int bt_lds[kBtLds];
+  __shared__ int bt_lds[kBt];
+  __shared__ __attribute__((aligned(16))) float exch[kKSplit ? 4 * 64 * 4 : 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const bool computes = wave < HG * CG;
@@ -253,7 +328,7 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 
   // a small block table (the balanced split over a few sequences, where
   // start-up latency matters most) is kept in LDS
-  const bool bt_local = a.splits == 0 && a.prefill_T == 0 && a.B * a.max_pages <= kBtLds;
+  const bool bt_local = a.splits == 0 && a.prefill_T == 0 && a.B * a.max_pages <= kBt;
   int P = 0;
   if (a.splits == 0 && a.prefill_T == 0)
     P = block_prefix(a.seq_lens, a.B, pfx, lens, bt_local ? block_table : nullptr, a.B * a.max_pages, bt_lds);
@@ -292,14 +367,15 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   // waiting for it does not also wait for the blocks issued after it; with
   // more head groups it is loaded into registers directly.  Either way the
   // first three blocks are in flight meanwhile.
-  WaveState<NT> st;
+  WaveState<NT, NQ> st;
+  const int k0 = kKSplit ? 9 * (wave >> 1) : 0;  // first K-step of the wave's query registers
   constexpr bool kQueryViaLds = HG <= 2;
   uint8_t* const qlds = FP8 ? smem + kNBuf * kStageBytes : smem + (kNBuf - 1) * kBlockBytes;
   static_assert(HG > 2 || 2 * 16 * kRowBytes <= kBlockBytes, "query staging space");
   if constexpr (kQueryViaLds) {
     issue_query_copy<HG>((const uint8_t*)qrow(cp.seg), a.H, qlds, wave, lane);
   } else {
-    load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4);
+    load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4, k0);
   }
   Cursor ld = cp;
   int issued = 0;
@@ -317,7 +393,7 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // lane: head h0 + l%16, channels 32kk + 8g .. +7 of its row
     const uint32_t qa = lds_addr(qlds) + (16 * hg + (lane & 15)) * kRowBytes + 16 * (lane >> 4);
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) st.q[kk] = __builtin_bit_cast(bf16x8, lds_read_b128_at(qa + 64 * kk));
+    for (int kk = 0; kk < NQ; ++kk) st.q[kk] = __builtin_bit_cast(bf16x8, lds_read_b128_at(qa + 64 * (k0 + kk)));
   } else {
     consume_query(st.q);
   }
@@ -358,10 +434,15 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         const int head = min(h0 + (lane_id_fresh() & 15), a.H - 1);
         hi = min(hi, cp.seg.L - (a.q_len - 1 - head / a.hs) - kBlock * cp.k);
       }
-      block_compute<NT>(st, lds_addr(buf), hi, lane, mt0, a.scale_log2, dma);
+      if constexpr (kKSplit) {
+        block_compute_ksplit<NT>(st, lds_addr(buf), lds_addr(exch), wave, hi, lane, mt0, a.scale_log2, dma);
+      } else {
+        block_compute<NT>(st, lds_addr(buf), hi, lane, mt0, a.scale_log2, dma);
+      }
     } else {
 #pragma unroll
       for (int t = 0; t < kCopiesLo; ++t) dma(t);
+      if constexpr (kKSplit) __syncthreads();  // the score exchange of the computing waves
     }
     if (ld.valid) {
       if constexpr (FP8) issue(ld, (i + kNBuf - 1) % kNBuf);
@@ -380,7 +461,7 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
       }
       cursor_next(a, cp);
       if (!cp.valid) break;
-      load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4);
+      load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4, k0);
       consume_query(st.q);
       reset_state(st);
       note_pieces(cp.seg);

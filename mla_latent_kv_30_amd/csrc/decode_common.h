@@ -416,25 +416,29 @@ __device__ __forceinline__ void cursor_next(const DecodeArgs& a, Cursor& c) {
 
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is refreshed
 
-__device__ __forceinline__ void load_query(bf16x8 (&q)[18], const bf16* __restrict__ src_rows, int H, int head,
-                                           int g) {
+// q[j] = channels 32(k0 + j) + 8g .. +7 of the lane's head row (zeros for a
+// head at or past H).
+template <int NQ>
+__device__ __forceinline__ void load_query(bf16x8 (&q)[NQ], const bf16* __restrict__ src_rows, int H, int head,
+                                           int g, int k0 = 0) {
   const int hc = head < H ? head : H - 1;
   const int keep = head < H ? -1 : 0;
-  const int4v* src = (const int4v*)(src_rows + (size_t)hc * kRow);
+  const int4v* src = (const int4v*)(src_rows + (size_t)hc * kRow) + 4 * k0;
 #pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    int4v v = src[4 * kk + g];
+  for (int j = 0; j < NQ; ++j) {
+    int4v v = src[4 * j + g];
     v &= keep;
-    q[kk] = __builtin_bit_cast(bf16x8, v);
+    q[j] = __builtin_bit_cast(bf16x8, v);
   }
 }
 
 // Use the query registers, so the compiler's own wait for their loads is
 // placed here and not at the first score product, where later page copies
 // (which its counter does not see) would be waited for as well.
-__device__ __forceinline__ void consume_query(bf16x8 (&q)[18]) {
+template <int NQ>
+__device__ __forceinline__ void consume_query(bf16x8 (&q)[NQ]) {
 #pragma unroll
-  for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(q[kk]));
+  for (int j = 0; j < NQ; ++j) asm volatile("" : "+v"(q[j]));
 }
 
 }  // namespace mla
