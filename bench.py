@@ -9,7 +9,9 @@ kernels).  Inputs are synthetic with the workload's
 shapes and distributions and are resident in HBM before timing starts.  To
 keep the 256 MB last-level cache from serving repeated reads, the step
 rotates over enough replicas of its inputs (cache, weights, queries) to
-exceed 600 MB.
+exceed 600 MB.  Consecutive steps are captured together in HIP graphs (as a
+model's layers share one graph per decode step), so that a graph launch is
+not charged to every step; --graph-steps 1 times one graph per step.
 
 With --layer the step starts from hidden states instead: the query path
 (mla_q_project: c^Q, q^C, q^R), the new token's cache append
@@ -53,6 +55,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=-1, help="num_splits (-1: the workload's own, 0: automatic)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0: enough for 600 MB)")
     ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of as a HIP graph")
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="decode steps per HIP graph (0: the largest divisor of --steps up to the replica count; "
+                         "1: a graph per step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -328,7 +333,13 @@ def main():
         step(k % R)
     torch.cuda.synchronize()
 
+    # Graphs of G consecutive steps, as the layers of a model share one graph
+    # per decode step.  G divides K, so the timed loop replays whole graphs;
+    # graph j runs steps jG .. jG+G-1 (modulo R) and the graphs rotate, so
+    # step k always reads replica k % R, as with a graph per step.
     graphs = None
+    G = 1
+    multis = []
     if not args.no_graph:
         try:
             graphs = []
@@ -340,7 +351,19 @@ def main():
                     with torch.cuda.graph(g, stream=side):
                         step(r)
                     graphs.append(g)
+            want = min(R, args.graph_steps) if args.graph_steps > 0 else R
+            G = max(d for d in range(1, want + 1) if args.steps % d == 0)
+            if G > 1:
+                with torch.cuda.stream(side):
+                    for j in range(R // math.gcd(G, R)):
+                        g = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(g, stream=side):
+                            for i in range(G):
+                                step((j * G + i) % R)
+                        multis.append(g)
             torch.cuda.current_stream().wait_stream(side)
+            for g in multis:
+                g.replay()
             for k in range(max(1, args.warmup)):
                 graphs[k % R].replay()
             torch.cuda.synchronize()
@@ -354,10 +377,14 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for k in range(K):
-        if graphs is not None:
+    if graphs is not None and G > 1:
+        for t in range(K // G):
+            multis[t % len(multis)].replay()
+    elif graphs is not None:
+        for k in range(K):
             graphs[k % R].replay()
-        else:
+    else:
+        for k in range(K):
             step(k % R)
     ev1.record()
     torch.cuda.synchronize()
@@ -463,6 +490,7 @@ def main():
             "workload": wl.name + (f"+layer(d={D})" if LAYER else ""), "batch": B, "heads": H, "cached_tokens": total,
             "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
             "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
+            "graph_steps": G if graphs is not None else 0,
             "step": ("qkv_project (cache append + query path) + absorb_q + decode_partial + decode_merge_upproj"
                      " + output_proj"
                      if LAYER else

@@ -380,6 +380,60 @@ def test_step_graph_replays_match_eager(H, lens):
         torch.cuda.synchronize()
 
 
+def test_multi_step_graph_over_replicas_matches_eager():
+    """Several decode steps in one HIP graph, each over its own replica of the
+    inputs (its own cache, queries and weights), as bench.py captures them:
+    after every replay each replica's outputs equal its eager step bit for bit,
+    with the graphs' replays alternating and eager work in between."""
+    lens = [3000, 1, 700, 64, 1500]
+    H, R, G = 16, 3, 3
+    _note(f"case multi-step graph H={H} replicas={R} lens={lens}")
+    reps = []
+    for r in range(R):
+        wl = W.make_workload("decode_h16", seed=r, B=len(lens), H=H, lens=lens)
+        dd = DI.decode_inputs(wl, DEV, keep_host=False)
+        B = wl.B
+        outs = (torch.empty((B, H, 576), dtype=torch.bfloat16, device=DEV), torch.empty((B, H, 512), device=DEV),
+                torch.empty((B, H), device=DEV), torch.empty((B, H, 128), device=DEV))
+        reps.append((dd, outs, mla.decode_workspace(B, H, 0, DEV)))
+
+    def step(r):
+        dd, (q_abs, z, lse, o), ws = reps[r]
+        mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk, out=q_abs)
+        mla.decode_partial(q_abs, dd.cache, dd.block_table, dd.seq_lens, ws, z, lse)
+        mla.decode_merge_upproj(dd.seq_lens, H, ws, z, dd.w_uv, lse=lse, out=o)
+
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    ref = [[t.clone() for t in reps[r][1]] for r in range(R)]
+    assert not torch.equal(ref[0][3], ref[1][3])  # the replicas differ
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for j in range(2):  # two graphs that start at different replicas
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(G):
+                    step((j + i) % R)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for r in range(R):
+            for t in reps[r][1]:
+                t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graphs[rep % 2].replay()
+        torch.cuda.synchronize()
+        for r in range(R):
+            for got, want in zip(reps[r][1], ref[r]):
+                assert torch.equal(got, want), (rep, r)
+        step(rep % R)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------- multi-token decode
 
 def _oracle_multi(dd, q_c, q_r, q_len, seqs=None):
