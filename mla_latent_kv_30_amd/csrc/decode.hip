@@ -17,7 +17,10 @@
 //   * Wave w owns 16 heads (hg = w % HG) and a slice of the 512 latent
 //     channels (cg = w / HG).  Its absorbed query and its accumulator Z^T
 //     stay in registers, and every value a lane holds belongs to one head, so
-//     the online softmax never leaves the lane.
+//     the online softmax never leaves the lane.  With a single head group the
+//     four computing waves would all compute the same scores; they split the
+//     score product instead (a 16-token subtile times half of the 576
+//     channels each) and add the partial products exchanged through LDS.
 //   * Score operand: 16-byte LDS reads of rows.  Value operand: gfx950's
 //     transposing LDS read (ds_read_b64_tr_b16) turns row-major c^KV into
 //     token-packed matrix-core operands without a transposed copy.

@@ -24,6 +24,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,19 +37,31 @@ COPY_KERNEL = "copyBuffer"    # the runtime's device-to-device copy kernel
 KERNEL_SOURCES = {
     "decode_mfma_kernel": ("decode.hip", "decode_common.h", "common.h", "kernels.h"),
     "decode_f32_kernel": ("decode.hip", "decode_common.h", "common.h", "kernels.h"),
+    "linear_kernel": ("linear.hip", "common.h", "kernels.h"),
 }
 
 
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_text(source: str) -> str:
+    """The code of a C++/HIP source without its comments and with whitespace
+    runs collapsed, so that an edit to comments alone leaves a digest as it
+    was."""
+    return " ".join(_COMMENTS.sub(" ", source).split())
+
+
 def source_digest(kernel: str = "") -> str:
-    """Digest of the sources `kernel` is built from (every kernel source if unknown)."""
+    """Digest of the code of the sources `kernel` is built from (every kernel
+    source if unknown)."""
     names = KERNEL_SOURCES.get(kernel)
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
         base = os.path.basename(path)
         if path.endswith((".hip", ".h")) and (names is None or base in names):
             h.update(base.encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
