@@ -37,6 +37,20 @@ constexpr int kStartCost = 4;
 // nbt <= 4 * blockDim.x entries (the whole block table) are copied into
 // bt_lds as well: the loads go out together with the length loads, so the
 // page lookups of the copy issue need no further round trip to memory.
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes (lanes shifted in from outside the row add 0),
+// then the total of row 0 is added to row 1 and that of row 2 to row 3
+// (row_bcast:15), and the total of rows 0-1 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 static __device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, int* pfx, int* lens,
                                    const int32_t* __restrict__ bt = nullptr, int nbt = 0, int* bt_lds = nullptr) {
   __shared__ int wsum[16];
@@ -49,6 +63,29 @@ static __device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, 
       const int i = tid + k * nthreads;
       btv[k] = i < nbt ? bt[i] : 0;
     }
+  }
+  if (B <= 64) {
+    // one sequence per lane of wave 0, and a single barrier for the prefix
+    // and the block-table copy
+    if (wave == 0) {
+      const int L = seq_lens[min(lane, B - 1)];
+      const int v = lane < B ? kStartCost + (L + kBlock - 1) / kBlock : 0;
+      const int x = wave_incl_scan(v);
+      if (lane < B) {
+        pfx[lane] = x - v;
+        lens[lane] = L;
+      }
+      if (lane == B - 1) pfx[B] = x;
+    }
+    if (bt != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = tid + k * nthreads;
+        if (i < nbt) bt_lds[i] = btv[k];
+      }
+    }
+    __syncthreads();
+    return uniform(pfx[B]);
   }
   const int per = (B + nthreads - 1) / nthreads;  // <= 4
   const int base = tid * per;
@@ -90,9 +127,16 @@ static __device__ int block_prefix(const int32_t* __restrict__ seq_lens, int B, 
   return uniform(pfx[B]);
 }
 
+// floor(x / d) for 0 <= x and 0 < d, in 32-bit arithmetic when x fits (the
+// operands are wave-uniform, so the branch is too).
+__device__ __forceinline__ long long udiv_fast(long long x, long long d) {
+  if (x < (1ll << 32) && d < (1ll << 32)) return (long long)((uint32_t)x / (uint32_t)d);
+  return x / d;
+}
+
 // Unit of the balanced split that owns block g (G units over P blocks).
 __device__ __forceinline__ int unit_of_block(long long g, long long G, long long P) {
-  return (int)(((g + 1) * G - 1) / P);
+  return (int)udiv_fast((g + 1) * G - 1, P);
 }
 
 // One piece of work: tokens [t0, t1) of sequence b, whose length is L.
@@ -129,14 +173,21 @@ __device__ __forceinline__ Schedule schedule_begin(const DecodeArgs& a, const in
     s.G = min((long long)a.units, (long long)P);
     s.done = s.w >= s.G;
     if (!s.done) {
-      s.g0 = (long long)s.w * s.P / s.G;
-      s.g1 = (long long)(s.w + 1) * s.P / s.G;
-      int lo = 0, hi = a.B;  // last b with pfx[b] <= g0
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pfx[mid] <= s.g0) lo = mid; else hi = mid;
+      s.g0 = udiv_fast((long long)s.w * s.P, s.G);
+      s.g1 = udiv_fast((long long)(s.w + 1) * s.P, s.G);
+      if (a.B <= 64) {
+        // pfx rises strictly, so the b with pfx[b] <= g0 are 0 .. lo
+        const int lane = threadIdx.x & 63;
+        const bool le = lane < a.B && pfx[min(lane, a.B - 1)] <= s.g0;
+        s.b = __popcll(__builtin_amdgcn_ballot_w64(le)) - 1;
+      } else {
+        int lo = 0, hi = a.B;  // last b with pfx[b] <= g0
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pfx[mid] <= s.g0) lo = mid; else hi = mid;
+        }
+        s.b = uniform(lo);
       }
-      s.b = uniform(lo);
     }
   }
   return s;

@@ -186,6 +186,26 @@ def test_bf16_many_short_sequences_share_units():
     assert np.abs(got["lse"][seqs] - ref["lse"]).max() <= 2e-2
 
 
+@pytest.mark.parametrize("B", [1, 63, 64, 65, 300])
+def test_bf16_balanced_split_on_both_sides_of_the_one_wave_prefix(B):
+    """The balanced split's prefix over the sequences is scanned by one wave
+    for up to 64 sequences and by the whole workgroup beyond that, and the
+    first sequence of a unit is found by a ballot or by a binary search
+    accordingly: both sides of that boundary, every sequence up to B = 65 and
+    a sample at B = 300."""
+    rng = np.random.default_rng(100 + B)
+    lens = [int(x) for x in rng.integers(1, 700, size=B)]
+    wl = W.make_workload("decode_h16", B=B, H=16, lens=lens)
+    _note(f"case balanced split B={B} total={sum(lens)}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    got = _run_decode(dd, num_splits=0)
+    seqs = list(range(B)) if B <= 65 else list(range(0, B, 11)) + [B - 1]
+    ref = _oracle_decode(dd, seqs=seqs)
+    assert _rel(got["o"][seqs], ref["o"]) <= 2e-2
+    assert _rel(got["z"][seqs], ref["z"]) <= 2e-2
+    assert np.abs(got["lse"][seqs] - ref["lse"]).max() <= 2e-2
+
+
 # --------------------------------------------------------------------------- fp8 cache decode
 
 def _oracle_decode_dequantised(dd, seqs=None):
