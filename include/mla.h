@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad dtype combination */
-  MLA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement    */
+  MLA_ERR_UNSUPPORTED = 2, /* valid request the library does not implement   */
   MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
   MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed      */
 } mla_status;

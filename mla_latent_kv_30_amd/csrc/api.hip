@@ -146,7 +146,7 @@ const char* mla_status_string(int32_t s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: not supported by this build";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: not supported by the library";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
     default: return "unknown mla_status";
