@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["api.hip", "absorb.hip", "cache_write.hip", "decode.hip", "linear.hip", "upproj.hip"]
+SOURCES = ["api.hip", "absorb.hip", "cache_write.hip", "decode.hip", "merge.hip", "linear.hip", "upproj.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 add/mul/fma.
