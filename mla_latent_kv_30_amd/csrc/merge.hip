@@ -78,7 +78,41 @@ __global__ void __launch_bounds__(128) merge_kernel(DecodeArgs a) {
 // loads go out before the merge, so the weight and partial latencies
 // overlap.  Every sequence re-reads W^UV_h (from L2), so this form is only
 // used for up to kFusedMaxB sequences.
-constexpr int kFusedBatch = 16;
+// The pieces of one sequence, NB per batch (one round trip each), folded
+// into a running maximum, weight sum and this thread's two channels of z.
+// The batch is 16 pieces for sequences of at most 16 and 32 otherwise, so
+// that up to 32 pieces cost one round trip; past the last piece a batch
+// re-loads that piece.
+template <int NB>
+__device__ __forceinline__ void fused_merge_pieces(const DecodeArgs& a, int slot0, int n, int head, int tid,
+                                                   float& mx, float& wsum, float2& acc) {
+  for (int c0 = 0; c0 < n; c0 += NB) {
+    float lv[NB];
+    float2 zv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int c = min(c0 + u, n - 1);  // every slot loaded holds a piece of this sequence
+      const size_t sl = (size_t)(slot0 + c) * a.H + head;
+      lv[u] = c0 + u < n ? a.lsep[sl] : -INFINITY;
+      zv[u] = *(const float2*)(a.zp + sl * kDc + 2 * tid);
+    }
+    float mb = mx;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) mb = fmaxf(mb, lv[u]);
+    const float alpha = __expf(mx - mb);  // mx = -inf on the first batch: alpha = 0
+    wsum *= alpha;
+    acc.x *= alpha;
+    acc.y *= alpha;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float w = __expf(lv[u] - mb);  // 0 for the padding entries
+      wsum += w;
+      acc.x += w * zv[u].x;
+      acc.y += w * zv[u].y;
+    }
+    mx = mb;
+  }
+}
 
 __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeUpArgs m) {
   const DecodeArgs& a = m.d;
@@ -105,32 +139,8 @@ __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeUpArgs m) {
   } else {
     float mx = -INFINITY, wsum = 0.f;
     float2 acc = make_float2(0.f, 0.f);
-    for (int c0 = 0; c0 < n; c0 += kFusedBatch) {
-      float lv[kFusedBatch];
-      float2 zv[kFusedBatch];
-#pragma unroll
-      for (int u = 0; u < kFusedBatch; ++u) {
-        const int c = min(c0 + u, n - 1);  // every slot loaded holds a piece of this sequence
-        const size_t sl = (size_t)(slot0 + c) * a.H + head;
-        lv[u] = c0 + u < n ? a.lsep[sl] : -INFINITY;
-        zv[u] = *(const float2*)(a.zp + sl * kDc + 2 * tid);
-      }
-      float mb = mx;
-#pragma unroll
-      for (int u = 0; u < kFusedBatch; ++u) mb = fmaxf(mb, lv[u]);
-      const float alpha = __expf(mx - mb);  // mx = -inf on the first batch: alpha = 0
-      wsum *= alpha;
-      acc.x *= alpha;
-      acc.y *= alpha;
-#pragma unroll
-      for (int u = 0; u < kFusedBatch; ++u) {
-        const float w = __expf(lv[u] - mb);  // 0 for the padding entries
-        wsum += w;
-        acc.x += w * zv[u].x;
-        acc.y += w * zv[u].y;
-      }
-      mx = mb;
-    }
+    if (n <= 16) fused_merge_pieces<16>(a, slot0, n, head, tid, mx, wsum, acc);
+    else fused_merge_pieces<32>(a, slot0, n, head, tid, mx, wsum, acc);
     const float inv = 1.0f / wsum;
     const float2 z2 = make_float2(acc.x * inv, acc.y * inv);
     zs[2 * tid] = z2.x;
