@@ -72,8 +72,9 @@ def parse():
 
 
 def cpu_baseline(wl, host, budget_s):
-    """The oracle as it stands, on whole sequences until the time budget is used."""
-    import numpy as np
+    """The oracle as it stands, on whole sequences until the time budget is
+    used: sequences in order, over the workload again when it is done before
+    the budget (a small workload takes well under a second per pass)."""
     from oracle import mla_oracle as orc
 
     cores = len(os.sched_getaffinity(0))
@@ -82,18 +83,18 @@ def cpu_baseline(wl, host, budget_s):
     tokens = 0
     seqs = 0
     t0 = time.perf_counter()
-    for b in range(wl.B):
+    while seqs == 0 or time.perf_counter() - t0 <= budget_s:
+        b = seqs % wl.B
         orc.decode_sequence(host["q_c"][b][heads], host["q_r"][b][heads], host["c_kv"][off[b]:off[b + 1]],
                             host["k_r"][off[b]:off[b + 1]], host["w_uk"][heads], host["w_uv"][heads])
         tokens += int(wl.lens[b])
         seqs += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
     dt = time.perf_counter() - t0
     # cached tokens per second with all of the workload's heads
     rate = tokens * len(heads) / wl.H / dt
+    passes = f"{seqs / wl.B:.1f} passes over the {wl.B} sequences" if seqs > wl.B else f"{seqs} of {wl.B} sequences"
     return {"value": rate, "unit": "cached-tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{seqs} of {wl.B} sequences ({tokens} cached tokens) x {len(heads)} of {wl.H} heads, "
+            "sample": f"{passes} ({tokens} cached tokens) x {len(heads)} of {wl.H} heads, "
                       f"fp64 NumPy, {dt:.1f} s; rate scaled to all {wl.H} heads"}
 
 
