@@ -410,8 +410,11 @@ template <int NTHREADS>
 __device__ __forceinline__ void dequant_block(const uint8_t* stage, uint8_t* buf, int wave) {
   // offsets recomputed per block, not held across the loop
   const int t0 = 64 * wave + lane_id_fresh();
+  constexpr int kItems = kBlockRows * 16, kKrItems = kBlockRows * 8;
 #pragma unroll
-  for (int t = t0; t < kBlockRows * 16; t += NTHREADS) {
+  for (int it = 0; it < (kItems + NTHREADS - 1) / NTHREADS; ++it) {
+    const int t = t0 + it * NTHREADS;
+    if (t >= kItems) break;
     const int r = t >> 4, sub = t & 15;
     const float sc = *(const float*)(stage + kStScale + (r * 4 + (sub >> 2)) * 4);
     const uint8_t* src = stage + kStCkv + r * kDc + sub * 32;
@@ -437,7 +440,9 @@ __device__ __forceinline__ void dequant_block(const uint8_t* stage, uint8_t* buf
     }
   }
 #pragma unroll
-  for (int t = t0; t < kBlockRows * 8; t += NTHREADS) {
+  for (int it = 0; it < (kKrItems + NTHREADS - 1) / NTHREADS; ++it) {
+    const int t = t0 + it * NTHREADS;
+    if (t >= kKrItems) break;
     const int kr_row = t >> 3, kc = t & 7;
     const int4v kr = lds_read_b128(stage + kStKr + kr_row * (kDr * 2) + kc * 16);
     *(MLA_LDS int4v*)(buf + lds_off(kr_row, kDc * 2 + kc * 16)) = kr;
