@@ -1,6 +1,6 @@
-// Device-side pieces shared by the matrix-core decode kernels (decode.hip,
-// decode_wide.hip): the work schedule, the LDS row layout, the page-block
-// copies and the fp8 expansion.
+// Device-side pieces of the decode kernels (decode.hip): the work schedule
+// (shared by the matrix-core and fp32 kernels), the LDS row layout, the
+// page-block copies and the fp8 expansion.
 #pragma once
 
 #include "common.h"
