@@ -1,0 +1,45 @@
+"""bench.py's command line and output: one JSON line with the fields its
+readers depend on, one GPU only."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench(*args, timeout=240):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT, capture_output=True,
+                          text=True, timeout=timeout)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = _bench("--gpus", "2")
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+def test_decode_line_has_every_field():
+    print("case bench.py --steps 4 --warmup 1 --no-cpu-baseline", flush=True)
+    r = _bench("--steps", "4", "--warmup", "1", "--no-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    for k, t in [("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int), ("warmup", int),
+                 ("ms_per_step", float), ("higher_is_better", bool), ("scaling", str), ("dtype", str), ("data", str),
+                 ("config", dict), ("roofline", dict)]:
+        assert isinstance(d[k], t), k
+    assert d["n_gpus"] == 1 and d["steps"] == 4 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["vs_baseline"] is None and d["cpu_baseline"] is None
+    assert d["config"]["workload"] == "decode_h16"
+    assert 1 <= d["config"]["graph_steps"] <= 4 and 4 % d["config"]["graph_steps"] == 0
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert 0 < rf["frac"] <= 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    # the achieved rate is the algorithmic bytes over the kernel's event-timed duration
+    assert abs(rf["achieved"] - rf["alg_bytes_per_launch"] / (rf["kernel_avg_us"] * 1e-6) / 1e9) < 1e-6 * rf["achieved"]
+    assert rf["traffic"] is None or rf["traffic"] > rf["alg_bytes_per_launch"]
