@@ -383,8 +383,12 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   }
   Cursor ld = cp;
   int issued = 0;
+  // With the query staged through LDS, block 0 goes out with it and blocks
+  // 1 and 2 only once it has landed: all workgroups start at once, and the
+  // query and first block would otherwise queue behind 27 MB of later blocks.
+  constexpr int kFirst = kQueryViaLds ? 1 : kNBuf - 1;
 #pragma unroll
-  for (int j = 0; j < kNBuf - 1; ++j) {
+  for (int j = 0; j < kFirst; ++j) {
     if (ld.valid) {
       issue(ld, j);
       ++issued;
@@ -400,6 +404,14 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     for (int kk = 0; kk < NQ; ++kk) st.q[kk] = __builtin_bit_cast(bf16x8, lds_read_b128_at(qa + 64 * (k0 + kk)));
   } else {
     consume_query(st.q);
+  }
+#pragma unroll
+  for (int j = kFirst; j < kNBuf - 1; ++j) {
+    if (ld.valid) {
+      issue(ld, j);
+      ++issued;
+      cursor_next(a, ld);
+    }
   }
   reset_state(st);
   note_pieces(cp.seg);
