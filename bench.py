@@ -20,9 +20,16 @@ output projection (mla_output_proj: u = W^O [o_1..o_H]), with synthetic
 bf16 weights at model width --d-model; each projection is also timed alone
 against its HBM roofline.
 
-Prints one JSON line: value = cached tokens per second over the whole step,
-plus the decode kernel's achieved HBM bandwidth and matrix-core rate against
-MI355X's published peaks, and the CPU oracle timed on a bounded sample.
+Prints one JSON line: value = cached tokens per second over the whole step
+(median, p10 and p90 of the per-step times beside the mean), the decode
+kernel's achieved HBM bandwidth and matrix-core rate against MI355X's
+published peaks and against ceilings measured in the same run (streaming
+HBM read, bf16 matrix-core loop, LDS reads: include/mla_ceilings.h), and the
+CPU oracle timed on a bounded sample.  The default workload is the largest
+one that fits one GPU, decode_h128 (B = 64 sequences, 128 heads, lengths
+U[8192, 32768]); with the default --config the line also carries, under
+"workloads", one record per other workload (decode_h16, long_bf16, long_fp8,
+prefill_h128) measured the same way with fewer steps.
 """
 
 from __future__ import annotations
@@ -43,6 +50,8 @@ PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix cores
 PEAK_F32_TFLOPS = 157.3        # fp32 matrix
 FLOP_PER_TOKEN_HEAD = 2 * 576 + 2 * 512   # score + latent accumulation
 REPLICA_TARGET_BYTES = 600 << 20
+HEADLINE = "decode_h128"
+SUB_WORKLOADS = ("decode_h16", "long_bf16", "long_fp8", "prefill_h128")
 
 
 def parse():
@@ -50,7 +59,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode_h16",
+    ap.add_argument("--config", default=HEADLINE,
                     choices=["decode_h16", "decode_h128", "long_bf16", "long_fp8", "tiny_f32", "prefill_h128"])
     ap.add_argument("--splits", type=int, default=-1, help="num_splits (-1: the workload's own, 0: automatic)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0: enough for 600 MB)")
@@ -68,13 +77,88 @@ def parse():
     ap.add_argument("--d-model", type=int, default=7168, help="model width d for --layer (not fixed by the pages)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence (multi-token decode, mla_decode_multi); decode workloads only")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-workload sub-records of the default run")
+    ap.add_argument("--sub-steps", type=int, default=20, help="timed steps of each sub-record")
+    ap.add_argument("--sub-cpu-seconds", type=float, default=3.0, help="CPU oracle budget of each sub-record")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling kernels")
     return ap.parse_args()
+
+
+def _pct(xs, q):
+    """q-th percentile (linear interpolation) of a list of floats."""
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def step_stats(step_ms):
+    return {"median": _pct(step_ms, 50), "p10": _pct(step_ms, 10), "p90": _pct(step_ms, 90), "n": len(step_ms)}
+
+
+def blas_info():
+    """The NumPy build and the BLAS library and thread count the oracle runs on."""
+    import numpy as np
+    try:
+        import threadpoolctl
+        info = [{k: d.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+                for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+    except Exception as e:  # threadpoolctl missing: record that
+        info = [{"error": str(e)}]
+    return {"numpy": np.__version__, "blas": info}
+
+
+def measure_ceilings(dev):
+    """Streaming HBM read (2 GiB), bf16 matrix-core loops (both shapes the
+    kernels issue) and LDS reads (16-byte and transposing), each the median
+    of five timed launches."""
+    import torch
+
+    import mla_latent_kv_30_amd as mla
+    from mla_latent_kv_30_amd import _lib as L
+
+    sink = L.ceiling_sink(dev)
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+
+    def timed(launch, reps=5):
+        launch()
+        torch.cuda.synchronize()
+        ms = []
+        work = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            work = launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        return work, ms[len(ms) // 2]
+
+    out = {}
+    w, ms = timed(lambda: L.ceiling_hbm_read(buf, sink))
+    out["hbm_read_GBps"] = w / (ms * 1e-3) / 1e9
+    del buf
+    for name, shape in (("mfma_bf16_32x32x16_TFLOPs", L.CEILING_MFMA_32X32X16),
+                        ("mfma_bf16_16x16x32_TFLOPs", L.CEILING_MFMA_16X16X32)):
+        w, ms = timed(lambda: L.ceiling_mfma_bf16(shape, 20000, sink))
+        out[name] = w / (ms * 1e-3) / 1e12
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    for name, kind in (("lds_read_b128_B_per_clk_cu", L.CEILING_LDS_B128),
+                       ("lds_read_tr_b64_B_per_clk_cu", L.CEILING_LDS_TR_B64)):
+        w, ms = timed(lambda: L.ceiling_lds_read(kind, 4000, sink))
+        out[name] = w / (ms * 1e-3) / cus / 2.4e9
+    out["note"] = ("medians of 5 launches; LDS bytes per clock per compute unit at the 2.4 GHz nominal clock; "
+                   f"{cus} compute units")
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, host, budget_s):
     """The oracle as it stands, on whole sequences until the time budget is
     used: sequences in order, over the workload again when it is done before
-    the budget (a small workload takes well under a second per pass)."""
+    the budget (a small workload takes well under a second per pass).  Every
+    head for up to 16 heads, else the first 8 (heads are independent)."""
     from oracle import mla_oracle as orc
 
     cores = len(os.sched_getaffinity(0))
@@ -95,10 +179,86 @@ def cpu_baseline(wl, host, budget_s):
     passes = f"{seqs / wl.B:.1f} passes over the {wl.B} sequences" if seqs > wl.B else f"{seqs} of {wl.B} sequences"
     return {"value": rate, "unit": "cached-tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{passes} ({tokens} cached tokens) x {len(heads)} of {wl.H} heads, "
-                      f"fp64 NumPy, {dt:.1f} s; rate scaled to all {wl.H} heads"}
+                      f"fp64 NumPy, {dt:.1f} s; rate scaled to all {wl.H} heads",
+            "extrapolated_full_step_s": wl.total_tokens / rate, "build": blas_info()}
 
 
-def run_prefill(args, wl, dev):
+def cpu_baseline_prefill(wl, host, budget_s, seed=0):
+    """The oracle's causal prefill on 8 heads, one query row at a time (row
+    T-1, row 0, then random rows) until the time budget is used; rate in the
+    method's algorithmic TFLOP/s (causal pairs x heads x 2176 FLOP)."""
+    import numpy as np
+
+    from oracle import mla_oracle as orc
+
+    cores = len(os.sched_getaffinity(0))
+    T = int(wl.lens[0])
+    heads = list(range(min(8, wl.H)))
+    rng = np.random.default_rng(seed)
+    order = [T - 1, 0] + [int(x) for x in rng.permutation(np.arange(1, T - 1))]
+    q_c, q_r = host["q_c"][:, heads], host["q_r"][:, heads]
+    w_uk, w_uv = host["w_uk"][heads], host["w_uv"][heads]
+    pairs = 0
+    rows = 0
+    t0 = time.perf_counter()
+    while rows == 0 or (time.perf_counter() - t0 <= budget_s and rows < len(order)):
+        t = order[rows]
+        orc.prefill_causal(q_c, q_r, host["c_kv"], host["k_r"], w_uk, w_uv, rows=[t])
+        pairs += t + 1
+        rows += 1
+    dt = time.perf_counter() - t0
+    rate = pairs * len(heads) * FLOP_PER_TOKEN_HEAD / dt / 1e12
+    full = T * (T + 1) // 2 * wl.H * FLOP_PER_TOKEN_HEAD / (rate * 1e12)
+    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} query rows (row {T - 1}, row 0, then random; {pairs} causal pairs) x {len(heads)} of "
+                      f"{wl.H} heads, fp64 NumPy, {dt:.1f} s",
+            "extrapolated_full_step_s": full, "build": blas_info()}
+
+
+def _timed_steps(run, n, group):
+    """Run `run(i)` for i < n between events: the total and one time per call
+    (each call runs `group` steps), in ms."""
+    import torch
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(n):
+        run(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) / group for i in range(n) for _ in range(group)]
+    return evs[0].elapsed_time(evs[n]), per, wall
+
+
+def _timed_batches(call, K, R):
+    """The kernel alone: K back-to-back launches between two events on the
+    stream it runs on, three times (sorted ms per launch); a GPU sleep first
+    lets the host enqueue every launch ahead of the device, so no host
+    latency lands inside the timed batch."""
+    import torch
+
+    out_ms = []
+    for _rep in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * K)))
+        except Exception:  # no device sleep available: host latency may inflate the kernel time
+            pass
+        e0.record()
+        for k in range(K):
+            call(k % R)
+        e1.record()
+        torch.cuda.synchronize()
+        out_ms.append(e0.elapsed_time(e1) / K)
+    out_ms.sort()
+    return out_ms
+
+
+def run_prefill(args, wl, dev, steps, warmup, cpu_seconds):
     """Causal prefill of one sequence: absorb_q + prefill_causal (cache append and
     causal attention) + upproj_v over all T rows; value = algorithmic TFLOP/s."""
     import numpy as np
@@ -111,6 +271,7 @@ def run_prefill(args, wl, dev):
     w_uk, w_uv = W.weights(wl)
     q_c, q_r = W.queries(wl)
     c, k = W.sequence_latents(wl, 0)
+    host = {"q_c": q_c, "q_r": q_r, "w_uk": w_uk, "w_uv": w_uv, "c_kv": c, "k_r": k}
     td = lambda x: torch.from_numpy(x).to(dev, torch.bfloat16)
     w_uk, w_uv, q_c, q_r, c, k = (td(x) for x in (w_uk, w_uv, q_c, q_r, c, k))
     npg = (T + 63) // 64
@@ -146,7 +307,7 @@ def run_prefill(args, wl, dev):
     def out_proj():
         mla.output_proj(o.view(T, H * 128), lw["w_o"], workspace=ws_o, out=u)
 
-    def step():
+    def step(_i=0):
         if LAYER:
             q_proj()
             kv_proj()
@@ -156,78 +317,63 @@ def run_prefill(args, wl, dev):
         if LAYER:
             out_proj()
 
-    for _ in range(max(1, args.warmup)):
+    for _ in range(max(1, warmup)):
         step()
     torch.cuda.synchronize()
-    K = args.steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(K):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / K
-    # the attention (cache append + causal decode kernel) alone: K launches between two events
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(K):
-        mla.prefill_causal(q_abs, c, k, cache, bt, z=z, lse=lse)
-    e1.record()
-    torch.cuda.synchronize()
-    kern_avg_ms = e0.elapsed_time(e1) / K
+    K = steps
+    total_ms, per_step, wall = _timed_steps(step, K, 1)
+    ms_per_step = total_ms / K
+    kern_ms = _timed_batches(lambda _r: mla.prefill_causal(q_abs, c, k, cache, bt, z=z, lse=lse), K, 1)
+    kern_avg_ms = kern_ms[1]
     pairs = T * (T + 1) // 2
     attn_flops = pairs * H * FLOP_PER_TOKEN_HEAD
     proj_flops = 2 * T * H * 2 * 128 * 512
     tflops_kernel = attn_flops / (kern_avg_ms * 1e-3) / 1e12
+    # the step's other parts alone
+    parts = {}
+    for name, call in (("absorb_q", lambda _r: mla.absorb_q(q_c, q_r, pos, w_uk, out=q_abs)),
+                       ("upproj_v", lambda _r: mla.upproj_v(z, w_uv, out=o, out_dtype=o.dtype))):
+        parts[name] = {"us": _timed_batches(call, K, 1)[1] * 1e3}
     layer = None
     if LAYER:
         flops = {"q_project": 2 * T * (D * dcq + dcq * H * 192), "kv_projection": 2 * T * D * 576,
                  "output_proj": 2 * T * H * 128 * D}
         layer = {"d_model": D, "d_cq": dcq}
         for name, call in (("q_project", q_proj), ("kv_projection", kv_proj), ("output_proj", out_proj)):
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a0.record()
-            for _ in range(K):
-                call()
-            a1.record()
-            torch.cuda.synchronize()
-            ms = a0.elapsed_time(a1) / K
+            ms = _timed_batches(lambda _r: call(), K, 1)[1]
             tf = flops[name] / (ms * 1e-3) / 1e12
             layer[name] = {"us": ms * 1e3, "alg_flops": flops[name], "TFLOP/s": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
         proj_flops += sum(flops.values())
-    out = {
+    from mla_latent_kv_30_amd import traffic as TR
+    mc = TR.load("decode_mfma_kernel", wl.name, os.path.join(ROOT, "profiles"), "mfma")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, host, cpu_seconds, args.seed)
+    return {
         "metric": "MLA causal prefill TFLOP/s (absorbed attention + absorb + up-projection)",
         "value": (attn_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": warmup, "ms_per_step": ms_per_step,
+        "step_ms": step_stats(per_step),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name + (f"+layer(d={D})" if LAYER else ""), "tokens": T, "heads": H,
                    "causal_pairs": pairs,
                    "step": ("q_project + kv projection + " if LAYER else "") +
                            "absorb_q + prefill_causal (cache append + causal attention) + upproj_v" +
                            (" + output_proj" if LAYER else "")},
-        "layer": layer,
+        "layer": layer, "parts": parts,
         "roofline": {
             "bound": "mfma", "achieved": tflops_kernel, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": tflops_kernel / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "decode_mfma_kernel (prefill)",
-            "kernel_avg_us": kern_avg_ms * 1e3, "alg_flops_per_launch": attn_flops,
+            "frac": tflops_kernel / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "prefill attention (mla_prefill_causal)",
+            "kernel_avg_us": kern_avg_ms * 1e3, "kernel_batches_us": [x * 1e3 for x in kern_ms],
+            "alg_flops_per_launch": attn_flops,
+            "mfma_counters": None if mc is None else {
+                "issued_tflops": mc["issued_tflops"], "busy_frac": mc["busy_frac"],
+                "issued_over_algorithmic": mc["mfma_flops_issued"] / attn_flops},
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "wall_s_timed": wall,
     }
-    print(json.dumps(out), flush=True)
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        sys.exit(f"bench.py measures the decode path on one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) "
-                 f"is not supported: sharding across GPUs is not part of this library.")
-
+def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
     import numpy as np
     import torch
 
@@ -235,15 +381,6 @@ def main():
     from mla_latent_kv_30_amd import device_inputs as DI
     from mla_latent_kv_30_amd import workload as W
 
-    if not torch.cuda.is_available():
-        sys.exit("bench.py needs a GPU")
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    wl = W.make_workload(args.config, seed=args.seed)
-    if wl.kind == "prefill":
-        run_prefill(args, wl, dev)
-        return
     splits = wl.splits if args.splits < 0 else args.splits
     t_setup = time.perf_counter()
     dd = DI.decode_inputs(wl, dev, keep_host=not args.no_cpu_baseline)
@@ -330,7 +467,7 @@ def main():
         if LAYER:
             out_proj(r)
 
-    for k in range(max(1, args.warmup)):
+    for k in range(max(1, warmup)):
         step(k % R)
     torch.cuda.synchronize()
 
@@ -338,6 +475,7 @@ def main():
     # per decode step.  G divides K, so the timed loop replays whole graphs;
     # graph j runs steps jG .. jG+G-1 (modulo R) and the graphs rotate, so
     # step k always reads replica k % R, as with a graph per step.
+    K = steps
     graphs = None
     G = 1
     multis = []
@@ -353,7 +491,7 @@ def main():
                         step(r)
                     graphs.append(g)
             want = min(R, args.graph_steps) if args.graph_steps > 0 else R
-            G = max(d for d in range(1, want + 1) if args.steps % d == 0)
+            G = max(d for d in range(1, want + 1) if K % d == 0)
             if G > 1:
                 with torch.cuda.stream(side):
                     for j in range(R // math.gcd(G, R)):
@@ -365,55 +503,25 @@ def main():
             torch.cuda.current_stream().wait_stream(side)
             for g in multis:
                 g.replay()
-            for k in range(max(1, args.warmup)):
+            for k in range(max(1, warmup)):
                 graphs[k % R].replay()
             torch.cuda.synchronize()
         except Exception as e:  # capture not available: fall back to eager launches
             print(f"note: graph capture failed ({e}); timing eager launches", file=sys.stderr)
             graphs = None
+            G = 1
 
-    # ---- timed region: exactly `steps` steps between two synchronisations
-    K = args.steps
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
+    # ---- timed region: exactly `steps` steps between two synchronisations,
+    # an event after every graph (G steps) for the per-step distribution
     if graphs is not None and G > 1:
-        for t in range(K // G):
-            multis[t % len(multis)].replay()
+        total_ms, per_step, wall = _timed_steps(lambda t: multis[t % len(multis)].replay(), K // G, G)
     elif graphs is not None:
-        for k in range(K):
-            graphs[k % R].replay()
+        total_ms, per_step, wall = _timed_steps(lambda k: graphs[k % R].replay(), K, 1)
     else:
-        for k in range(K):
-            step(k % R)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / K
+        total_ms, per_step, wall = _timed_steps(lambda k: step(k % R), K, 1)
+    ms_per_step = total_ms / K
 
-    # ---- the decode kernel alone (mla_decode_partial): K back-to-back launches
-    # between two events on the stream it runs on, three times; a GPU sleep
-    # first lets the host enqueue every launch ahead of the device, so no host
-    # latency lands inside the timed batch
-    def timed_batches(call):
-        out_ms = []
-        for _rep in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            try:
-                torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * K)))
-            except Exception:  # no device sleep available: host latency may inflate the kernel time
-                pass
-            e0.record()
-            for k in range(K):
-                call(k % R)
-            e1.record()
-            torch.cuda.synchronize()
-            out_ms.append(e0.elapsed_time(e1) / K)
-        out_ms.sort()
-        return out_ms
-
+    # ---- the decode kernel alone (mla_decode_partial)
     def decode_only(r):
         cache = reps[r][0]
         if QL > 1:  # the multi-token entry point is decode + merge
@@ -422,8 +530,17 @@ def main():
         else:
             mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
 
-    kern_ms = timed_batches(decode_only)
+    kern_ms = _timed_batches(decode_only, K, R)
     kern_avg_ms = kern_ms[1]  # median of the three batches
+    parts = None
+    if QL == 1 and not LAYER:
+        parts = {
+            "absorb_q": {"us": _timed_batches(lambda r: mla.absorb_q(reps[r][1], reps[r][2], pos_q, reps[r][3],
+                                                                     out=q_abs), K, R)[1] * 1e3},
+            "decode_merge_upproj": {"us": _timed_batches(
+                lambda r: mla.decode_merge_upproj(dd.seq_lens, H, ws, z, reps[r][4], lse=lse, num_splits=splits,
+                                                  out=o, out_dtype=o.dtype), K, R)[1] * 1e3},
+        }
 
     layer = None
     if LAYER:
@@ -439,7 +556,7 @@ def main():
         layer = {"d_model": D, "d_cq": dcq}
         for name, call in (("qkv_project", qkv_proj), ("q_project", q_proj), ("kv_append", kv_app),
                            ("output_proj", out_proj)):
-            ms = timed_batches(call)[1]
+            ms = _timed_batches(call, K, R)[1]
             gbs_p = nbytes[name] / (ms * 1e-3) / 1e9
             layer[name] = {"us": ms * 1e3, "alg_bytes": nbytes[name], "GB/s": gbs_p, "hbm_frac": gbs_p / PEAK_HBM_GBS}
 
@@ -460,10 +577,12 @@ def main():
     gbs = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
     tflops = alg_flops / (kern_avg_ms * 1e-3) / 1e12
     mfma_peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+    # the bound at MI355X's ridge (matrix-core peak / HBM peak, FLOP per byte)
+    mfma_bound = alg_flops / alg_bytes > mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
 
     cpu = None
     if not args.no_cpu_baseline and QL == 1:
-        cpu = cpu_baseline(wl, dd.host, args.cpu_seconds)
+        cpu = cpu_baseline(wl, dd.host, cpu_seconds)
 
     # HBM bytes per launch from the stored counter runs, if they were taken on
     # the current kernel sources
@@ -474,14 +593,34 @@ def main():
     if QL > 1:
         kname += " + merge_kernel"
 
-    out = {
+    roof = {
+        "bound": "mfma" if mfma_bound else "hbm",
+        "achieved": tflops if mfma_bound else gbs,
+        "peak": mfma_peak if mfma_bound else PEAK_HBM_GBS,
+        "unit": "TFLOP/s" if mfma_bound else "GB/s",
+        "frac": tflops / mfma_peak if mfma_bound else gbs / PEAK_HBM_GBS,
+        "traffic": None if tr is None else tr["traffic_bytes"], "kernel": kname,
+        "traffic_fetch_bytes": None if tr is None else tr["fetch_bytes"],
+        "traffic_write_bytes": None if tr is None else tr["write_bytes"],
+        "kernel_avg_us": kern_avg_ms * 1e3, "kernel_batches_us": [x * 1e3 for x in kern_ms],
+        "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
+        "hbm_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+        "tflops": tflops, "mfma_peak_tflops": mfma_peak, "mfma_frac": tflops / mfma_peak,
+        # matrix-core counters of the same kernel (stored run on the current sources)
+        "mfma_counters": None if mc is None else {
+            "issued_tflops": mc["issued_tflops"], "busy_frac": mc["busy_frac"],
+            "issued_over_algorithmic": mc["mfma_flops_issued"] / alg_flops},
+    }
+    del reps, dd
+    return {
         "metric": METRIC,
         "value": total / (ms_per_step * 1e-3),
         "unit": "cached-tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
+        "step_ms": step_stats(per_step),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -499,25 +638,70 @@ def main():
                      else "absorb_q + decode_multi_upproj (decode, then split merge + W_UV up-projection)"),
             "q_len": QL, "query_tokens_per_s": B * QL / (ms_per_step * 1e-3),
         },
-        "layer": layer,
-        "roofline": {
-            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-            "traffic": None if tr is None else tr["traffic_bytes"], "kernel": kname,
-            "traffic_fetch_bytes": None if tr is None else tr["fetch_bytes"],
-            "traffic_write_bytes": None if tr is None else tr["write_bytes"],
-            "kernel_avg_us": kern_avg_ms * 1e3, "kernel_batches_us": [x * 1e3 for x in kern_ms],
-            "alg_bytes_per_launch": alg_bytes,
-            "alg_flops_per_launch": alg_flops, "tflops": tflops, "mfma_peak_tflops": mfma_peak,
-            "mfma_frac": tflops / mfma_peak,
-            # matrix-core counters of the same kernel (stored run on the current sources)
-            "mfma_counters": None if mc is None else {
-                "issued_tflops": mc["issued_tflops"], "busy_frac": mc["busy_frac"],
-                "issued_over_algorithmic": mc["mfma_flops_issued"] / alg_flops},
-        },
+        "layer": layer, "parts": parts,
+        "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
         "setup_s": setup_s,
     }
+
+
+def against_ceilings(rec, ceil):
+    """Fractions of the measured ceilings beside those of the published peaks."""
+    if not ceil or not rec or "roofline" not in rec:
+        return
+    rf = rec["roofline"]
+    m16 = ceil.get("mfma_bf16_16x16x32_TFLOPs")
+    if rf.get("hbm_GBps") is not None and ceil.get("hbm_read_GBps"):
+        rf["hbm_frac_of_measured"] = rf["hbm_GBps"] / ceil["hbm_read_GBps"]
+    tf = rf.get("tflops", rf["achieved"] if rf["unit"] == "TFLOP/s" else None)
+    if tf is not None and m16 and rec.get("dtype") != "f32":
+        rf["mfma_frac_of_measured"] = tf / m16
+
+
+def run(args, name, dev, steps, warmup, cpu_seconds):
+    from mla_latent_kv_30_amd import workload as W
+
+    wl = W.make_workload(name, seed=args.seed)
+    if wl.kind == "prefill":
+        return run_prefill(args, wl, dev, steps, warmup, cpu_seconds)
+    return run_decode(args, wl, dev, steps, warmup, cpu_seconds)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit(f"bench.py measures the decode path on one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) "
+                 f"is not supported: sharding across GPUs is not part of this library.")
+
+    import torch
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    out = run(args, args.config, dev, args.steps, args.warmup, args.cpu_seconds)
+    torch.cuda.empty_cache()
+    ceil = None
+    if not args.no_ceilings:
+        ceil = measure_ceilings(dev)
+        against_ceilings(out, ceil)
+    out["ceilings"] = ceil
+    if (args.config == HEADLINE and not args.no_extra and not args.layer and args.q_len == 1
+            and args.splits < 0):
+        subs = {}
+        for name in SUB_WORKLOADS:
+            print(f"sub-record {name}", file=sys.stderr, flush=True)
+            try:
+                rec = run(args, name, dev, args.sub_steps, min(args.warmup, 3), args.sub_cpu_seconds)
+                against_ceilings(rec, ceil)
+            except Exception as e:  # a sub-record must not cost the headline line
+                rec = {"error": f"{type(e).__name__}: {e}"}
+            subs[name] = rec
+            torch.cuda.empty_cache()
+        out["workloads"] = subs
     print(json.dumps(out), flush=True)
 
 

@@ -21,6 +21,9 @@
  *   - All tensor arguments are device pointers owned by the caller, dense and
  *     row-major in the shapes given.  The library allocates no memory and
  *     keeps no state except a per-device property cache.
+ *   - Every tensor pointer (and every workspace) must be 16-byte aligned:
+ *     the kernels move 16-byte vectors.  A misaligned pointer is rejected
+ *     with MLA_ERR_INVALID_ARG (int32 index arrays are exempt).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Arguments are validated on the host before any HIP call; a
  *     rejected call launches nothing and returns its status synchronously.

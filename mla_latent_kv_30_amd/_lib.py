@@ -18,7 +18,8 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "mla.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADER = os.path.join(INCLUDE, "mla.h")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
@@ -134,14 +135,28 @@ def lib() -> ctypes.CDLL:
     L.mla_output_proj.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
     L.mla_fold_wuv_wo.restype = _i32
     L.mla_fold_wuv_wo.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
+    # mla_ceilings.h
+    _dp = ctypes.POINTER(ctypes.c_double)
+    L.mla_ceiling_sink_floats.restype = _i32
+    L.mla_ceiling_sink_floats.argtypes = []
+    L.mla_ceiling_hbm_read.restype = _i32
+    L.mla_ceiling_hbm_read.argtypes = [_vp, _sz, _vp, _dp, _vp]
+    L.mla_ceiling_mfma_bf16.restype = _i32
+    L.mla_ceiling_mfma_bf16.argtypes = [_i32, _i32, _vp, _dp, _vp]
+    L.mla_ceiling_lds_read.restype = _i32
+    L.mla_ceiling_lds_read.argtypes = [_i32, _i32, _vp, _dp, _vp]
     _LIB = L
     return L
 
 
 def declared_symbols() -> list:
-    """Names of the functions include/mla.h declares."""
-    txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(mla_\w+)\s*\(", txt, flags=re.M)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            txt = open(os.path.join(INCLUDE, f)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(mla_\w+)\s*\(", txt, flags=re.M))
+    return sorted(names)
 
 
 def status_string(status: int) -> str:
@@ -631,3 +646,38 @@ def validate_decode_inputs(seq_lens, block_table, num_pages: int, q_len: int = 1
     return int(lib().mla_validate_decode_inputs(lens.ctypes.data_as(_vp), None if bt is None else bt.ctypes.data_as(_vp),
                                                 B, max_pages if bt is not None else max(1, int(lens.max() + 63) // 64),
                                                 int(num_pages), int(q_len)))
+
+
+# ---------------------------------------------------------------------------
+# Measured ceilings (include/mla_ceilings.h)
+# ---------------------------------------------------------------------------
+CEILING_MFMA_32X32X16, CEILING_MFMA_16X16X32 = 0, 1
+CEILING_LDS_B128, CEILING_LDS_TR_B64 = 0, 1
+
+
+def ceiling_sink(device) -> torch.Tensor:
+    return torch.empty(int(lib().mla_ceiling_sink_floats()), dtype=torch.float32, device=device)
+
+
+def ceiling_hbm_read(buf: torch.Tensor, sink: torch.Tensor) -> float:
+    """Launch the streaming read of `buf`; returns the bytes it reads."""
+    work = ctypes.c_double(0.0)
+    _check(lib().mla_ceiling_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), ctypes.byref(work),
+                                      _stream(buf.device)), "mla_ceiling_hbm_read")
+    return work.value
+
+
+def ceiling_mfma_bf16(shape: int, iters: int, sink: torch.Tensor) -> float:
+    """Launch the bf16 matrix-core loop; returns the FLOPs it issues."""
+    work = ctypes.c_double(0.0)
+    _check(lib().mla_ceiling_mfma_bf16(int(shape), int(iters), _ptr(sink), ctypes.byref(work), _stream(sink.device)),
+           "mla_ceiling_mfma_bf16")
+    return work.value
+
+
+def ceiling_lds_read(kind: int, iters: int, sink: torch.Tensor) -> float:
+    """Launch the LDS read loop; returns the bytes it reads from LDS."""
+    work = ctypes.c_double(0.0)
+    _check(lib().mla_ceiling_lds_read(int(kind), int(iters), _ptr(sink), ctypes.byref(work), _stream(sink.device)),
+           "mla_ceiling_lds_read")
+    return work.value

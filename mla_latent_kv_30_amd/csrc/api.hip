@@ -62,9 +62,19 @@ bool dtype_ok(int32_t d) { return d == MLA_F32 || d == MLA_BF16; }
 
 mla_status launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Every tensor pointer: the kernels read and write them with 16-byte vectors
+// (NULL passes; required pointers are checked for NULL separately).
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
 // Validate the cache descriptor; returns the kernel kind or -1.
 int cache_kind(const mla_cache* c) {
   if (c == nullptr || c->page_size != MLA_PAGE || c->num_pages < 1) return -1;
+  if (!all_aligned16({c->rows, c->ckv_fp8, c->ckv_scale, c->kr})) return -1;
   switch (c->dtype) {
     case MLA_F32:
       return (c->rows && !c->ckv_fp8 && !c->ckv_scale && !c->kr) ? kKindF32 : -1;
@@ -103,14 +113,6 @@ Plan make_plan(int32_t B, int32_t num_splits) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Every pointer the projection kernels read or write with 16-byte vectors.
-bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
-bool all_aligned16(std::initializer_list<const void*> ps) {
-  for (const void* p : ps)
-    if (!aligned16(p)) return false;
-  return true;
-}
 
 // Workspace layout: [per-sequence piece record: B x (first slot, count) int32]
 //                   [partial z: slots x H x 512 fp32][partial lse: slots x H fp32]
@@ -159,6 +161,7 @@ mla_status mla_absorb_q_rope(const void* q_c, const void* q_r, const int32_t* po
                              int32_t N, int32_t H, int32_t dtype, const mla_rope* rope, void* stream) {
   const mla_rope r = rope ? *rope : plain_rope(10000.0f);
   if (!q_c || !q_r || !pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({q_c, q_r, w_uk, q_abs})) return MLA_ERR_INVALID_ARG;
   if (N < 1 || H < 1 || H > MLA_MAX_HEADS || !dtype_ok(dtype)) return MLA_ERR_INVALID_ARG;
   if (!rope_ok(r)) return MLA_ERR_INVALID_ARG;
   if ((long long)N * H > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
@@ -178,6 +181,7 @@ mla_status mla_cache_write_rope(const void* c_kv, const void* k_r, const int32_t
                                 void* stream) {
   const mla_rope r = rope ? *rope : plain_rope(10000.0f);
   if (!c_kv || !k_r || !pos || !slot || T < 1 || !dtype_ok(in_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({c_kv, k_r})) return MLA_ERR_INVALID_ARG;
   if (!rope_ok(r)) return MLA_ERR_INVALID_ARG;
   const int kind = cache_kind(cache);
   if (kind < 0) return MLA_ERR_INVALID_ARG;
@@ -259,6 +263,7 @@ mla_status prepare_decode(const void* q_abs, const mla_cache* cache, const int32
                           int32_t num_splits, void* workspace, size_t ws_bytes, float* z, float* lse, DecodeArgs& a,
                           int& kind, Plan& p) {
   if (!q_abs || !block_table || !seq_lens || !z) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({q_abs, z, workspace})) return MLA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || H > MLA_MAX_HEADS || max_pages < 1) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
@@ -311,6 +316,7 @@ mla_status mla_decode_partial(const void* q_abs, const mla_cache* cache, const i
 mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits, void* workspace,
                             size_t ws_bytes, float* z, float* lse, void* stream) {
   if (!seq_lens || !z || B < 1 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({z, workspace})) return MLA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
   const Plan p = make_plan(B, num_splits);
   const size_t need = workspace_bytes(B, H, p);
@@ -334,6 +340,7 @@ mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H
                                    size_t ws_bytes, float* z, float* lse, const void* w_uv, int32_t w_dtype, void* o,
                                    int32_t o_dtype, void* stream) {
   if (!seq_lens || !z || !w_uv || !o || B < 1 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({z, w_uv, o, workspace})) return MLA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 256) return MLA_ERR_INVALID_ARG;
   if (!dtype_ok(w_dtype) || !dtype_ok(o_dtype)) return MLA_ERR_INVALID_ARG;
   if ((long long)B * H > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
@@ -408,6 +415,7 @@ mla_status mla_decode_multi_upproj(const void* q_abs, const mla_cache* cache, co
                                    void* stream) {
   if (q_len < 1 || H < 1 || (long long)q_len * H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
   if (!w_uv || !o || !dtype_ok(w_dtype) || !dtype_ok(o_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({w_uv, o})) return MLA_ERR_INVALID_ARG;
   DecodeArgs a;
   int kind;
   Plan p;
@@ -452,6 +460,7 @@ mla_status mla_prefill_causal_rope(const void* q_abs, const void* c_kv, const vo
                                    float softmax_scale, const mla_rope* rope, float* z, float* lse, void* stream) {
   const mla_rope rp = rope ? *rope : plain_rope(10000.0f);
   if (!q_abs || !block_table_row || !z || !c_kv || !k_r) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({q_abs, z, c_kv, k_r})) return MLA_ERR_INVALID_ARG;
   if (T < 1 || H < 1 || H > MLA_MAX_HEADS || pos0 < 0) return MLA_ERR_INVALID_ARG;
   if ((long long)pos0 + T > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
@@ -492,6 +501,7 @@ mla_status mla_prefill_causal_rope(const void* q_abs, const void* c_kv, const vo
 mla_status mla_upproj_v(const float* z, const void* w_uv, void* o, int32_t N, int32_t H, int32_t w_dtype,
                         int32_t o_dtype, void* stream) {
   if (!z || !w_uv || !o || N < 1 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({z, w_uv, o})) return MLA_ERR_INVALID_ARG;
   if (!dtype_ok(w_dtype) || !dtype_ok(o_dtype)) return MLA_ERR_INVALID_ARG;
   if ((long long)N * H > 0x7fffffffLL) return MLA_ERR_INVALID_ARG;
   UpprojArgs a{z, w_uv, o, N, H, o_dtype == MLA_BF16 ? 1 : 0};

@@ -372,7 +372,12 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   // more head groups it is loaded into registers directly.  Either way the
   // first three blocks are in flight meanwhile.
   WaveState<NT, NQ> st;
-  const int k0 = kKSplit ? 9 * (wave >> 1) : 0;  // first K-step of the wave's query registers
+  // first K-step of the wave's query registers: 0 or 9 for the four waves
+  // that split the scores, 0 for a wave that only copies (it loads a query
+  // it never uses, and must not read past the head's 576 elements)
+  const int k0 = kKSplit && computes ? 9 * (wave >> 1) : 0;
+  static_assert(32 * (9 + NQ) <= kRow || !kKSplit, "split query registers stay inside the head's row");
+  static_assert(32 * NQ <= kRow, "query registers stay inside the head's row");
   constexpr bool kQueryViaLds = HG <= 2;
   uint8_t* const qlds = FP8 ? smem + kNBuf * kStageBytes : smem + (kNBuf - 1) * kBlockBytes;
   static_assert(HG > 2 || 2 * 16 * kRowBytes <= kBlockBytes, "query staging space");

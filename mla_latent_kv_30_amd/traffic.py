@@ -53,9 +53,12 @@ def code_text(source: str) -> str:
 
 def source_digest(kernel: str = "") -> str:
     """Digest of the code of the sources `kernel` is built from (every kernel
-    source if unknown)."""
+    source if unknown) and of the compiler flags they are built with."""
+    from mla_latent_kv_30_amd import build as _build
+
     names = KERNEL_SOURCES.get(kernel)
     h = hashlib.sha256()
+    h.update(" ".join(f for f in _build.CFLAGS if not os.path.isabs(f)).encode())
     for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
         base = os.path.basename(path)
         if path.endswith((".hip", ".h")) and (names is None or base in names):

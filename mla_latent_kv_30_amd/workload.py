@@ -257,3 +257,46 @@ def hidden_states(wl: Workload, b: int, d: int = D_MODEL, rows: Optional[int] = 
 def new_token_hidden(wl: Workload, d: int = D_MODEL) -> np.ndarray:
     """h [B, d] ~ N(0, 1) bf16: the hidden state of each sequence's new token."""
     return round_bf16(_normal(stream(wl.seed, wl.name, "h_new", d), (wl.B, d)))
+
+
+def fp8_edge_rows(seed: int = 0) -> np.ndarray:
+    """Latent rows [8, 512] (bf16 values, as fp32) that reach every branch of
+    an E4M3 tile quantiser: all-zero tiles (with negative zeros mixed in),
+    a single non-zero element, tiles whose amax is 448 (scale exactly 1) with
+    values on the rounding ties of the subnormal grid (odd multiples of
+    2^-10), of the normal grid and near the top of the range, tiny and huge
+    amax, and magnitudes spread log-uniformly from amax down to 2^-24 amax
+    (normal codes, subnormal codes and values that round to zero)."""
+    g = stream(seed, "fp8_edges", "rows")
+    r = np.zeros((8, D_C), dtype=np.float32)
+    # row 0: four all-zero tiles; tiles 1 and 3 mix negative zeros in
+    r[0, 128:256:2] = -0.0
+    r[0, 384:512:3] = -0.0
+    # row 1: tile 0 zero; tile 1 one non-zero element; tile 2 negative amax;
+    # tile 3 log-uniform magnitudes below amax = 1
+    r[1, 128 + 37] = -3.5
+    r[1, 256:384] = g.standard_normal(128) * 0.25
+    r[1, 256 + 5] = -7.0
+    r[1, 384] = 1.0
+    r[1, 385:512] = g.choice([-1.0, 1.0], 127) * np.exp2(g.uniform(-24.0, 0.0, 127))
+    # row 2: amax 448 (scale 1): subnormal ties (2m+1) 2^-10, normal ties,
+    # values near 448, signed zeros
+    t = np.zeros(128, dtype=np.float32)
+    t[0] = 448.0
+    t[1:17] = np.concatenate([(2 * np.arange(8) + 1) * 2.0 ** -10, -(2 * np.arange(8) + 1) * 2.0 ** -10])
+    t[17:25] = [1.0625, 1.1875, -1.3125, 2.125, 0.02734375, 0.0146484375, 30.0, -31.0]
+    t[25:33] = [440.0, 432.0, -424.0, 400.0, 416.0, 447.0, 3.0 * 2.0 ** -10, 2.0 ** -10]
+    t[33] = -0.0
+    t[34:128] = g.standard_normal(94)
+    r[2, :128] = t
+    r[2, 128:256] = -t
+    r[2, 256:384] = t * 2.0 ** -60     # tiny amax (scale 2^-60)
+    r[2, 384:512] = t * 2.0 ** 100     # huge amax (scale 2^100)
+    # rows 3..7: log-uniform magnitudes over 2^-24 .. 1 of a random amax
+    for i in range(3, 8):
+        amax = np.exp2(g.uniform(-20.0, 20.0, 4))
+        mag = np.exp2(g.uniform(-24.0, 0.0, (4, 128)))
+        mag[:, 0] = 1.0
+        sgn = g.choice([-1.0, 1.0], (4, 128))
+        r[i] = (sgn * mag * amax[:, None]).reshape(D_C)
+    return round_bf16(r)

@@ -208,3 +208,40 @@ def test_projections_reject_misaligned_pointers():
     assert L.mla_linear(P, P, 64, NULL, 0, odd, NULL, 8, 128, _lib.MLA_F32, NULL, 0, NULL) == bad
     assert L.mla_output_proj(P, odd, P, 8, 2048, 256, _lib.MLA_F32, P, 1 << 30, NULL) == bad
     assert L.mla_q_project(P, P, P, P, P, P, 4, 256, 1536, 16, _lib.MLA_BF16, odd, 1 << 30, NULL) == bad
+
+
+def test_attention_entry_points_reject_misaligned_pointers():
+    """Every kernel on the attention path moves 16-byte vectors, so each entry
+    point rejects a tensor pointer that is not 16-byte aligned on the host."""
+    bad = _lib.MLA_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    c = _cache()
+    cref = ctypes.byref(c)
+    # absorb: q_c, q_r, w_uk, q_abs
+    for i in (0, 1, 3, 4):
+        a = [P, P, P, P, P]
+        a[i] = odd
+        assert L.mla_absorb_q(*a, 1, 16, 1, 10000.0, NULL) == bad, i
+    # cache write: c_kv, k_r; and a cache whose rows are misaligned
+    assert L.mla_cache_write(odd, P, P, P, 5, 1, cref, 10000.0, NULL) == bad
+    assert L.mla_cache_write(P, odd, P, P, 5, 1, cref, 10000.0, NULL) == bad
+    c_odd = _cache(rows=odd)
+    assert L.mla_cache_write(P, P, P, P, 5, 1, ctypes.byref(c_odd), 10000.0, NULL) == bad
+    # decode: q_abs, z, workspace
+    big = 1 << 30
+    assert L.mla_decode(odd, cref, P, P, 2, 16, 4, 0.07, 0, P, big, P, NULL, NULL) == bad
+    assert L.mla_decode(P, cref, P, P, 2, 16, 4, 0.07, 0, P, big, odd, NULL, NULL) == bad
+    assert L.mla_decode(P, cref, P, P, 2, 16, 4, 0.07, 0, odd, big, P, NULL, NULL) == bad
+    # merge + up-projection (the fused path for B <= 32): z, w_uv, o, workspace
+    for i in range(4):
+        zp, wuv, o, ws = [odd if j == i else P for j in range(4)]
+        assert L.mla_decode_merge_upproj(P, 2, 16, 0, ws, big, zp, NULL, wuv, _lib.MLA_BF16, o, _lib.MLA_F32,
+                                         NULL) == bad, i
+    # up-projection alone: z, w_uv, o
+    for i in range(3):
+        zp, wuv, o = [odd if j == i else P for j in range(3)]
+        assert L.mla_upproj_v(zp, wuv, o, 2, 16, _lib.MLA_BF16, _lib.MLA_F32, NULL) == bad, i
+    # prefill: q_abs, c_kv, k_r, z
+    for i in range(4):
+        q, ckv, kr, zp = [odd if j == i else P for j in range(4)]
+        assert L.mla_prefill_causal(q, ckv, kr, 0, cref, P, 8, 16, 0.07, 10000.0, zp, NULL, NULL) == bad, i

@@ -127,6 +127,26 @@ def test_yarn_frequencies_regions():
     np.testing.assert_allclose(orc.rope(x, 4000, theta=y)[46:], orc.rope(x, 100)[46:], rtol=1e-9, atol=1e-12)
 
 
+def test_yarn_frequencies_ramp_interior_worked_values():
+    """Inside the ramp (§YaRN 扩展 blend, the pages' s = 40, alpha = 1,
+    beta = 32 and a 4K original context), worked by hand for three groups:
+
+      j = 11: theta = 10^(-11/8) = 0.0421696503; r = 4096 theta / 2pi
+              = 27.490338 turns; gamma = (r - 1) / 31 = 0.8545270;
+              theta'/theta = gamma + (1 - gamma)/40 = 0.85816386.
+      j = 16: theta = 0.01; r = 6.5189865; gamma = 0.1780318;
+              theta'/theta = 0.19858103.
+      j = 22: theta = 10^(-22/8) = 0.0017782794; r = 1.1592579;
+              gamma = 0.0051374; theta'/theta = 0.030008919.
+
+    A ramp with another denominator ((r - alpha)/beta gives 0.82782 at
+    j = 11), a ramp in theta instead of turns, or swapped ends fails."""
+    y = orc.yarn_frequencies()
+    worked = {11: (0.0421696503, 0.85816386), 16: (0.01, 0.19858103), 22: (0.0017782794, 0.030008919)}
+    for j, (theta_j, ratio) in worked.items():
+        assert math.isclose(y[j], theta_j * ratio, rel_tol=1e-7), (j, y[j], theta_j * ratio)
+
+
 def test_yarn_attention_factor():
     assert orc.yarn_attention_factor(1.0) == 1.0
     assert math.isclose(orc.yarn_attention_factor(40.0), 1.0 + 0.1 * math.log(40.0), rel_tol=1e-15)
@@ -321,6 +341,32 @@ def test_quantiser_matches_torch_cast_bit_exact():
     # each tile's largest magnitude maps to +-448
     big = np.abs(orc.e4m3_decode(codes)).reshape(300, 4, 128).max(axis=2)
     assert (big[amax.numpy() > 0] == 448.0).all()
+
+
+def test_quantiser_edge_rows_match_torch_cast_bit_exact():
+    """The edge-case rows (all-zero tiles with signed zeros, one non-zero
+    element, amax 448 with values on the rounding ties of the subnormal and
+    normal grids, tiny and huge amax, magnitudes down to 2^-24 amax) against
+    torch's float8_e4m3fn cast after the fp32 scale and clamp."""
+    from mla_latent_kv_30_amd import workload as W
+
+    c = W.fp8_edge_rows()
+    codes, scales = orc.quantize_latent_e4m3(c)
+    t = torch.from_numpy(c).view(-1, 4, 128)
+    amax = t.abs().amax(dim=2)
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    assert torch.equal(sc, torch.from_numpy(scales))
+    x = (t / sc[:, :, None]).clamp(-448.0, 448.0)
+    ref = x.to(torch.float8_e4m3fn).view(torch.uint8).view(-1, 512).numpy()
+    np.testing.assert_array_equal(codes, ref)
+    # what the rows are for: signed zeros, every subnormal code, ties
+    assert (codes[0, 128:256:2] == 0x80).all() and (codes[0, 129:256:2] == 0x00).all()
+    assert (scales[0] == 1.0).all()
+    sub = codes[(codes & 0x78) == 0] & 0x07
+    assert set(sub.tolist()) == set(range(8))
+    # (2m+1) 2^-10 ties to even on the 2^-9 grid: 1,3,5,7,9,11,13,15 -> codes 0,2,2,4,4,6,6,8
+    np.testing.assert_array_equal(codes[2, 1:9], [0, 2, 2, 4, 4, 6, 6, 8])
+    np.testing.assert_array_equal(codes[2, 9:17], [0x80, 0x82, 0x82, 0x84, 0x84, 0x86, 0x86, 0x88])
 
 
 def test_quantiser_error_bound():
