@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
 SOURCES = ["api.hip", "absorb.hip", "cache_write.hip", "decode.hip", "merge.hip", "linear.hip", "upproj.hip",
-           "ceilings.hip"]
+           "ceilings.hip", "decode_wide.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 add/mul/fma.
@@ -27,6 +27,12 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+
+
+# Extra flags per source.  The wide decode kernel keeps its latent
+# accumulators in the accumulation registers itself (one-instruction
+# products) and wants every compiler-built matrix product in ordinary VGPRs.
+FILE_FLAGS = {"decode_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -38,7 +44,7 @@ def hipcc() -> str:
 
 def _compile(src: str, save_temps: bool) -> str:
     obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if save_temps:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -8,7 +8,7 @@
 #include <initializer_list>
 #include <mutex>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "kernels.h"
 
 namespace {

@@ -6,7 +6,7 @@
 // and folds what it read into one value per workgroup so that no load or
 // product can be removed.  The caller times the launch; the work per launch
 // is returned by the entry point (mla_ceilings.h).
-#include "../../include/mla_ceilings.h"
+#include "mla_ceilings.h"
 #include "common.h"
 
 namespace mla {
@@ -37,8 +37,13 @@ __global__ void __launch_bounds__(kHbmThreads) hbm_read_kernel(const int4v* __re
 
 // Dense matrix-core issue: every wave runs `iters` rounds of NCHAIN
 // independent accumulation chains (so no product waits for the one before).
+// Two waves per SIMD, as in the attention kernels; under that register
+// budget the products accumulate in ordinary VGPRs in place (with the
+// accumulation registers free, 16x16 accumulators were copied between them
+// every round).
 template <int SHAPE>
-__global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float* __restrict__ sink) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mfma_loop_kernel(int iters, float* __restrict__ sink) {
   const int tid = threadIdx.x;
   bf16x8 a, b;
 #pragma unroll

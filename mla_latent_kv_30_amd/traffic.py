@@ -36,6 +36,7 @@ COPY_KERNEL = "copyBuffer"    # the runtime's device-to-device copy kernel
 # it includes); other kernels are digested over every source.
 KERNEL_SOURCES = {
     "decode_mfma_kernel": ("decode.hip", "decode_common.h", "common.h", "kernels.h"),
+    "decode_wide_kernel": ("decode_wide.hip", "decode_common.h", "common.h", "kernels.h"),
     "decode_f32_kernel": ("decode.hip", "decode_common.h", "common.h", "kernels.h"),
     "linear_kernel": ("linear.hip", "common.h", "kernels.h"),
 }
@@ -59,6 +60,8 @@ def source_digest(kernel: str = "") -> str:
     names = KERNEL_SOURCES.get(kernel)
     h = hashlib.sha256()
     h.update(" ".join(f for f in _build.CFLAGS if not os.path.isabs(f)).encode())
+    for src in sorted(names or _build.FILE_FLAGS):
+        h.update(" ".join(_build.FILE_FLAGS.get(src, [])).encode())
     for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
         base = os.path.basename(path)
         if path.endswith((".hip", ".h")) and (names is None or base in names):

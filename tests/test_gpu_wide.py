@@ -1,0 +1,155 @@
+"""GPU parity of the decode paths for 65..128 heads over a bf16 cache (four
+waves of 32 heads) against the fp64 oracle, on the cases that path treats
+specially:
+
+  * running maxima that jump by far more than 2^8 inside one piece (the
+    accumulated sums are re-based through the piece's output rows);
+  * many short sequences in the balanced split (a unit switches pieces and
+    reloads its queries often);
+  * head counts that leave a wave partly or wholly empty (65, 97);
+  * multi-token decode with q_len * H in that range.
+
+Tolerance: bf16, max |gpu - oracle| / max |oracle| <= 2e-2 over the tensor
+(lse: absolute 2e-2), as in the other decode tests.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_30_amd as mla
+from mla_latent_kv_30_amd import device_inputs as DI
+from mla_latent_kv_30_amd import workload as W
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _rel(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(gpu).all(), "non-finite GPU output"
+    return float(np.abs(gpu - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def _oracle(dd, c_all, k_all):
+    h = dd.host
+    off = dd.layout.offsets
+    out = {"o": [], "z": [], "lse": []}
+    for b in range(dd.wl.B):
+        r = orc.decode_sequence(h["q_c"][b], h["q_r"][b], c_all[off[b]:off[b + 1]], k_all[off[b]:off[b + 1]],
+                                h["w_uk"], h["w_uv"])
+        for k in out:
+            out[k].append(r[k])
+    return {k: np.stack(v) for k, v in out.items()}
+
+
+def _check(dd, ref, splits=(0, 1, 3)):
+    for S in splits:
+        q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+        z, lse = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=S)
+        o = mla.upproj_v(z, dd.w_uv)
+        torch.cuda.synchronize()
+        assert _rel(o.cpu().numpy(), ref["o"]) <= 2e-2, ("o", S)
+        assert _rel(z.cpu().numpy(), ref["z"]) <= 2e-2, ("z", S)
+        assert np.abs(lse.cpu().numpy() - ref["lse"]).max() <= 2e-2, ("lse", S)
+
+
+@pytest.mark.parametrize("H,lens,ramps", [
+    # token ranges whose rows are scaled up: each step lifts the running
+    # maximum by many times 2^8 within one piece
+    (128, [1000, 300], [(200, 4.0), (400, 12.0)]),
+    (96, [700], [(33, 3.0), (64, 6.0), (500, 20.0)]),
+])
+def test_running_max_jumps(H, lens, ramps):
+    wl = W.make_workload("decode_h16", B=len(lens), H=H, lens=lens)
+    _note(f"case wide decode, running-max jumps H={H} lens={lens}")
+    c_all, k_all = W.all_latents(wl)
+    lay = W.paged_layout(wl, spare_pages=2)
+    scale = np.ones(c_all.shape[0], dtype=np.float32)
+    for b in range(wl.B):
+        j = np.arange(lens[b])
+        for start, f in ramps:
+            scale[lay.offsets[b] + j[j >= start]] = f
+    c_all = W.round_bf16(c_all * scale[:, None])
+    k_all = W.round_bf16(k_all * scale[:, None])
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2, latents=(c_all, k_all))
+    # Queries whose absorbed form is exact in bf16: q_C = 16 e_k (a different
+    # k per head), so q~ = 16 W^UK[k] is a row of the bf16 weights times a
+    # power of two, and q_R = 0.  With scores this large, the bf16 rounding of
+    # a general q~ would move them by tenths (far beyond the tolerance) in
+    # the kernel's input alone; here only the kernel's own arithmetic differs
+    # from the oracle's.
+    q_c = np.zeros((wl.B, H, 128), dtype=np.float32)
+    for b in range(wl.B):
+        q_c[b, np.arange(H), (np.arange(H) * 7 + 3 * b) % 128] = 16.0
+    q_r = np.zeros((wl.B, H, 64), dtype=np.float32)
+    dd.host["q_c"], dd.host["q_r"] = q_c, q_r
+    dd.q_c.copy_(torch.from_numpy(q_c))
+    dd.q_r.copy_(torch.from_numpy(q_r))
+    ref = _oracle(dd, c_all, k_all)
+    # the jumps are real: the last range's scores reach far past the first's
+    assert ref["lse"].max() - np.log(max(lens)) > 20.0
+    _check(dd, ref)
+
+
+def test_many_short_sequences():
+    lens = [int(x) for x in np.random.default_rng(7).integers(1, 300, 70)]
+    wl = W.make_workload("decode_h16", B=len(lens), H=128, lens=lens)
+    _note(f"case wide decode, {len(lens)} short sequences")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    c_all, k_all = dd.host["c_kv"], dd.host["k_r"]
+    _check(dd, _oracle(dd, c_all, k_all))
+
+
+@pytest.mark.parametrize("H,lens", [(65, [129, 64, 1]), (97, [2000, 31])])
+def test_partial_head_groups(H, lens):
+    wl = W.make_workload("decode_h16", B=len(lens), H=H, lens=lens)
+    _note(f"case wide decode H={H} lens={lens}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    _check(dd, _oracle(dd, dd.host["c_kv"], dd.host["k_r"]))
+
+
+def test_repeated_calls_are_bit_identical():
+    lens = [3000, 1, 700, 65]
+    wl = W.make_workload("decode_h16", B=len(lens), H=128, lens=lens)
+    _note("case wide decode determinism")
+    dd = DI.decode_inputs(wl, DEV, spare_pages=2)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    z1, l1 = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=0)
+    z2, l2 = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(z1, z2) and torch.equal(l1, l2)
+
+
+def test_units_spanning_sequences():
+    """Lengths long enough that the balanced split gives each unit about 2.6
+    blocks: units end one sequence's piece mid-stream and go on with the next
+    sequence's, whose partial is then merged (the accumulators are reset
+    between the two pieces).  Sampled heads of every wave, against the
+    oracle's absorbed form."""
+    lens = [5000, 6000, 7000, 3000]
+    wl = W.make_workload("decode_h16", B=len(lens), H=128, lens=lens)
+    _note(f"case wide decode, units spanning sequences lens={lens}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    z, lse = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=0)
+    torch.cuda.synchronize()
+    z, lse = z.cpu().numpy(), lse.cpu().numpy()
+    h = dd.host
+    off = dd.layout.offsets
+    heads = [0, 31, 32, 63, 64, 95, 96, 127]
+    for b in range(wl.B):
+        r = orc.decode_sequence_absorbed(h["q_c"][b][heads], h["q_r"][b][heads], h["c_kv"][off[b]:off[b + 1]],
+                                         h["k_r"][off[b]:off[b + 1]], h["w_uk"][heads], h["w_uv"][heads])
+        assert _rel(z[b][heads], r["z"]) <= 2e-2, ("z", b)
+        assert np.abs(lse[b][heads] - r["lse"]).max() <= 2e-2, ("lse", b)
