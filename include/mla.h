@@ -254,6 +254,33 @@ mla_status mla_decode_partial(const void* q_abs, const mla_cache* cache, const i
 mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits, void* workspace,
                             size_t ws_bytes, float* z, float* lse, void* stream);
 
+/* Bytes of device memory mla_decode_noalloc holds on every device it runs on. */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/*
+ * mla_decode_noalloc — mla_decode for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): it takes no workspace and calls no allocator.  Its
+ * split partials go to a device array of MLA_DECODE_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per device, held from the first use of the
+ * library's code on that device until the process ends.  Arguments, outputs
+ * and results are those of mla_decode (same kernels, same launch shapes,
+ * bit-identical z and lse); the caller still provides q_abs, the cache, the
+ * block table, the lengths, z and lse.  The debug mode's host-side checks
+ * are not run.
+ * Every call on one device shares that device's array and leaves its
+ * contents behind (no call needs them cleared): calls that overlap in time on
+ * one device race and must be ordered by the caller (one stream, or events).
+ * Errors: as mla_decode; MLA_ERR_WORKSPACE when the call needs more than
+ * MLA_DECODE_NOALLOC_SCRATCH_BYTES (mla_decode_workspace_size(B, H,
+ * num_splits) bytes: with the automatic split, (CUs + B) * H * 2 KiB plus a
+ * little, so B = 64, H = 128 fits); MLA_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+mla_status mla_decode_noalloc(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages,
+                              float softmax_scale, int32_t num_splits, float* z, float* lse, void* stream);
+
 /*
  * mla_decode_multi — q_len new tokens per sequence attend at once (the
  * multi-token decode of speculative verification, "DeepSeek-V3" notes

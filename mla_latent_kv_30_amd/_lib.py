@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_multi.restype = _i32
     L.mla_decode_multi.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                    ctypes.c_size_t, _vp, _vp, _vp]
+    L.mla_decode_noalloc.restype = _i32
+    L.mla_decode_noalloc.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp,
+                                     _vp]
     L.mla_validate_decode_inputs.restype = _i32
     L.mla_validate_decode_inputs.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32]
     L.mla_set_debug.restype = None
@@ -350,6 +353,30 @@ def decode_merge(seq_lens: torch.Tensor, H: int, workspace: Optional[torch.Tenso
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_merge(_ptr(seq_lens), B, int(H), int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
                                   _ptr(lse), _stream(z.device)), "mla_decode_merge")
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20  # MLA_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                   z: torch.Tensor, lse: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
+                   num_splits: int = 0) -> None:
+    """mla_decode_noalloc: decode() into caller-provided z (and lse) with the split partials in the
+    library's own device array; nothing is allocated on either side of the call."""
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    _need(q_abs, "q_abs", cache.input_dtype, (B, H, ROW))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(z, "z", torch.float32, (B, H, D_C))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H))
+    scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
+    desc = cache.descriptor()
+    _check(lib().mla_decode_noalloc(_ptr(q_abs), ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), B, H,
+                                    block_table.shape[1], scale, int(num_splits), _ptr(z), _ptr(lse),
+                                    _stream(q_abs.device)), "mla_decode_noalloc")
 
 
 def decode_multi(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,

@@ -386,6 +386,56 @@ mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* 
   return launched(launch_merge(a, s));
 }
 
+}  // extern "C"
+
+// Device memory of mla_decode_noalloc: the split partials and the piece
+// records go to this file-scope array instead of a caller's workspace.  Every
+// device the library runs on holds its own copy, from the first use of the
+// library's code there until the process ends.  On the host the name is a
+// stand-in for the symbol, not a device address: host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MLA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current); NULL if the lookup failed.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_noalloc(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
+                              int32_t num_splits, float* z, float* lse, void* stream) {
+  void* ws = scratch_address();
+  if (ws == nullptr) return MLA_ERR_HIP;
+  DecodeArgs a;
+  int kind;
+  Plan p;
+  // a call whose partials exceed the array fails here with MLA_ERR_WORKSPACE
+  mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
+                                 ws, MLA_DECODE_NOALLOC_SCRATCH_BYTES, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  st = launched(launch_decode(a, kind, s));
+  if (st != MLA_OK || p.slots == 0) return st;
+  return launched(launch_merge(a, s));
+}
+
 mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
                             const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t H, int32_t max_pages,
                             float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes, float* z,

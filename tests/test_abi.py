@@ -245,3 +245,14 @@ def test_attention_entry_points_reject_misaligned_pointers():
     for i in range(4):
         q, ckv, kr, zp = [odd if j == i else P for j in range(4)]
         assert L.mla_prefill_causal(q, ckv, kr, 0, cref, P, 8, 16, 0.07, 10000.0, zp, NULL, NULL) == bad, i
+
+
+def test_noalloc_scratch_size_matches_header():
+    import os
+    import re
+    text = open(os.path.join(_lib.INCLUDE, "mla.h")).read()
+    m = re.search(r"#define MLA_DECODE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m is not None
+    assert _lib.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    # the 128-head decode of 64 sequences with the automatic split fits
+    assert 0 < _lib.decode_workspace_size(64, 128, 0) <= _lib.NOALLOC_SCRATCH_BYTES
