@@ -20,12 +20,17 @@
 //     row reads for the scores and 131 KB of transposing reads for the value
 //     product, 278 KB per block;
 //   * the products are bf16 32x32x16 matrix-core operations (32 tokens x 32
-//     heads of scores in two chains; 32 channels x 32 heads per value tile);
+//     heads of scores in one accumulation chain; 32 channels x 32 heads per
+//     value tile);
 //   * the value product of block i-1 runs after the scores of block i, so
 //     the softmax of block i can issue while the matrix cores work through
 //     the value products; that keeps block i-1 readable for one more step,
 //     so two blocks (not three) are in flight while one is scored and one is
-//     accumulated (four 36 KB buffers).
+//     accumulated (four 36 KB buffers);
+//   * with one wave per SIMD nothing hides a stall, so a step is one fixed
+//     sequence of products with their operand reads issued a few products
+//     ahead and the softmax and copy instructions placed between them
+//     (wide_step).
 // The work schedule, the paged copies (LDS-DMA), the row layout in LDS and
 // the split-KV partials are those of decode.hip (decode_common.h).
 #include "decode_common.h"
@@ -39,8 +44,7 @@ constexpr int kWNBuf = 4;                   // value(i-1), scores(i), blocks i+1
 constexpr int kWAhead = 2;                  // blocks copied ahead of the one being scored
 constexpr int kWCopies = kCopiesPerGroup;   // 9 copies per wave and block: wave w moves 8-row group w
 constexpr int kWBt = 4 * kWThreads;         // block-table entries block_prefix can copy with 256 threads
-constexpr int kWScoreDepth = 6;             // score operand reads in flight
-constexpr int kWValueDepth = 3;             // value operand tiles (two transposing reads each) in flight
+constexpr int kWDepth = 4;                  // operand reads in flight, in products
 
 static_assert(kWWaves * kGroupRows == kBlockRows, "four waves move the four 8-row groups of a block");
 
@@ -118,52 +122,10 @@ __device__ __forceinline__ WideCopies plan_block_wide(const uint8_t* page, int h
   return c;
 }
 
-// Copy j of this wave: lane i fills LDS chunk 64j + i of the 8-row group,
-// i.e. chunk cc of row r = (64j + i) / 72, which holds source chunk
-// cc ^ swzw(8g + r).
-__device__ __forceinline__ void issue_copy_wide(const WideCopies& c, int j) {
-  const int lane = lane_id_fresh();
-  const int q = 64 * j + lane;
-  const int r = q / 72, cc = q - 72 * r;
-  const uint32_t vo = (uint32_t)(r * kRowBytes + 16 * (cc ^ swzw(kGroupRows * c.g + r)));
-  lds_dma16(c.rs, c.lb + kCopyBytes * j, vo, c.g * kGroupBytes);
-}
-
 // Wait until at most the copies of this wave's n (0 or 1) most recently
 // issued blocks are in flight.
 __device__ __forceinline__ void wait_blocks_wide(int n) {
   if (n >= 1) wait_vmcnt<kWCopies>(); else wait_vmcnt<0>();
-}
-
-// Scores of the 32 rows of a block buffer: S^T = R Q^T (32 tokens x 32
-// heads), K = 576 in 36 steps of 16, accumulated in two chains (even and odd
-// steps) so that consecutive products do not wait on each other.  Lane l of
-// the result holds head h0 + l % 32 and tokens 8(r / 4) + 4h + r % 4.
-// dma(t) (t = 0..8) is called after every fourth K-step.
-template <class Dma>
-__device__ __forceinline__ floatx16 scores_wide(const WideQuery& Q, uint32_t buf, Dma&& dma) {
-  const int lane = lane_id_fresh();
-  const int row = lane & 31, h = lane >> 5;
-  // A operand at K-step kk: row `row`, bytes 32kk + 16h; the permutation
-  // touches bits 4..6, so kk % 4 picks one of four bases and kk / 4 adds 128
-  uint32_t ap[4];
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) ap[k4] = buf + lds_off_w(row, 32 * k4 + 16 * h);
-  asm volatile("" : "+v"(ap[0]), "+v"(ap[1]), "+v"(ap[2]), "+v"(ap[3]));
-  auto rd = [&](int kk) { return lds_read_b128_at(ap[kk & 3] + 128 * (kk >> 2)); };
-  floatx16 S0 = floatx16{}, S1 = floatx16{};
-  constexpr int D = kWScoreDepth;
-  int4v a[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) a[i] = rd(i);
-#pragma unroll
-  for (int kk = 0; kk < 36; ++kk) {
-    const bf16x8 c = __builtin_bit_cast(bf16x8, a[kk % D]);
-    if (kk + D < 36) a[kk % D] = rd(kk + D);
-    if (kk & 1) S1 = mfma32(c, Q.q[kk], S1); else S0 = mfma32(c, Q.q[kk], S0);
-    if ((kk & 3) == 3) dma(kk >> 2);
-  }
-  return S0 + S1;
 }
 
 // Z^T tile += A B on the matrix cores with the accumulator in the
@@ -180,87 +142,6 @@ __device__ __forceinline__ void mfma32_acc(floatx16& acc, const bf16x8& a, const
 // reads or writes an accumulator tile (more than the 18 a 16-pass product
 // needs), and between such a write and the next accumulation.
 __device__ __forceinline__ void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
-// Value product of one block buffer: Z^T_ct += C^T_ct P^T over the two
-// K-steps t of 16 tokens.  Slot 8h + j of step t is token 16t + 4h + j
-// (j < 4) or 16t + 8 + 4h + (j - 4): P[t] is then score registers 8t .. 8t+7
-// of the lane as they are, and the A operand (32 channels x 16 tokens) comes
-// from two transposing reads: in 16-lane group G (h = G / 2, hf = G % 2)
-// lane s points at row 16t + 4h + s / 4 (resp. + 8), bytes
-// 64ct + 32hf + 8(s % 4) .. +7, and receives channel 32ct + 16hf + s.
-__device__ __forceinline__ void value_wide(WideAcc& Z, const bf16x8 (&P)[2], uint32_t buf) {
-  const int lane = lane_id_fresh();
-  const int G = lane >> 4, s = lane & 15;
-  const int h = G >> 1, hf = G & 1;
-  const int x = 32 * hf + 8 * (s & 3);
-  uint32_t vb[2][2][2];  // [t][lo / hi rows][ct % 2]; ct / 2 adds 128 bytes
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) vb[t][hh][c2] = buf + lds_off_w(16 * t + 8 * hh + 4 * h + (s >> 2), 64 * c2 + x);
-  asm volatile("" : "+v"(vb[0][0][0]), "+v"(vb[0][0][1]), "+v"(vb[0][1][0]), "+v"(vb[0][1][1]));
-  asm volatile("" : "+v"(vb[1][0][0]), "+v"(vb[1][0][1]), "+v"(vb[1][1][0]), "+v"(vb[1][1][1]));
-  // operand n: K-step n / 16, channel tile n % 16 (a tile's two products
-  // are 16 products apart, so none waits for the one before)
-  auto vread = [&](int n) {
-    const int ct = n & 15, t = n >> 4;
-    const bf16x4 lo = lds_read_tr16_at(vb[t][0][ct & 1] + 128 * (ct >> 1));
-    const bf16x4 hi = lds_read_tr16_at(vb[t][1][ct & 1] + 128 * (ct >> 1));
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-  constexpr int D = 2 * kWValueDepth;
-  bf16x8 va[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) va[i] = vread(i);
-#pragma unroll
-  for (int n = 0; n < 32; ++n) {
-    const bf16x8 cur = va[n % D];
-    if (n + D < 32) va[n % D] = vread(n + D);
-    mfma32_acc(Z.z[n & 15], cur, P[n >> 4]);
-  }
-}
-
-// Online softmax of a block's scores for the lane's head.  Tokens at or past
-// hi are masked (it may differ per head in multi-token decode).  Returns the
-// block's probabilities as the value product's B operands and, when the
-// running maximum moved, the factor the accumulators must be scaled by
-// before this block's value product (rescale set, alpha).
-__device__ __forceinline__ void softmax_wide(WideSoftmax& st, const floatx16& S, int hi, float scale_log2,
-                                             bf16x8 (&P)[2], bool& rescale, float& alpha) {
-  const int h = lane_id_fresh() >> 5;
-  float x[16];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float y = 8 * (r >> 2) + 4 * h + (r & 3) < hi ? S[r] * scale_log2 : -INFINITY;
-    x[r] = y;
-    mx = fmaxf(mx, y);
-  }
-  mx = pair32_max(mx);
-  const float mnew = fmaxf(st.m, mx);
-  // the first scores of a piece set the maximum (the accumulators are
-  // zero); later ones move it only when it grows by more than 2^8
-  const bool need = st.m != -INFINITY && mnew > st.m + kLazyRescale;
-  if (st.m == -INFINITY) st.m = mnew;
-  rescale = __builtin_amdgcn_ballot_w64(need) != 0;
-  if (__builtin_expect(rescale, 0)) {
-    alpha = need ? fast_exp2(st.m - mnew) : 1.0f;
-    if (need) st.m = mnew;
-    st.l *= alpha;
-  }
-  // a head that has seen only masked scores keeps m = -inf: probabilities 0
-  const float mref = st.m == -INFINITY ? 0.f : st.m;
-  float sum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = fast_exp2(x[r] - mref);
-    sum += p;
-    P[r >> 3][r & 7] = f2bf(p);
-  }
-  st.l += sum;
-}
 
 // Outside the matrix cores the accumulators are only read, one register at
 // a time through explicit accumulation-register reads: arithmetic written on
@@ -370,6 +251,186 @@ __device__ __forceinline__ void store_wide(const WideAcc& Z, float l_tot, float 
   if (ldst != nullptr && h == 0) ldst[head] = (m + __log2f(l_tot)) * kLn2;
 }
 
+// Per-lane LDS offsets of the operand reads within a block buffer, advanced
+// by one buffer per step (all reads then take immediate offsets on top).
+//   sa[k4]          score operand of K-step kk (kk % 4 == k4): row lane % 32,
+//                   bytes 32 kk + 16 (lane / 32); kk / 4 adds 128 bytes;
+//   va[t][hh][c2]   value operand of K-step t, tile ct (ct % 2 == c2): the
+//                   rows 16 t + 8 hh + 4 h + s / 4 of value_wide's pattern;
+//                   ct / 2 adds 128 bytes.
+struct WideAddr {
+  uint32_t sa[4];
+  uint32_t va[2][2][2];
+};
+
+__device__ __forceinline__ WideAddr wide_addr(uint32_t score_buf, uint32_t value_buf) {
+  const int lane = lane_id_fresh();
+  WideAddr A;
+  const int row = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) A.sa[k4] = score_buf + lds_off_w(row, 32 * k4 + 16 * h);
+  const int G = lane >> 4, s = lane & 15;
+  const int hv = G >> 1, hf = G & 1;
+  const int x = 32 * hf + 8 * (s & 3);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+        A.va[t][hh][c2] = value_buf + lds_off_w(16 * t + 8 * hh + 4 * hv + (s >> 2), 64 * c2 + x);
+  return A;
+}
+
+// From step i to step i+1: the score reads move from buffer i % 4 to the
+// next one, the value reads from buffer (i - 1) % 4 to the next one.
+__device__ __forceinline__ void advance_addr(WideAddr& A, int i) {
+  constexpr uint32_t kNext = kBlockBytes, kWrap = (uint32_t)(-(kWNBuf - 1) * kBlockBytes);
+  const uint32_t ds = i % kWNBuf == kWNBuf - 1 ? kWrap : kNext;
+  const uint32_t dv = i % kWNBuf == 0 ? kWrap : kNext;
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) A.sa[k4] += ds;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) A.va[t][hh][c2] += dv;
+}
+
+__device__ __forceinline__ bf16x8 score_operand(const WideAddr& A, int kk) {
+  return __builtin_bit_cast(bf16x8, lds_read_b128_at(A.sa[kk & 3] + 128 * (kk >> 2)));
+}
+
+// Value operand n: K-step n / 16, channel tile n % 16 (a tile's two
+// products are 16 products apart).
+__device__ __forceinline__ bf16x8 value_operand(const WideAddr& A, int n) {
+  const int ct = n & 15, t = n >> 4;
+  const bf16x4 lo = lds_read_tr16_at(A.va[t][0][ct & 1] + 128 * (ct >> 1));
+  const bf16x4 hi = lds_read_tr16_at(A.va[t][1][ct & 1] + 128 * (ct >> 1));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Per-lane source offsets of this wave's nine copies of an 8-row group (they
+// depend only on the lane and the group): copy j, lane i fills LDS chunk
+// 64 j + i of the group, i.e. chunk cc of row r = (64 j + i) / 72, which holds
+// source chunk cc ^ swzw(8 g + r).
+struct WideCopyOffsets {
+  uint32_t vo[kWCopies];
+};
+
+__device__ __forceinline__ WideCopyOffsets copy_offsets(int g) {
+  const int lane = lane_id_fresh();
+  WideCopyOffsets o;
+#pragma unroll
+  for (int j = 0; j < kWCopies; ++j) {
+    const int q = 64 * j + lane;
+    const int r = q / 72, cc = q - 72 * r;
+    o.vo[j] = (uint32_t)(r * kRowBytes + 16 * (cc ^ swzw(kGroupRows * g + r)));
+  }
+#pragma unroll
+  for (int j = 0; j < kWCopies; ++j) asm volatile("" : "+v"(o.vo[j]));
+  return o;
+}
+
+// Keep a value computed at this point of the instruction sequence.
+__device__ __forceinline__ void anchor(float& x) { asm volatile("" : "+v"(x)); }
+
+// Maxima that need no quieting of their inputs (the operands are scores or
+// -inf, never NaN): gfx950's three-input maximum.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ float pair32_maximum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// One step of the unit's block stream: the scores of block i (buffer
+// `A.sa`), the online softmax of block i, and the value product of block
+// i-1 (buffer `A.va`) with its probabilities Pp.  Written as one straight
+// sequence of matrix-core products, each with the operand reads it needs
+// D products ahead, the page copies of block i+2 after every fourth score
+// product and the softmax arithmetic spread over the value products; the
+// scheduling barriers keep that order (left to itself the compiler gathered
+// the reads next to their products and the softmax ahead of them, and the
+// one wave on each SIMD then waited on every LDS round trip).
+// mask (uniform): tokens at or past hi (per lane) are excluded.
+__device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const WideAddr& A, const WideCopies& nb,
+                                          const WideCopyOffsets& co, const bf16x8 (&Pp)[2], bf16x8 (&Pc)[2],
+                                          WideSoftmax& st, float scale_log2, bool mask, int hi, bool& rescale,
+                                          float& alpha) {
+  constexpr int D = kWDepth;
+  bf16x8 rb[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) rb[j] = score_operand(A, j);
+  floatx16 S = floatx16{};
+  // score phase: 36 products; the last D steps read the first value operands
+#pragma unroll
+  for (int kk = 0; kk < 36; ++kk) {
+    const bf16x8 a = rb[kk % D];
+    rb[kk % D] = kk + D < 36 ? score_operand(A, kk + D) : value_operand(A, kk + D - 36);
+    S = mfma32(a, Q.q[kk], S);
+    if ((kk & 3) == 3) lds_dma16(nb.rs, nb.lb + kCopyBytes * (kk >> 2), co.vo[kk >> 2], nb.g * kGroupBytes);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // value phase: 32 products with the softmax of S woven in
+  const int h = lane_id_fresh() >> 5;
+  float mx = -INFINITY, sum = 0.f, nm = 0.f;
+  bool need = false;
+#pragma unroll
+  for (int n = 0; n < 32; ++n) {
+    const bf16x8 a = rb[n % D];
+    if (n + D < 32) rb[n % D] = value_operand(A, n + D);
+    mfma32_acc(Z.z[n & 15], a, Pp[n >> 4]);
+    // each piece of the softmax is pinned to its step (anchor()): its
+    // results are used only in the next step, and the compiler would
+    // otherwise move the arithmetic out of this sequence
+    if (n == 2) {
+      if (__builtin_expect(mask, 0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * h + (r & 3) >= hi) S[r] = -INFINITY;
+      }
+      mx = max3f(max3f(max3f(S[0], S[1], S[2]), max3f(S[3], S[4], S[5]), max3f(S[6], S[7], S[8])),
+                 max3f(S[9], S[10], S[11]), max3f(max3f(S[12], S[13], S[14]), S[15], -INFINITY));
+      anchor(mx);
+    } else if (n == 3) {
+      mx = pair32_maximum(mx) * scale_log2;  // scale > 0: the maximum commutes with it
+      anchor(mx);
+    } else if (n == 4) {
+      // the first scores of a piece set the maximum (the accumulators are
+      // zero); later ones move it only when it grows by more than 2^8
+      const float mnew = __builtin_elementwise_maximum(st.m, mx);
+      const bool first = st.m == -INFINITY;
+      need = !first && mnew > st.m + kLazyRescale;
+      alpha = need ? fast_exp2(st.m - mnew) : 1.0f;
+      st.l *= alpha;
+      st.m = (need || first) ? mnew : st.m;
+      // a head that has seen only masked scores keeps m = -inf: probabilities 0
+      nm = st.m == -INFINITY ? 0.f : -st.m;
+      anchor(nm);
+      anchor(alpha);
+      anchor(st.l);
+      anchor(st.m);
+    } else if (n == 5) {
+      rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+    } else if (n >= 6 && n < 22) {
+      const int r = n - 6;
+      float p = fast_exp2(fmaf(S[r], scale_log2, nm));
+      anchor(p);
+      sum += p;
+      anchor(sum);
+      Pc[r >> 3][r & 7] = f2bf(p);
+      if (r & 1) asm volatile("" : "+v"(Pc[r >> 3]));
+    } else if (n == 22) {
+      st.l += sum;
+      anchor(st.l);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <bool FP8>
 __global__ void __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
@@ -409,9 +470,15 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     return plan_block_wide(page, c.valid ? c.k & 1 : 0, smem + slot * kBlockBytes, c.valid ? block_hi(c) : 0, wave);
   };
 
+  // The value product of step 0 reads buffer kWNBuf - 1 with zero
+  // probabilities: its rows must be finite, so it starts as zeros.
+  for (int j = tid; j < kBlockBytes / 16; j += kWThreads)
+    *(int4v*)(smem + (kWNBuf - 1) * kBlockBytes + 16 * j) = int4v{0, 0, 0, 0};
+
   WideQuery Q;
   WideAcc Z;
   WideSoftmax st;
+  const WideCopyOffsets co = copy_offsets(wave);
   load_query_wide(Q, qrow(cp.seg), a.H, h0);
   Cursor ld = cp;
 #pragma unroll
@@ -420,19 +487,23 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // rows: it moves nothing and keeps the count of copies per block fixed)
     const WideCopies nb = plan_wide(ld, j);
 #pragma unroll
-    for (int t = 0; t < kWCopies; ++t) issue_copy_wide(nb, t);
+    for (int t = 0; t < kWCopies; ++t) lds_dma16(nb.rs, nb.lb + kCopyBytes * t, co.vo[t], nb.g * kGroupBytes);
     if (ld.valid) cursor_next(a, ld);
   }
+  WideCopies nb = plan_wide(ld, kWAhead);
+  if (ld.valid) cursor_next(a, ld);
   consume_query_wide(Q);
   reset_acc_mfma(Z);
   st.m = -INFINITY;
   st.l = 0.f;
   note_pieces(cp.seg);
+  const uint32_t base = lds_addr(smem);
+  WideAddr A = wide_addr(base, base + (kWNBuf - 1) * kBlockBytes);
 
   // The block scored in the previous step, whose value product is still to
   // be done: its probabilities, where its piece goes and, if it ended the
   // piece, the piece's softmax totals.
-  bf16x8 Pp[2];
+  bf16x8 Pp[2] = {bf16x8{}, bf16x8{}};
   bool prev_last = false;
   float* zdst = nullptr;    // its piece's output rows
   float* ldst = nullptr;
@@ -445,29 +516,24 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // after this one are the last nine issued
     wait_blocks_wide(1);
     __syncthreads();  // block i has landed; every wave is done with step i-1
-    // the copies of block i + 2 go into the buffer of block i - 2
-    const WideCopies nb = plan_wide(ld, (i + kWAhead) % kWNBuf);
-    if (ld.valid) cursor_next(a, ld);
-    // scores of block i (of stale rows when there is no block i: unused)
-    const floatx16 S = scores_wide(Q, lds_addr(smem + (i % kWNBuf) * kBlockBytes),
-                                   [&](int t) { issue_copy_wide(nb, t); });
-    // softmax of block i: its probabilities go to the next step's value
-    // product, after block i-1's (which still needs Pp)
+    // multi-token decode: query token t of the sequence sees keys up to
+    // L - q_len + t, so the last q_len - 1 - t keys are masked for it
+    int hi = cur ? block_hi(cp) : kBlock;
+    const bool mask = hi < kBlock || a.q_len > 1;
+    if (a.q_len > 1 && cur) {
+      const int head = min(h0 + (lane_id_fresh() & 31), a.H - 1);
+      hi = min(hi, cp.seg.L - (a.q_len - 1 - head / a.hs) - kBlock * cp.k);
+    }
     bf16x8 Pc[2];
     bool rescale_c = false;
     float alpha_c = 1.f;
-    if (cur) {
-      // multi-token decode: query token t of the sequence sees keys up to
-      // L - q_len + t, so the last q_len - 1 - t keys are masked for it
-      int hi = block_hi(cp);
-      if (a.q_len > 1) {
-        const int head = min(h0 + (lane_id_fresh() & 31), a.H - 1);
-        hi = min(hi, cp.seg.L - (a.q_len - 1 - head / a.hs) - kBlock * cp.k);
-      }
-      softmax_wide(st, S, hi, a.scale_log2, Pc, rescale_c, alpha_c);
-    }
+    // scores and softmax of block i (of stale rows when there is no block i:
+    // unused), value product of block i-1 (zero probabilities at i = 0), and
+    // the copies of block i+2 into the buffer of block i-2
+    wide_step(Q, Z, A, nb, co, Pp, Pc, st, a.scale_log2, mask, hi, rescale_c, alpha_c);
+    advance_addr(A, i);
+    if (!cur) rescale_c = false;
     if (i > 0) {
-      value_wide(Z, Pp, lds_addr(smem + ((i + kWNBuf - 1) % kWNBuf) * kBlockBytes));
       if (__builtin_expect(rescale_c, 0)) {
         // block i moved a running maximum: the sums up to block i-1 are
         // relative to the old one (block i's value product comes next)
@@ -482,7 +548,13 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         reset_acc_mfma(Z);
       }
     }
-    if (!cur) break;
+    if (!cur) {
+      wait_vmcnt<0>();  // no copy into this workgroup's LDS outlives it
+      break;
+    }
+    // the copies of block i+3, issued in the next step
+    nb = plan_wide(ld, (i + kWAhead + 1) % kWNBuf);
+    if (ld.valid) cursor_next(a, ld);
     Pp[0] = Pc[0];
     Pp[1] = Pc[1];
     prev_last = cp.k == (cp.seg.t1 - 1) / kBlock;
