@@ -49,19 +49,24 @@ constexpr int kWDepth = 4;                  // operand reads in flight, in produ
 static_assert(kWWaves * kGroupRows == kBlockRows, "four waves move the four 8-row groups of a block");
 
 // LDS row layout of this kernel: rows of 1152 bytes, the 16-byte chunks of
-// row r permuted inside each aligned group of eight as c -> c ^ swzw(r).
-// swzw(r) = 4 ((r >> 2) & 1) + ((r >> 3) & 3) is a different permutation from
-// decode.hip's, chosen for the 32x32 operand patterns (gfx950 serves a 16-byte
-// read per half-wave and a transposing 8-byte read per wave from 128 banks of
-// 4 bytes):
-//   * score operand: a half-wave reads one chunk of all 32 rows; rows of equal
-//     r % 4 sit in the same 128-byte bank window, and swzw takes eight
-//     distinct values over r >> 2, so the 32 reads fill 512 distinct bytes;
-//   * value operand: a wave reads 8 rows base + 4h + k (h, k < 4; base a
-//     multiple of 8) at four chunks 4(ct & 1) + 2hf + e; bit 2 of swzw is h,
-//     so the two row halves land in disjoint halves of each chunk group, and
-//     the 64 eight-byte reads again fill 512 distinct bytes.
-__device__ __forceinline__ int swzw(int r) { return 4 * ((r >> 2) & 1) + ((r >> 3) & 3); }
+// row r permuted inside each aligned group of eight as c -> c ^ swzw(r),
+//     swzw(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3).
+// Bank model (measured on gfx950 with the bank-conflict counter over lane
+// patterns): a 16-byte read is served a quarter-wave (16 consecutive lanes)
+// at a time and a transposing 8-byte read a half-wave at a time, each pass
+// over 64 banks of 4 bytes; a pass is conflict-free when its lanes touch
+// distinct 16-byte (resp. 8-byte) units modulo 256 bytes.  A row is 4.5 such
+// windows long, so rows r and r + 2 start at the same bank and only the
+// permutation tells them apart:
+//   * score operand: a quarter-wave reads the same chunk of 16 consecutive
+//     rows; for each row parity, swzw takes eight distinct values over the
+//     eight rows (it is a bijection of (r >> 1) & 7), so the 16 reads land
+//     on 16 distinct units;
+//   * value operand: a half-wave reads rows b .. b+3 (b a multiple of 4) at
+//     the four chunks 4(ct & 1) + 0..3 of a group of eight; bit 2 of swzw is
+//     (r >> 1) & 1, so rows r and r + 2 (same parity) take opposite halves of
+//     the group, and the 32 eight-byte reads land on 32 distinct units.
+__device__ __forceinline__ int swzw(int r) { return 4 * ((r >> 1) & 1) + ((r >> 2) & 3); }
 __device__ __forceinline__ int lds_off_w(int r, int x) { return r * kRowBytes + (x ^ (swzw(r) << 4)); }
 
 // The absorbed query of a wave for 32x32x16 products: K-step kk holds
