@@ -43,7 +43,6 @@ constexpr int kWThreads = kWWaves * 64;
 constexpr int kWNBuf = 4;                   // value(i-1), scores(i), blocks i+1 and i+2 in flight
 constexpr int kWAhead = 2;                  // blocks copied ahead of the one being scored
 constexpr int kWCopies = kCopiesPerGroup;   // 9 copies per wave and block: wave w moves 8-row group w
-constexpr int kWBt = 4 * kWThreads;         // block-table entries block_prefix can copy with 256 threads
 constexpr int kWDepth = 4;                  // operand reads in flight, in products
 
 static_assert(kWWaves * kGroupRows == kBlockRows, "four waves move the four 8-row groups of a block");
@@ -443,15 +442,12 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kWNBuf * kBlockBytes];
   __shared__ int pfx[kMaxSchedB + 1];
   __shared__ int lens[kMaxSchedB];
-  __shared__ int bt_lds[kWBt];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h0 = 32 * wave;
 
-  const bool bt_local = a.splits == 0 && a.prefill_T == 0 && a.B * a.max_pages <= kWBt;
   int P = 0;
-  if (a.splits == 0 && a.prefill_T == 0)
-    P = block_prefix(a.seq_lens, a.B, pfx, lens, bt_local ? block_table : nullptr, a.B * a.max_pages, bt_lds);
+  if (a.splits == 0 && a.prefill_T == 0) P = block_prefix(a.seq_lens, a.B, pfx, lens, nullptr, 0, nullptr);
   Cursor cp;
   cp.sch = schedule_begin(a, pfx, lens, P);
   cp.valid = schedule_next(a, cp.sch, cp.seg);
@@ -460,8 +456,11 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 
   auto qrow = [&](const Segment& s) { return (const bf16*)a.q + (size_t)s.b * a.H * kRow; };
   auto block_hi = [&](const Cursor& c) { return min(c.seg.t1 - c.k * kBlock, kBlock); };
-  auto page_of = [&](const Cursor& c) {
-    if (bt_local) return uniform(bt_lds[c.seg.b * a.max_pages + (c.k >> 1)]);
+  // The page of the block at cursor c, a block-table entry read with a
+  // scalar load.  In the loop it is read one step before the copy plan that
+  // uses it, so that the read's latency passes under a step's products.
+  auto page_fetch = [&](const Cursor& c) {
+    if (!c.valid) return 0;
     const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)c.seg.b * a.max_pages;
     return bt[uniform(c.k >> 1)];
   };
@@ -470,9 +469,16 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   };
   // copies of the block at cursor c into buffer `slot`; no rows when c is
   // past the unit's work
-  auto plan_wide = [&](const Cursor& c, int slot) {
-    const uint8_t* page = c.valid ? a.rows + (size_t)page_of(c) * kPageBytes : a.rows;
+  auto plan_wide = [&](const Cursor& c, int pg, int slot) {
+    const uint8_t* page = a.rows + (size_t)uniform(pg) * kPageBytes;
     return plan_block_wide(page, c.valid ? c.k & 1 : 0, smem + slot * kBlockBytes, c.valid ? block_hi(c) : 0, wave);
+  };
+  // where a piece's normalised sums go: z and lse for a whole sequence, a
+  // partial slot otherwise
+  auto piece_out = [&](const Segment& sg, float*& zo, float*& lo) {
+    const bool whole = sg.parts == 1;
+    zo = whole ? a.z + (size_t)sg.b * a.H * kDc : a.zp + (size_t)sg.slot * a.H * kDc;
+    lo = whole ? (a.lse ? a.lse + (size_t)sg.b * a.H : nullptr) : a.lsep + (size_t)sg.slot * a.H;
   };
 
   // The value product of step 0 reads buffer kWNBuf - 1 with zero
@@ -490,13 +496,14 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   for (int j = 0; j < kWAhead; ++j) {
     // the first two blocks (a piece shorter than that leaves a copy of no
     // rows: it moves nothing and keeps the count of copies per block fixed)
-    const WideCopies nb = plan_wide(ld, j);
+    const WideCopies nb = plan_wide(ld, page_fetch(ld), j);
 #pragma unroll
     for (int t = 0; t < kWCopies; ++t) lds_dma16(nb.rs, nb.lb + kCopyBytes * t, co.vo[t], nb.g * kGroupBytes);
     if (ld.valid) cursor_next(a, ld);
   }
-  WideCopies nb = plan_wide(ld, kWAhead);
+  WideCopies nb = plan_wide(ld, page_fetch(ld), kWAhead);
   if (ld.valid) cursor_next(a, ld);
+  int pg = page_fetch(ld);  // of block 3, planned at the end of step 0
   consume_query_wide(Q);
   reset_acc_mfma(Z);
   st.m = -INFINITY;
@@ -504,6 +511,7 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   note_pieces(cp.seg);
   const uint32_t base = lds_addr(smem);
   WideAddr A = wide_addr(base, base + (kWNBuf - 1) * kBlockBytes);
+  __syncthreads();  // the zeroed buffer is visible to every wave
 
   // The block scored in the previous step, whose value product is still to
   // be done: its probabilities, where its piece goes and, if it ended the
@@ -512,6 +520,9 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   bool prev_last = false;
   float* zdst = nullptr;    // its piece's output rows
   float* ldst = nullptr;
+  float *zcur, *lcur;       // those of the piece being scored
+  piece_out(cp.seg, zcur, lcur);
+  int klast = (cp.seg.t1 - 1) / kBlock;  // its last block
   bool has_stored = false;  // a flush left part of its piece's sums there
   float l_end = 0.f, m_end = 0.f;
 
@@ -520,7 +531,13 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // every wave issues nine copies per block, so the copies of the block
     // after this one are the last nine issued
     wait_blocks_wide(1);
-    __syncthreads();  // block i has landed; every wave is done with step i-1
+    // block i has landed; every wave is done with step i-1.  A bare barrier:
+    // the copies are complete by the wait above, every LDS read of step i-1
+    // was consumed by its product, and no ordinary LDS store is in flight, so
+    // no fence (and no wait for the page read in flight) is needed; the empty
+    // asm keeps the compiler from moving LDS reads across it.
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     // multi-token decode: query token t of the sequence sees keys up to
     // L - q_len + t, so the last q_len - 1 - t keys are masked for it
     int hi = cur ? block_hi(cp) : kBlock;
@@ -558,17 +575,14 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
       break;
     }
     // the copies of block i+3, issued in the next step
-    nb = plan_wide(ld, (i + kWAhead + 1) % kWNBuf);
+    nb = plan_wide(ld, pg, (i + kWAhead + 1) % kWNBuf);
     if (ld.valid) cursor_next(a, ld);
+    pg = page_fetch(ld);
     Pp[0] = Pc[0];
     Pp[1] = Pc[1];
-    prev_last = cp.k == (cp.seg.t1 - 1) / kBlock;
-    {
-      const Segment& sg = cp.seg;
-      const bool whole = sg.parts == 1;
-      zdst = whole ? a.z + (size_t)sg.b * a.H * kDc : a.zp + (size_t)sg.slot * a.H * kDc;
-      ldst = whole ? (a.lse ? a.lse + (size_t)sg.b * a.H : nullptr) : a.lsep + (size_t)sg.slot * a.H;
-    }
+    prev_last = cp.k == klast;
+    zdst = zcur;
+    ldst = lcur;
     if (prev_last) {
       l_end = pair32_sum(st.l);
       m_end = st.m;
@@ -582,6 +596,8 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
       st.m = -INFINITY;
       st.l = 0.f;
       note_pieces(cp.seg);
+      piece_out(cp.seg, zcur, lcur);
+      klast = (cp.seg.t1 - 1) / kBlock;
     }
   }
 }
