@@ -91,6 +91,15 @@ def _pct(xs, q):
     return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
+def decode_kernel_name(dtype: str, heads: int) -> str:
+    """The attention kernel the library launches for a cache dtype and a
+    (query tokens x heads) count: the fp32 kernel, the four-wave kernel for
+    65..128 heads over a bf16 cache, else the eight-wave kernel."""
+    if dtype == "f32":
+        return "decode_f32_kernel"
+    return "decode_wide_kernel" if dtype == "bf16" and heads > 64 else "decode_mfma_kernel"
+
+
 def step_stats(step_ms):
     return {"median": _pct(step_ms, 50), "p10": _pct(step_ms, 10), "p90": _pct(step_ms, 90), "n": len(step_ms)}
 
@@ -345,7 +354,7 @@ def run_prefill(args, wl, dev, steps, warmup, cpu_seconds):
             layer[name] = {"us": ms * 1e3, "alg_flops": flops[name], "TFLOP/s": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
         proj_flops += sum(flops.values())
     from mla_latent_kv_30_amd import traffic as TR
-    mc = TR.load("decode_mfma_kernel", wl.name, os.path.join(ROOT, "profiles"), "mfma")
+    mc = TR.load(decode_kernel_name(wl.dtype, H), wl.name, os.path.join(ROOT, "profiles"), "mfma")
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, host, cpu_seconds, args.seed)
     return {
         "metric": "MLA causal prefill TFLOP/s (absorbed attention + absorb + up-projection)",
@@ -587,7 +596,7 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
     # HBM bytes per launch from the stored counter runs, if they were taken on
     # the current kernel sources
     from mla_latent_kv_30_amd import traffic as TR
-    kname = "decode_mfma_kernel" if wl.dtype != "f32" else "decode_f32_kernel"
+    kname = decode_kernel_name(wl.dtype, wl.H * QL)
     tr = TR.load(kname, wl.name, os.path.join(ROOT, "profiles")) if QL == 1 else None
     mc = TR.load(kname, wl.name, os.path.join(ROOT, "profiles"), "mfma") if QL == 1 else None
     if QL > 1:

@@ -43,7 +43,8 @@ constexpr int kWThreads = kWWaves * 64;
 constexpr int kWNBuf = 4;                   // value(i-1), scores(i), blocks i+1 and i+2 in flight
 constexpr int kWAhead = 2;                  // blocks copied ahead of the one being scored
 constexpr int kWCopies = kCopiesPerGroup;   // 9 copies per wave and block: wave w moves 8-row group w
-constexpr int kWDepth = 4;                  // operand reads in flight, in products
+constexpr int kWDepth = 3;                  // operand reads in flight, in products
+static_assert(36 % kWDepth == 0, "the value reads issued under the last score products land in rb[0 .. D-1]");
 
 static_assert(kWWaves * kGroupRows == kBlockRows, "four waves move the four 8-row groups of a block");
 
@@ -359,11 +360,15 @@ __device__ __forceinline__ float pair32_maximum(float v) {
 // scheduling barriers keep that order (left to itself the compiler gathered
 // the reads next to their products and the softmax ahead of them, and the
 // one wave on each SIMD then waited on every LDS round trip).
-// mask (uniform): tokens at or past hi (per lane) are excluded.
+// mask (uniform): tokens at or past hi (per lane) are excluded.  book(t),
+// t = 0, 1, 2, runs the step's scalar bookkeeping (the next copy plan and
+// the block cursors) after score products 1, 5 and 9, where it issues
+// between products instead of after them.
+template <class Book>
 __device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const WideAddr& A, const WideCopies& nb,
                                           const WideCopyOffsets& co, const bf16x8 (&Pp)[2], bf16x8 (&Pc)[2],
                                           WideSoftmax& st, float scale_log2, bool mask, int hi, bool& rescale,
-                                          float& alpha) {
+                                          float& alpha, Book&& book) {
   constexpr int D = kWDepth;
   bf16x8 rb[D];
 #pragma unroll
@@ -376,6 +381,7 @@ __device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const 
     rb[kk % D] = kk + D < 36 ? score_operand(A, kk + D) : value_operand(A, kk + D - 36);
     S = mfma32(a, Q.q[kk], S);
     if ((kk & 3) == 3) lds_dma16(nb.rs, nb.lb + kCopyBytes * (kk >> 2), co.vo[kk >> 2], nb.g * kGroupBytes);
+    if ((kk & 3) == 1 && kk < 12) book(kk >> 2);
     __builtin_amdgcn_sched_barrier(0);
   }
   // value phase: 32 products with the softmax of S woven in
@@ -503,7 +509,8 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   }
   WideCopies nb = plan_wide(ld, page_fetch(ld), kWAhead);
   if (ld.valid) cursor_next(a, ld);
-  int pg = page_fetch(ld);  // of block 3, planned at the end of step 0
+  int pg = page_fetch(ld);  // of block 3, planned in step 0
+  int ld_klast = (ld.seg.t1 - 1) / kBlock;  // the copy cursor's last block in its piece
   consume_query_wide(Q);
   reset_acc_mfma(Z);
   st.m = -INFINITY;
@@ -549,56 +556,83 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     bf16x8 Pc[2];
     bool rescale_c = false;
     float alpha_c = 1.f;
+    // Bookkeeping inside the step (the common case of each cursor move; a
+    // move to another piece is finished after the step): the copy plan of
+    // block i+3, then the copy cursor and the scoring cursor one block on.
+    WideCopies nb_next;
+    bool ld_switch = false;
+    const bool last_now = cur && cp.k == klast;  // block i ends its piece
+    auto book = [&](int t) {
+      if (t == 0) {
+        nb_next = plan_wide(ld, pg, (i + kWAhead + 1) % kWNBuf);
+      } else if (t == 1) {
+        ld_switch = ld.valid && ld.k == ld_klast;
+        ld.k += (ld.valid && !ld_switch) ? 1 : 0;
+      } else {
+        cp.k += (cur && !last_now) ? 1 : 0;
+      }
+    };
     // scores and softmax of block i (of stale rows when there is no block i:
     // unused), value product of block i-1 (zero probabilities at i = 0), and
     // the copies of block i+2 into the buffer of block i-2
-    wide_step(Q, Z, A, nb, co, Pp, Pc, st, a.scale_log2, mask, hi, rescale_c, alpha_c);
+    wide_step(Q, Z, A, nb, co, Pp, Pc, st, a.scale_log2, mask, hi, rescale_c, alpha_c, book);
     advance_addr(A, i);
-    if (!cur) rescale_c = false;
-    if (i > 0) {
-      if (__builtin_expect(rescale_c, 0)) {
+    // Everything that does not happen at every block (a moved maximum, the
+    // end of a piece, a cursor moving to another piece, the end of the
+    // unit's work) behind one branch.
+    const bool rare = !cur || rescale_c || prev_last || ld_switch || last_now;
+    if (__builtin_expect(rare, 0)) {
+      if (i > 0 && cur && rescale_c) {
         // block i moved a running maximum: the sums up to block i-1 are
         // relative to the old one (block i's value product comes next)
         acc_settle();
         flush_wide(Z, alpha_c, has_stored, zdst, h0, a.H);
         has_stored = true;
       }
-      if (prev_last) {
+      if (i > 0 && prev_last) {
+        // block i-1 ended its piece: its sums are complete
         acc_settle();
         store_wide(Z, l_end, m_end, has_stored, zdst, ldst, h0, a.H);
         has_stored = false;
         reset_acc_mfma(Z);
       }
+      if (!cur) {
+        wait_vmcnt<0>();  // no copy into this workgroup's LDS outlives it
+        break;
+      }
+      if (ld_switch) {
+        cursor_next(a, ld);  // to the copy cursor's next piece
+        ld_klast = (ld.seg.t1 - 1) / kBlock;
+      }
+      zdst = zcur;
+      ldst = lcur;
+      if (last_now) {
+        // block i ends its piece: keep its totals for the store after the
+        // next value product, and move to the next piece
+        l_end = pair32_sum(st.l);
+        m_end = st.m;
+        cursor_next(a, cp);
+        if (cp.valid) {
+          // its query replaces this one (only the value product of the
+          // finished piece remains, and it does not use the query)
+          load_query_wide(Q, qrow(cp.seg), a.H, h0);
+          consume_query_wide(Q);
+          st.m = -INFINITY;
+          st.l = 0.f;
+          note_pieces(cp.seg);
+          piece_out(cp.seg, zcur, lcur);
+          klast = (cp.seg.t1 - 1) / kBlock;
+        }
+      }
+    } else {
+      zdst = zcur;
+      ldst = lcur;
     }
-    if (!cur) {
-      wait_vmcnt<0>();  // no copy into this workgroup's LDS outlives it
-      break;
-    }
-    // the copies of block i+3, issued in the next step
-    nb = plan_wide(ld, pg, (i + kWAhead + 1) % kWNBuf);
-    if (ld.valid) cursor_next(a, ld);
+    nb = nb_next;  // the copies of block i+3, issued in the next step
     pg = page_fetch(ld);
     Pp[0] = Pc[0];
     Pp[1] = Pc[1];
-    prev_last = cp.k == klast;
-    zdst = zcur;
-    ldst = lcur;
-    if (prev_last) {
-      l_end = pair32_sum(st.l);
-      m_end = st.m;
-    }
-    cursor_next(a, cp);
-    if (prev_last && cp.valid) {
-      // next piece: its query replaces this one (only the value product of
-      // the finished piece remains, and it does not use the query)
-      load_query_wide(Q, qrow(cp.seg), a.H, h0);
-      consume_query_wide(Q);
-      st.m = -INFINITY;
-      st.l = 0.f;
-      note_pieces(cp.seg);
-      piece_out(cp.seg, zcur, lcur);
-      klast = (cp.seg.t1 - 1) / kBlock;
-    }
+    prev_last = last_now;
   }
 }
 

@@ -10,7 +10,9 @@ counter reads for a plain device copy of known size run in the same command
         --kernel decode_mfma_kernel --workload decode_h16 --out profiles/X.json
 
 The same module summarises a matrix-core counter run (mfma subcommand:
-SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE).
+SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) and an
+LDS counter run (lds subcommand: SQ_INSTS_LDS, SQ_INSTS_LDS_LOAD_BANDWIDTH,
+SQ_LDS_BANK_CONFLICT, SQ_ACTIVE_INST_LDS, GRBM_GUI_ACTIVE).
 
 The summary records a digest of the sources the kernel is built from;
 bench.py reports the traffic only while those sources still have that digest.
@@ -150,6 +152,37 @@ def summarize_mfma(run_dir: str, kernel: str, workload: str, simds: int = 1024, 
     }
 
 
+LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+                "GRBM_GUI_ACTIVE")
+
+
+def summarize_lds(run_dir: str, kernel: str, workload: str) -> dict:
+    """LDS counters of `kernel` (median over its dispatches): LDS
+    instructions issued, bytes loaded from LDS (SQ_INSTS_LDS_LOAD_BANDWIDTH
+    counts 64-byte units), cycles lost to bank conflicts and cycles with an
+    LDS instruction in flight (both summed over the compute units), and the
+    GPU's active cycles."""
+    path = _counter_csv(run_dir)
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    rows = [d for d in per.values() if all(c in d for c in LDS_COUNTERS)]
+    if not rows:
+        raise RuntimeError(f"no dispatches of {kernel} with LDS counters in {run_dir}")
+    med = {c: statistics.median(d[c] for d in rows) for c in LDS_COUNTERS}
+    return {
+        "workload": workload, "kernel": kernel, "source_digest": source_digest(kernel), "dispatches": len(rows),
+        "lds_instructions": med["SQ_INSTS_LDS"], "lds_load_bytes": med["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64.0,
+        "bank_conflict_cycles": med["SQ_LDS_BANK_CONFLICT"], "lds_active_cycles": med["SQ_ACTIVE_INST_LDS"],
+        "gui_active_cycles": med["GRBM_GUI_ACTIVE"], "duration_ns": statistics.median(d["ns"] for d in rows),
+    }
+
+
 def load(kernel: str, workload: str, profiles_dir: str, what: str = "traffic"):
     """The stored summary (traffic or mfma) for (kernel, workload) if it
     matches the current sources, else None."""
@@ -178,11 +211,24 @@ def main():
     mf.add_argument("--command", default="")
     mf.add_argument("--largest", action="store_true", help="only the dispatches of the largest product")
     mf.add_argument("--out", required=True)
+    ld = sub.add_parser("lds")
+    ld.add_argument("--dir", required=True)
+    ld.add_argument("--kernel", required=True)
+    ld.add_argument("--workload", required=True)
+    ld.add_argument("--command", default="")
+    ld.add_argument("--out", required=True)
     d = sub.add_parser("digest")
     d.add_argument("--kernel", default="")
     args = ap.parse_args()
     if args.cmd == "digest":
         print(source_digest(args.kernel))
+        return
+    if args.cmd == "lds":
+        out = summarize_lds(args.dir, args.kernel, args.workload)
+        out["command"] = args.command
+        with open(args.out, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out))
         return
     if args.cmd == "mfma":
         out = summarize_mfma(args.dir, args.kernel, args.workload, largest=args.largest)
