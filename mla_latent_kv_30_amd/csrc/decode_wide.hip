@@ -463,8 +463,7 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   auto qrow = [&](const Segment& s) { return (const bf16*)a.q + (size_t)s.b * a.H * kRow; };
   auto block_hi = [&](const Cursor& c) { return min(c.seg.t1 - c.k * kBlock, kBlock); };
   // The page of the block at cursor c, a block-table entry read with a
-  // scalar load.  In the loop it is read one step before the copy plan that
-  // uses it, so that the read's latency passes under a step's products.
+  // scalar load.
   auto page_fetch = [&](const Cursor& c) {
     if (!c.valid) return 0;
     const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)c.seg.b * a.max_pages;
@@ -509,7 +508,6 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   }
   WideCopies nb = plan_wide(ld, page_fetch(ld), kWAhead);
   if (ld.valid) cursor_next(a, ld);
-  int pg = page_fetch(ld);  // of block 3, planned in step 0
   int ld_klast = (ld.seg.t1 - 1) / kBlock;  // the copy cursor's last block in its piece
   consume_query_wide(Q);
   reset_acc_mfma(Z);
@@ -545,6 +543,10 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // asm keeps the compiler from moving LDS reads across it.
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // the page of block i+3 for the copy plan in this step: a scalar load
+    // whose latency passes under that of the first score reads (the first
+    // product waits for both)
+    const int pg = page_fetch(ld);
     // multi-token decode: query token t of the sequence sees keys up to
     // L - q_len + t, so the last q_len - 1 - t keys are masked for it
     int hi = cur ? block_hi(cp) : kBlock;
@@ -629,7 +631,6 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
       ldst = lcur;
     }
     nb = nb_next;  // the copies of block i+3, issued in the next step
-    pg = page_fetch(ld);
     Pp[0] = Pc[0];
     Pp[1] = Pc[1];
     prev_last = last_now;
