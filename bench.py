@@ -94,10 +94,10 @@ def _pct(xs, q):
 def decode_kernel_name(dtype: str, heads: int) -> str:
     """The attention kernel the library launches for a cache dtype and a
     (query tokens x heads) count: the fp32 kernel, the four-wave kernel for
-    65..128 heads over a bf16 cache, else the eight-wave kernel."""
+    65..128 heads over a bf16 or fp8 cache, else the eight-wave kernel."""
     if dtype == "f32":
         return "decode_f32_kernel"
-    return "decode_wide_kernel" if dtype == "bf16" and heads > 64 else "decode_mfma_kernel"
+    return "decode_wide_kernel" if heads > 64 else "decode_mfma_kernel"
 
 
 def step_stats(step_ms):

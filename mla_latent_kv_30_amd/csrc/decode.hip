@@ -586,10 +586,8 @@ static void launch_mfma(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_mfma_kernel<2, 4, FP8>), grid, blk, 0, s, a, a.block_table);
   } else if (a.H <= 64) {
     hipLaunchKernelGGL((decode_mfma_kernel<4, 2, FP8>), grid, blk, 0, s, a, a.block_table);
-  } else if constexpr (FP8) {
-    hipLaunchKernelGGL((decode_mfma_kernel<8, 1, FP8>), grid, blk, 0, s, a, a.block_table);
   } else {
-    (void)launch_decode_wide(a, s);  // 65..128 heads over a bf16 cache: decode_wide.hip (error read by the caller)
+    (void)launch_decode_wide(a, FP8, s);  // 65..128 heads: decode_wide.hip (error read by the caller)
   }
 }
 

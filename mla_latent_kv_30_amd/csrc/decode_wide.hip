@@ -41,6 +41,7 @@ namespace {
 constexpr int kWWaves = 4;                  // one wave per SIMD
 constexpr int kWThreads = kWWaves * 64;
 constexpr int kWNBuf = 4;                   // value(i-1), scores(i), blocks i+1 and i+2 in flight
+constexpr int kWNBuf8 = 3;                  // fp8: value(i-1), scores(i), expansion of i+1
 constexpr int kWAhead = 2;                  // blocks copied ahead of the one being scored
 constexpr int kWCopies = kCopiesPerGroup;   // 9 copies per wave and block: wave w moves 8-row group w
 constexpr int kWDepth = 3;                  // operand reads in flight, in products
@@ -287,12 +288,14 @@ __device__ __forceinline__ WideAddr wide_addr(uint32_t score_buf, uint32_t value
   return A;
 }
 
-// From step i to step i+1: the score reads move from buffer i % 4 to the
-// next one, the value reads from buffer (i - 1) % 4 to the next one.
+// From step i to step i+1 in a ring of NB buffers: the score reads move
+// from buffer i % NB to the next one, the value reads from buffer
+// (i - 1) % NB to the next one.
+template <int NB>
 __device__ __forceinline__ void advance_addr(WideAddr& A, int i) {
-  constexpr uint32_t kNext = kBlockBytes, kWrap = (uint32_t)(-(kWNBuf - 1) * kBlockBytes);
-  const uint32_t ds = i % kWNBuf == kWNBuf - 1 ? kWrap : kNext;
-  const uint32_t dv = i % kWNBuf == 0 ? kWrap : kNext;
+  constexpr uint32_t kNext = kBlockBytes, kWrap = (uint32_t)(-(NB - 1) * kBlockBytes);
+  const uint32_t ds = i % NB == NB - 1 ? kWrap : kNext;
+  const uint32_t dv = i % NB == 0 ? kWrap : kNext;
 #pragma unroll
   for (int k4 = 0; k4 < 4; ++k4) A.sa[k4] += ds;
 #pragma unroll
@@ -338,6 +341,143 @@ __device__ __forceinline__ WideCopyOffsets copy_offsets(int g) {
   return o;
 }
 
+// ---------------------------------------------------------------------------
+// fp8 cache (E4M3 latent codes, one fp32 scale per token and 128 channels,
+// bf16 k^R): each block's codes, scales and k^R land in a staging buffer and
+// are expanded into a bf16 block buffer (code * scale rounded to bf16, the
+// 8-wave kernel's arithmetic) during the step before the block is scored,
+// between that step's score products.  The products are the bf16 path's.
+// ---------------------------------------------------------------------------
+// Staging layout: codes [32 rows][512], the 16-byte chunk c of row r at
+// chunk position c ^ 8 (r & 1); scales [32][4] fp32, then 128 bytes that the
+// scale copies may overrun with zeros; k^R [32][64] bf16.
+constexpr int kW8Codes = 0;
+constexpr int kW8Scales = kBlockRows * kDc;                   // 16384
+constexpr int kW8Kr = kW8Scales + kBlockRows * 16 + 128;      // 17024
+constexpr int kW8Stage = kW8Kr + kBlockRows * kDr * 2;        // 21120
+static_assert(kW8Stage % 16 == 0, "staging buffers stay 16-byte aligned");
+
+struct WideFp8Copies {
+  __amdgpu_buffer_rsrc_t rc, rk, rs;  // codes, k^R, scales of the block's rows (zeros past the valid ones)
+  uint32_t lb;                        // the staging buffer
+};
+
+__device__ __forceinline__ WideFp8Copies plan_block_fp8w(const DecodeArgs& a, int page, int half, int hi,
+                                                         uint32_t stage) {
+  const size_t row0 = (size_t)page * kPage + half * kBlockRows;
+  WideFp8Copies c;
+  c.rc = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.ckv8 + row0 * kDc), (short)0, uniform(hi * kDc),
+                                           kRsrcWord3);
+  c.rk = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.kr8 + row0 * (kDr * 2)), (short)0,
+                                           uniform(hi * kDr * 2), kRsrcWord3);
+  c.rs = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.scale8 + row0 * 4), (short)0, uniform(hi * 16),
+                                           kRsrcWord3);
+  c.lb = stage;
+  return c;
+}
+
+// Copy t (0..5) of wave w for one block: t < 4 moves codes of rows
+// 2(4w+t), 2(4w+t)+1 (1 KB, in the staging permutation: lane l fills chunk
+// position l & 31 of row 2(4w+t) + (l >> 5), which holds chunk
+// (l & 31) ^ 8 (l >> 5)); t = 4 the k^R of rows 8w .. 8w+7; t = 5 the scales
+// of rows 8w .. 8w+15 with 4-byte copies (the last 8 of them also land, with
+// the same values, in the next wave's; wave 3's extra rows are past the
+// block and arrive as zeros in the pad).
+__device__ __forceinline__ void issue_copy_fp8w(const WideFp8Copies& c, int t, int w, uint32_t code_voff) {
+  const int lane = lane_id_fresh();
+  if (t < 4) {
+    const uint32_t off = (uint32_t)(4 * w + t) * kCopyBytes;
+    lds_dma16(c.rc, c.lb + kW8Codes + off, code_voff, off);
+  } else if (t == 4) {
+    lds_dma16(c.rk, c.lb + kW8Kr + w * kCopyBytes, (uint32_t)(16 * lane), w * kCopyBytes);
+  } else if (t == 5) {
+    lds_dma4(c.rs, c.lb + kW8Scales + w * 128, (uint32_t)(4 * lane), w * 128);
+  }
+}
+constexpr int kW8Copies = 6;
+
+// The expansion of one block by the 256 threads.  Thread t takes row r and
+// the four 16-code chunks g + 8j' (one per 128-channel tile) of it: with
+// q = t >> 4, e = (t >> 3) & 1, g = t & 7, r = b(q) or b(q) ^ 5 for
+// b(q) = (q & 3) + 8 (q >> 2).  Rows r and r ^ 5 share a quarter-wave and
+// differ in parity and in bit 2, which makes both the staging reads (slot j
+// at chunk position g + 8j, i.e. chunk g + 8 (j ^ (r & 1))) and the writes
+// into the bf16 layout free of bank conflicts.  Slices by score product kk:
+// scales at 0, k^R read at 2 and written at 12, per-block setup at 4, slot
+// j read at 8j + 1 and converted in two halves at 8j + 5/6 (written at
+// 8j + 7) and 8j + 8/9 (written at 8j + 10).
+struct WideExpand {
+  int r, g;        // the thread's row and chunk (fixed)
+  floatx4 sc;      // the row's four scales, in slot order
+  int4v kr;        // a 16-byte piece of k^R
+  int4v code[2];   // slot codes in flight (two slots overlap)
+  bf16x8 out;      // half a slot, converted
+  uint32_t w0, w1; // write bases of the two halves (slot 0 position)
+  int p;           // r & 1
+};
+
+__device__ __forceinline__ int expand_row(int t) {
+  const int q = t >> 4, e = (t >> 3) & 1;
+  const int b = (q & 3) + 8 * (q >> 2);
+  return e ? (b ^ 5) : b;
+}
+
+__device__ __forceinline__ void expand_init(WideExpand& X) {
+  const int t = threadIdx.x;
+  X.r = expand_row(t);
+  X.g = t & 7;
+}
+
+__device__ __forceinline__ void expand_slice(WideExpand& X, int kk, uint32_t stage, uint32_t buf) {
+  const int r = X.r, g = X.g;
+  if (kk == 0) {
+    X.sc = *(const MLA_LDS floatx4*)(uintptr_t)(stage + kW8Scales + 16 * r);
+  } else if (kk == 2) {
+    // k^R piece of row thread / 8, chunk thread % 8
+    const int t = (int)threadIdx.x;
+    X.kr = lds_read_b128_at(stage + kW8Kr + (t >> 3) * (kDr * 2) + 16 * (t & 7));
+  } else if (kk == 4) {
+    // slot j holds tile j ^ p: swap the scales into slot order
+    X.p = r & 1;
+    const floatx4 s0 = X.sc;
+    const bool sw1 = X.p != 0;
+    X.sc[0] = sw1 ? s0[1] : s0[0];
+    X.sc[1] = sw1 ? s0[0] : s0[1];
+    X.sc[2] = sw1 ? s0[3] : s0[2];
+    X.sc[3] = sw1 ? s0[2] : s0[3];
+    const int sw = swzw(r) << 4;
+    X.w0 = buf + r * kRowBytes + 128 * (g >> 2) + ((32 * (g & 3)) ^ sw);
+    X.w1 = buf + r * kRowBytes + 128 * (g >> 2) + ((32 * (g & 3) + 16) ^ sw);
+  } else if (kk == 12) {
+    const int t = (int)threadIdx.x;
+    const int rk = t >> 3, kc = t & 7;
+    *(MLA_LDS int4v*)(uintptr_t)(buf + lds_off_w(rk, kDc * 2 + 16 * kc)) = X.kr;
+  }
+  if (kk >= 1 && kk <= 25 && (kk - 1) % 8 == 0) {
+    const int j = (kk - 1) / 8;
+    X.code[j & 1] = lds_read_b128_at(stage + kW8Codes + r * kDc + 16 * g + 128 * j);
+  }
+  if (kk >= 5 && kk <= 34) {
+    const int j = (kk - 5) / 8, ph = (kk - 5) % 8;  // phases 0,1: words 0,1; 2: write; 3,4: words 2,3; 5: write
+    if (j < 4 && ph != 2 && ph != 5 && ph < 5) {
+      const int wd = ph < 2 ? ph : ph - 1;           // word 0..3
+      const float scj = X.sc[j];
+      const int word = X.code[j & 1][wd];
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      const int o = 4 * (wd & 1);
+      X.out[o + 0] = f2bf(lo[0] * scj);
+      X.out[o + 1] = f2bf(lo[1] * scj);
+      X.out[o + 2] = f2bf(hi[0] * scj);
+      X.out[o + 3] = f2bf(hi[1] * scj);
+      asm volatile("" : "+v"(X.out));
+    } else if (j < 4 && (ph == 2 || ph == 5)) {
+      const uint32_t dst = (ph == 2 ? X.w0 : X.w1) + ((uint32_t)(j ^ X.p) << 8);
+      *(MLA_LDS bf16x8*)(uintptr_t)dst = X.out;
+    }
+  }
+}
+
 // Keep a value computed at this point of the instruction sequence.
 __device__ __forceinline__ void anchor(float& x) { asm volatile("" : "+v"(x)); }
 
@@ -360,15 +500,17 @@ __device__ __forceinline__ float pair32_maximum(float v) {
 // scheduling barriers keep that order (left to itself the compiler gathered
 // the reads next to their products and the softmax ahead of them, and the
 // one wave on each SIMD then waited on every LDS round trip).
-// mask (uniform): tokens at or past hi (per lane) are excluded.  book(t),
-// t = 0, 1, 2, runs the step's scalar bookkeeping (the next copy plan and
-// the block cursors) after score products 1, 5 and 9, where it issues
-// between products instead of after them.
-template <class Book>
-__device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const WideAddr& A, const WideCopies& nb,
-                                          const WideCopyOffsets& co, const bf16x8 (&Pp)[2], bf16x8 (&Pc)[2],
-                                          WideSoftmax& st, float scale_log2, bool mask, int hi, bool& rescale,
-                                          float& alpha, Book&& book) {
+// mask (uniform): tokens at or past hi (per lane) are excluded.  The
+// callbacks place the rest of a step's work between score products, where
+// it issues in their shadow instead of after them: copy(t) issues copy t of
+// a later block after products 3, 7, .., 35 (t = 0..8); book(t), t = 0, 1,
+// 2, the scalar bookkeeping (the next copy plan, the block cursors) after
+// products 1, 5 and 9; expand(kk) a slice of the fp8 expansion of the next
+// block after every product kk.
+template <class Copy, class Book, class Expand>
+__device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const WideAddr& A, const bf16x8 (&Pp)[2],
+                                          bf16x8 (&Pc)[2], WideSoftmax& st, float scale_log2, bool mask, int hi,
+                                          bool& rescale, float& alpha, Copy&& copy, Book&& book, Expand&& expand) {
   constexpr int D = kWDepth;
   bf16x8 rb[D];
 #pragma unroll
@@ -380,8 +522,9 @@ __device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const 
     const bf16x8 a = rb[kk % D];
     rb[kk % D] = kk + D < 36 ? score_operand(A, kk + D) : value_operand(A, kk + D - 36);
     S = mfma32(a, Q.q[kk], S);
-    if ((kk & 3) == 3) lds_dma16(nb.rs, nb.lb + kCopyBytes * (kk >> 2), co.vo[kk >> 2], nb.g * kGroupBytes);
+    if ((kk & 3) == 3) copy(kk >> 2);
     if ((kk & 3) == 1 && kk < 12) book(kk >> 2);
+    expand(kk);
     __builtin_amdgcn_sched_barrier(0);
   }
   // value phase: 32 products with the softmax of S woven in
@@ -444,8 +587,12 @@ __device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const 
 template <bool FP8>
 __global__ void __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
-  static_assert(!FP8, "the fp8 cache takes the 16-head kernel");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWNBuf * kBlockBytes];
+  // bf16: four block buffers.  fp8: three bf16 block buffers and two
+  // staging buffers (the copies of block i+2 land in one while block i+1 is
+  // expanded from the other).
+  constexpr int NB = FP8 ? kWNBuf8 : kWNBuf;
+  constexpr int kBufBytes = NB * kBlockBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufBytes + (FP8 ? 2 * kW8Stage : 0)];
   __shared__ int pfx[kMaxSchedB + 1];
   __shared__ int lens[kMaxSchedB];
   const int tid = threadIdx.x;
@@ -472,11 +619,17 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   auto note_pieces = [&](const Segment& s) {
     if (a.meta != nullptr && s.slot == s.slot0 && tid == 0) *(int2*)(a.meta + 2 * s.b) = make_int2(s.slot0, s.parts);
   };
-  // copies of the block at cursor c into buffer `slot`; no rows when c is
-  // past the unit's work
-  auto plan_wide = [&](const Cursor& c, int pg, int slot) {
-    const uint8_t* page = a.rows + (size_t)uniform(pg) * kPageBytes;
-    return plan_block_wide(page, c.valid ? c.k & 1 : 0, smem + slot * kBlockBytes, c.valid ? block_hi(c) : 0, wave);
+  // copies of block j (at cursor c, on page pg) into its buffer (bf16) or
+  // staging buffer (fp8); no rows when c is past the unit's work
+  const uint32_t stage0 = lds_addr(smem + kBufBytes);
+  auto plan_wide = [&](const Cursor& c, int pg, int j) {
+    const int half = c.valid ? c.k & 1 : 0, rows = c.valid ? block_hi(c) : 0;
+    if constexpr (FP8) {
+      return plan_block_fp8w(a, uniform(pg), half, rows, stage0 + (uint32_t)(j & 1) * kW8Stage);
+    } else {
+      const uint8_t* page = a.rows + (size_t)uniform(pg) * kPageBytes;
+      return plan_block_wide(page, half, smem + (j % NB) * kBlockBytes, rows, wave);
+    }
   };
   // where a piece's normalised sums go: z and lse for a whole sequence, a
   // partial slot otherwise
@@ -486,27 +639,52 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     lo = whole ? (a.lse ? a.lse + (size_t)sg.b * a.H : nullptr) : a.lsep + (size_t)sg.slot * a.H;
   };
 
-  // The value product of step 0 reads buffer kWNBuf - 1 with zero
+  // The value product of step 0 reads buffer NB - 1 with zero
   // probabilities: its rows must be finite, so it starts as zeros.
   for (int j = tid; j < kBlockBytes / 16; j += kWThreads)
-    *(int4v*)(smem + (kWNBuf - 1) * kBlockBytes + 16 * j) = int4v{0, 0, 0, 0};
+    *(int4v*)(smem + (NB - 1) * kBlockBytes + 16 * j) = int4v{0, 0, 0, 0};
 
   WideQuery Q;
   WideAcc Z;
   WideSoftmax st;
-  const WideCopyOffsets co = copy_offsets(wave);
+  WideCopyOffsets co;      // bf16: source offsets of the nine copies
+  uint32_t code_voff = 0;  // fp8: source offset of the lane in a code copy
+  WideExpand X;
+  if constexpr (FP8) {
+    const int lane = lane_id_fresh();
+    code_voff = (uint32_t)((lane >> 5) * kDc + 16 * ((lane & 31) ^ (8 * (lane >> 5))));
+    asm volatile("" : "+v"(code_voff));
+    expand_init(X);
+  } else {
+    co = copy_offsets(wave);
+  }
+  auto issue_block = [&](const auto& nbk, int t) {
+    if constexpr (FP8) {
+      if (t < kW8Copies) issue_copy_fp8w(nbk, t, wave, code_voff);
+    } else {
+      lds_dma16(nbk.rs, nbk.lb + kCopyBytes * t, co.vo[t], nbk.g * kGroupBytes);
+    }
+  };
   load_query_wide(Q, qrow(cp.seg), a.H, h0);
   Cursor ld = cp;
 #pragma unroll
   for (int j = 0; j < kWAhead; ++j) {
     // the first two blocks (a piece shorter than that leaves a copy of no
     // rows: it moves nothing and keeps the count of copies per block fixed)
-    const WideCopies nb = plan_wide(ld, page_fetch(ld), j);
+    const auto nbj = plan_wide(ld, page_fetch(ld), j);
 #pragma unroll
-    for (int t = 0; t < kWCopies; ++t) lds_dma16(nb.rs, nb.lb + kCopyBytes * t, co.vo[t], nb.g * kGroupBytes);
+    for (int t = 0; t < kWCopies; ++t) issue_block(nbj, t);
     if (ld.valid) cursor_next(a, ld);
   }
-  WideCopies nb = plan_wide(ld, page_fetch(ld), kWAhead);
+  if constexpr (FP8) {
+    // block 0 is expanded before the loop (its copies are the older half of
+    // the two blocks in flight); block 1 is expanded in step 0
+    wait_vmcnt<kW8Copies>();
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 36; ++kk) expand_slice(X, kk, stage0, lds_addr(smem));
+  }
+  auto nb = plan_wide(ld, page_fetch(ld), kWAhead);
   if (ld.valid) cursor_next(a, ld);
   int ld_klast = (ld.seg.t1 - 1) / kBlock;  // the copy cursor's last block in its piece
   consume_query_wide(Q);
@@ -515,8 +693,8 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   st.l = 0.f;
   note_pieces(cp.seg);
   const uint32_t base = lds_addr(smem);
-  WideAddr A = wide_addr(base, base + (kWNBuf - 1) * kBlockBytes);
-  __syncthreads();  // the zeroed buffer is visible to every wave
+  WideAddr A = wide_addr(base, base + (NB - 1) * kBlockBytes);
+  __syncthreads();  // the zeroed buffer (and fp8: block 0) is visible to every wave
 
   // The block scored in the previous step, whose value product is still to
   // be done: its probabilities, where its piece goes and, if it ended the
@@ -533,9 +711,16 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 
   for (int i = 0;; ++i) {
     const bool cur = cp.valid;  // block i exists (else only block i-1's value product is left)
-    // every wave issues nine copies per block, so the copies of the block
-    // after this one are the last nine issued
-    wait_blocks_wide(1);
+    if constexpr (FP8) {
+      // the staged copies of block i+1 (the only ones in flight) and this
+      // wave's expansion of block i (LDS stores) are complete
+      wait_vmcnt<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+      // every wave issues nine copies per block, so the copies of the block
+      // after this one are the last nine issued
+      wait_blocks_wide(1);
+    }
     // block i has landed; every wave is done with step i-1.  A bare barrier:
     // the copies are complete by the wait above, every LDS read of step i-1
     // was consumed by its product, and no ordinary LDS store is in flight, so
@@ -561,12 +746,12 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // Bookkeeping inside the step (the common case of each cursor move; a
     // move to another piece is finished after the step): the copy plan of
     // block i+3, then the copy cursor and the scoring cursor one block on.
-    WideCopies nb_next;
+    decltype(nb) nb_next;
     bool ld_switch = false;
     const bool last_now = cur && cp.k == klast;  // block i ends its piece
     auto book = [&](int t) {
       if (t == 0) {
-        nb_next = plan_wide(ld, pg, (i + kWAhead + 1) % kWNBuf);
+        nb_next = plan_wide(ld, pg, i + kWAhead + 1);
       } else if (t == 1) {
         ld_switch = ld.valid && ld.k == ld_klast;
         ld.k += (ld.valid && !ld_switch) ? 1 : 0;
@@ -577,8 +762,15 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // scores and softmax of block i (of stale rows when there is no block i:
     // unused), value product of block i-1 (zero probabilities at i = 0), and
     // the copies of block i+2 into the buffer of block i-2
-    wide_step(Q, Z, A, nb, co, Pp, Pc, st, a.scale_log2, mask, hi, rescale_c, alpha_c, book);
-    advance_addr(A, i);
+    auto copy = [&](int t) { issue_block(nb, t); };
+    // fp8: block i+1 from its staging buffer into the buffer of block i-2
+    const uint32_t xs = stage0 + (uint32_t)((i + 1) & 1) * kW8Stage;
+    const uint32_t xb = base + (uint32_t)((i + 1) % NB) * kBlockBytes;
+    auto expand = [&](int kk) {
+      if constexpr (FP8) expand_slice(X, kk, xs, xb);
+    };
+    wide_step(Q, Z, A, Pp, Pc, st, a.scale_log2, mask, hi, rescale_c, alpha_c, copy, book, expand);
+    advance_addr<NB>(A, i);
     // Everything that does not happen at every block (a moved maximum, the
     // end of a piece, a cursor moving to another piece, the end of the
     // unit's work) behind one branch.
@@ -639,8 +831,12 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 
 }  // namespace
 
-hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_wide_kernel<false>), dim3(a.units), dim3(kWThreads), 0, s, a, a.block_table);
+hipError_t launch_decode_wide(const DecodeArgs& a, bool fp8, hipStream_t s) {
+  if (fp8) {
+    hipLaunchKernelGGL((decode_wide_kernel<true>), dim3(a.units), dim3(kWThreads), 0, s, a, a.block_table);
+  } else {
+    hipLaunchKernelGGL((decode_wide_kernel<false>), dim3(a.units), dim3(kWThreads), 0, s, a, a.block_table);
+  }
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s);
 // 65..128 heads over a bf16 cache (four waves of 32 heads)
-hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_wide(const DecodeArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 
 // merge + value up-projection in one launch (bf16 W^UV, B <= kFusedMaxB)

@@ -153,3 +153,98 @@ def test_units_spanning_sequences():
                                          h["k_r"][off[b]:off[b + 1]], h["w_uk"][heads], h["w_uv"][heads])
         assert _rel(z[b][heads], r["z"]) <= 2e-2, ("z", b)
         assert np.abs(lse[b][heads] - r["lse"]).max() <= 2e-2, ("lse", b)
+
+
+# --------------------------------------------------------------------------- multi-token decode (q_len * H > 64)
+
+def _oracle_multi_tokens(dd, q_len, H, hq_c, hq_r, c_all):
+    """Query token t of sequence b: the one-token decode on the prefix of
+    length L - q_len + t + 1 (causal among the new tokens)."""
+    h = dd.host
+    off = dd.layout.offsets
+    out = {"o": [], "z": [], "lse": []}
+    for b in range(dd.wl.B):
+        L = off[b + 1] - off[b]
+        per = {"o": [], "z": [], "lse": []}
+        for t in range(q_len):
+            n = L - q_len + t + 1
+            r = orc.decode_sequence(hq_c[b, t], hq_r[b, t], c_all[off[b]:off[b] + n], h["k_r"][off[b]:off[b] + n],
+                                    h["w_uk"], h["w_uv"])
+            for k in per:
+                per[k].append(r[k])
+        for k in out:
+            out[k].append(np.stack(per[k]))
+    return {k: np.stack(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("name,H,q_len,lens", [
+    ("decode_h16", 48, 2, [2, 700, 65]),      # 96 query heads
+    ("decode_h16", 32, 4, [4, 1500]),         # 128
+    ("long_fp8", 48, 2, [300, 2]),            # the fp8 cache
+])
+def test_multi_token_wide(name, H, q_len, lens):
+    wl = W.make_workload(name, B=len(lens), H=H, lens=lens)
+    _note(f"case wide multi-token {name} H={H} q_len={q_len} lens={lens}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    q_c, q_r, pos, hq_c, hq_r = DI.multi_query_inputs(dd, q_len)
+    c_all = dd.host["c_kv"]
+    fp8 = wl.dtype == "fp8"
+    if fp8:  # against what the cache holds: the kernel's own rounding only
+        codes, scales = orc.quantize_latent_e4m3(c_all)
+        c_all = orc.dequantize_latent_e4m3(codes, scales)
+    ref = _oracle_multi_tokens(dd, q_len, H, hq_c, hq_r, c_all)
+    B = wl.B
+    q_abs = mla.absorb_q(q_c, q_r, pos, dd.w_uk).view(B, q_len, H, 576)
+    for S in (0, 1, 3):
+        z, lse = mla.decode_multi(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=S)
+        o = mla.upproj_v(z.view(B * q_len, H, 512), dd.w_uv).view(B, q_len, H, 128)
+        torch.cuda.synchronize()
+        assert _rel(o.cpu().numpy(), ref["o"]) <= 2e-2, ("o", S)
+        assert _rel(z.cpu().numpy(), ref["z"]) <= 2e-2, ("z", S)
+        assert np.abs(lse.cpu().numpy() - ref["lse"]).max() <= 2e-2, ("lse", S)
+
+
+# --------------------------------------------------------------------------- fp8 cache on the wide kernel
+
+def _oracle_dequantised(dd):
+    """The oracle on the cache contents the fp8 path holds (codes x scale):
+    the kernel's own rounding is all that differs."""
+    codes, scales = orc.quantize_latent_e4m3(dd.host["c_kv"])
+    return _oracle(dd, orc.dequantize_latent_e4m3(codes, scales), dd.host["k_r"])
+
+
+@pytest.mark.parametrize("H,lens", [
+    (128, [int(x) for x in np.random.default_rng(9).integers(1, 200, 40)]),  # many short sequences
+    (97, [2000, 31, 64]),                                                      # partial head groups
+    (65, [1, 129, 33]),
+])
+def test_fp8_wide_matches_oracle(H, lens):
+    wl = W.make_workload("long_fp8", B=len(lens), H=H, lens=lens)
+    _note(f"case wide fp8 H={H} B={len(lens)}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    ref = _oracle_dequantised(dd)
+    _check(dd, ref)
+
+
+def test_fp8_wide_units_spanning_sequences():
+    """fp8 cache, lengths that make units end one piece and start the next
+    mid-stream (as test_units_spanning_sequences); sampled heads of every
+    wave against the absorbed oracle on the dequantised cache."""
+    lens = [5000, 6000, 3000]
+    wl = W.make_workload("long_fp8", B=len(lens), H=128, lens=lens)
+    _note(f"case wide fp8 units spanning sequences lens={lens}")
+    dd = DI.decode_inputs(wl, DEV, poison=True, spare_pages=2)
+    q_abs = mla.absorb_q(dd.q_c, dd.q_r, dd.pos, dd.w_uk)
+    z, lse = mla.decode(q_abs, dd.cache, dd.block_table, dd.seq_lens, num_splits=0)
+    torch.cuda.synchronize()
+    z, lse = z.cpu().numpy(), lse.cpu().numpy()
+    h = dd.host
+    codes, scales = orc.quantize_latent_e4m3(h["c_kv"])
+    deq = orc.dequantize_latent_e4m3(codes, scales)
+    off = dd.layout.offsets
+    heads = [0, 33, 64, 127]
+    for b in range(wl.B):
+        r = orc.decode_sequence_absorbed(h["q_c"][b][heads], h["q_r"][b][heads], deq[off[b]:off[b + 1]],
+                                         h["k_r"][off[b]:off[b + 1]], h["w_uk"][heads], h["w_uv"][heads])
+        assert _rel(z[b][heads], r["z"]) <= 2e-2, ("z", b)
+        assert np.abs(lse[b][heads] - r["lse"]).max() <= 2e-2, ("lse", b)
