@@ -441,6 +441,10 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
     lse = torch.empty((B * QL, H), dtype=torch.float32, device=dev)
     o = torch.empty((B * QL, H, 128), dtype=torch.bfloat16 if LAYER else torch.float32, device=dev)
     ws = mla.decode_workspace(B, QL * H, splits, dev)
+    # one token per sequence: decode, merge and W_UV in one call, a single
+    # launch where the library can (the decode kernel runs the merge jobs)
+    ws_up = mla.decode_upproj_workspace(B, H, splits, dev) if QL == 1 else None
+    one_launch = QL == 1 and mla.decode_upproj_launches(B, H, splits, dd.cache.code) == 1
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -471,8 +475,8 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
                                     num_splits=splits, workspace=ws, z=z.view(B, QL, H, 512),
                                     lse=lse.view(B, QL, H), out=o.view(B, QL, H, 128))
         else:
-            mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
-            mla.decode_merge_upproj(dd.seq_lens, H, ws, z, w_uv, lse=lse, num_splits=splits, out=o, out_dtype=o.dtype)
+            mla.decode_upproj(q_abs, cache, dd.block_table, dd.seq_lens, w_uv, num_splits=splits, workspace=ws_up,
+                              z=z, lse=lse, out=o, out_dtype=o.dtype)
         if LAYER:
             out_proj(r)
 
@@ -530,12 +534,16 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
         total_ms, per_step, wall = _timed_steps(lambda k: step(k % R), K, 1)
     ms_per_step = total_ms / K
 
-    # ---- the decode kernel alone (mla_decode_partial)
+    # ---- the decode kernel alone (mla_decode_partial; in the one-launch form
+    # the kernel also merges and up-projects, so it is timed as that call)
     def decode_only(r):
         cache = reps[r][0]
         if QL > 1:  # the multi-token entry point is decode + merge
             mla.decode_multi(q_abs.view(B, QL, H, 576), cache, dd.block_table, dd.seq_lens, num_splits=splits,
                              workspace=ws, z=z.view(B, QL, H, 512), lse=lse.view(B, QL, H))
+        elif one_launch:
+            mla.decode_upproj(q_abs, cache, dd.block_table, dd.seq_lens, reps[r][4], num_splits=splits,
+                              workspace=ws_up, z=z, lse=lse, out=o, out_dtype=o.dtype)
         else:
             mla.decode_partial(q_abs, cache, dd.block_table, dd.seq_lens, ws, z, lse, num_splits=splits)
 
@@ -546,10 +554,14 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
         parts = {
             "absorb_q": {"us": _timed_batches(lambda r: mla.absorb_q(reps[r][1], reps[r][2], pos_q, reps[r][3],
                                                                      out=q_abs), K, R)[1] * 1e3},
-            "decode_merge_upproj": {"us": _timed_batches(
-                lambda r: mla.decode_merge_upproj(dd.seq_lens, H, ws, z, reps[r][4], lse=lse, num_splits=splits,
-                                                  out=o, out_dtype=o.dtype), K, R)[1] * 1e3},
         }
+        if one_launch:
+            parts["decode_upproj (one launch)"] = {"us": kern_avg_ms * 1e3}
+        else:
+            # mla_decode_upproj's second launch, after decode_partial
+            parts["decode_merge_upproj"] = {"us": _timed_batches(
+                lambda r: mla.decode_merge_upproj(dd.seq_lens, H, ws_up, z, reps[r][4], lse=lse, num_splits=splits,
+                                                  out=o, out_dtype=o.dtype), K, R)[1] * 1e3}
 
     layer = None
     if LAYER:
@@ -583,6 +595,9 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
     # query token t of a sequence of L cached tokens sees L - q_len + t + 1 of them
     seen = int(sum(QL * int(L) - QL * (QL - 1) // 2 for L in wl.lens))
     alg_flops = seen * H * FLOP_PER_TOKEN_HEAD
+    if one_launch:  # W_UV read once and o written, o = W_UV z per (sequence, head)
+        alg_bytes += H * 128 * 512 * 2 + B * H * 128 * o.element_size()
+        alg_flops += B * H * 128 * 512 * 2
     gbs = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
     tflops = alg_flops / (kern_avg_ms * 1e-3) / 1e12
     mfma_peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
@@ -601,6 +616,8 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
     mc = TR.load(kname, wl.name, os.path.join(ROOT, "profiles"), "mfma") if QL == 1 else None
     if QL > 1:
         kname += " + merge_kernel"
+    elif one_launch:
+        kname += " (decode + split merge + W_UV up-projection in one launch)"
 
     roof = {
         "bound": "mfma" if mfma_bound else "hbm",
@@ -640,10 +657,11 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
             "seq_len_min": int(wl.lens.min()), "seq_len_max": int(wl.lens.max()), "page_size": 64,
             "num_splits": splits if splits > 0 else "auto", "replicas": R, "graph": graphs is not None,
             "graph_steps": G if graphs is not None else 0,
-            "step": ("qkv_project (cache append + query path) + absorb_q + decode_partial + decode_merge_upproj"
-                     " + output_proj"
+            "step": ("qkv_project (cache append + query path) + absorb_q + decode_upproj + output_proj"
                      if LAYER else
-                     "absorb_q + decode_partial + decode_merge_upproj (split merge + W_UV up-projection)" if QL == 1
+                     ("absorb_q + decode_upproj (decode, split merge and W_UV up-projection in one launch)"
+                      if one_launch else
+                      "absorb_q + decode_upproj (decode_partial, then split merge + W_UV up-projection)") if QL == 1
                      else "absorb_q + decode_multi_upproj (decode, then split merge + W_UV up-projection)"),
             "q_len": QL, "query_tokens_per_s": B * QL / (ms_per_step * 1e-3),
         },

@@ -333,6 +333,44 @@ mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H
                                    int32_t w_dtype, void* o, int32_t o_dtype, void* stream);
 
 /*
+ * mla_decode_upproj — one new token per sequence from the absorbed query to
+ * the head outputs: mla_decode followed by o_i = W_i^UV z_i (the "DeepSeek-V3"
+ * notes, ekkoxiao.github.io, §潜在向量的作用), i.e. mla_decode_partial then
+ * mla_decode_merge_upproj, with the same arguments and the same results
+ * (z, lse and o bit for bit).
+ * Where it can, the whole step is one launch: with a bf16 or fp8 cache,
+ * H <= 64, a bf16 W^UV, B <= 32 and no more work units than compute units,
+ * the decode kernel merges and up-projects itself.  A finished piece of a
+ * sequence increments a counter in the workspace; a (sequence, head) job
+ * waits, inside the kernel, until the counter shows every piece, and the
+ * last job of the sequence sets the counters back to zero.
+ *   w_uv       [H][128][512] in w_dtype (MLA_BF16 or MLA_F32)
+ *   o          [B][H][128] out in o_dtype (MLA_BF16 or MLA_F32)
+ *   workspace  at least mla_decode_upproj_workspace_size(B, H, num_splits)
+ *              bytes.  Its last 256*B bytes (from byte
+ *              mla_decode_workspace_size(B, H, num_splits): two counters per
+ *              sequence, on separate cache lines) must be zero before the
+ *              first call; every call leaves them zero.  Calls
+ *              that share a workspace must not run concurrently, and the
+ *              one-launch form needs the GPU's compute units to itself
+ *              (every unit resident at once).  A job whose pieces have not
+ *              arrived within 0.2 s writes NaN to its z, lse and o rows; the
+ *              counters must then be zeroed again.
+ * Errors: those of mla_decode and mla_decode_merge_upproj.
+ */
+mla_status mla_decode_upproj(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
+                             int32_t num_splits, void* workspace, size_t ws_bytes, float* z, float* lse,
+                             const void* w_uv, int32_t w_dtype, void* o, int32_t o_dtype, void* stream);
+/* Workspace bytes of mla_decode_upproj (0 for invalid arguments). */
+size_t mla_decode_upproj_workspace_size(int32_t B, int32_t H, int32_t num_splits);
+/* Launches mla_decode_upproj makes for these arguments on the current
+ * device: 1 (the one-launch form), 2, or 0 for invalid arguments
+ * (cache_dtype and w_dtype are MLA_* dtype codes). */
+int32_t mla_decode_upproj_launches(int32_t B, int32_t H, int32_t num_splits, int32_t cache_dtype,
+                                   int32_t w_dtype);
+
+/*
  * mla_prefill_causal — T new tokens of one sequence, at positions
  * pos0 .. pos0+T-1, are written into the cache and attend causally: query t
  * sees cached tokens 0 .. pos0+t inclusive (§注意力计算 sums up to the

@@ -107,6 +107,13 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_multi_upproj.restype = _i32
     L.mla_decode_multi_upproj.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp, _i32, _vp]
+    L.mla_decode_upproj.restype = _i32
+    L.mla_decode_upproj.argtypes = [_vp, ctypes.POINTER(MlaCache), _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp,
+                                    ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp, _i32, _vp]
+    L.mla_decode_upproj_workspace_size.restype = ctypes.c_size_t
+    L.mla_decode_upproj_workspace_size.argtypes = [_i32, _i32, _i32]
+    L.mla_decode_upproj_launches.restype = _i32
+    L.mla_decode_upproj_launches.argtypes = [_i32, _i32, _i32, _i32, _i32]
     L.mla_decode_merge_upproj.restype = _i32
     L.mla_decode_merge_upproj.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp, _i32, _vp,
                                           _i32, _vp]
@@ -458,6 +465,52 @@ def decode_merge_upproj(seq_lens: torch.Tensor, H: int, workspace: Optional[torc
                                          _ptr(z), _ptr(lse), _ptr(w_uv), _dt_code(w_uv.dtype), _ptr(out),
                                          _dt_code(out_dtype), _stream(z.device)), "mla_decode_merge_upproj")
     return out
+
+
+def decode_upproj_workspace(B: int, H: int, num_splits: int = 0, device="cuda") -> torch.Tensor:
+    """A workspace for mla_decode_upproj: zeroed, as its counters must be before the first call."""
+    need = int(lib().mla_decode_upproj_workspace_size(int(B), int(H), int(num_splits)))
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
+def decode_upproj_launches(B: int, H: int, num_splits: int, cache_dtype: int, w_dtype=torch.bfloat16) -> int:
+    """Launches mla_decode_upproj makes on the current device (1: the one-launch form)."""
+    return int(lib().mla_decode_upproj_launches(int(B), int(H), int(num_splits), int(cache_dtype),
+                                                _dt_code(w_dtype)))
+
+
+def decode_upproj(q_abs: torch.Tensor, cache: PagedCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                  w_uv: torch.Tensor, softmax_scale: Optional[float] = None, num_splits: int = 0,
+                  workspace: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, out_dtype=torch.float32, out: Optional[torch.Tensor] = None):
+    """(o[B,H,128], z, lse) of one new token per sequence (mla_decode_upproj: decode, merge and W^UV,
+    in one launch where the library can)."""
+    B, H = q_abs.shape[0], q_abs.shape[1]
+    _need(q_abs, "q_abs", cache.input_dtype, (B, H, ROW))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(w_uv, "w_uv", None, (H, D_V, D_C))
+    dev = q_abs.device
+    if z is None:
+        z = torch.empty((B, H, D_C), dtype=torch.float32, device=dev)
+    _need(z, "z", torch.float32, (B, H, D_C))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H))
+    if out is None:
+        out = torch.empty((B, H, D_V), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, (B, H, D_V))
+    if workspace is None:
+        workspace = decode_upproj_workspace(B, H, num_splits, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale() if softmax_scale is None else float(softmax_scale)
+    desc = cache.descriptor()
+    _check(lib().mla_decode_upproj(_ptr(q_abs), ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), B, H,
+                                   block_table.shape[1], scale, int(num_splits), _ptr(workspace), ws_bytes, _ptr(z),
+                                   _ptr(lse), _ptr(w_uv), _dt_code(w_uv.dtype), _ptr(out), _dt_code(out_dtype),
+                                   _stream(dev)), "mla_decode_upproj")
+    return out, z, lse
 
 
 def prefill_causal(q_abs: torch.Tensor, c_kv: torch.Tensor, k_r: torch.Tensor, cache: PagedCache,

@@ -368,6 +368,62 @@ mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H
   return mla_upproj_v(z, w_uv, o, B, H, w_dtype, o_dtype, stream);
 }
 
+size_t mla_decode_upproj_workspace_size(int32_t B, int32_t H, int32_t num_splits) {
+  if (B < 1 || H < 1 || H > MLA_MAX_HEADS || num_splits < 0 || num_splits > 256) return 0;
+  return workspace_bytes(B, H, make_plan(B, num_splits)) + (size_t)B * kTicketInts * sizeof(int32_t);
+}
+
+namespace {
+
+// The one-launch form of mla_decode_upproj: the matrix-core kernel of up to
+// 64 heads (it runs the merge jobs), a bf16 weight, few sequences (each job
+// re-reads its W^UV block), and no more units than CUs, so that every unit
+// is resident while a job waits for the pieces of others.
+bool upproj_one_launch(int kind, int32_t B, int32_t H, int32_t w_dtype, const Plan& p) {
+  return kind != kKindF32 && H <= 64 && w_dtype == MLA_BF16 && B <= kFusedMaxB && p.units <= device_cus();
+}
+
+}  // namespace
+
+int32_t mla_decode_upproj_launches(int32_t B, int32_t H, int32_t num_splits, int32_t cache_dtype, int32_t w_dtype) {
+  if (B < 1 || H < 1 || H > MLA_MAX_HEADS || num_splits < 0 || num_splits > 256) return 0;
+  const int kind = cache_dtype == MLA_F32 ? kKindF32 : cache_dtype == MLA_BF16 ? kKindBf16
+                   : cache_dtype == MLA_FP8_E4M3 ? kKindFp8 : -1;
+  if (kind < 0 || !dtype_ok(w_dtype)) return 0;
+  return upproj_one_launch(kind, B, H, w_dtype, make_plan(B, num_splits)) ? 1 : 2;
+}
+
+mla_status mla_decode_upproj(const void* q_abs, const mla_cache* cache, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t B, int32_t H, int32_t max_pages, float softmax_scale,
+                             int32_t num_splits, void* workspace, size_t ws_bytes, float* z, float* lse,
+                             const void* w_uv, int32_t w_dtype, void* o, int32_t o_dtype, void* stream) {
+  if (!w_uv || !o || !dtype_ok(w_dtype) || !dtype_ok(o_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!all_aligned16({w_uv, o})) return MLA_ERR_INVALID_ARG;
+  DecodeArgs a;
+  int kind;
+  Plan p;
+  mla_status st = prepare_decode(q_abs, cache, block_table, seq_lens, B, H, max_pages, softmax_scale, num_splits,
+                                 workspace, ws_bytes, z, lse, a, kind, p);
+  if (st != MLA_OK) return st;
+  const size_t base = workspace_bytes(B, H, p);
+  if (workspace == nullptr || ws_bytes < base + (size_t)B * kTicketInts * sizeof(int32_t)) return MLA_ERR_WORKSPACE;
+  st = debug_check(a, 1, cache->num_pages, (hipStream_t)stream);
+  if (st != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (upproj_one_launch(kind, B, H, w_dtype, p)) {
+    a.tickets = (int32_t*)((char*)workspace + base);
+    a.w_uv = w_uv;
+    a.o = o;
+    a.o_bf16 = o_dtype == MLA_BF16 ? 1 : 0;
+    return launched(launch_decode(a, kind, s));
+  }
+  st = launched(launch_decode(a, kind, s));
+  if (st != MLA_OK) return st;
+  return mla_decode_merge_upproj(seq_lens, B, H, num_splits, workspace, ws_bytes, z, lse, w_uv, w_dtype, o, o_dtype,
+                                 stream);
+}
+
 mla_status mla_decode(const void* q_abs, const mla_cache* cache, const int32_t* block_table, const int32_t* seq_lens,
                       int32_t B, int32_t H, int32_t max_pages, float softmax_scale, int32_t num_splits, void* workspace,
                       size_t ws_bytes, float* z, float* lse, void* stream) {

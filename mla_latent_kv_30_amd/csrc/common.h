@@ -162,4 +162,79 @@ __device__ __forceinline__ void rope_cs(int pos, double theta, float& c, float& 
   sincosf((float)a, &s, &c);
 }
 
+
+// ---- split merge and value up-projection ----------------------------------
+// Shared by the merge + up-projection kernel and the merge that the decode
+// launch runs itself, so that both give the same bits.  A split sequence's
+// pieces c (each normalised over its own keys, log-sum-exp lse_c) combine
+// as lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c (the
+// "DeepSeek-V3" notes, ekkoxiao.github.io, §潜在向量的作用: o = W^UV z).
+// One batch of NB pieces folded into the running maximum mx, the weight sum
+// wsum and NCH channel accumulators; padding entries carry lv = -inf.
+template <int NB, int NCH>
+__device__ __forceinline__ void merge_batch(const float (&lv)[NB], const float (&zv)[NB][NCH], float& mx,
+                                            float& wsum, float (&acc)[NCH]) {
+  float mb = mx;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) mb = fmaxf(mb, lv[u]);
+  const float alpha = __expf(mx - mb);  // mx = -inf on the first batch: alpha = 0
+  wsum *= alpha;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) acc[c] *= alpha;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const float w = __expf(lv[u] - mb);
+    wsum += w;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc[c] = fmaf(w, zv[u][c], acc[c]);
+  }
+  mx = mb;
+}
+
+// Eight bf16 weights (one 16-byte load) times channels z0 (first four) and
+// z1 (last four), accumulated in order.
+__device__ __forceinline__ float dot8_bf16(int4v w, float4 z0, float4 z1) {
+  const uint32_t w0 = (uint32_t)w[0], w1 = (uint32_t)w[1], w2 = (uint32_t)w[2], w3 = (uint32_t)w[3];
+  float t = __uint_as_float(w0 << 16) * z0.x;
+  t = fmaf(__uint_as_float(w0 & 0xffff0000u), z0.y, t);
+  t = fmaf(__uint_as_float(w1 << 16), z0.z, t);
+  t = fmaf(__uint_as_float(w1 & 0xffff0000u), z0.w, t);
+  t = fmaf(__uint_as_float(w2 << 16), z1.x, t);
+  t = fmaf(__uint_as_float(w2 & 0xffff0000u), z1.y, t);
+  t = fmaf(__uint_as_float(w3 << 16), z1.z, t);
+  t = fmaf(__uint_as_float(w3 & 0xffff0000u), z1.w, t);
+  return t;
+}
+
+// Sums of NR row partials over the 64 lanes of a wave (v[r]: this lane's
+// partial of row r).  At distance 2^k, k = 5 .. 6 - log2(NR), each lane
+// keeps the half of its rows selected by lane bit k and adds its partner's
+// copy of that half; the remaining distances add plainly.  Lane l ends with
+// row l >> (6 - log2 NR).  Every row is summed over the same pairing
+// (distances 32, 16, 8, 4, 2, 1) whatever NR is.
+template <int NR>
+__device__ __forceinline__ float wave_rows_sum(float (&v)[NR], int lane) {
+  constexpr int n = NR == 32 ? 5 : NR == 16 ? 4 : NR == 8 ? 3 : -1;
+  static_assert(n > 0, "8, 16 or 32 rows");
+#pragma unroll
+  for (int k = 5; k >= 6 - n; --k) {
+    const int half = 1 << (k - (6 - n));
+    const bool upper = (lane >> k) & 1;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      // opaque copies: a select between two array elements would otherwise be
+      // folded into a run-time array index, lowered as a compare chain
+      float lo = v[i], hi = v[i + half];
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      const float keep = upper ? hi : lo;
+      const float send = upper ? lo : hi;
+      v[i] = keep + __shfl_xor(send, 1 << k);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int d = (1 << (6 - n)) >> 1; d >= 1; d >>= 1) r += __shfl_xor(r, d);
+  return r;
+}
+
 }  // namespace mla

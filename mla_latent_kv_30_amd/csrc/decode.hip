@@ -34,6 +34,8 @@
 //   * Long sequences are cut into chunks; each chunk leaves a normalised
 //     partial (z_c, lse_c) that the merge kernel combines exactly:
 //     lse = log sum_c e^{lse_c}, z = sum_c e^{lse_c - lse} z_c.
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace mla {
@@ -264,9 +266,14 @@ __device__ __forceinline__ void softmax_value(WaveState<NT, NQ>& st, const float
   }
 }
 
+// Cache policy of a buffer access at device scope (sc1): it is coherent
+// across the XCDs' separate L2 caches without any cache maintenance.
+constexpr int kDeviceScope = 16;
+
 // Normalise and write one wave's part: z rows [head][512] at channels
-// c0 .. c0 + 16 NT, and lse[head] if with_lse.
-template <int NT, int NQ>
+// c0 .. c0 + 16 NT, and lse[head] if with_lse.  DEV: the stores are made at
+// device scope, for a reader in the same launch on another CU.
+template <bool DEV = false, int NT, int NQ>
 __device__ __forceinline__ void store_state(const WaveState<NT, NQ>& st, float l_tot, float* zdst, float* ldst, int h0,
                                             int H, int lane, int c0, bool with_lse) {
   constexpr float kLn2 = 0.69314718055994530942f;
@@ -276,13 +283,175 @@ __device__ __forceinline__ void store_state(const WaveState<NT, NQ>& st, float l
   // l_tot = 0: a piece all of whose keys lie after this query token (multi-
   // token decode); it leaves z = 0 and lse = -inf, which the merge weighs 0
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  float* row = zdst + (size_t)head * kDc + c0;
+  const float lse = (st.m + __log2f(l_tot)) * kLn2;
+  if constexpr (DEV) {
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(zdst), (short)0, 0x7fffffff, kRsrcWord3);
+    const uint32_t off = (uint32_t)(head * kDc + c0 + 4 * g) * 4u;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    *(float4*)(row + 16 * j + 4 * g) = make_float4(st.zacc[j][0] * inv, st.zacc[j][1] * inv,
-                                                   st.zacc[j][2] * inv, st.zacc[j][3] * inv);
+    for (int j = 0; j < NT; ++j) {
+      const int4v v = int4v{__float_as_int(st.zacc[j][0] * inv), __float_as_int(st.zacc[j][1] * inv),
+                            __float_as_int(st.zacc[j][2] * inv), __float_as_int(st.zacc[j][3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rz, off + 64u * j, 0, kDeviceScope);
+    }
+    if (with_lse && ldst != nullptr && g == 0) {
+      const __amdgpu_buffer_rsrc_t rl =
+          __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(ldst), (short)0, 0x7fffffff, kRsrcWord3);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse), rl, 4u * head, 0, kDeviceScope);
+    }
+  } else {
+    float* row = zdst + (size_t)head * kDc + c0;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      *(float4*)(row + 16 * j + 4 * g) = make_float4(st.zacc[j][0] * inv, st.zacc[j][1] * inv,
+                                                     st.zacc[j][2] * inv, st.zacc[j][3] * inv);
+    }
+    if (with_lse && ldst != nullptr && g == 0) ldst[head] = lse;
   }
-  if (with_lse && ldst != nullptr && g == 0) ldst[head] = (st.m + __log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Merge and value up-projection inside the decode launch
+// ---------------------------------------------------------------------------
+// With a.tickets set, the launch also does the work of merge_upproj_kernel
+// (o_i = W_i^UV z_i, the "DeepSeek-V3" notes, ekkoxiao.github.io,
+// §潜在向量的作用; the exact log-sum-exp merge of the pieces first):
+//   * the pieces are stored at device scope (sc1: coherent across the XCDs'
+//     L2 caches); when a unit has finished all its pieces, every wave waits
+//     for its stores to complete and one thread adds 1 to ticket[b].piece
+//     for every sequence b the unit stored a piece of;
+//   * then workgroup u takes the (sequence, head) jobs u, u + U, ...: it
+//     loads its W^UV rows, waits until ticket[b].piece counts every piece of
+//     b, reads the pieces at device scope, merges them in slot order exactly
+//     as merge_upproj_kernel does (same helpers, same bits) and multiplies;
+//   * the job that brings ticket[b].job to H clears both counters, so the
+//     next launch starts from zero without a memset.
+// A release / acquire fence pair at agent scope instead writes back and
+// invalidates whole L2 caches; on the 16-head decode that made the launch
+// several times slower than the two-launch form.
+// The launch has at most one workgroup per CU, so every producer is
+// resident while a job waits.  The wait is bounded all the same: a job whose
+// pieces have not all arrived within 0.2 s writes NaN.
+
+// Pieces of sequence b: first partial slot and count (the producer side's
+// Segment::slot0 and Segment::parts).
+struct PieceRange {
+  int slot0, parts;
+};
+
+__device__ __forceinline__ PieceRange piece_range(const DecodeArgs& a, const int* pfx, int P, int b) {
+  if (a.splits == 0) {
+    const long long G = min((long long)a.units, (long long)P);
+    const int r0 = uniform(pfx[b]) + kStartCost, r1 = uniform(pfx[b + 1]);
+    const int first = unit_of_block(r0, G, P), last = unit_of_block(r1 - 1, G, P);
+    return PieceRange{first + b, last - first + 1};
+  }
+  const int S = a.splits;
+  const int L = a.seq_lens[b];
+  const int np = (L + kPage - 1) / kPage;
+  const int chunk = (np + S - 1) / S;
+  return PieceRange{b * S, (np + chunk - 1) / chunk};
+}
+
+// A device-scope load of one float at byte offset off from base (uniform).
+__device__ __forceinline__ float load_dev(const float* base, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(base), (short)0, 0x7fffffff, kRsrcWord3);
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kDeviceScope));
+}
+
+// Longest wait for the pieces of a job: 0.2 s of the 100 MHz real-time counter.
+constexpr uint64_t kWaitTicks = 20000000;
+
+// One (sequence, head) job by the whole 512-thread workgroup; zs is 2 KB of
+// LDS and flag one int of it.
+__device__ __forceinline__ void merge_job(const DecodeArgs& a, const int* pfx, int P, int job, float* zs,
+                                          int* flag) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = job / a.H, head = job - b * a.H;
+  const PieceRange pr = piece_range(a, pfx, P, b);
+  int32_t* const ticket = a.tickets + kTicketInts * b;
+  // the first poll goes out before the weight rows, so that its answer does
+  // not wait for them (vector loads complete in order)
+  int seen = 0;
+  if (tid == 0) seen = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // wave w: rows 16w .. 16w+15 of W^UV_head, lane l: channels 8l .. 8l+7
+  const int4v* wrow = (const int4v*)((const bf16*)a.w_uv + ((size_t)(head % a.hs) * kDv + 16 * wave) * kDc) + lane;
+  int4v wv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wv[r] = wrow[r * (kDc / 8)];
+  if (tid == 0) {
+    int ok = seen >= pr.parts;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (!ok) {
+      __builtin_amdgcn_s_sleep(1);
+      ok = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= pr.parts;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) break;
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *(volatile int*)flag != 0;
+  float* zrow = a.z + ((size_t)b * a.H + head) * kDc;
+  float zval;
+  if (!ok) {
+    zval = __builtin_nanf("");
+    zrow[tid] = zval;
+    if (a.lse != nullptr && tid == 0) a.lse[(size_t)b * a.H + head] = zval;
+  } else if (pr.parts == 1) {  // finished in one piece: z is final
+    zval = load_dev(zrow, 4u * tid);
+  } else {
+    float mx = -INFINITY, wsum = 0.f;
+    float acc[1] = {0.f};
+    const int n = pr.parts;
+    const float* zp0 = a.zp + (size_t)pr.slot0 * a.H * kDc;
+    const float* lp0 = a.lsep + (size_t)pr.slot0 * a.H;
+    // batches as merge_upproj_kernel takes them
+    auto batches = [&](auto nb) {
+      constexpr int kNB = decltype(nb)::value;
+      for (int c0 = 0; c0 < n; c0 += kNB) {
+        float lv[kNB];
+        float zv[kNB][1];
+#pragma unroll
+        for (int u = 0; u < kNB; ++u) {
+          // past the last piece: weight e^{-inf} = 0 times 0 (merge_upproj_kernel
+          // re-loads the last piece there; 0 times it adds the same zero)
+          const uint32_t sl = (uint32_t)((c0 + u) * a.H + head);
+          const bool in = c0 + u < n;
+          lv[u] = in ? load_dev(lp0, 4u * sl) : -INFINITY;
+          zv[u][0] = in ? load_dev(zp0, 4u * (sl * kDc + tid)) : 0.f;
+        }
+        merge_batch(lv, zv, mx, wsum, acc);
+      }
+    };
+    if (n <= 16) batches(std::integral_constant<int, 16>{});
+    else batches(std::integral_constant<int, 32>{});
+    const float inv = 1.0f / wsum;
+    zval = acc[0] * inv;
+    zrow[tid] = zval;
+    if (a.lse != nullptr && tid == 0) a.lse[(size_t)b * a.H + head] = mx + __logf(wsum);
+  }
+  zs[tid] = zval;
+  __syncthreads();
+  // every piece of this job has been read: count the job (its answer is
+  // needed only after the product below)
+  int prev = 0;
+  if (tid == 0) prev = __hip_atomic_fetch_add(ticket + kTicketInts / 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float4 z0 = *(const float4*)(zs + 8 * lane), z1 = *(const float4*)(zs + 8 * lane + 4);
+  float v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = dot8_bf16(wv[r], z0, z1);
+  const float o_val = wave_rows_sum(v, lane);  // row lane >> 2 of the wave's 16
+  if ((lane & 3) == 0) {
+    const size_t oi = ((size_t)b * a.H + head) * kDv + 16 * wave + (lane >> 2);
+    if (a.o_bf16) ((bf16*)a.o)[oi] = f2bf(o_val);
+    else ((float*)a.o)[oi] = o_val;
+  }
+  if (tid == 0 && prev == a.H - 1) {  // the sequence's last job clears its counters
+    __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ticket + kTicketInts / 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();  // zs and flag are reused by the next job
 }
 
 // ---------------------------------------------------------------------------
@@ -336,160 +505,182 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   int P = 0;
   if (a.splits == 0 && a.prefill_T == 0)
     P = block_prefix(a.seq_lens, a.B, pfx, lens, bt_local ? block_table : nullptr, a.B * a.max_pages, bt_lds);
-  Cursor cp;
-  cp.sch = schedule_begin(a, pfx, lens, P);
-  cp.valid = schedule_next(a, cp.sch, cp.seg);
-  if (!cp.valid) return;
-  cp.k = cp.seg.t0 / kBlock;
+  // the launch's own merge and up-projection jobs, after the unit's pieces
+  // (of sequences pub0 .. pub1), which are published first
+  int pub0 = 0, pub1 = -1;
+  auto merge_jobs = [&]() {
+    if (a.tickets == nullptr) return;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's piece stores are complete
+    __syncthreads();  // ... and every other wave's; the block buffers are free
+    if (tid == 0) {
+      for (int b = pub0; b <= pub1; ++b)
+        __hip_atomic_fetch_add(a.tickets + kTicketInts * b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float* zs = (float*)smem;
+    int* flag = (int*)(smem + kDc * sizeof(float));
+    for (int job = blockIdx.x; job < a.B * a.H; job += gridDim.x) merge_job(a, pfx, P, job, zs, flag);
+  };
+  // the unit's own pieces (a unit with none returns at once)
+  [&]() {
+    Cursor cp;
+    cp.sch = schedule_begin(a, pfx, lens, P);
+    cp.valid = schedule_next(a, cp.sch, cp.seg);
+    if (!cp.valid) return;
+    cp.k = cp.seg.t0 / kBlock;
 
-  auto qrow = [&](const Segment& s) { return (const bf16*)a.q + (size_t)s.b * a.H * kRow; };
-  auto block_hi = [&](const Cursor& c) { return min(c.seg.t1 - c.k * kBlock, kBlock); };
-  // block-table reads use a uniform index, so they are scalar loads that do
-  // not wait behind the copies in flight
-  auto page_of = [&](const Cursor& c) {
-    if (bt_local) return uniform(bt_lds[c.seg.b * a.max_pages + (c.k >> 1)]);
-    const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)c.seg.b * a.max_pages;
-    return bt[uniform(c.k >> 1)];
-  };
-  auto issue = [&](const Cursor& c, int slot) {
-    const int page = page_of(c);
-    if constexpr (FP8) {
-      issue_block_fp8(a.ckv8, a.scale8, a.kr8, page, c.k & 1, smem + slot * kStageBytes, block_hi(c), wave, lane);
-    } else {
-      issue_block_bf16(a.rows + (size_t)page * kPageBytes, c.k & 1, smem + slot * kBlockBytes, block_hi(c), wave,
-                       lane);
-    }
-  };
-  // The first piece of every sequence records where its partials start and
-  // how many pieces there are (1: finished here), for the merge kernel.
-  auto note_pieces = [&](const Segment& s) {
-    if (a.meta != nullptr && s.slot == s.slot0 && tid == 0) *(int2*)(a.meta + 2 * s.b) = make_int2(s.slot0, s.parts);
-  };
-
-  // First query: for up to two head groups it is copied into LDS like the
-  // blocks (into the one buffer the first three blocks leave free), so that
-  // waiting for it does not also wait for the blocks issued after it; with
-  // more head groups it is loaded into registers directly.  Either way the
-  // first three blocks are in flight meanwhile.
-  WaveState<NT, NQ> st;
-  // first K-step of the wave's query registers: 0 or 9 for the four waves
-  // that split the scores, 0 for a wave that only copies (it loads a query
-  // it never uses, and must not read past the head's 576 elements)
-  const int k0 = kKSplit && computes ? 9 * (wave >> 1) : 0;
-  static_assert(32 * (9 + NQ) <= kRow || !kKSplit, "split query registers stay inside the head's row");
-  static_assert(32 * NQ <= kRow, "query registers stay inside the head's row");
-  constexpr bool kQueryViaLds = HG <= 2;
-  uint8_t* const qlds = FP8 ? smem + kNBuf * kStageBytes : smem + (kNBuf - 1) * kBlockBytes;
-  static_assert(HG > 2 || 2 * 16 * kRowBytes <= kBlockBytes, "query staging space");
-  if constexpr (kQueryViaLds) {
-    issue_query_copy<HG>((const uint8_t*)qrow(cp.seg), a.H, qlds, wave, lane);
-  } else {
-    load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4, k0);
-  }
-  Cursor ld = cp;
-  int issued = 0;
-  // With the query staged through LDS, block 0 goes out with it and blocks
-  // 1 and 2 only once it has landed: all workgroups start at once, and the
-  // query and first block would otherwise queue behind 27 MB of later blocks.
-  constexpr int kFirst = kQueryViaLds ? 1 : kNBuf - 1;
-#pragma unroll
-  for (int j = 0; j < kFirst; ++j) {
-    if (ld.valid) {
-      issue(ld, j);
-      ++issued;
-      cursor_next(a, ld);
-    }
-  }
-  if constexpr (kQueryViaLds) {
-    wait_blocks<kCopyLo, kCopyHi>(issued, wave);  // the query copies, issued before the blocks, are done
-    __syncthreads();
-    // lane: head h0 + l%16, channels 32kk + 8g .. +7 of its row
-    const uint32_t qa = lds_addr(qlds) + (16 * hg + (lane & 15)) * kRowBytes + 16 * (lane >> 4);
-#pragma unroll
-    for (int kk = 0; kk < NQ; ++kk) st.q[kk] = __builtin_bit_cast(bf16x8, lds_read_b128_at(qa + 64 * (k0 + kk)));
-  } else {
-    consume_query(st.q);
-  }
-#pragma unroll
-  for (int j = kFirst; j < kNBuf - 1; ++j) {
-    if (ld.valid) {
-      issue(ld, j);
-      ++issued;
-      cursor_next(a, ld);
-    }
-  }
-  reset_state(st);
-  note_pieces(cp.seg);
-  for (int i = 0;; ++i) {
-    // wait for this wave's part of block i: the copies issued after it may stay in flight
-    wait_blocks<kCopyLo, kCopyHi>(issued - i - 1, wave);
-    __syncthreads();
-    uint8_t* buf;
-    if constexpr (FP8) {
-      dequant_block<kWaves * 64>(smem + (i % kNBuf) * kStageBytes, smem + kNBuf * kStageBytes, wave);
-      __syncthreads();
-      buf = smem + kNBuf * kStageBytes;
-    } else {
-      buf = smem + (i % kNBuf) * kBlockBytes;
-    }
-    // The copy of block i+3 goes into the buffer of block i-1, which every
-    // wave finished before the barrier.  bf16: a computing wave issues its
-    // copies one by one between its score products.
-    BlockCopies nb;
-    nb.n = 0;
-    if constexpr (!FP8) {
-      if (ld.valid)
-        nb = plan_block_bf16(a.rows + (size_t)page_of(ld) * kPageBytes, ld.k & 1,
-                             smem + ((i + kNBuf - 1) % kNBuf) * kBlockBytes, block_hi(ld), wave);
-    }
-    auto dma = [&](int t) {
-      if constexpr (!FP8) {
-        if (t < nb.n) issue_copy(nb, t);
+    auto qrow = [&](const Segment& s) { return (const bf16*)a.q + (size_t)s.b * a.H * kRow; };
+    auto block_hi = [&](const Cursor& c) { return min(c.seg.t1 - c.k * kBlock, kBlock); };
+    // block-table reads use a uniform index, so they are scalar loads that do
+    // not wait behind the copies in flight
+    auto page_of = [&](const Cursor& c) {
+      if (bt_local) return uniform(bt_lds[c.seg.b * a.max_pages + (c.k >> 1)]);
+      const int32_t* bt = a.prefill_T > 0 ? block_table : block_table + (size_t)c.seg.b * a.max_pages;
+      return bt[uniform(c.k >> 1)];
+    };
+    auto issue = [&](const Cursor& c, int slot) {
+      const int page = page_of(c);
+      if constexpr (FP8) {
+        issue_block_fp8(a.ckv8, a.scale8, a.kr8, page, c.k & 1, smem + slot * kStageBytes, block_hi(c), wave, lane);
+      } else {
+        issue_block_bf16(a.rows + (size_t)page * kPageBytes, c.k & 1, smem + slot * kBlockBytes, block_hi(c), wave,
+                         lane);
       }
     };
-    if (computes) {
-      // multi-token decode: query token t of the sequence sees keys up to
-      // L - q_len + t, so the last q_len - 1 - t keys are masked for it
-      int hi = block_hi(cp);
-      if (a.q_len > 1) {
-        const int head = min(h0 + (lane_id_fresh() & 15), a.H - 1);
-        hi = min(hi, cp.seg.L - (a.q_len - 1 - head / a.hs) - kBlock * cp.k);
-      }
-      if constexpr (kKSplit) {
-        block_compute_ksplit<NT>(st, lds_addr(buf), lds_addr(exch), wave, hi, lane, mt0, a.scale_log2, dma);
-      } else {
-        block_compute<NT>(st, lds_addr(buf), hi, lane, mt0, a.scale_log2, dma);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < kCopiesLo; ++t) dma(t);
-      if constexpr (kKSplit) __syncthreads();  // the score exchange of the computing waves
-    }
-    if (ld.valid) {
-      if constexpr (FP8) issue(ld, (i + kNBuf - 1) % kNBuf);
-      ++issued;
-      cursor_next(a, ld);
-    }
+    // The first piece of every sequence records where its partials start and
+    // how many pieces there are (1: finished here), for the merge kernel.
+    auto note_pieces = [&](const Segment& s) {
+      if (a.meta != nullptr && s.slot == s.slot0 && tid == 0) *(int2*)(a.meta + 2 * s.b) = make_int2(s.slot0, s.parts);
+    };
 
-    if (cp.k == (cp.seg.t1 - 1) / kBlock) {  // last block of this piece
-      const float l_tot = pair32_sum(pair16_sum(st.l));
-      if (computes) {
-        const Segment& sg = cp.seg;
-        const bool whole = sg.parts == 1;
-        float* zdst = whole ? a.z + (size_t)sg.b * a.H * kDc : a.zp + (size_t)sg.slot * a.H * kDc;
-        float* ldst = whole ? (a.lse ? a.lse + (size_t)sg.b * a.H : nullptr) : a.lsep + (size_t)sg.slot * a.H;
-        store_state(st, l_tot, zdst, ldst, h0, a.H, lane, mt0 * 16, cg == 0);
-      }
-      cursor_next(a, cp);
-      if (!cp.valid) break;
-      load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4, k0);
-      consume_query(st.q);
-      reset_state(st);
-      note_pieces(cp.seg);
+    // First query: for up to two head groups it is copied into LDS like the
+    // blocks (into the one buffer the first three blocks leave free), so that
+    // waiting for it does not also wait for the blocks issued after it; with
+    // more head groups it is loaded into registers directly.  Either way the
+    // first three blocks are in flight meanwhile.
+    WaveState<NT, NQ> st;
+    // first K-step of the wave's query registers: 0 or 9 for the four waves
+    // that split the scores, 0 for a wave that only copies (it loads a query
+    // it never uses, and must not read past the head's 576 elements)
+    const int k0 = kKSplit && computes ? 9 * (wave >> 1) : 0;
+    static_assert(32 * (9 + NQ) <= kRow || !kKSplit, "split query registers stay inside the head's row");
+    static_assert(32 * NQ <= kRow, "query registers stay inside the head's row");
+    constexpr bool kQueryViaLds = HG <= 2;
+    uint8_t* const qlds = FP8 ? smem + kNBuf * kStageBytes : smem + (kNBuf - 1) * kBlockBytes;
+    static_assert(HG > 2 || 2 * 16 * kRowBytes <= kBlockBytes, "query staging space");
+    if constexpr (kQueryViaLds) {
+      issue_query_copy<HG>((const uint8_t*)qrow(cp.seg), a.H, qlds, wave, lane);
     } else {
-      cursor_next(a, cp);
+      load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4, k0);
     }
-  }
+    Cursor ld = cp;
+    int issued = 0;
+    // With the query staged through LDS, block 0 goes out with it and blocks
+    // 1 and 2 only once it has landed: all workgroups start at once, and the
+    // query and first block would otherwise queue behind 27 MB of later blocks.
+    constexpr int kFirst = kQueryViaLds ? 1 : kNBuf - 1;
+  #pragma unroll
+    for (int j = 0; j < kFirst; ++j) {
+      if (ld.valid) {
+        issue(ld, j);
+        ++issued;
+        cursor_next(a, ld);
+      }
+    }
+    if constexpr (kQueryViaLds) {
+      wait_blocks<kCopyLo, kCopyHi>(issued, wave);  // the query copies, issued before the blocks, are done
+      __syncthreads();
+      // lane: head h0 + l%16, channels 32kk + 8g .. +7 of its row
+      const uint32_t qa = lds_addr(qlds) + (16 * hg + (lane & 15)) * kRowBytes + 16 * (lane >> 4);
+  #pragma unroll
+      for (int kk = 0; kk < NQ; ++kk) st.q[kk] = __builtin_bit_cast(bf16x8, lds_read_b128_at(qa + 64 * (k0 + kk)));
+    } else {
+      consume_query(st.q);
+    }
+  #pragma unroll
+    for (int j = kFirst; j < kNBuf - 1; ++j) {
+      if (ld.valid) {
+        issue(ld, j);
+        ++issued;
+        cursor_next(a, ld);
+      }
+    }
+    reset_state(st);
+    note_pieces(cp.seg);
+    for (int i = 0;; ++i) {
+      // wait for this wave's part of block i: the copies issued after it may stay in flight
+      wait_blocks<kCopyLo, kCopyHi>(issued - i - 1, wave);
+      __syncthreads();
+      uint8_t* buf;
+      if constexpr (FP8) {
+        dequant_block<kWaves * 64>(smem + (i % kNBuf) * kStageBytes, smem + kNBuf * kStageBytes, wave);
+        __syncthreads();
+        buf = smem + kNBuf * kStageBytes;
+      } else {
+        buf = smem + (i % kNBuf) * kBlockBytes;
+      }
+      // The copy of block i+3 goes into the buffer of block i-1, which every
+      // wave finished before the barrier.  bf16: a computing wave issues its
+      // copies one by one between its score products.
+      BlockCopies nb;
+      nb.n = 0;
+      if constexpr (!FP8) {
+        if (ld.valid)
+          nb = plan_block_bf16(a.rows + (size_t)page_of(ld) * kPageBytes, ld.k & 1,
+                               smem + ((i + kNBuf - 1) % kNBuf) * kBlockBytes, block_hi(ld), wave);
+      }
+      auto dma = [&](int t) {
+        if constexpr (!FP8) {
+          if (t < nb.n) issue_copy(nb, t);
+        }
+      };
+      if (computes) {
+        // multi-token decode: query token t of the sequence sees keys up to
+        // L - q_len + t, so the last q_len - 1 - t keys are masked for it
+        int hi = block_hi(cp);
+        if (a.q_len > 1) {
+          const int head = min(h0 + (lane_id_fresh() & 15), a.H - 1);
+          hi = min(hi, cp.seg.L - (a.q_len - 1 - head / a.hs) - kBlock * cp.k);
+        }
+        if constexpr (kKSplit) {
+          block_compute_ksplit<NT>(st, lds_addr(buf), lds_addr(exch), wave, hi, lane, mt0, a.scale_log2, dma);
+        } else {
+          block_compute<NT>(st, lds_addr(buf), hi, lane, mt0, a.scale_log2, dma);
+        }
+      } else {
+  #pragma unroll
+        for (int t = 0; t < kCopiesLo; ++t) dma(t);
+        if constexpr (kKSplit) __syncthreads();  // the score exchange of the computing waves
+      }
+      if (ld.valid) {
+        if constexpr (FP8) issue(ld, (i + kNBuf - 1) % kNBuf);
+        ++issued;
+        cursor_next(a, ld);
+      }
+
+      if (cp.k == (cp.seg.t1 - 1) / kBlock) {  // last block of this piece
+        const float l_tot = pair32_sum(pair16_sum(st.l));
+        if (computes) {
+          const Segment& sg = cp.seg;
+          const bool whole = sg.parts == 1;
+          float* zdst = whole ? a.z + (size_t)sg.b * a.H * kDc : a.zp + (size_t)sg.slot * a.H * kDc;
+          float* ldst = whole ? (a.lse ? a.lse + (size_t)sg.b * a.H : nullptr) : a.lsep + (size_t)sg.slot * a.H;
+          if (a.tickets != nullptr) store_state<true>(st, l_tot, zdst, ldst, h0, a.H, lane, mt0 * 16, cg == 0);
+          else store_state(st, l_tot, zdst, ldst, h0, a.H, lane, mt0 * 16, cg == 0);
+        }
+        if (pub1 < pub0) pub0 = cp.seg.b;
+        pub1 = cp.seg.b;
+        cursor_next(a, cp);
+        if (!cp.valid) break;
+        load_query(st.q, qrow(cp.seg), a.H, h0 + (lane & 15), lane >> 4, k0);
+        consume_query(st.q);
+        reset_state(st);
+        note_pieces(cp.seg);
+      } else {
+        cursor_next(a, cp);
+      }
+    }
+  }();
+  merge_jobs();
 }
 
 // ---------------------------------------------------------------------------

@@ -9,6 +9,7 @@
 namespace mla {
 
 constexpr int kMaxSchedB = 512;  // sequences a balanced (auto) split can schedule
+constexpr int kTicketInts = 64;  // 256 bytes of counters per sequence (decode + merge in one launch)
 constexpr int kBtLds = 2048;     // block-table entries a decode workgroup keeps in LDS
 constexpr int kKindF32 = 0;
 constexpr int kKindBf16 = 1;
@@ -37,6 +38,14 @@ struct DecodeArgs {
   float* lsep;                 // partials [slots][H]
   int32_t* meta;               // [B][2] first partial slot and piece count of each
                                // split sequence (written by decode, read by merge)
+  // Merge and value up-projection inside the decode launch (tickets != NULL;
+  // one workgroup per CU at most, so that every unit is resident at once):
+  int32_t* tickets;            // [B][kTicketInts]: piece counter at 0, job counter at
+                               // kTicketInts / 2 (separate 128-byte lines); zero
+                               // before the launch and left zero by it
+  const void* w_uv;            // [hs][128][512] bf16
+  void* o;                     // [B][H][128] out
+  int32_t o_bf16;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t s);

@@ -79,38 +79,27 @@ __global__ void __launch_bounds__(128) merge_kernel(DecodeArgs a) {
 // overlap.  Every sequence re-reads W^UV_h (from L2), so this form is only
 // used for up to kFusedMaxB sequences.
 // The pieces of one sequence, NB per batch (one round trip each), folded
-// into a running maximum, weight sum and this thread's two channels of z.
+// into a running maximum, weight sum and this thread's two channels of z
+// (merge_batch).
 // The batch is 16 pieces for sequences of at most 16 and 32 otherwise, so
 // that up to 32 pieces cost one round trip; past the last piece a batch
 // re-loads that piece.
 template <int NB>
 __device__ __forceinline__ void fused_merge_pieces(const DecodeArgs& a, int slot0, int n, int head, int tid,
-                                                   float& mx, float& wsum, float2& acc) {
+                                                   float& mx, float& wsum, float (&acc)[2]) {
   for (int c0 = 0; c0 < n; c0 += NB) {
     float lv[NB];
-    float2 zv[NB];
+    float zv[NB][2];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int c = min(c0 + u, n - 1);  // every slot loaded holds a piece of this sequence
       const size_t sl = (size_t)(slot0 + c) * a.H + head;
       lv[u] = c0 + u < n ? a.lsep[sl] : -INFINITY;
-      zv[u] = *(const float2*)(a.zp + sl * kDc + 2 * tid);
+      const float2 v = *(const float2*)(a.zp + sl * kDc + 2 * tid);
+      zv[u][0] = v.x;
+      zv[u][1] = v.y;
     }
-    float mb = mx;
-#pragma unroll
-    for (int u = 0; u < NB; ++u) mb = fmaxf(mb, lv[u]);
-    const float alpha = __expf(mx - mb);  // mx = -inf on the first batch: alpha = 0
-    wsum *= alpha;
-    acc.x *= alpha;
-    acc.y *= alpha;
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const float w = __expf(lv[u] - mb);  // 0 for the padding entries
-      wsum += w;
-      acc.x += w * zv[u].x;
-      acc.y += w * zv[u].y;
-    }
-    mx = mb;
+    merge_batch(lv, zv, mx, wsum, acc);
   }
 }
 
@@ -138,11 +127,11 @@ __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeUpArgs m) {
     zs[2 * tid + 1] = v.y;
   } else {
     float mx = -INFINITY, wsum = 0.f;
-    float2 acc = make_float2(0.f, 0.f);
+    float acc[2] = {0.f, 0.f};
     if (n <= 16) fused_merge_pieces<16>(a, slot0, n, head, tid, mx, wsum, acc);
     else fused_merge_pieces<32>(a, slot0, n, head, tid, mx, wsum, acc);
     const float inv = 1.0f / wsum;
-    const float2 z2 = make_float2(acc.x * inv, acc.y * inv);
+    const float2 z2 = make_float2(acc[0] * inv, acc[1] * inv);
     zs[2 * tid] = z2.x;
     zs[2 * tid + 1] = z2.y;
     *(float2*)(zrow + 2 * tid) = z2;
@@ -153,38 +142,8 @@ __global__ void __launch_bounds__(256) merge_upproj_kernel(MergeUpArgs m) {
   const float4 z0 = *(const float4*)(zs + 8 * lane), z1 = *(const float4*)(zs + 8 * lane + 4);
   float v[32];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const uint32_t w0 = (uint32_t)wv[r][0], w1 = (uint32_t)wv[r][1], w2 = (uint32_t)wv[r][2], w3 = (uint32_t)wv[r][3];
-    float t = __uint_as_float(w0 << 16) * z0.x;
-    t += __uint_as_float(w0 & 0xffff0000u) * z0.y;
-    t += __uint_as_float(w1 << 16) * z0.z;
-    t += __uint_as_float(w1 & 0xffff0000u) * z0.w;
-    t += __uint_as_float(w2 << 16) * z1.x;
-    t += __uint_as_float(w2 & 0xffff0000u) * z1.y;
-    t += __uint_as_float(w3 << 16) * z1.z;
-    t += __uint_as_float(w3 & 0xffff0000u) * z1.w;
-    v[r] = t;
-  }
-  // Butterfly: at distance 2^k (k = 5 .. 1) each lane keeps the half of its
-  // rows selected by lane bit k and adds its partner's copy of that half, so
-  // lane l ends with row l >> 1 summed over the lanes that differ in bits
-  // 5..1; the final step at distance 1 adds the other half of the wave.
-#pragma unroll
-  for (int k = 5; k >= 1; --k) {
-    const int half = 1 << (k - 1);
-    const bool upper = (lane >> k) & 1;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      // opaque copies: a select between two array elements would otherwise be
-      // folded into a run-time array index, lowered as a compare chain
-      float lo = v[i], hi = v[i + half];
-      asm volatile("" : "+v"(lo), "+v"(hi));
-      const float keep = upper ? hi : lo;
-      const float send = upper ? lo : hi;
-      v[i] = keep + __shfl_xor(send, 1 << k);
-    }
-  }
-  const float o_val = v[0] + __shfl_xor(v[0], 1);
+  for (int r = 0; r < 32; ++r) v[r] = dot8_bf16(wv[r], z0, z1);
+  const float o_val = wave_rows_sum(v, lane);  // row lane >> 1 of the wave's 32
   if ((lane & 1) == 0) {
     const size_t oi = ((size_t)b * a.H + head) * kDv + 32 * wave + (lane >> 1);
     if (m.o_bf16) ((bf16*)m.o)[oi] = f2bf(o_val);
