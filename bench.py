@@ -549,6 +549,12 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
 
     kern_ms = _timed_batches(decode_only, K, R)
     kern_avg_ms = kern_ms[1]  # median of the three batches
+    # in the one-launch form, the same kernel without the merge jobs as well
+    # (mla_decode_partial: decode and piece stores only)
+    alone_ms = None
+    if one_launch:
+        alone_ms = _timed_batches(lambda r: mla.decode_partial(q_abs, reps[r][0], dd.block_table, dd.seq_lens, ws, z,
+                                                               lse, num_splits=splits), K, R)[1]
     parts = None
     if QL == 1 and not LAYER:
         parts = {
@@ -592,6 +598,7 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
     q_bytes = B * QL * H * 576 * (4 if wl.dtype == "f32" else 2)
     out_bytes = B * QL * H * (512 + 1) * 4
     alg_bytes = total * tok_bytes + q_bytes + out_bytes
+    decode_alg_bytes = alg_bytes
     # query token t of a sequence of L cached tokens sees L - q_len + t + 1 of them
     seen = int(sum(QL * int(L) - QL * (QL - 1) // 2 for L in wl.lens))
     alg_flops = seen * H * FLOP_PER_TOKEN_HEAD
@@ -632,6 +639,9 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
         "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
         "hbm_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
         "tflops": tflops, "mfma_peak_tflops": mfma_peak, "mfma_frac": tflops / mfma_peak,
+        "decode_without_merge": None if alone_ms is None else {
+            "us": alone_ms * 1e3, "alg_bytes": decode_alg_bytes,
+            "hbm_frac": decode_alg_bytes / (alone_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         # matrix-core counters of the same kernel (stored run on the current sources)
         "mfma_counters": None if mc is None else {
             "issued_tflops": mc["issued_tflops"], "busy_frac": mc["busy_frac"],

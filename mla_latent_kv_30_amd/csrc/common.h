@@ -117,6 +117,33 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t ld
                : "memory");
 }
 
+// The same copies with the non-temporal hint (nt) when NT: for rows that are
+// read once, so that they do not displace reused data from the caches.
+template <bool NT>
+__device__ __forceinline__ void lds_dma4_hint(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, uint32_t voff,
+                                              uint32_t soff) {
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen nt lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rs), "s"(soff)
+                 : "memory");
+  } else {
+    lds_dma4(rs, lds_base, voff, soff);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void lds_dma16_hint(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, uint32_t voff,
+                                               uint32_t soff) {
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rs), "s"(soff)
+                 : "memory");
+  } else {
+    lds_dma16(rs, lds_base, voff, soff);
+  }
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

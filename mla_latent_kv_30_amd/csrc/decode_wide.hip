@@ -383,15 +383,16 @@ __device__ __forceinline__ WideFp8Copies plan_block_fp8w(const DecodeArgs& a, in
 // of rows 8w .. 8w+15 with 4-byte copies (the last 8 of them also land, with
 // the same values, in the next wave's; wave 3's extra rows are past the
 // block and arrive as zeros in the pad).
+template <bool NT>
 __device__ __forceinline__ void issue_copy_fp8w(const WideFp8Copies& c, int t, int w, uint32_t code_voff) {
   const int lane = lane_id_fresh();
   if (t < 4) {
     const uint32_t off = (uint32_t)(4 * w + t) * kCopyBytes;
-    lds_dma16(c.rc, c.lb + kW8Codes + off, code_voff, off);
+    lds_dma16_hint<NT>(c.rc, c.lb + kW8Codes + off, code_voff, off);
   } else if (t == 4) {
-    lds_dma16(c.rk, c.lb + kW8Kr + w * kCopyBytes, (uint32_t)(16 * lane), w * kCopyBytes);
+    lds_dma16_hint<NT>(c.rk, c.lb + kW8Kr + w * kCopyBytes, (uint32_t)(16 * lane), w * kCopyBytes);
   } else if (t == 5) {
-    lds_dma4(c.rs, c.lb + kW8Scales + w * 128, (uint32_t)(4 * lane), w * 128);
+    lds_dma4_hint<NT>(c.rs, c.lb + kW8Scales + w * 128, (uint32_t)(4 * lane), w * 128);
   }
 }
 constexpr int kW8Copies = 6;
@@ -584,7 +585,10 @@ __device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const 
   }
 }
 
-template <bool FP8>
+// NT: the copies carry the non-temporal hint (decode streams every row
+// once; prefill re-reads the same keys for every query row and keeps them
+// cached).
+template <bool FP8, bool NT>
 __global__ void __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   // bf16: four block buffers.  fp8: three bf16 block buffers and two
@@ -660,9 +664,9 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   }
   auto issue_block = [&](const auto& nbk, int t) {
     if constexpr (FP8) {
-      if (t < kW8Copies) issue_copy_fp8w(nbk, t, wave, code_voff);
+      if (t < kW8Copies) issue_copy_fp8w<NT>(nbk, t, wave, code_voff);
     } else {
-      lds_dma16(nbk.rs, nbk.lb + kCopyBytes * t, co.vo[t], nbk.g * kGroupBytes);
+      lds_dma16_hint<NT>(nbk.rs, nbk.lb + kCopyBytes * t, co.vo[t], nbk.g * kGroupBytes);
     }
   };
   load_query_wide(Q, qrow(cp.seg), a.H, h0);
@@ -832,11 +836,12 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 }  // namespace
 
 hipError_t launch_decode_wide(const DecodeArgs& a, bool fp8, hipStream_t s) {
-  if (fp8) {
-    hipLaunchKernelGGL((decode_wide_kernel<true>), dim3(a.units), dim3(kWThreads), 0, s, a, a.block_table);
-  } else {
-    hipLaunchKernelGGL((decode_wide_kernel<false>), dim3(a.units), dim3(kWThreads), 0, s, a, a.block_table);
-  }
+  const dim3 grid(a.units), blk(kWThreads);
+  const bool nt = a.prefill_T == 0;
+  if (fp8 && nt) hipLaunchKernelGGL((decode_wide_kernel<true, true>), grid, blk, 0, s, a, a.block_table);
+  else if (fp8) hipLaunchKernelGGL((decode_wide_kernel<true, false>), grid, blk, 0, s, a, a.block_table);
+  else if (nt) hipLaunchKernelGGL((decode_wide_kernel<false, true>), grid, blk, 0, s, a, a.block_table);
+  else hipLaunchKernelGGL((decode_wide_kernel<false, false>), grid, blk, 0, s, a, a.block_table);
   return hipGetLastError();
 }
 
