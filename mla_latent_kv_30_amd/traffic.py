@@ -90,9 +90,18 @@ def per_dispatch(run_dir: str, counter: str, kernel_substr: str) -> list:
     return [vals[k] for k in sorted(vals)]
 
 
-def summarize(fetch_dir: str, write_dir: str, kernel: str, workload: str) -> dict:
+def _largest(vals: list) -> list:
+    """The dispatches within 1% of the largest (one kernel run in two forms:
+    keep the form that moves more bytes)."""
+    top = max(vals) if vals else 0.0
+    return [v for v in vals if v >= 0.99 * top]
+
+
+def summarize(fetch_dir: str, write_dir: str, kernel: str, workload: str, largest: bool = False) -> dict:
     fk = per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
     wk = per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    if largest:
+        fk, wk = _largest(fk), _largest(wk)
     fc = per_dispatch(fetch_dir, "FETCH_SIZE", COPY_KERNEL)
     wc = per_dispatch(write_dir, "WRITE_SIZE", COPY_KERNEL)
     if not fk or not wk:
@@ -203,6 +212,7 @@ def main():
     s.add_argument("--kernel", required=True)
     s.add_argument("--workload", required=True)
     s.add_argument("--command", default="", help="the profiled command, recorded in the summary")
+    s.add_argument("--largest", action="store_true", help="only the dispatches that move the most bytes")
     s.add_argument("--out", required=True)
     mf = sub.add_parser("mfma")
     mf.add_argument("--dir", required=True)
@@ -237,7 +247,7 @@ def main():
             json.dump(out, f, indent=1)
         print(json.dumps(out))
         return
-    out = summarize(args.fetch, args.write, args.kernel, args.workload)
+    out = summarize(args.fetch, args.write, args.kernel, args.workload, largest=args.largest)
     out["command"] = args.command
     with open(args.out, "w") as f:
         json.dump(out, f, indent=1)
