@@ -291,6 +291,33 @@ def test_upproj_bf16_and_f32():
         assert np.abs(of.cpu().numpy() - ref).max() <= 1e-5
 
 
+@pytest.mark.parametrize("N", [1, 16, 31, 32, 33, 64, 100, 128, 129, 300])
+def test_absorb_and_upproj_row_counts(N):
+    """mla_absorb_q and mla_upproj_v (bf16) at row counts on both sides of
+    the few-rows kernels' limit (128 rows, in groups of 32) and of their
+    row groups, against the oracle's absorption and RoPE and an fp64
+    product.  Rows and heads are ragged against the tiles (H = 24)."""
+    _note(f"case absorb/upproj N={N}")
+    g = torch.Generator().manual_seed(100 + N)
+    H = 24
+    q_c = torch.randn(N, H, 128, generator=g).to(torch.bfloat16)
+    q_r = torch.randn(N, H, 64, generator=g).to(torch.bfloat16)
+    pos = torch.randint(0, 40000, (N,), generator=g, dtype=torch.int32)
+    w_uk = (torch.randn(H, 128, 512, generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    q_abs = mla.absorb_q(q_c.to(DEV), q_r.to(DEV), pos.to(DEV), w_uk.to(DEV))
+    z = torch.randn(N, H, 512, generator=g)
+    w_uv = (torch.randn(H, 128, 512, generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    o = mla.upproj_v(z.to(DEV), w_uv.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qa = q_abs.float().cpu().numpy()
+    ref_c = orc.absorb_query(q_c.double().numpy(), w_uk.double().numpy())
+    ref_r = orc.rope(q_r.double().numpy(), pos.numpy()[:, None])
+    assert _rel(qa[..., :512], ref_c) <= 1e-2
+    assert _rel(qa[..., 512:], ref_r) <= 1e-2
+    ref_o = np.einsum("hdc,nhc->nhd", w_uv.double().numpy(), z.double().numpy())
+    assert _rel(o.cpu().numpy(), ref_o) <= 1e-2
+
+
 @pytest.mark.parametrize("H,lens,S", [
     (16, [1, 17, 64, 65, 130, 1000, 2500], 0),   # balanced split: pieces merged, some sequences whole
     (16, [300, 1000], 3),                        # uniform split
