@@ -176,6 +176,74 @@ __global__ void __launch_bounds__(256) upproj_bf16_small_kernel(UpprojArgs a) {
   }
 }
 
+// Mid-sized row counts (33 .. 256 rows, the 64 tokens of a 64-sequence
+// decode step): workgroup = (head, 32 query rows), wave w = output rows
+// d = 32w .. 32w+31, one 32x32 tile over the 512 channels in 32 steps of 16
+// on 32x32x16 matrix cores.  A launch has H * ceil(N / 32) workgroups of four
+// busy waves (the 64x128 wave tile of upproj_bf16_kernel leaves three of four
+// waves idle and a quarter of the CUs busy at such N).  The W rows of a wave
+// (32 KB) are its own; the z rows are shared by the four waves through L2.
+// Loads run eight steps ahead of the products in two register sets.
+constexpr int kUpMidMaxN = 256;
+
+struct UpMidChunk {
+  int4v w[4];       // W[32w + l%32][c .. c+7] for the chunk's four steps
+  float4 z[4][2];   // z[n0 + l%32][c .. c+7]
+};
+
+__global__ void __launch_bounds__(256) upproj_bf16_mid_kernel(UpprojArgs a) {
+  const int h = blockIdx.x, n0 = 32 * blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int n = n0 + (lane & 31);
+  const bool nok = n < a.N;
+  // a row past N reads the workgroup's first row: it only feeds its own
+  // output column, which is not stored
+  const float* zr = a.z + ((size_t)(nok ? n : n0) * a.H + h) * kDc + 8 * g;
+  const bf16* wr = (const bf16*)a.w_uv + ((size_t)h * kDv + 32 * wave + (lane & 31)) * kDc + 8 * g;
+  auto load = [&](UpMidChunk& ch, int k0) {  // steps k0 .. k0+3 (channels 16 k0 ..)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 16 * (k0 + s);
+      ch.w[s] = *(const int4v*)(wr + c);
+      ch.z[s][0] = *(const float4*)(zr + c);
+      ch.z[s][1] = *(const float4*)(zr + c + 4);
+    }
+  };
+  floatx16 acc = floatx16{};
+  auto compute = [&](const UpMidChunk& ch) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float4 u0 = ch.z[s][0], u1 = ch.z[s][1];
+      const bf16x8 bz = {f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
+                         f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
+      acc = mfma32(__builtin_bit_cast(bf16x8, ch.w[s]), bz, acc);
+    }
+  };
+  UpMidChunk ca, cb;
+  load(ca, 0);
+  load(cb, 4);
+  for (int k0 = 0; k0 < kDc / 16; k0 += 8) {
+    compute(ca);
+    if (k0 + 8 < kDc / 16) load(ca, k0 + 8);
+    compute(cb);
+    if (k0 + 12 < kDc / 16) load(cb, k0 + 12);
+  }
+  // C layout: column = query row n0 + l%32, rows d = 32w + 8(r/4) + 4g + r%4
+  if (!nok) return;
+  const size_t base = ((size_t)n * a.H + h) * kDv + 32 * wave;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int d = 8 * q4 + 4 * g;
+    if (a.o_bf16) {
+      *(bf16x4*)((bf16*)a.o + base + d) =
+          bf16x4{f2bf(acc[4 * q4]), f2bf(acc[4 * q4 + 1]), f2bf(acc[4 * q4 + 2]), f2bf(acc[4 * q4 + 3])};
+    } else {
+      *(float4*)((float*)a.o + base + d) = make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+    }
+  }
+}
+
 // fp32 weights: one workgroup per (row, head), z in LDS, one thread per d
 // with 2 threads sharing a row of W (halves of c), exact fp32 FMA chains.
 __global__ void __launch_bounds__(256) upproj_f32_kernel(UpprojArgs a) {
@@ -204,6 +272,8 @@ hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s) {
     hipLaunchKernelGGL(upproj_f32_kernel, dim3(a.N * a.H), dim3(256), 0, s, a);
   } else if (a.N <= kUpSmallMaxN) {
     hipLaunchKernelGGL(upproj_bf16_small_kernel, dim3(a.H, kDv / 16), dim3(256), 0, s, a);
+  } else if (a.N <= kUpMidMaxN) {
+    hipLaunchKernelGGL(upproj_bf16_mid_kernel, dim3(a.H, (a.N + 31) / 32), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(upproj_bf16_kernel, dim3(a.H, (a.N + 255) / 256), dim3(256), 0, s, a);
   }
