@@ -15,6 +15,8 @@ constexpr int kAbsRowsPerWave = 32;
 constexpr int kAbsRowsPerBlock = 4 * kAbsRowsPerWave;   // 128 query tokens per workgroup
 constexpr int kAbsCols = 128;                           // c-slice of W per workgroup
 constexpr int kAbsLdsStride = kAbsCols * 2 + 32;        // padded row stride (bytes): rows 8 banks apart
+constexpr int kAbsOutStride = kAbsCols * 2 + 8;         // output staging row stride (bytes)
+static_assert(4 * kAbsRowsPerWave * kAbsOutStride <= kDn * kAbsLdsStride, "output staging fits the W slice's LDS");
 
 // grid: (H * 4 c-quarters, ceil(N / 128)); 4 waves, each 32 query rows x 128 c.
 // Every global load of a workgroup (its W slice, the q_c operand of each
@@ -76,36 +78,50 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a) {
       *(bf16x2*)out = bf16x2{f2bf(x0 * c - x1 * sn), f2bf(x0 * sn + x1 * c)};
     }
   }
-  if (n0 >= a.N) return;
   // A operand: W^T (m = c, k = d) by transposing reads: 16-lane group G owns
   // columns 16*(G%2) .. +15 of the 32-wide tile and rows d0 + 4*(lane%16 / 4)
+  const bool has_rows = n0 < a.N;
   const int dsub = (lane & 15) >> 2;
   const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   floatx16 acc[4];
+  if (has_rows) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt] = floatx16{};
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt] = floatx16{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int d0 = 16 * kk + 8 * g + dsub;
-      const uint8_t* p0 = w_lds + d0 * kAbsLdsStride + (32 * mt + cl) * 2;
-      bf16x4 lo = lds_read_tr16(p0);
-      bf16x4 hi = lds_read_tr16(p0 + 4 * kAbsLdsStride);
-      bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[mt] = mfma32(av, qb[kk], acc[mt]);
+      for (int kk = 0; kk < 8; ++kk) {
+        const int d0 = 16 * kk + 8 * g + dsub;
+        const uint8_t* p0 = w_lds + d0 * kAbsLdsStride + (32 * mt + cl) * 2;
+        bf16x4 lo = lds_read_tr16(p0);
+        bf16x4 hi = lds_read_tr16(p0 + 4 * kAbsLdsStride);
+        bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[mt] = mfma32(av, qb[kk], acc[mt]);
+      }
     }
   }
-  // C layout: column = query row n0 + lane%32, rows c = 32mt + 8(r/4) + 4g + r%4
-  if (!nok) return;
-  bf16* out = (bf16*)a.q_abs + ((size_t)nrow * a.H + h) * kRow + cq * kAbsCols;
+  __syncthreads();  // every wave is done with the W slice: its LDS now stages the outputs
+  if (!has_rows) return;
+  // C layout: column = query row n0 + lane%32, rows c = 32mt + 8(r/4) + 4g + r%4.
+  // The wave's 32 rows x 128 channels go to its own part of the LDS (rows
+  // 264 bytes apart: a store instruction's 32 rows land 2 banks apart), and
+  // leave as 256-byte row slices, 16 bytes per lane and 4 rows per
+  // instruction, instead of 16-byte pieces of 32 rows per instruction.
+  uint8_t* const stage = w_lds + wave * (kAbsRowsPerWave * kAbsOutStride);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 v = {f2bf(acc[mt][4 * q4]), f2bf(acc[mt][4 * q4 + 1]), f2bf(acc[mt][4 * q4 + 2]),
                   f2bf(acc[mt][4 * q4 + 3])};
-      *(bf16x4*)(out + 32 * mt + 8 * q4 + 4 * g) = v;
+      *(bf16x4*)(stage + (lane & 31) * kAbsOutStride + (32 * mt + 8 * q4 + 4 * g) * 2) = v;
     }
+#pragma unroll
+  for (int i = 0; i < kAbsRowsPerWave / 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int4v v = *(const int4v*)(stage + r * kAbsOutStride + 16 * (lane & 15));
+    if (n0 + r < a.N)
+      *(int4v*)((bf16*)a.q_abs + ((size_t)(n0 + r) * a.H + h) * kRow + cq * kAbsCols + 8 * (lane & 15)) = v;
+  }
 }
 
 // Few query rows (decode, N <= 32): workgroup = (head, 64-channel slice of
