@@ -2,16 +2,17 @@
 """Throughput of absorbed-MLA decode on one MI355X, against its roofline.
 
 One step = the whole decode path for one batch: absorbed query
-(mla_absorb_q), attention over the paged latent cache (mla_decode_partial),
-and the split merge with the W_UV up-projection (mla_decode_merge_upproj:
-one launch for up to 32 sequences, else the merge and up-projection
-kernels).  Inputs are synthetic with the workload's
+(mla_absorb_q), then attention over the paged latent cache, the split merge
+and the W_UV up-projection (mla_decode_upproj: one launch for up to 64 heads
+and 32 sequences, else mla_decode_partial followed by the merge and
+up-projection kernels).  Inputs are synthetic with the workload's
 shapes and distributions and are resident in HBM before timing starts.  To
 keep the 256 MB last-level cache from serving repeated reads, the step
 rotates over enough replicas of its inputs (cache, weights, queries) to
-exceed 600 MB.  Consecutive steps are captured together in HIP graphs (as a
-model's layers share one graph per decode step), so that a graph launch is
-not charged to every step; --graph-steps 1 times one graph per step.
+exceed 600 MB.  Consecutive steps are captured together in HIP graphs of up
+to 10 steps (as a model's layers share one graph per decode step), so that a
+graph launch is not charged to every step; --graph-steps 1 times one graph
+per step.
 
 With --layer the step starts from hidden states instead: the query path
 (mla_q_project: c^Q, q^C, q^R), the new token's cache append
@@ -65,7 +66,7 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0: enough for 600 MB)")
     ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of as a HIP graph")
     ap.add_argument("--graph-steps", type=int, default=0,
-                    help="decode steps per HIP graph (0: the largest divisor of --steps up to the replica count; "
+                    help="decode steps per HIP graph (0: the largest divisor of --steps up to 10; "
                          "1: a graph per step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
@@ -503,7 +504,7 @@ def run_decode(args, wl, dev, steps, warmup, cpu_seconds):
                     with torch.cuda.graph(g, stream=side):
                         step(r)
                     graphs.append(g)
-            want = min(R, args.graph_steps) if args.graph_steps > 0 else R
+            want = args.graph_steps if args.graph_steps > 0 else 10
             G = max(d for d in range(1, want + 1) if K % d == 0)
             if G > 1:
                 with torch.cuda.stream(side):
