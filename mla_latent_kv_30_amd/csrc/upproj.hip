@@ -178,59 +178,85 @@ __global__ void __launch_bounds__(256) upproj_bf16_small_kernel(UpprojArgs a) {
 
 // Mid-sized row counts (33 .. 256 rows, the 64 tokens of a 64-sequence
 // decode step): workgroup = (head, 32 query rows), wave w = output rows
-// d = 32w .. 32w+31, one 32x32 tile over the 512 channels in 32 steps of 16
-// on 32x32x16 matrix cores.  A launch has H * ceil(N / 32) workgroups of four
-// busy waves (the 64x128 wave tile of upproj_bf16_kernel leaves three of four
-// waves idle and a quarter of the CUs busy at such N).  The W rows of a wave
-// (32 KB) are its own; the z rows are shared by the four waves through L2.
-// Loads run eight steps ahead of the products in two register sets.
+// d = 32w .. 32w+31, one 32x32 tile over the 512 channels on 32x32x16 matrix
+// cores.  A launch has H * ceil(N / 32) workgroups of four busy waves (the
+// 64x128 wave tile of upproj_bf16_kernel leaves three of four waves idle at
+// such N).  The contraction runs in four chunks of 128 channels: the
+// chunk's W^UV block (128 rows x 256 B) and z rows (32 x 512 B, rounded to
+// bf16) are loaded with whole rows per instruction (16 bytes per lane,
+// consecutive lanes along a row) and staged in LDS, from which the matrix
+// cores read their operands; the next chunk's loads are in flight while a
+// chunk is multiplied.  (Loading the operands straight in the matrix-core
+// layout touched 32 rows, so 32 cache lines, per load instruction, and ran
+// at 2.2 TB/s.)
 constexpr int kUpMidMaxN = 256;
+constexpr int kUpMidChunk = 128;                     // channels per chunk
+constexpr int kUpMidWStride = kUpMidChunk * 2 + 16;  // LDS row stride (bytes) of the W block
+constexpr int kUpMidZStride = kUpMidChunk * 2 + 16;  // and of the z rows (bf16)
 
-struct UpMidChunk {
-  int4v w[4];       // W[32w + l%32][c .. c+7] for the chunk's four steps
-  float4 z[4][2];   // z[n0 + l%32][c .. c+7]
+struct UpMidRegs {
+  int4v w[8];    // W rows (t + 256 i) / 16, 16 bytes at (t % 16)
+  float4 z[4];   // z rows (t + 256 i) / 32, 4 channels at 4 (t % 32)
 };
 
 __global__ void __launch_bounds__(256) upproj_bf16_mid_kernel(UpprojArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[kDv * kUpMidWStride];   // 34,816 B
+  __shared__ __attribute__((aligned(16))) uint8_t z_lds[32 * kUpMidZStride];    // 8,704 B
   const int h = blockIdx.x, n0 = 32 * blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5;
-  const int n = n0 + (lane & 31);
-  const bool nok = n < a.N;
-  // a row past N reads the workgroup's first row: it only feeds its own
-  // output column, which is not stored
-  const float* zr = a.z + ((size_t)(nok ? n : n0) * a.H + h) * kDc + 8 * g;
-  const bf16* wr = (const bf16*)a.w_uv + ((size_t)h * kDv + 32 * wave + (lane & 31)) * kDc + 8 * g;
-  auto load = [&](UpMidChunk& ch, int k0) {  // steps k0 .. k0+3 (channels 16 k0 ..)
+  const bf16* wh = (const bf16*)a.w_uv + (size_t)h * kDv * kDc;
+  auto load = [&](UpMidRegs& r, int c0) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 16 * (k0 + s);
-      ch.w[s] = *(const int4v*)(wr + c);
-      ch.z[s][0] = *(const float4*)(zr + c);
-      ch.z[s][1] = *(const float4*)(zr + c + 4);
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 4, ch = idx & 15;
+      r.w[i] = *(const int4v*)(wh + (size_t)row * kDc + c0 + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 5, q = idx & 31;
+      const int n = min(n0 + row, a.N - 1);  // a row past N repeats the last one; its column is not stored
+      r.z[i] = *(const float4*)(a.z + ((size_t)n * a.H + h) * kDc + c0 + 4 * q);
     }
   };
+  auto stage = [&](const UpMidRegs& r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 4, ch = idx & 15;
+      *(int4v*)(w_lds + row * kUpMidWStride + 16 * ch) = r.w[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 5, q = idx & 31;
+      const float4 u = r.z[i];
+      *(bf16x4*)(z_lds + row * kUpMidZStride + 8 * q) = bf16x4{f2bf(u.x), f2bf(u.y), f2bf(u.z), f2bf(u.w)};
+    }
+  };
+  // operands of step j (16 channels) of a chunk: A lane l = W row 32w + l%32,
+  // channels 16j + 8g .. +7; B lane l = z row l%32, the same channels
+  const uint8_t* wa = w_lds + (32 * wave + (lane & 31)) * kUpMidWStride + 16 * g;
+  const uint8_t* zb = z_lds + (lane & 31) * kUpMidZStride + 16 * g;
   floatx16 acc = floatx16{};
-  auto compute = [&](const UpMidChunk& ch) {
+  UpMidRegs ra, rb;
+  load(ra, 0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float4 u0 = ch.z[s][0], u1 = ch.z[s][1];
-      const bf16x8 bz = {f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
-                         f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
-      acc = mfma32(__builtin_bit_cast(bf16x8, ch.w[s]), bz, acc);
+  for (int k = 0; k < kDc / kUpMidChunk; ++k) {
+    UpMidRegs& cur = (k & 1) ? rb : ra;
+    UpMidRegs& nxt = (k & 1) ? ra : rb;
+    if (k > 0) __syncthreads();  // every wave is done with the previous chunk's LDS
+    stage(cur);
+    if (k + 1 < kDc / kUpMidChunk) load(nxt, kUpMidChunk * (k + 1));
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kUpMidChunk / 16; ++j) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, *(const int4v*)(wa + 32 * j));
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const int4v*)(zb + 32 * j));
+      acc = mfma32(av, bv, acc);
     }
-  };
-  UpMidChunk ca, cb;
-  load(ca, 0);
-  load(cb, 4);
-  for (int k0 = 0; k0 < kDc / 16; k0 += 8) {
-    compute(ca);
-    if (k0 + 8 < kDc / 16) load(ca, k0 + 8);
-    compute(cb);
-    if (k0 + 12 < kDc / 16) load(cb, k0 + 12);
   }
   // C layout: column = query row n0 + l%32, rows d = 32w + 8(r/4) + 4g + r%4
-  if (!nok) return;
+  const int n = n0 + (lane & 31);
+  if (n >= a.N) return;
   const size_t base = ((size_t)n * a.H + h) * kDv + 32 * wave;
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
