@@ -7,105 +7,6 @@
 
 namespace mla {
 
-// bf16 weights: o^T[d, n] = sum_c W[d, c] z^T[c, n] on 32x32x16 matrix cores.
-// Workgroup = (head, 256 query rows); wave = 64 rows (2 column tiles) x all
-// 128 d (4 row tiles).  z is rounded to bf16 on load; accumulation is fp32.
-// The contraction runs in chunks of two 16-wide steps whose 16 operand loads
-// are issued one chunk ahead, so memory latency overlaps the products.
-struct UpChunk {
-  int4v w[2][4];     // [step][row tile]: W[32mt + l%32][c0 .. c0+7]
-  float4 z[2][2][2]; // [step][column tile][half]: z[row][c0 .. c0+7]
-};
-
-// A query row past N reads the workgroup's first row instead: it only feeds
-// its own output column, which is not stored.
-__device__ __forceinline__ void up_load(UpChunk& ch, const bf16* __restrict__ w, const float* const (&zr)[2], int k0,
-                                        int lane) {
-  const int g = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int c0 = 16 * (k0 + s) + 8 * g;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ch.w[s][mt] = *(const int4v*)(w + (size_t)(32 * mt + (lane & 31)) * kDc + c0);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float4* zp = (const float4*)(zr[nt] + c0);
-      ch.z[s][nt][0] = zp[0];
-      ch.z[s][nt][1] = zp[1];
-    }
-  }
-}
-
-__global__ void __launch_bounds__(256) upproj_bf16_kernel(UpprojArgs a) {
-  const int h = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.y * 256 + wave * 64;
-  if (n0 >= a.N) return;
-  const int g = lane >> 5;
-  const bf16* __restrict__ w = (const bf16*)a.w_uv + (size_t)h * kDv * kDc;
-  int nrow[2];
-  bool nok[2];
-  const float* zr[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    nrow[nt] = n0 + 32 * nt + (lane & 31);
-    nok[nt] = nrow[nt] < a.N;
-    zr[nt] = a.z + ((size_t)(nok[nt] ? nrow[nt] : n0) * a.H + h) * kDc;
-  }
-  floatx16 acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = floatx16{};
-  auto compute = [&](const UpChunk& ch) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 bz[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float4 u0 = ch.z[s][nt][0], u1 = ch.z[s][nt][1];
-        bz[nt] = bf16x8{f2bf(u0.x), f2bf(u0.y), f2bf(u0.z), f2bf(u0.w),
-                        f2bf(u1.x), f2bf(u1.y), f2bf(u1.z), f2bf(u1.w)};
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 aw = __builtin_bit_cast(bf16x8, ch.w[s][mt]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(aw, bz[nt], acc[mt][nt]);
-      }
-    }
-  };
-  // two chunk buffers used in turn (no copy between them, so a chunk's loads
-  // are only waited for when that chunk is consumed)
-  UpChunk ca, cb;
-  up_load(ca, w, zr, 0, lane);
-  for (int k0 = 0; k0 < kDc / 16; k0 += 4) {
-    up_load(cb, w, zr, k0 + 2, lane);
-    compute(ca);
-    if (k0 + 4 < kDc / 16) up_load(ca, w, zr, k0 + 4, lane);
-    compute(cb);
-  }
-  // C layout: column = query row, rows d = 32mt + 8(r/4) + 4g + r%4
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    if (!nok[nt]) continue;
-    const size_t base = ((size_t)nrow[nt] * a.H + h) * kDv;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * mt + 8 * q4 + 4 * g;
-        const floatx16& v = acc[mt][nt];
-        if (a.o_bf16) {
-          bf16x4 ov = {f2bf(v[4 * q4]), f2bf(v[4 * q4 + 1]), f2bf(v[4 * q4 + 2]), f2bf(v[4 * q4 + 3])};
-          *(bf16x4*)((bf16*)a.o + base + d) = ov;
-        } else {
-          *(float4*)((float*)a.o + base + d) = make_float4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
-        }
-      }
-  }
-}
-
 // Few query rows (decode, N <= 32): workgroup = (head, 16-row tile of d), so
 // a launch has H * 8 workgroups.  The 4 waves split the contraction over c
 // (128 each); every operand load of a lane is issued before the first
@@ -179,9 +80,8 @@ __global__ void __launch_bounds__(256) upproj_bf16_small_kernel(UpprojArgs a) {
 // Mid-sized row counts (33 .. 256 rows, the 64 tokens of a 64-sequence
 // decode step): workgroup = (head, 32 query rows), wave w = output rows
 // d = 32w .. 32w+31, one 32x32 tile over the 512 channels on 32x32x16 matrix
-// cores.  A launch has H * ceil(N / 32) workgroups of four busy waves (the
-// 64x128 wave tile of upproj_bf16_kernel leaves three of four waves idle at
-// such N).  The contraction runs in four chunks of 128 channels: the
+// cores.  A launch has H * ceil(N / 32) workgroups of four busy waves (a
+// 64-row wave tile would leave three of four waves idle at such N).  The contraction runs in four chunks of 128 channels: the
 // chunk's W^UV block (128 rows x 256 B) and z rows (32 x 512 B, rounded to
 // bf16) are loaded with whole rows per instruction (16 bytes per lane,
 // consecutive lanes along a row) and staged in LDS, from which the matrix
@@ -270,6 +170,111 @@ __global__ void __launch_bounds__(256) upproj_bf16_mid_kernel(UpprojArgs a) {
   }
 }
 
+// Many rows (prefill): workgroup = (head, 128 query rows), wave w = rows
+// 32w .. 32w+31 against all 128 outputs (four 32x32 tiles), so W^UV_h is
+// read once per 128 rows.  As in the mid-sized kernel, each chunk of 64
+// channels of W^UV_h (128 rows x 128 B) and of the z rows (128 x 256 B,
+// rounded to bf16) is loaded along whole rows, 16 bytes per lane, and
+// staged in LDS (two buffers: the next chunk is stored while the current
+// one is multiplied, one barrier per chunk; loads run two chunks ahead).
+constexpr int kUpBigChunk = 64;                      // channels per chunk
+constexpr int kUpBigStride = kUpBigChunk * 2 + 16;   // LDS row stride (bytes), W and z alike
+constexpr int kUpBigBuf = 2 * 128 * kUpBigStride;    // one chunk: W block + z rows
+
+struct UpBigRegs {
+  int4v w[4];    // W rows (t + 256 i) / 8, 16 bytes at (t % 8)
+  float4 z[8];   // z rows (t + 256 i) / 16, 4 channels at 4 (t % 16)
+};
+
+__global__ void __launch_bounds__(256) upproj_bf16_rows_kernel(UpprojArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kUpBigBuf];  // 73,728 B
+  const int h = blockIdx.x, n0 = 128 * blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5;
+  const bf16* wh = (const bf16*)a.w_uv + (size_t)h * kDv * kDc;
+  auto load = [&](UpBigRegs& r, int c0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+      r.w[i] = *(const int4v*)(wh + (size_t)row * kDc + c0 + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 4, q = idx & 15;
+      const int n = min(n0 + row, a.N - 1);  // a row past N repeats the last one; its column is not stored
+      r.z[i] = *(const float4*)(a.z + ((size_t)n * a.H + h) * kDc + c0 + 4 * q);
+    }
+  };
+  auto stage = [&](const UpBigRegs& r, uint8_t* buf) {
+    uint8_t* wl = buf;
+    uint8_t* zl = buf + 128 * kUpBigStride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+      *(int4v*)(wl + row * kUpBigStride + 16 * ch) = r.w[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 4, q = idx & 15;
+      const float4 u = r.z[i];
+      *(bf16x4*)(zl + row * kUpBigStride + 8 * q) = bf16x4{f2bf(u.x), f2bf(u.y), f2bf(u.z), f2bf(u.w)};
+    }
+  };
+  floatx16 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = floatx16{};
+  // chunk c is loaded into r[c & 1] two chunks before it is staged
+  UpBigRegs r[2];
+  load(r[0], 0);
+  load(r[1], kUpBigChunk);
+  stage(r[0], lds);
+  load(r[0], 2 * kUpBigChunk);
+  __syncthreads();
+  constexpr int kChunks = kDc / kUpBigChunk;  // 8
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const uint8_t* buf = lds + (k & 1) * kUpBigBuf;
+    // operands of step j (16 channels): A lane l = W row 32mt + l%32, B lane
+    // l = z row 32w + l%32, channels 16j + 8g .. +7
+    const uint8_t* wa = buf + (lane & 31) * kUpBigStride + 16 * g;
+    const uint8_t* zb = buf + 128 * kUpBigStride + (32 * wave + (lane & 31)) * kUpBigStride + 16 * g;
+#pragma unroll
+    for (int j = 0; j < kUpBigChunk / 16; ++j) {
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, *(const int4v*)(zb + 32 * j));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const int4v*)(wa + 32 * mt * kUpBigStride + 32 * j));
+        acc[mt] = mfma32(av, bv, acc[mt]);
+      }
+    }
+    if (k + 1 < kChunks) {
+      // chunk k+1 goes into the other buffer, last read in chunk k-1 (done
+      // by every wave before the previous barrier); its registers then take
+      // the loads of chunk k+3
+      stage(r[(k + 1) & 1], lds + ((k + 1) & 1) * kUpBigBuf);
+      if (k + 3 < kChunks) load(r[(k + 1) & 1], kUpBigChunk * (k + 3));
+      __syncthreads();
+    }
+  }
+  // C layout: column = query row n0 + 32w + l%32, rows d = 32mt + 8(r/4) + 4g + r%4
+  const int n = n0 + 32 * wave + (lane & 31);
+  if (n >= a.N) return;
+  const size_t base = ((size_t)n * a.H + h) * kDv;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * mt + 8 * q4 + 4 * g;
+      const floatx16& v = acc[mt];
+      if (a.o_bf16) {
+        *(bf16x4*)((bf16*)a.o + base + d) = bf16x4{f2bf(v[4 * q4]), f2bf(v[4 * q4 + 1]), f2bf(v[4 * q4 + 2]),
+                                                   f2bf(v[4 * q4 + 3])};
+      } else {
+        *(float4*)((float*)a.o + base + d) = make_float4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
+      }
+    }
+}
+
 // fp32 weights: one workgroup per (row, head), z in LDS, one thread per d
 // with 2 threads sharing a row of W (halves of c), exact fp32 FMA chains.
 __global__ void __launch_bounds__(256) upproj_f32_kernel(UpprojArgs a) {
@@ -301,7 +306,7 @@ hipError_t launch_upproj(const UpprojArgs& a, int w_kind, hipStream_t s) {
   } else if (a.N <= kUpMidMaxN) {
     hipLaunchKernelGGL(upproj_bf16_mid_kernel, dim3(a.H, (a.N + 31) / 32), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(upproj_bf16_kernel, dim3(a.H, (a.N + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(upproj_bf16_rows_kernel, dim3(a.H, (a.N + 127) / 128), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
