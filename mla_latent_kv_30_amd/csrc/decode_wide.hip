@@ -44,8 +44,11 @@ constexpr int kWNBuf = 4;                   // value(i-1), scores(i), blocks i+1
 constexpr int kWNBuf8 = 3;                  // fp8: value(i-1), scores(i), expansion of i+1
 constexpr int kWAhead = 2;                  // blocks copied ahead of the one being scored
 constexpr int kWCopies = kCopiesPerGroup;   // 9 copies per wave and block: wave w moves 8-row group w
-constexpr int kWDepth = 3;                  // operand reads in flight, in products
-static_assert(36 % kWDepth == 0, "the value reads issued under the last score products land in rb[0 .. D-1]");
+// Operand reads in flight, in products, and value products led with
+// operands read before the loop's barrier (wide_step): bf16 4 and 4; fp8 3
+// and none (its registers are full).
+constexpr int kWDepth = 4, kWLead = 4;
+constexpr int kWDepth8 = 3, kWLead8 = 0;
 
 static_assert(kWWaves * kGroupRows == kBlockRows, "four waves move the four 8-row groups of a block");
 
@@ -495,52 +498,92 @@ __device__ __forceinline__ float pair32_maximum(float v) {
 // One step of the unit's block stream: the scores of block i (buffer
 // `A.sa`), the online softmax of block i, and the value product of block
 // i-1 (buffer `A.va`) with its probabilities Pp.  Written as one straight
-// sequence of matrix-core products, each with the operand reads it needs
-// D products ahead, the page copies of block i+2 after every fourth score
-// product and the softmax arithmetic spread over the value products; the
-// scheduling barriers keep that order (left to itself the compiler gathered
-// the reads next to their products and the softmax ahead of them, and the
-// one wave on each SIMD then waited on every LDS round trip).
+// sequence of 68 matrix-core products, each with the operand read it needs
+// D products ahead (the ring rb), the page copies of block i+2 after every
+// fourth score product and the softmax arithmetic spread over the value
+// products; the scheduling barriers keep that order (left to itself the
+// compiler gathered the reads next to their products and the softmax ahead
+// of them, and the one wave on each SIMD then waited on every LDS round
+// trip).
+// Order of the products: value products 0 .. V0-1, the 36 score products,
+// value products V0 .. 31.  With V0 > 0 the operands of the first V0 come
+// from reads issued at the end of the previous step, before the loop's
+// barrier: they read block i-1, which has been in place since the step
+// before and is not overwritten before the next barrier, so right after the
+// barrier the matrix cores have work whose operands are already in
+// registers while the first score reads of the newly landed block are in
+// flight.  With V0 = 0 a step reads its first D operands itself.  Every
+// value tile still accumulates its products in the same order.
+// advance() moves A to the next step's buffers; it is called once the last
+// read of this step's operands is issued.
 // mask (uniform): tokens at or past hi (per lane) are excluded.  The
 // callbacks place the rest of a step's work between score products, where
 // it issues in their shadow instead of after them: copy(t) issues copy t of
-// a later block after products 3, 7, .., 35 (t = 0..8); book(t), t = 0, 1,
-// 2, the scalar bookkeeping (the next copy plan, the block cursors) after
-// products 1, 5 and 9; expand(kk) a slice of the fp8 expansion of the next
-// block after every product kk.
-template <class Copy, class Book, class Expand>
-__device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const WideAddr& A, const bf16x8 (&Pp)[2],
-                                          bf16x8 (&Pc)[2], WideSoftmax& st, float scale_log2, bool mask, int hi,
-                                          bool& rescale, float& alpha, Copy&& copy, Book&& book, Expand&& expand) {
-  constexpr int D = kWDepth;
-  bf16x8 rb[D];
+// a later block after score products 3, 7, .., 35 (t = 0..8); book(t), t =
+// 0, 1, 2, the scalar bookkeeping (the next copy plan, the block cursors)
+// after score products 1, 5 and 9; expand(kk) a slice of the fp8 expansion
+// of the next block after every score product kk.
+template <int D, int V0, class Copy, class Book, class Expand, class Advance>
+__device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, WideAddr& A, bf16x8 (&rb)[D],
+                                          const bf16x8 (&Pp)[2], bf16x8 (&Pc)[2], WideSoftmax& st,
+                                          float scale_log2, bool mask, int hi, bool& rescale, float& alpha,
+                                          Copy&& copy, Book&& book, Expand&& expand, Advance&& advance) {
+  constexpr int kP = 68;  // 36 score + 32 value products
+  static_assert(V0 == 0 || (V0 >= D && V0 <= 16 && kP % D == 0),
+                "lead value products: their reads fill the ring in order and never read the new block");
+  // the operand of product p of this step
+  auto operand = [&](int p) {
+    return p < V0 ? value_operand(A, p) : p < V0 + 36 ? score_operand(A, p - V0) : value_operand(A, p - 36);
+  };
+  if constexpr (V0 == 0) {
 #pragma unroll
-  for (int j = 0; j < D; ++j) rb[j] = score_operand(A, j);
+    for (int j = 0; j < D; ++j) rb[j] = operand(j);
+  }
+  // issue the read for product p + D into the slot product p frees
+  auto refill = [&](int p) {
+    if (p + D < kP) {
+      rb[p % D] = operand(p + D);
+    } else if constexpr (V0 > 0) {
+      rb[p % D] = value_operand(A, p + D - kP);  // the next step's lead products (A advanced)
+    }
+    if (p + D == kP - 1) advance();
+  };
+  // lead value products 0 .. V0-1, each issued before the read that
+  // refills its slot: the first waits only for operands read before the
+  // barrier (and the page load), not for a read of the new block
+#pragma unroll
+  for (int p = 0; p < V0; ++p) {
+    mfma32_acc(Z.z[p & 15], rb[p % D], Pp[0]);
+    refill(p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // scores
   floatx16 S = floatx16{};
-  // score phase: 36 products; the last D steps read the first value operands
 #pragma unroll
   for (int kk = 0; kk < 36; ++kk) {
-    const bf16x8 a = rb[kk % D];
-    rb[kk % D] = kk + D < 36 ? score_operand(A, kk + D) : value_operand(A, kk + D - 36);
+    const int p = V0 + kk;
+    const bf16x8 a = rb[p % D];
+    refill(p);
     S = mfma32(a, Q.q[kk], S);
     if ((kk & 3) == 3) copy(kk >> 2);
     if ((kk & 3) == 1 && kk < 12) book(kk >> 2);
     expand(kk);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // value phase: 32 products with the softmax of S woven in
+  // value products V0 .. 31 with the softmax of S woven in
   const int h = lane_id_fresh() >> 5;
   float mx = -INFINITY, sum = 0.f, nm = 0.f;
   bool need = false;
 #pragma unroll
-  for (int n = 0; n < 32; ++n) {
-    const bf16x8 a = rb[n % D];
-    if (n + D < 32) rb[n % D] = value_operand(A, n + D);
+  for (int m = 0; m < 32 - V0; ++m) {
+    const int n = V0 + m, p = 36 + n;
+    const bf16x8 a = rb[p % D];
+    refill(p);
     mfma32_acc(Z.z[n & 15], a, Pp[n >> 4]);
     // each piece of the softmax is pinned to its step (anchor()): its
     // results are used only in the next step, and the compiler would
     // otherwise move the arithmetic out of this sequence
-    if (n == 2) {
+    if (m == 2) {
       if (__builtin_expect(mask, 0)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -549,10 +592,10 @@ __device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const 
       mx = max3f(max3f(max3f(S[0], S[1], S[2]), max3f(S[3], S[4], S[5]), max3f(S[6], S[7], S[8])),
                  max3f(S[9], S[10], S[11]), max3f(max3f(S[12], S[13], S[14]), S[15], -INFINITY));
       anchor(mx);
-    } else if (n == 3) {
+    } else if (m == 3) {
       mx = pair32_maximum(mx) * scale_log2;  // scale > 0: the maximum commutes with it
       anchor(mx);
-    } else if (n == 4) {
+    } else if (m == 4) {
       // the first scores of a piece set the maximum (the accumulators are
       // zero); later ones move it only when it grows by more than 2^8
       const float mnew = __builtin_elementwise_maximum(st.m, mx);
@@ -567,17 +610,17 @@ __device__ __forceinline__ void wide_step(const WideQuery& Q, WideAcc& Z, const 
       anchor(alpha);
       anchor(st.l);
       anchor(st.m);
-    } else if (n == 5) {
+    } else if (m == 5) {
       rescale = __builtin_amdgcn_ballot_w64(need) != 0;
-    } else if (n >= 6 && n < 22) {
-      const int r = n - 6;
-      float p = fast_exp2(fmaf(S[r], scale_log2, nm));
-      anchor(p);
-      sum += p;
+    } else if (m >= 6 && m < 22) {
+      const int r = m - 6;
+      float pr = fast_exp2(fmaf(S[r], scale_log2, nm));
+      anchor(pr);
+      sum += pr;
       anchor(sum);
-      Pc[r >> 3][r & 7] = f2bf(p);
+      Pc[r >> 3][r & 7] = f2bf(pr);
       if (r & 1) asm volatile("" : "+v"(Pc[r >> 3]));
-    } else if (n == 22) {
+    } else if (m == 22) {
       st.l += sum;
       anchor(st.l);
     }
@@ -595,6 +638,7 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   // staging buffers (the copies of block i+2 land in one while block i+1 is
   // expanded from the other).
   constexpr int NB = FP8 ? kWNBuf8 : kWNBuf;
+  constexpr int D = FP8 ? kWDepth8 : kWDepth, V0 = FP8 ? kWLead8 : kWLead;
   constexpr int kBufBytes = NB * kBlockBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufBytes + (FP8 ? 2 * kW8Stage : 0)];
   __shared__ int pfx[kMaxSchedB + 1];
@@ -699,6 +743,11 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
   const uint32_t base = lds_addr(smem);
   WideAddr A = wide_addr(base, base + (NB - 1) * kBlockBytes);
   __syncthreads();  // the zeroed buffer (and fp8: block 0) is visible to every wave
+  bf16x8 rb[D];     // operand reads in flight (wide_step)
+  if constexpr (V0 > 0) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) rb[j] = value_operand(A, j);  // step 0's lead products (zero rows)
+  }
 
   // The block scored in the previous step, whose value product is still to
   // be done: its probabilities, where its piece goes and, if it ended the
@@ -715,6 +764,12 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 
   for (int i = 0;; ++i) {
     const bool cur = cp.valid;  // block i exists (else only block i-1's value product is left)
+    // the page of block i+3 for the copy plan in this step: a scalar load.
+    // bf16: issued before the barrier, so that it arrives under the wait
+    // there (the first product waits for every LDS read and scalar load in
+    // flight); fp8: after it, under the first score reads.
+    int pg = 0;
+    if constexpr (!FP8) pg = page_fetch(ld);
     if constexpr (FP8) {
       // the staged copies of block i+1 (the only ones in flight) and this
       // wave's expansion of block i (LDS stores) are complete
@@ -727,15 +782,14 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     }
     // block i has landed; every wave is done with step i-1.  A bare barrier:
     // the copies are complete by the wait above, every LDS read of step i-1
-    // was consumed by its product, and no ordinary LDS store is in flight, so
-    // no fence (and no wait for the page read in flight) is needed; the empty
-    // asm keeps the compiler from moving LDS reads across it.
+    // was consumed by its product except the lead reads of this step (of
+    // block i-1, whose buffer the copies of this step do not touch), and no
+    // ordinary LDS store is in flight, so no fence (and no wait for the page
+    // read in flight) is needed; the empty asm keeps the compiler from moving
+    // LDS reads across it.
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // the page of block i+3 for the copy plan in this step: a scalar load
-    // whose latency passes under that of the first score reads (the first
-    // product waits for both)
-    const int pg = page_fetch(ld);
+    if constexpr (FP8) pg = page_fetch(ld);
     // multi-token decode: query token t of the sequence sees keys up to
     // L - q_len + t, so the last q_len - 1 - t keys are masked for it
     int hi = cur ? block_hi(cp) : kBlock;
@@ -773,8 +827,9 @@ decode_wide_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     auto expand = [&](int kk) {
       if constexpr (FP8) expand_slice(X, kk, xs, xb);
     };
-    wide_step(Q, Z, A, Pp, Pc, st, a.scale_log2, mask, hi, rescale_c, alpha_c, copy, book, expand);
-    advance_addr<NB>(A, i);
+    auto advance = [&]() { advance_addr<NB>(A, i); };
+    wide_step<D, V0>(Q, Z, A, rb, Pp, Pc, st, a.scale_log2, mask, hi, rescale_c, alpha_c, copy, book, expand,
+                     advance);
     // Everything that does not happen at every block (a moved maximum, the
     // end of a piece, a cursor moving to another piece, the end of the
     // unit's work) behind one branch.
