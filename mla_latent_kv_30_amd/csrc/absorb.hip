@@ -18,15 +18,26 @@ constexpr int kAbsLdsStride = kAbsCols * 2 + 32;        // padded row stride (by
 constexpr int kAbsOutStride = kAbsCols * 2 + 8;         // output staging row stride (bytes)
 static_assert(4 * kAbsRowsPerWave * kAbsOutStride <= kDn * kAbsLdsStride, "output staging fits the W slice's LDS");
 
-// grid: (H * 4 c-quarters, ceil(N / 128)); 4 waves, each 32 query rows x 128 c.
+// One job = (block of 128 query rows, head h), job = row block * H + h;
+// four workgroups per job, one per 128-channel quarter of q~.  4 waves, each
+// 32 query rows x 128 c.
+// Grid: 32 * ceil(H * RB / 8) workgroups in one dimension, RB = ceil(N / 128).
+// Workgroups go to the eight XCDs in turn, so workgroup L takes quarter
+// (L >> 3) & 3 of job (L & 7) + 8 (L >> 5): the four quarters of a job run on
+// one XCD, and its q_c rows come from HBM once into that XCD's L2 instead of
+// once into each of four.  Jobs that run at the same time are neighbouring
+// heads of the same rows, whose q_c and q~ rows are neighbours in memory.
 // Every global load of a workgroup (its W slice, the q_c operand of each
 // wave, and the q_r rows it rotates) is issued before any result is used,
 // so a workgroup costs one memory round trip before its products; the
-// rotation of the 128 rows is shared by the four c-quarter workgroups.
-__global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a) {
+// rotation of the 128 rows is shared by the four quarter workgroups.
+__global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a, int RB) {
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kDn * kAbsLdsStride];  // W[d][c-slice]
-  const int h = blockIdx.x >> 2, cq = blockIdx.x & 3;
-  const int n_blk = blockIdx.y * kAbsRowsPerBlock;
+  const int L = blockIdx.x;
+  const int job = (L & 7) + 8 * (L >> 5), cq = (L >> 3) & 3;
+  if (job >= a.H * RB) return;
+  const int rb = job / a.H, h = job - rb * a.H;
+  const int n_blk = rb * kAbsRowsPerBlock;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5;
   const bf16* __restrict__ w = (const bf16*)a.w_uk + (size_t)h * kDn * kDc + cq * kAbsCols;
@@ -246,8 +257,8 @@ hipError_t launch_absorb(const AbsorbArgs& a, int kind, hipStream_t s) {
   } else if (a.N <= kAbsSmallMaxN) {
     hipLaunchKernelGGL(absorb_small_kernel, dim3(a.H, kDc / kAbsSmallCols), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(absorb_bf16_kernel, dim3(a.H * 4, (a.N + kAbsRowsPerBlock - 1) / kAbsRowsPerBlock),
-                       dim3(256), 0, s, a);
+    const int RB = (a.N + kAbsRowsPerBlock - 1) / kAbsRowsPerBlock;
+    hipLaunchKernelGGL(absorb_bf16_kernel, dim3(32 * ((a.H * RB + 7) / 8)), dim3(256), 0, s, a, RB);
   }
   return hipGetLastError();
 }

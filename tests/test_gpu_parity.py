@@ -291,15 +291,17 @@ def test_upproj_bf16_and_f32():
         assert np.abs(of.cpu().numpy() - ref).max() <= 1e-5
 
 
-@pytest.mark.parametrize("N", [1, 16, 31, 32, 33, 64, 100, 128, 129, 300])
-def test_absorb_and_upproj_row_counts(N):
+@pytest.mark.parametrize("N,H", [(1, 24), (16, 24), (31, 24), (32, 24), (33, 24), (64, 24), (100, 24), (128, 24),
+                                 (129, 24), (300, 24), (300, 5), (129, 3), (40, 1)])
+def test_absorb_and_upproj_row_counts(N, H):
     """mla_absorb_q and mla_upproj_v (bf16) at row counts on both sides of
-    the few-rows kernels' limit (128 rows, in groups of 32) and of their
-    row groups, against the oracle's absorption and RoPE and an fp64
-    product.  Rows and heads are ragged against the tiles (H = 24)."""
-    _note(f"case absorb/upproj N={N}")
-    g = torch.Generator().manual_seed(100 + N)
-    H = 24
+    the few-rows kernels' limit (32 rows) and of the tiled kernels' row
+    blocks, against the oracle's absorption and RoPE and an fp64 product.
+    Rows and heads are ragged against the tiles; with H = 5, 3 and 1 the
+    absorb's (head, row block) jobs are not a whole number of its groups of
+    eight, so some of its workgroups have no job."""
+    _note(f"case absorb/upproj N={N} H={H}")
+    g = torch.Generator().manual_seed(100 + N + 1000 * H)
     q_c = torch.randn(N, H, 128, generator=g).to(torch.bfloat16)
     q_r = torch.randn(N, H, 64, generator=g).to(torch.bfloat16)
     pos = torch.randint(0, 40000, (N,), generator=g, dtype=torch.int32)
