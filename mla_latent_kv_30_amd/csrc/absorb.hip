@@ -6,6 +6,8 @@
 // stored [128 d][512 c] (row block of the up-projection), so the contraction
 // index d is the slow one; a 128 x 128 slice of it is staged in LDS and the
 // gfx950 transposing LDS read hands the matrix cores d-packed operands.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -16,28 +18,31 @@ constexpr int kAbsRowsPerBlock = 4 * kAbsRowsPerWave;   // 128 query tokens per 
 constexpr int kAbsCols = 128;                           // c-slice of W per workgroup
 constexpr int kAbsLdsStride = kAbsCols * 2 + 32;        // padded row stride (bytes): rows 8 banks apart
 constexpr int kAbsOutStride = kAbsCols * 2 + 8;         // output staging row stride (bytes)
-static_assert(4 * kAbsRowsPerWave * kAbsOutStride <= kDn * kAbsLdsStride, "output staging fits the W slice's LDS");
 
-// One job = (block of 128 query rows, head h), job = row block * H + h;
-// four workgroups per job, one per 128-channel quarter of q~.  4 waves, each
-// 32 query rows x 128 c.
-// Grid: 32 * ceil(H * RB / 8) workgroups in one dimension, RB = ceil(N / 128).
+// Many query rows.  A workgroup owns one 128-channel quarter cq of q~ for
+// one head h and a stripe of row blocks (128 query rows each): row blocks
+// s, s + RS, s + 2 RS, ... of RB = ceil(N / 128).  Its W slice (128 d x 128
+// c) is loaded into LDS once and stays there; the q_c operand of the next
+// row block is loaded while the current one is multiplied and stored.
+// 4 waves, each 32 query rows x 128 c per row block.
+// Grid: 32 * ceil(H * RS / 8) workgroups in one dimension; job = s * H + h.
 // Workgroups go to the eight XCDs in turn, so workgroup L takes quarter
 // (L >> 3) & 3 of job (L & 7) + 8 (L >> 5): the four quarters of a job run on
-// one XCD, and its q_c rows come from HBM once into that XCD's L2 instead of
-// once into each of four.  Jobs that run at the same time are neighbouring
-// heads of the same rows, whose q_c and q~ rows are neighbours in memory.
-// Every global load of a workgroup (its W slice, the q_c operand of each
-// wave, and the q_r rows it rotates) is issued before any result is used,
-// so a workgroup costs one memory round trip before its products; the
-// rotation of the 128 rows is shared by the four quarter workgroups.
-__global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a, int RB) {
+// one XCD, and the q_c rows they share come from HBM once into that XCD's
+// L2 instead of once into each of four.  Jobs that run at the same time are
+// neighbouring heads of the same rows, whose q_c and q~ rows are neighbours
+// in memory.  RS is chosen so that there are about two workgroups per CU.
+// The rotation of a row block's 128 rows is shared by the four quarters.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+absorb_bf16_kernel(AbsorbArgs a, int RB, int RS) {
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kDn * kAbsLdsStride];  // W[d][c-slice]
+  // each wave's 32 rows x 128 channels of output (rows 264 bytes apart: a
+  // store instruction's 32 rows land 2 banks apart)
+  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[4 * kAbsRowsPerWave * kAbsOutStride];
   const int L = blockIdx.x;
   const int job = (L & 7) + 8 * (L >> 5), cq = (L >> 3) & 3;
-  if (job >= a.H * RB) return;
-  const int rb = job / a.H, h = job - rb * a.H;
-  const int n_blk = rb * kAbsRowsPerBlock;
+  if (job >= a.H * RS) return;
+  const int stripe = job / a.H, h = job - stripe * a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5;
   const bf16* __restrict__ w = (const bf16*)a.w_uk + (size_t)h * kDn * kDc + cq * kAbsCols;
@@ -48,54 +53,73 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a, int RB) 
     const int idx = tid + 256 * i, d = idx >> 4, ch = idx & 15;
     wv[i] = *(const int4v*)(w + (size_t)d * kDc + ch * 8);
   }
-  // B operand: q_c^T (k = d, n = query row): lane holds row n0 + lane%32, d = 16kk + 8g + j
-  const int n0 = n_blk + wave * kAbsRowsPerWave;
-  const int nrow = n0 + (lane & 31);
-  const bool nok = nrow < a.N;
-  const bf16* __restrict__ qc = (const bf16*)a.q_c + ((size_t)(nok ? nrow : 0) * a.H + h) * kDn;
-  int4v qv[8];
+  // Per row block: the B operand q_c^T (k = d, n = query row; lane holds row
+  // n0 + lane%32, d = 16kk + 8g + j), and this quarter's 32 rows of the
+  // rotation, n_blk + 32cq .. +31, one pair (2m, 2m+1) per item.
+  struct Operands {
+    int4v qv[8];
+    uint32_t rx[4];
+    int rpos[4];
+    double rth[4];
+  };
+  auto load_operands = [&](int rb, Operands& o) {
+    const int nrow = rb * kAbsRowsPerBlock + wave * kAbsRowsPerWave + (lane & 31);
+    const bf16* __restrict__ qc = (const bf16*)a.q_c + ((size_t)(nrow < a.N ? nrow : 0) * a.H + h) * kDn;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) qv[kk] = *(const int4v*)(qc + 16 * kk + 8 * g);
-  // rotation: this workgroup's 32 rows n_blk + 32cq .. +31, one pair (2m, 2m+1) per item
-  uint32_t rx[4];
-  int rpos[4];
-  double rth[4];
+    for (int kk = 0; kk < 8; ++kk) o.qv[kk] = *(const int4v*)(qc + 16 * kk + 8 * g);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int item = tid + 256 * j, n = n_blk + 32 * cq + (item >> 5), m = item & 31;
-    const int nc = n < a.N ? n : 0;
-    rx[j] = *(const uint32_t*)((const bf16*)a.q_r + ((size_t)nc * a.H + h) * kDr + 2 * m);
-    rpos[j] = a.pos[nc];
-    rth[j] = a.rope.theta[m];
-  }
+    for (int j = 0; j < 4; ++j) {
+      const int item = tid + 256 * j, n = rb * kAbsRowsPerBlock + 32 * cq + (item >> 5), m = item & 31;
+      const int nc = n < a.N ? n : 0;
+      o.rx[j] = *(const uint32_t*)((const bf16*)a.q_r + ((size_t)nc * a.H + h) * kDr + 2 * m);
+      o.rpos[j] = a.pos[nc];
+      o.rth[j] = a.rope.theta[m];
+    }
+  };
+  Operands op;
+  load_operands(stripe, op);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int idx = tid + 256 * i, d = idx >> 4, ch = idx & 15;
     *(int4v*)(w_lds + d * kAbsLdsStride + ch * 16) = wv[i];
   }
-  bf16x8 qb[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, nok ? qv[kk] : int4v{0, 0, 0, 0});
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {  // after the barrier: the operands arrived with the W slice
-    const int item = tid + 256 * j, n = n_blk + 32 * cq + (item >> 5), m = item & 31;
-    if (n < a.N) {
-      asm volatile("" : "+v"(rpos[j]));  // converted here, not where it was loaded
-      float c, sn;
-      rope_cs(rpos[j], rth[j], c, sn);
-      const float x0 = __uint_as_float(rx[j] << 16), x1 = __uint_as_float(rx[j] & 0xffff0000u);
-      bf16* out = (bf16*)a.q_abs + ((size_t)n * a.H + h) * kRow + kDc + 2 * m;
-      *(bf16x2*)out = bf16x2{f2bf(x0 * c - x1 * sn), f2bf(x0 * sn + x1 * c)};
-    }
-  }
+  __syncthreads();  // the W slice stays in place for every row block
   // A operand: W^T (m = c, k = d) by transposing reads: 16-lane group G owns
   // columns 16*(G%2) .. +15 of the 32-wide tile and rows d0 + 4*(lane%16 / 4)
-  const bool has_rows = n0 < a.N;
   const int dsub = (lane & 15) >> 2;
   const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  floatx16 acc[4];
-  if (has_rows) {
+  uint8_t* const stage = stage_lds + wave * (kAbsRowsPerWave * kAbsOutStride);
+  for (int rb = stripe; rb < RB; rb += RS) {
+    const int n_blk = rb * kAbsRowsPerBlock;
+    const int n0 = n_blk + wave * kAbsRowsPerWave;
+    const bool nok = n0 + (lane & 31) < a.N;
+    bf16x8 qb[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, nok ? op.qv[kk] : int4v{0, 0, 0, 0});
+    uint32_t rx[4];
+    int rpos[4];
+    double rth[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      rx[j] = op.rx[j];
+      rpos[j] = op.rpos[j];
+      rth[j] = op.rth[j];
+    }
+    // the next row block's operands load under this one's products and stores
+    if (rb + RS < RB) load_operands(rb + RS, op);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int item = tid + 256 * j, n = n_blk + 32 * cq + (item >> 5), m = item & 31;
+      if (n < a.N) {
+        float c, sn;
+        rope_cs(rpos[j], rth[j], c, sn);
+        const float x0 = __uint_as_float(rx[j] << 16), x1 = __uint_as_float(rx[j] & 0xffff0000u);
+        bf16* out = (bf16*)a.q_abs + ((size_t)n * a.H + h) * kRow + kDc + 2 * m;
+        *(bf16x2*)out = bf16x2{f2bf(x0 * c - x1 * sn), f2bf(x0 * sn + x1 * c)};
+      }
+    }
+    if (n0 >= a.N) continue;  // this wave has no rows in the block (uniform per wave)
+    floatx16 acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       acc[mt] = floatx16{};
@@ -109,29 +133,25 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(AbsorbArgs a, int RB) 
         acc[mt] = mfma32(av, qb[kk], acc[mt]);
       }
     }
-  }
-  __syncthreads();  // every wave is done with the W slice: its LDS now stages the outputs
-  if (!has_rows) return;
-  // C layout: column = query row n0 + lane%32, rows c = 32mt + 8(r/4) + 4g + r%4.
-  // The wave's 32 rows x 128 channels go to its own part of the LDS (rows
-  // 264 bytes apart: a store instruction's 32 rows land 2 banks apart), and
-  // leave as 256-byte row slices, 16 bytes per lane and 4 rows per
-  // instruction, instead of 16-byte pieces of 32 rows per instruction.
-  uint8_t* const stage = w_lds + wave * (kAbsRowsPerWave * kAbsOutStride);
+    // C layout: column = query row n0 + lane%32, rows c = 32mt + 8(r/4) + 4g + r%4.
+    // The rows go through the wave's own staging area and leave as 256-byte
+    // row slices, 16 bytes per lane and 4 rows per instruction, instead of
+    // 16-byte pieces of 32 rows per instruction.
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 v = {f2bf(acc[mt][4 * q4]), f2bf(acc[mt][4 * q4 + 1]), f2bf(acc[mt][4 * q4 + 2]),
-                  f2bf(acc[mt][4 * q4 + 3])};
-      *(bf16x4*)(stage + (lane & 31) * kAbsOutStride + (32 * mt + 8 * q4 + 4 * g) * 2) = v;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v = {f2bf(acc[mt][4 * q4]), f2bf(acc[mt][4 * q4 + 1]), f2bf(acc[mt][4 * q4 + 2]),
+                    f2bf(acc[mt][4 * q4 + 3])};
+        *(bf16x4*)(stage + (lane & 31) * kAbsOutStride + (32 * mt + 8 * q4 + 4 * g) * 2) = v;
+      }
+#pragma unroll
+    for (int i = 0; i < kAbsRowsPerWave / 4; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int4v v = *(const int4v*)(stage + r * kAbsOutStride + 16 * (lane & 15));
+      if (n0 + r < a.N)
+        *(int4v*)((bf16*)a.q_abs + ((size_t)(n0 + r) * a.H + h) * kRow + cq * kAbsCols + 8 * (lane & 15)) = v;
     }
-#pragma unroll
-  for (int i = 0; i < kAbsRowsPerWave / 4; ++i) {
-    const int r = 4 * i + (lane >> 4);
-    const int4v v = *(const int4v*)(stage + r * kAbsOutStride + 16 * (lane & 15));
-    if (n0 + r < a.N)
-      *(int4v*)((bf16*)a.q_abs + ((size_t)(n0 + r) * a.H + h) * kRow + cq * kAbsCols + 8 * (lane & 15)) = v;
   }
 }
 
@@ -257,8 +277,14 @@ hipError_t launch_absorb(const AbsorbArgs& a, int kind, hipStream_t s) {
   } else if (a.N <= kAbsSmallMaxN) {
     hipLaunchKernelGGL(absorb_small_kernel, dim3(a.H, kDc / kAbsSmallCols), dim3(256), 0, s, a);
   } else {
+    // row-block stripes: about two workgroups per CU, each stripe at least one row block
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
     const int RB = (a.N + kAbsRowsPerBlock - 1) / kAbsRowsPerBlock;
-    hipLaunchKernelGGL(absorb_bf16_kernel, dim3(32 * ((a.H * RB + 7) / 8)), dim3(256), 0, s, a, RB);
+    const int RS = std::max(1, std::min(RB, (2 * cus + 4 * a.H - 1) / (4 * a.H)));
+    hipLaunchKernelGGL(absorb_bf16_kernel, dim3(32 * ((a.H * RS + 7) / 8)), dim3(256), 0, s, a, RB, RS);
   }
   return hipGetLastError();
 }
