@@ -292,14 +292,15 @@ def test_upproj_bf16_and_f32():
 
 
 @pytest.mark.parametrize("N,H", [(1, 24), (16, 24), (31, 24), (32, 24), (33, 24), (64, 24), (100, 24), (128, 24),
-                                 (129, 24), (300, 24), (300, 5), (129, 3), (40, 1)])
+                                 (129, 24), (300, 24), (300, 5), (129, 3), (40, 1), (300, 128), (1000, 64)])
 def test_absorb_and_upproj_row_counts(N, H):
     """mla_absorb_q and mla_upproj_v (bf16) at row counts on both sides of
     the few-rows kernels' limit (32 rows) and of the tiled kernels' row
     blocks, against the oracle's absorption and RoPE and an fp64 product.
     Rows and heads are ragged against the tiles; with H = 5, 3 and 1 the
-    absorb's (head, row block) jobs are not a whole number of its groups of
-    eight, so some of its workgroups have no job."""
+    absorb's jobs are not a whole number of its groups of eight, so some of
+    its workgroups have no job; with H = 128 and 64 each absorb workgroup
+    walks several row blocks (3 and 4), the last one ragged."""
     _note(f"case absorb/upproj N={N} H={H}")
     g = torch.Generator().manual_seed(100 + N + 1000 * H)
     q_c = torch.randn(N, H, 128, generator=g).to(torch.bfloat16)
