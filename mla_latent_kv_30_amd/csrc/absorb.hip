@@ -279,8 +279,8 @@ hipError_t launch_absorb(const AbsorbArgs& a, int kind, hipStream_t s) {
   } else {
     // row-block stripes: about two workgroups per CU, each stripe at least one row block
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
     const int RB = (a.N + kAbsRowsPerBlock - 1) / kAbsRowsPerBlock;
     const int RS = std::max(1, std::min(RB, (2 * cus + 4 * a.H - 1) / (4 * a.H)));
