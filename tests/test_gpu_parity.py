@@ -684,8 +684,9 @@ def test_bf16_prefill_matches_oracle(H, T):
     assert np.abs(pool[slot, 512:] - ref["k_r_rot"]).max() <= 2 ** -8 * np.abs(ref["k_r_rot"]).max()
 
 
-def test_prefill_row_equals_decode_at_length_t_plus_1():
-    wl = W.make_workload("prefill_h128", H=16, lens=[150])
+@pytest.mark.parametrize("H", [16, 128])
+def test_prefill_row_equals_decode_at_length_t_plus_1(H):
+    wl = W.make_workload("prefill_h128", H=H, lens=[150])
     dt = torch.bfloat16
     w_uk, _ = W.weights(wl)
     q_c, q_r = W.queries(wl)
@@ -703,8 +704,12 @@ def test_prefill_row_equals_decode_at_length_t_plus_1():
     assert _rel(zd.cpu().numpy(), zp[rows].cpu().numpy()) <= 1e-3
 
 
-def test_fp8_prefill_matches_oracle():
-    T, H = 150, 16
+@pytest.mark.parametrize("H", [16, 128])
+def test_fp8_prefill_matches_oracle(H):
+    """fp8 cache in prefill mode: the eight-wave kernel (16 heads) and the
+    four-wave kernel (128 heads, staged expansion without the non-temporal
+    hint)."""
+    T = 150
     wl = W.make_workload("prefill_h128", H=H, lens=[T])
     _note(f"case fp8 prefill H={H} T={T}")
     dt = torch.bfloat16
