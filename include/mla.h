@@ -305,9 +305,9 @@ mla_status mla_decode_multi(const void* q_abs, const mla_cache* cache, const int
 /*
  * mla_decode_multi_upproj: mla_decode_multi followed by the value
  * up-projection o = W_i^UV z (§潜在向量的作用) of every query token's heads:
- * o [B][q_len][H][128] in o_dtype.  With a bf16 weight and B <= 32 the
- * split merge and the up-projection run as one launch (as in
- * mla_decode_merge_upproj; z stays fp32 in that product), otherwise as
+ * o [B][q_len][H][128] in o_dtype.  With a bf16 weight, B <= 32 and
+ * q_len*H <= 64 the split merge and the up-projection run as one launch (as
+ * in mla_decode_merge_upproj; z stays fp32 in that product), otherwise as
  * the merge and mla_upproj_v with N = B*q_len.  z and lse are written as
  * mla_decode_multi writes them.  Errors: those of mla_decode_multi, plus
  * MLA_ERR_INVALID_ARG for a NULL w_uv or o, or a dtype outside
@@ -323,9 +323,10 @@ mla_status mla_decode_multi_upproj(const void* q_abs, const mla_cache* cache, co
  * mla_decode_merge_upproj: mla_decode_merge followed by mla_upproj_v on its z
  * (o_i = W_i^UV z_i, §潜在向量的作用), with N = B.  Arguments as for those
  * two calls; z and lse are written as mla_decode_merge writes them.  With a
- * bf16 weight and B <= 32 both run in one launch, whose product keeps z in
- * fp32 (bf16 weight values, fp32 accumulation); otherwise it is the two
- * calls.  Errors: those of mla_decode_merge, plus MLA_ERR_INVALID_ARG for a
+ * bf16 weight, B <= 32 and H <= 64 both run in one launch, whose product
+ * keeps z in fp32 (bf16 weight values, fp32 accumulation); otherwise it is
+ * the two calls (each of that launch's workgroups reads a head's whole
+ * W^UV, which costs more than it saves with many heads).  Errors: those of mla_decode_merge, plus MLA_ERR_INVALID_ARG for a
  * NULL w_uv or o, or a dtype outside {MLA_F32, MLA_BF16}.
  */
 mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits,

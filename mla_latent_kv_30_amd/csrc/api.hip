@@ -336,6 +336,19 @@ mla_status mla_decode_merge(const int32_t* seq_lens, int32_t B, int32_t H, int32
   return launched(launch_merge(a, (hipStream_t)stream));
 }
 
+namespace {
+
+// The merge and the up-projection in one launch (merge_upproj_kernel) for a
+// bf16 W^UV and few sequences.  Each of its (sequence, head) workgroups
+// reads the head's 128 KB of W^UV, so with many heads the separate merge and
+// tiled up-projection are faster: 8 sequences of 128 heads, 22.0 us in one
+// launch against 19.5 us in two.
+bool merge_upproj_fused(int B, int heads, int32_t w_dtype) {
+  return w_dtype == MLA_BF16 && B <= kFusedMaxB && heads <= 64;
+}
+
+}  // namespace
+
 mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H, int32_t num_splits, void* workspace,
                                    size_t ws_bytes, float* z, float* lse, const void* w_uv, int32_t w_dtype, void* o,
                                    int32_t o_dtype, void* stream) {
@@ -349,7 +362,7 @@ mla_status mla_decode_merge_upproj(const int32_t* seq_lens, int32_t B, int32_t H
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  if (w_dtype == MLA_BF16 && B <= kFusedMaxB) {
+  if (merge_upproj_fused(B, H, w_dtype)) {
     MergeUpArgs m;
     memset(&m, 0, sizeof(m));
     m.d.B = B;
@@ -536,7 +549,7 @@ mla_status mla_decode_multi_upproj(const void* q_abs, const mla_cache* cache, co
   (void)hipGetLastError();
   st = launched(launch_decode(a, kind, s));
   if (st != MLA_OK) return st;
-  if (w_dtype == MLA_BF16 && B <= kFusedMaxB) {
+  if (merge_upproj_fused(B, q_len * H, w_dtype)) {
     MergeUpArgs m;
     memset(&m, 0, sizeof(m));
     m.d = a;

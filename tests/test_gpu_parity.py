@@ -354,11 +354,15 @@ def test_merge_upproj_matches_oracle_and_separate_calls(H, lens, S):
     o2n, o1n = o2.cpu().numpy(), o1.cpu().numpy()
     assert _rel(o2n, ref["o"]) <= 2e-2
     assert _rel(o2b.float().cpu().numpy(), ref["o"]) <= 2e-2
-    # the fused product keeps z in fp32; the matrix-core one rounds it to bf16
-    assert _rel(o2n, o1n) <= 1e-2
-    zz = z2.double().cpu().numpy()
-    o_exact = np.einsum("hdc,bhc->bhd", dd.host["w_uv"], zz)
-    assert np.abs(o2n - o_exact).max() <= 1e-4 * max(1.0, np.abs(o_exact).max())
+    if H <= 64:
+        # the fused product keeps z in fp32; the matrix-core one rounds it to bf16
+        assert _rel(o2n, o1n) <= 1e-2
+        zz = z2.double().cpu().numpy()
+        o_exact = np.einsum("hdc,bhc->bhd", dd.host["w_uv"], zz)
+        assert np.abs(o2n - o_exact).max() <= 1e-4 * max(1.0, np.abs(o_exact).max())
+    else:
+        # more than 64 heads: mla_decode_merge_upproj is the two separate calls
+        np.testing.assert_array_equal(o2n, o1n)
 
 
 def test_merge_upproj_many_sequences_and_f32_weights_take_the_two_launch_path():
